@@ -1,0 +1,235 @@
+"""Benchmark: adaptive-tiling block-sparse attention at the Wan 2.1 latent shape.
+
+One step = the whole hot path over one batch already resident in HBM:
+  select tiling (cohesion of q under (1,8,8) and (4,4,4)) -> permute q, k, v
+  -> min/max block scores -> top-k (81 of 480, + sink + diagonal)
+  -> block-sparse attention -> inverse permute of the output.
+Workload: B=1, H=40, grid 20x32x48 (S=30720), D=128, bf16, seeded synthetic
+inputs (the Fourier-feature q/k recipe, v ~ N(0, 1)).
+
+Prints ONE JSON line.  `value` is kept-block attention FLOPs per step
+(4 * 64 * 64 * 128 per kept block, from the step's own kv_cnt) divided by the
+whole step time.  `roofline` reports the attention kernel alone, timed with
+HIP events on its stream.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TILES = [(1, 8, 8), (4, 4, 4)]
+DROPPED_TILES = [(16, 2, 2)]  # 16 does not divide T=20
+FRAC = 0.17
+CFG = 4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_wan_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_permute_amd", "csrc", "attention.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attention_source_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attention_source_sha256_16") != attention_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, wl, block, kk, budget_s=12.0):
+    """Time the oracle on head 0: its own tiling choice, scores, top-k, then the
+    dense-definition attention rows of consecutive query blocks (512 rows per
+    call) until about `budget_s` seconds of attention work are done."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from block_sparse_attention_permute_amd import synth
+    from oracle import attention as OA
+    from oracle import blocks as OB
+    from oracle import tiling as OT
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    qf, kf, vf = (synth.stored_to_f64(x[0, 0]) for x in (q, k, v))
+    choice, _ = OT.select_tiling(qf[None, None], wl.grid, TILES)
+    perm = OT.tile_permutation(wl.grid, TILES[int(choice[0, 0])])
+    qp, kp, vp = (OT.permute_tokens(x, perm) for x in (qf, kf, vf))
+    keep = OB.topk_block_mask(OB.minmax_block_scores(qp, kp, block), kk, 1, True)
+    t_pre = time.perf_counter() - t0
+    scale = wl.D ** -0.5
+    nb = wl.S // block
+    done, t_attn, per_call = 0, 0.0, 8
+    while done < nb and t_attn < budget_s:
+        rows = np.arange(done * block, min(nb, done + per_call) * block)
+        t1 = time.perf_counter()
+        OA.block_sparse_rows(qp, kp, vp, keep, block, rows, scale)
+        t_attn += time.perf_counter() - t1
+        done = min(nb, done + per_call)
+    flops = int(keep[:done].sum()) * 4 * block * block * wl.D
+    return {
+        "value": flops / (t_pre * done / nb + t_attn) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"head 0 of the same inputs: tiling choice, scores and top-k for the head "
+                   f"({t_pre:.1f} s, prorated to the sample), then the float64 dense-definition attention "
+                   f"rows of query blocks 0..{done - 1} ({done * block} rows, {t_attn:.1f} s); kept-block "
+                   f"FLOPs of those rows / time"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path shards by heads with no communication, so a multi-GPU figure is the per-GPU "
+              "figure at H/N heads and is not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_permute_amd import bsa, synth
+
+    wl = synth.WORKLOADS[CFG]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating inputs: {wl.name}")
+    q, k, v = synth.qkv(CFG)
+    qg, kg, vg = (synth.to_torch(x, dev) for x in (q, k, v))
+    pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, TILES, FRAC, qg.dtype, dev)
+    out = torch.empty_like(qg)
+    block = pipe.block
+
+    ev = []
+
+    def hook(start):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        ev.append(e)
+
+    for _ in range(args.warmup):
+        pipe(qg, kg, vg, out=out)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    kept_blocks = []
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        pipe(qg, kg, vg, out=out, attention_hook=hook)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    attn_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
+    attn_ms_avg = float(np.mean(attn_ms))
+    kv_cnt = pipe.kv[1]
+    kept = int(kv_cnt.sum().item())
+    flops = kept * 4 * block * block * wl.D
+    log(f"step {ms_step:.3f} ms, attention {attn_ms_avg:.3f} ms, kept blocks {kept}")
+
+    # per-stage breakdown (separate, untimed pass)
+    stages = {}
+    marks = []
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        marks.append((name, e))
+
+    for _ in range(3):
+        marks.clear()
+        mark("start")
+        choice, _, _ = bsa.bsa_select_tiling(qg, wl.grid, TILES, workspace=pipe.ws_select)
+        mark("select_tiling")
+        for src, dst in ((qg, pipe.qp), (kg, pipe.kp), (vg, pipe.vp)):
+            bsa.bsa_tile_permute(src, wl.grid, TILES, head_choice=choice, out=dst)
+        mark("tile_permute_qkv")
+        scores, _ = bsa.bsa_minmax_block_scores(pipe.qp, pipe.kp, block, out=pipe.ws_scores)
+        mark("minmax_block_scores")
+        kv_idx, kv_cnt2 = bsa.bsa_topk_block_mask(scores, pipe.k, 1, True, max_kept=pipe.max_kept,
+                                                  out=pipe.ws_topk)[:2]
+        mark("topk_block_mask")
+        bsa.bsa_block_sparse_attention(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt2, block, out=pipe.op)
+        mark("block_sparse_attention")
+        bsa.bsa_invert_permute(pipe.op, wl.grid, TILES, head_choice=choice, out=out)
+        mark("invert_permute")
+        torch.cuda.synchronize()
+        for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
+            stages.setdefault(name, []).append(a.elapsed_time(b))
+    stage_ms = {n: round(float(np.median(t)), 4) for n, t in stages.items()}
+
+    achieved = flops / (attn_ms_avg * 1e-3) / 1e12
+    result = {
+        "metric": "block-sparse attn effective TFLOP/s + ms/call at Wan2.1 shape, % bf16 MFMA peak",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "adaptive-tiling block-sparse attention, Wan 2.1 latent shape",
+            "B": 1, "H": wl.H, "grid": list(wl.grid), "S": wl.S, "D": wl.D, "block": block,
+            "tiles": [list(t) for t in TILES], "tiles_dropped_not_dividing": [list(t) for t in DROPPED_TILES],
+            "budget_frac": FRAC, "k": pipe.k, "sink_blocks": 1, "diagonal": True,
+            "kept_blocks_per_step": kept, "kept_fraction": round(kept / (wl.H * pipe.nb * pipe.nb), 4),
+        },
+        "attention": {
+            "ms_per_call": round(attn_ms_avg, 4),
+            "tflops": round(achieved, 2),
+            "frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "kernel": "attn_mfma_kernel<128, 64, block list>",
+        },
+        "stage_ms": stage_ms,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic(),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(q, k, v, wl, block, pipe.k)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

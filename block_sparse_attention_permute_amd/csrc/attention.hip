@@ -1,0 +1,545 @@
+// Block-sparse and sliding-window attention: bsa_block_sparse_attention and
+// bsa_windowed_attention.
+//
+// Both compute dense scaled dot-product attention under an additive 0/-inf
+// mask while visiting only the key blocks the mask keeps:
+//  * block-sparse: query block I attends to the key blocks of its compact
+//    list ([Adaptive tiling (SPADE), "Recipe": the block mask expanded to
+//    tokens; "Dense by design": skipping masked blocks is where the speed
+//    comes from]);
+//  * windowed: query i attends to keys with abs(i - j) <= window/2 and to the
+//    sinks j < sink, and a query block reads only the key tiles of its local
+//    slice and the sink tiles ([FastVideo windowed_attention.py, "Window
+//    policy" and "Implementation note (FLOPs)"]).
+//
+// MFMA path (bf16, D in {64, 128}, block in {32, 64}), one workgroup per
+// query block, (BLK/32) x (BLK/32) waves:
+//  * wave (wr, wk) owns query rows 32*wr..+32 and key columns 32*wk..+32 of
+//    every key block, so all waves share each K/V tile staged in LDS;
+//  * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
+//    (A = K from LDS, B = Q held in registers for the whole kernel): each lane
+//    then holds 16 scores of ONE query row, which is exactly the B-operand
+//    layout of O^T = V^T P^T, so P never leaves registers;
+//  * V is written to LDS transposed (d-major) while staging, so the V^T
+//    operand is two 8-byte LDS reads per MFMA;
+//  * online softmax in fp32 with exp2 (log2 e folded into the scale) and a
+//    lazy rescale: the running max is only moved when a row's max grows by
+//    more than 2^8, which skips almost every O rescale;
+//  * K/V tiles are double-buffered (global loads for tile n+1 are in flight
+//    while tile n is multiplied), one barrier per tile;
+//  * the key halves of a block are merged through LDS at the end;
+//  * workgroups are remapped so consecutive query blocks of a head run on
+//    the same XCD and share its L2 (neighbouring query blocks keep many of
+//    the same key blocks).
+// A scalar fp32 kernel covers fp32 inputs and the other shapes.
+#include "common.h"
+
+namespace bsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kRescaleSlack = 8.0f;  // log2 units: P may grow to 2^8 before a rescale
+
+enum Mode { kBlockList = 0, kWindow = 1 };
+
+struct AttnParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* out;
+    uint32_t S, nq;        // sequence length, query blocks per head
+    uint32_t n_wg;         // workgroups in the grid
+    uint32_t xcd_remap;    // 1: spread heads over XCDs in contiguous ranges
+    float scale_log2;      // softmax scale * log2(e)
+    // block list
+    const int32_t* kv_idx;
+    const int32_t* kv_cnt;
+    uint32_t max_kept;
+    // window
+    int32_t half, sink;
+};
+
+template <int D, int BLK>
+struct Cfg {
+    static constexpr int NWR = BLK / 32, NWK = BLK / 32, NW = NWR * NWK, NT = 64 * NW;
+    static constexpr int KS = D + 8;    // K row stride in LDS (bf16), 16-byte pad
+    static constexpr int VS = BLK + 4;  // V^T row stride in LDS (bf16), 8-byte pad
+    static constexpr int K_BYTES = BLK * KS * 2;
+    static constexpr int V_BYTES = D * VS * 2;
+    static constexpr int STAGE = K_BYTES + V_BYTES;
+    static constexpr int CK = BLK * D / 8 / NT;         // 16-byte K chunks per thread
+    static constexpr int CV = (BLK / 2) * (D / 8) / NT; // V key-pair chunks per thread
+    static constexpr int MERGE = (NW - NWR) * 64 * (D / 2 + 2) * 4;
+    static constexpr int SMEM = (2 * STAGE > MERGE) ? 2 * STAGE : MERGE;
+    static_assert(CK >= 1 && CV >= 1, "tile too small for the workgroup");
+    static_assert(BLK * D / 8 % NT == 0 && (BLK / 2) * (D / 8) % NT == 0, "uneven staging");
+};
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Registers holding one K/V tile on its way from global memory to LDS.
+template <int D, int BLK>
+struct Staging {
+    u32x4 k[Cfg<D, BLK>::CK];
+    u32x4 v0[Cfg<D, BLK>::CV], v1[Cfg<D, BLK>::CV];
+};
+
+// Load key tile rows [j0, j0 + BLK) of one head (rows >= S read as zero).
+template <int D, int BLK>
+__device__ __forceinline__ void stage_load(Staging<D, BLK>& st, const uint16_t* kh, const uint16_t* vh, int j0,
+                                           uint32_t S, int tid) {
+    using C = Cfg<D, BLK>;
+#pragma unroll
+    for (int j = 0; j < C::CK; ++j) {
+        const int c = tid + C::NT * j;
+        const int row = c / (D / 8), col8 = c % (D / 8);
+        const uint32_t key = j0 + row;
+        st.k[j] = key < S ? ldg16(kh + (size_t)key * D + col8 * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < C::CV; ++j) {
+        const int c = tid + C::NT * j;
+        const int p = c % (BLK / 2), col8 = c / (BLK / 2);
+        const uint32_t key = j0 + 2 * p;
+        st.v0[j] = key < S ? ldg16(vh + (size_t)key * D + col8 * 8) : u32x4{0, 0, 0, 0};
+        st.v1[j] = key + 1 < S ? ldg16(vh + (size_t)(key + 1) * D + col8 * 8) : u32x4{0, 0, 0, 0};
+    }
+}
+
+// Write staged registers to one LDS stage: K row-major, V transposed.
+template <int D, int BLK>
+__device__ __forceinline__ void stage_store(const Staging<D, BLK>& st, char* stage, int tid) {
+    using C = Cfg<D, BLK>;
+    uint16_t* ks = reinterpret_cast<uint16_t*>(stage);
+    uint32_t* vt = reinterpret_cast<uint32_t*>(stage + C::K_BYTES);
+#pragma unroll
+    for (int j = 0; j < C::CK; ++j) {
+        const int c = tid + C::NT * j;
+        const int row = c / (D / 8), col8 = c % (D / 8);
+        *reinterpret_cast<u32x4*>(ks + row * C::KS + col8 * 8) = st.k[j];
+    }
+#pragma unroll
+    for (int j = 0; j < C::CV; ++j) {
+        const int c = tid + C::NT * j;
+        const int p = c % (BLK / 2), col8 = c / (BLK / 2);
+        // Vt[d][2p .. 2p+1] = (V[2p][d], V[2p+1][d]) for d = 8*col8 .. +7
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t a = st.v0[j][w], b = st.v1[j][w];
+            const int d = col8 * 8 + 2 * w;
+            vt[(d * C::VS) / 2 + p] = (a & 0xffffu) | (b << 16);
+            vt[((d + 1) * C::VS) / 2 + p] = (a >> 16) | (b & 0xffff0000u);
+        }
+    }
+}
+
+template <int D, int BLK, int MODE>
+__global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)) void attn_mfma_kernel(const AttnParams P) {
+    using C = Cfg<D, BLK>;
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wr = wave % C::NWR, wk = wave / C::NWR;
+    const int half_id = lane >> 5, col = lane & 31;
+
+    uint32_t wg = blockIdx.x;
+    if (P.xcd_remap) wg = (wg & 7u) * (P.n_wg >> 3) + (wg >> 3);
+    const uint32_t bh = wg / P.nq, I = wg % P.nq;
+    const size_t head = (size_t)bh * P.S * D;
+    const uint16_t* qh = P.q + head;
+    const uint16_t* kh = P.k + head;
+    const uint16_t* vh = P.v + head;
+    const int q0 = (int)I * BLK;
+
+    // ---- key tiles to visit
+    int n_iter;
+    const int32_t* list = nullptr;
+    int n_sink_tiles = 0, local_first = 0;
+    if (MODE == kBlockList) {
+        const size_t row = (size_t)bh * P.nq + I;
+        n_iter = min(P.kv_cnt[row], (int)P.max_kept);
+        list = P.kv_idx + row * P.max_kept;
+    } else {
+        n_sink_tiles = (P.sink + BLK - 1) / BLK;
+        const int lo = max(0, q0 - P.half);
+        const int hi = min((int)P.S, q0 + BLK - 1 + P.half + 1);  // exclusive
+        const int t_lo = lo / BLK, t_hi = (hi - 1) / BLK;
+        local_first = max(t_lo, n_sink_tiles);
+        n_iter = n_sink_tiles + max(0, t_hi - local_first + 1);
+    }
+    auto tile_at = [&](int it) -> int {
+        if (MODE == kBlockList) return list[it];
+        return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
+    };
+
+    // ---- Q fragment (B operand): row q0 + 32*wr + col, D cols 16*s + 8*half_id + 0..7
+    bf16x8 qf[D / 16];
+    {
+        const int qrow = q0 + 32 * wr + col;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            u32x4 raw = qrow < (int)P.S ? ldg16(qh + (size_t)qrow * D + 16 * s + 8 * half_id) : u32x4{0, 0, 0, 0};
+            qf[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[t][v] = 0.f;
+    float m_used = -1e30f, l_part = 0.f;
+    const int my_row = q0 + 32 * wr + col;
+
+    Staging<D, BLK> st;
+    if (n_iter > 0) {
+        stage_load<D, BLK>(st, kh, vh, tile_at(0) * BLK, P.S, tid);
+        stage_store<D, BLK>(st, smem, tid);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < n_iter; ++it) {
+        const bool more = it + 1 < n_iter;
+        if (more) stage_load<D, BLK>(st, kh, vh, tile_at(it + 1) * BLK, P.S, tid);
+        const char* stage = smem + (it & 1) * C::STAGE;
+        const uint16_t* ks = reinterpret_cast<const uint16_t*>(stage);
+        const uint16_t* vt = reinterpret_cast<const uint16_t*>(stage + C::K_BYTES);
+        const int j0 = tile_at(it) * BLK;
+
+        // S^T (32 keys x 32 query rows) = K Q^T over D
+        f32x16 sacc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+        const uint16_t* krow = ks + (32 * wk + col) * C::KS + 8 * half_id;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * s));
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
+        }
+
+        // scores in log2 units; value v of this lane is key 8*(v/4) + 4*half_id + v%4 of the wave's half
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = sacc[v] * P.scale_log2;
+        if (MODE == kWindow) {
+            const int kbase = j0 + 32 * wk + 4 * half_id;
+            const bool full = (j0 + BLK - 1 < P.sink) ||
+                              (q0 + BLK - 1 - j0 <= P.half && j0 + BLK - 1 - q0 <= P.half && j0 + BLK <= (int)P.S);
+            if (!full) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int j = kbase + 8 * (v / 4) + (v % 4);
+                    const int d = my_row - j;
+                    const bool vis = (j < (int)P.S) && ((d <= P.half && -d <= P.half) || j < P.sink);
+                    if (!vis) x[v] = -__builtin_inff();
+                }
+            }
+        }
+        float mloc = x[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, x[v]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const bool grow = mloc > m_used + kRescaleSlack;
+        if (__ballot(grow)) {
+            const float m_new = grow ? mloc : m_used;
+            const float alpha = exp2f(m_used - m_new);
+            m_used = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+        }
+        bf16x8 pb[2];
+        float psum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float p = exp2f(x[v] - m_used);
+            psum += p;
+            pb[v / 8][v % 8] = (__bf16)p;
+        }
+        l_part += psum;
+
+        // O^T (D x 32 rows) += V^T P^T; slot jj of MFMA m is key 16m + 8*(jj/4) + 4*half_id + jj%4
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+            const uint16_t* vrow = vt + (32 * t + col) * C::VS + 32 * wk + 4 * half_id;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * m);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * m + 8);
+                const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), pb[m], o[t], 0, 0, 0);
+            }
+        }
+
+        if (more) stage_store<D, BLK>(st, smem + ((it + 1) & 1) * C::STAGE, tid);
+        __syncthreads();
+    }
+
+    // ---- merge the key halves of each row and write out
+    float l_row = l_part + __shfl_xor(l_part, 32);
+    float* mbuf = reinterpret_cast<float*>(smem);
+    constexpr int REGS = D / 2 + 2;
+    if (wk > 0) {
+        float* dst = mbuf + ((size_t)((wk - 1) * C::NWR + wr) * REGS) * 64 + lane;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dst[(t * 16 + v) * 64] = o[t][v];
+        dst[(D / 2) * 64] = m_used;
+        dst[(D / 2 + 1) * 64] = l_row;
+    }
+    __syncthreads();
+    if (wk > 0) return;
+#pragma unroll
+    for (int w = 1; w < C::NWK; ++w) {
+        const float* src = mbuf + ((size_t)((w - 1) * C::NWR + wr) * REGS) * 64 + lane;
+        const float m2 = src[(D / 2) * 64], l2 = src[(D / 2 + 1) * 64];
+        const float mf = fmaxf(m_used, m2);
+        const float a1 = exp2f(m_used - mf), a2 = exp2f(m2 - mf);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[t][v] = o[t][v] * a1 + src[(t * 16 + v) * 64] * a2;
+        l_row = l_row * a1 + l2 * a2;
+        m_used = mf;
+    }
+    if (my_row >= (int)P.S) return;
+    const float inv = 1.0f / l_row;
+    uint16_t* orow = P.out + head + (size_t)my_row * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            // values 4g .. 4g+3 are d = 32t + 8g + 4*half_id + 0..3
+            uint32_t w0 = f32_to_bf16(o[t][4 * g + 0] * inv) | ((uint32_t)f32_to_bf16(o[t][4 * g + 1] * inv) << 16);
+            uint32_t w1 = f32_to_bf16(o[t][4 * g + 2] * inv) | ((uint32_t)f32_to_bf16(o[t][4 * g + 3] * inv) << 16);
+            *reinterpret_cast<u32x2*>(orow + 32 * t + 8 * g + 4 * half_id) = u32x2{w0, w1};
+        }
+}
+
+// ----------------------------------------------------------------- scalar ---
+// One thread per query row, fp32 math, exact online softmax.  For fp32
+// tensors and shapes the MFMA kernel does not cover.
+
+struct ScalarParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    uint32_t S, BH, block;
+    float scale_log2;
+    const int32_t* kv_idx;
+    const int32_t* kv_cnt;
+    uint32_t max_kept, nq;
+    int32_t half, sink;
+};
+
+template <bool BF16>
+__device__ __forceinline__ float ld(const void* base, size_t i) {
+    if (BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
+    return static_cast<const float*>(base)[i];
+}
+
+template <int D, bool BF16, int MODE>
+__global__ __launch_bounds__(64) void attn_scalar_kernel(const ScalarParams P) {
+    const uint64_t gid = (uint64_t)blockIdx.x * 64 + threadIdx.x;
+    if (gid >= (uint64_t)P.BH * P.S) return;
+    const uint32_t bh = (uint32_t)(gid / P.S), i = (uint32_t)(gid % P.S);
+    const size_t head = (size_t)bh * P.S * D;
+    float qv[D], acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        qv[d] = ld<BF16>(P.q, head + (size_t)i * D + d);
+        acc[d] = 0.f;
+    }
+    float m = -__builtin_inff(), l = 0.f;
+    auto visit = [&](uint32_t j) {
+        float s = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) s = fmaf(qv[d], ld<BF16>(P.k, head + (size_t)j * D + d), s);
+        s *= P.scale_log2;
+        const float mn = fmaxf(m, s);
+        const float a = exp2f(m - mn), p = exp2f(s - mn);
+        l = l * a + p;
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] = fmaf(p, ld<BF16>(P.v, head + (size_t)j * D + d), acc[d] * a);
+        m = mn;
+    };
+    if (MODE == kBlockList) {
+        const size_t row = (size_t)bh * P.nq + i / P.block;
+        const int cnt = min(P.kv_cnt[row], (int)P.max_kept);
+        for (int t = 0; t < cnt; ++t) {
+            const uint32_t J = (uint32_t)P.kv_idx[row * P.max_kept + t];
+            if (J >= P.nq) continue;  // invalid lists are reported by bsa_validate_block_list
+            for (uint32_t j = J * P.block; j < (J + 1) * P.block; ++j) visit(j);
+        }
+    } else {
+        const uint32_t sink = (uint32_t)P.sink;
+        for (uint32_t j = 0; j < sink; ++j) visit(j);
+        const int64_t lo = max((int64_t)sink, (int64_t)i - P.half);
+        const int64_t hi = min((int64_t)P.S - 1, (int64_t)i + P.half);
+        for (int64_t j = lo; j <= hi; ++j) visit((uint32_t)j);
+    }
+    const float inv = 1.0f / l;
+    for (int d = 0; d < D; ++d) {
+        const float r = acc[d] * inv;
+        if (BF16)
+            static_cast<uint16_t*>(P.out)[head + (size_t)i * D + d] = f32_to_bf16(r);
+        else
+            static_cast<float*>(P.out)[head + (size_t)i * D + d] = r;
+    }
+}
+
+template <int MODE>
+int launch_scalar(const ScalarParams& P, int dtype, int64_t D, hipStream_t st, const char* name) {
+    const uint64_t rows = (uint64_t)P.BH * P.S;
+    const unsigned blocks = (unsigned)((rows + 63) / 64);
+    const bool bf = dtype == BSA_BF16;
+#define BSA_SC(DD) \
+    (bf ? attn_scalar_kernel<DD, true, MODE><<<blocks, 64, 0, st>>>(P) : attn_scalar_kernel<DD, false, MODE><<<blocks, 64, 0, st>>>(P))
+    switch (D) {
+        case 16: BSA_SC(16); break;
+        case 32: BSA_SC(32); break;
+        case 64: BSA_SC(64); break;
+        case 128: BSA_SC(128); break;
+        default: BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: D=%lld unsupported (16, 32, 64, 128)", name, (long long)D);
+    }
+#undef BSA_SC
+    return check_launch(name);
+}
+
+template <int D, int BLK, int MODE>
+void launch_mfma(const AttnParams& P, hipStream_t st) {
+    attn_mfma_kernel<D, BLK, MODE><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P);
+}
+
+int common_checks(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B, int64_t H, int64_t S,
+                  int64_t D, const char* name) {
+    BSA_REQUIRE(elem_size(dtype) != 0, "%s: unknown dtype %d", name, dtype);
+    BSA_REQUIRE(q && k && v && out, "%s: NULL tensor", name);
+    BSA_REQUIRE(B >= 1 && H >= 1, "%s: B and H must be >= 1", name);
+    BSA_REQUIRE(S >= 1, "%s: sequence length must be > 0", name);
+    BSA_REQUIRE(D >= 1, "%s: head dim must be > 0", name);
+    BSA_REQUIRE(S < ((int64_t)1 << 30), "%s: S too large", name);
+    BSA_REQUIRE(B * H * S * D < ((int64_t)1 << 40), "%s: tensor too large", name);
+    BSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), "%s: tensors must be 16-byte aligned",
+                name);
+    return BSA_OK;
+}
+
+float resolve_scale_log2(float scale, int64_t D) {
+    const double s = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
+    return (float)(s * 1.4426950408889634);
+}
+
+}  // namespace
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B,
+                                          int64_t H, int64_t S, int64_t D, int block, const int32_t* kv_idx,
+                                          const int32_t* kv_cnt, int max_kept, float scale, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_block_sparse_attention";
+    int rc = common_checks(q, k, v, out, dtype, B, H, S, D, name);
+    if (rc) return rc;
+    BSA_REQUIRE(kv_idx && kv_cnt, "%s: NULL block list", name);
+    BSA_REQUIRE(block >= 1 && S % block == 0, "%s: block %d must divide S=%lld", name, block, (long long)S);
+    BSA_REQUIRE(max_kept >= 1, "%s: max_kept must be >= 1", name);
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t nq = S / block;
+    const float sl2 = resolve_scale_log2(scale, D);
+    const bool mfma = dtype == BSA_BF16 && (D == 64 || D == 128) && (block == 32 || block == 64);
+    if (mfma) {
+        const int64_t nwg = B * H * nq;
+        BSA_REQUIRE(nwg < ((int64_t)1 << 31), "%s: too many blocks", name);
+        AttnParams P{};
+        P.q = static_cast<const uint16_t*>(q);
+        P.k = static_cast<const uint16_t*>(k);
+        P.v = static_cast<const uint16_t*>(v);
+        P.out = static_cast<uint16_t*>(out);
+        P.S = (uint32_t)S;
+        P.nq = (uint32_t)nq;
+        P.n_wg = (uint32_t)nwg;
+        P.xcd_remap = (nwg % 8 == 0) ? 1u : 0u;
+        P.scale_log2 = sl2;
+        P.kv_idx = kv_idx;
+        P.kv_cnt = kv_cnt;
+        P.max_kept = (uint32_t)max_kept;
+        if (D == 128 && block == 64) launch_mfma<128, 64, kBlockList>(P, st);
+        else if (D == 128 && block == 32) launch_mfma<128, 32, kBlockList>(P, st);
+        else if (D == 64 && block == 64) launch_mfma<64, 64, kBlockList>(P, st);
+        else launch_mfma<64, 32, kBlockList>(P, st);
+        return check_launch(name);
+    }
+    ScalarParams P{};
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.out = out;
+    P.S = (uint32_t)S;
+    P.BH = (uint32_t)(B * H);
+    P.block = (uint32_t)block;
+    P.scale_log2 = sl2;
+    P.kv_idx = kv_idx;
+    P.kv_cnt = kv_cnt;
+    P.max_kept = (uint32_t)max_kept;
+    P.nq = (uint32_t)nq;
+    return launch_scalar<kBlockList>(P, dtype, D, st, name);
+}
+
+extern "C" int bsa_windowed_attention(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B,
+                                      int64_t H, int64_t S, int64_t D, int window, int sink, float scale, int chunk,
+                                      bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_windowed_attention";
+    int rc = common_checks(q, k, v, out, dtype, B, H, S, D, name);
+    if (rc) return rc;
+    BSA_REQUIRE(window >= 1, "%s: window must be >= 1, got %d", name, window);
+    BSA_REQUIRE(sink >= 0, "%s: sink must be >= 0, got %d", name, sink);
+    BSA_REQUIRE(sink <= S, "%s: sink (%d) cannot exceed the sequence length (%lld)", name, sink, (long long)S);
+    BSA_REQUIRE(chunk >= 0, "%s: chunk must be >= 1 (or 0 for the default), got %d", name, chunk);
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t half = window / 2;
+    const float sl2 = resolve_scale_log2(scale, D);
+    const bool mfma = dtype == BSA_BF16 && (D == 64 || D == 128);
+    if (mfma) {
+        constexpr int BLK = 64;
+        const int64_t nq = (S + BLK - 1) / BLK;
+        const int64_t nwg = B * H * nq;
+        BSA_REQUIRE(nwg < ((int64_t)1 << 31), "%s: too many blocks", name);
+        AttnParams P{};
+        P.q = static_cast<const uint16_t*>(q);
+        P.k = static_cast<const uint16_t*>(k);
+        P.v = static_cast<const uint16_t*>(v);
+        P.out = static_cast<uint16_t*>(out);
+        P.S = (uint32_t)S;
+        P.nq = (uint32_t)nq;
+        P.n_wg = (uint32_t)nwg;
+        P.xcd_remap = (nwg % 8 == 0) ? 1u : 0u;
+        P.scale_log2 = sl2;
+        P.half = half;
+        P.sink = sink;
+        if (D == 128) launch_mfma<128, BLK, kWindow>(P, st);
+        else launch_mfma<64, BLK, kWindow>(P, st);
+        return check_launch(name);
+    }
+    ScalarParams P{};
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.out = out;
+    P.S = (uint32_t)S;
+    P.BH = (uint32_t)(B * H);
+    P.scale_log2 = sl2;
+    P.half = half;
+    P.sink = sink;
+    return launch_scalar<kWindow>(P, dtype, D, st, name);
+}

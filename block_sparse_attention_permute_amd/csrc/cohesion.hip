@@ -1,0 +1,269 @@
+// Query cohesion per tile and per-head tiling choice: bsa_block_cohesion and
+// bsa_select_tiling.
+//
+// [Adaptive tiling (SPADE), "The idea" step 1]: each candidate tiling is
+// scored per head by the cohesion (SICS) of its tiles, the mean pairwise
+// cosine of the queries inside a tile, and the most cohesive tiling is kept.
+// [Adaptive tiling (SPADE), "Deviations and notes"]: tokens of zero norm are
+// left out and the tiling score is the plain average of the per-tile values.
+//
+// Design: the mean over ordered pairs i != j of cos(q_i, q_j) equals
+// (|sum_i q_i/|q_i||^2 - n) / (n (n - 1)), so a tile costs one pass over its
+// tokens (O(vol * D)) instead of O(vol^2 * D).  One wave owns one tile and
+// reads its tokens straight from the T-major tensor through the tile
+// geometry, so no candidate tiling is ever materialised.  Per-tile values go
+// to a caller-provided buffer and a second small kernel averages them per
+// (b, h, candidate) in double in a fixed order, so results are deterministic.
+#include "common.h"
+
+namespace bsa {
+namespace {
+
+constexpr int kWaves = 4;
+
+struct CohParams {
+    const char* x;
+    int dtype;
+    uint32_t S, Hg, Wg, D;
+    uint32_t vecs_per_row;  // 16-byte vectors per token row
+    uint32_t n_tiles, max_nb;
+    uint32_t nb[BSA_MAX_TILINGS];
+    TileGeo geo[BSA_MAX_TILINGS];
+    float* tile_coh;  // [B*H][n_tiles][max_nb]
+};
+
+template <int EPV>
+__device__ __forceinline__ void load_vec(const char* p, float (&v)[EPV]) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    if (EPV == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) v[i] = __uint_as_float(w[i]);
+    }
+}
+
+// LPT lanes cooperate on one token (16 bytes each); 64/LPT tokens per step.
+template <int EPV, int LPT>
+__global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohParams P) {
+    constexpr int TPI = 64 / LPT;
+    const int lane = threadIdx.x & 63;
+    const uint32_t tile = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const uint32_t cand = blockIdx.y;
+    const uint32_t bh = blockIdx.z;
+    if (tile >= P.nb[cand]) return;
+    const TileGeo& g = P.geo[cand];
+    const uint32_t origin = tile_origin(tile, g, P.Hg, P.Wg);
+    const size_t row_bytes = (size_t)P.vecs_per_row * 16;
+    const char* head = P.x + (size_t)bh * P.S * row_bytes;
+    const int sub = lane % LPT;   // which 16-byte slice of the row
+    const int slot = lane / LPT;  // which token of the step
+
+    float u[EPV];
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) u[i] = 0.f;
+    float n = 0.f;
+    for (uint32_t base = 0; base < g.vol; base += TPI) {
+        const uint32_t cell = base + slot;
+        float v[EPV];
+        float ss = 0.f;
+        if (cell < g.vol) {
+            const uint32_t s = origin + cell_offset(cell, g, P.Hg, P.Wg);
+            load_vec<EPV>(head + (size_t)s * row_bytes + (size_t)sub * 16, v);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) ss = fmaf(v[i], v[i], ss);
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) v[i] = 0.f;
+        }
+#pragma unroll
+        for (int off = LPT / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        if (ss > 0.f) {
+            const float inv = 1.0f / sqrtf(ss);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) u[i] = fmaf(v[i], inv, u[i]);
+            n += 1.f;
+        }
+    }
+    // sum the normalised vectors over token slots (lanes with equal `sub`)
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) u[i] += __shfl_xor(u[i], off);
+        n += __shfl_xor(n, off);
+    }
+    float uu = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) uu = fmaf(u[i], u[i], uu);
+#pragma unroll
+    for (int off = LPT / 2; off >= 1; off >>= 1) uu += __shfl_xor(uu, off);
+    if (lane == 0) {
+        // after the slot reduction n is the number of non-zero tokens
+        const float cnt = n;
+        const float sics = cnt >= 2.f ? (uu - cnt) / (cnt * (cnt - 1.f)) : __builtin_nanf("");
+        P.tile_coh[((size_t)bh * P.n_tiles + cand) * P.max_nb + tile] = sics;
+    }
+}
+
+struct SelParams {
+    const float* tile_coh;
+    uint32_t n_tiles, max_nb;
+    uint32_t nb[BSA_MAX_TILINGS];
+    float* score;
+    int32_t* choice;
+};
+
+// One wave per (b, h): mean over tiles of each candidate, then the argmax.
+__global__ __launch_bounds__(64) void select_kernel(const SelParams P) {
+    const uint32_t bh = blockIdx.x;
+    const int lane = threadIdx.x;
+    double best = 0.0;
+    int best_i = -1;
+    for (uint32_t c = 0; c < P.n_tiles; ++c) {
+        const float* row = P.tile_coh + ((size_t)bh * P.n_tiles + c) * P.max_nb;
+        double sum = 0.0;
+        double cnt = 0.0;
+        for (uint32_t t = lane; t < P.nb[c]; t += 64) {
+            const float v = row[t];
+            if (v == v) {
+                sum += (double)v;
+                cnt += 1.0;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            sum += __shfl_xor(sum, off);
+            cnt += __shfl_xor(cnt, off);
+        }
+        const double mean = cnt > 0.0 ? sum / cnt : -__builtin_inf();
+        if (lane == 0) P.score[(size_t)bh * P.n_tiles + c] = (float)mean;
+        if (best_i < 0 || mean > best) {  // strict: ties keep the lower index
+            best = mean;
+            best_i = (int)c;
+        }
+    }
+    if (lane == 0) P.choice[bh] = best_i;
+}
+
+int launch_tile_cohesion(const CohParams& P, uint32_t BH, hipStream_t stream, const char* name) {
+    dim3 grid((P.max_nb + kWaves - 1) / kWaves, P.n_tiles, BH);
+    const int lpt = (int)P.vecs_per_row;
+#define BSA_COH(EPV, LPT) tile_cohesion_kernel<EPV, LPT><<<grid, 64 * kWaves, 0, stream>>>(P)
+    if (P.dtype == BSA_BF16) {
+        switch (lpt) {
+            case 1: BSA_COH(8, 1); break;
+            case 2: BSA_COH(8, 2); break;
+            case 4: BSA_COH(8, 4); break;
+            case 8: BSA_COH(8, 8); break;
+            case 16: BSA_COH(8, 16); break;
+            case 32: BSA_COH(8, 32); break;
+            default: BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: bf16 D=%u unsupported", name, P.D);
+        }
+    } else {
+        switch (lpt) {
+            case 1: BSA_COH(4, 1); break;
+            case 2: BSA_COH(4, 2); break;
+            case 4: BSA_COH(4, 4); break;
+            case 8: BSA_COH(4, 8); break;
+            case 16: BSA_COH(4, 16); break;
+            case 32: BSA_COH(4, 32); break;
+            default: BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: fp32 D=%u unsupported", name, P.D);
+        }
+    }
+#undef BSA_COH
+    return check_launch(name);
+}
+
+int fill_common(CohParams& P, const void* x, int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                const char* name) {
+    const int es = elem_size(dtype);
+    BSA_REQUIRE(es != 0, "%s: unknown dtype %d", name, dtype);
+    BSA_REQUIRE(x != nullptr, "%s: NULL tensor", name);
+    BSA_REQUIRE(B >= 1 && H >= 1 && S >= 1 && D >= 1, "%s: sizes must be >= 1", name);
+    BSA_REQUIRE(B * H <= 65535, "%s: B*H too large", name);
+    BSA_REQUIRE(S < ((int64_t)1 << 31), "%s: S too large", name);
+    BSA_REQUIRE(aligned16(x), "%s: tensor must be 16-byte aligned", name);
+    const int64_t row_bytes = D * es;
+    BSA_REQUIRE(row_bytes % 16 == 0, "%s: D*elem_size must be a multiple of 16 bytes", name);
+    const int64_t vecs = row_bytes / 16;
+    if (!(vecs == 1 || vecs == 2 || vecs == 4 || vecs == 8 || vecs == 16 || vecs == 32))
+        BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: D=%lld unsupported (row of 16..512 bytes, power of two)", name,
+                 (long long)D);
+    P.x = static_cast<const char*>(x);
+    P.dtype = dtype;
+    P.S = (uint32_t)S;
+    P.D = (uint32_t)D;
+    P.vecs_per_row = (uint32_t)vecs;
+    return BSA_OK;
+}
+
+}  // namespace
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" int bsa_block_cohesion(const void* x, int dtype, int64_t B, int64_t H, int64_t S, int64_t D, int block,
+                                  float* coh, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_block_cohesion";
+    CohParams P;
+    int rc = fill_common(P, x, dtype, B, H, S, D, name);
+    if (rc) return rc;
+    BSA_REQUIRE(coh != nullptr, "%s: NULL output", name);
+    BSA_REQUIRE(block >= 1 && S % block == 0, "%s: block %d must divide S=%lld", name, block, (long long)S);
+    // consecutive runs = tiles (1, 1, block) of a 1 x 1 x S grid
+    P.Hg = 1;
+    P.Wg = (uint32_t)S;
+    P.n_tiles = 1;
+    P.max_nb = (uint32_t)(S / block);
+    for (int i = 0; i < BSA_MAX_TILINGS; ++i) {
+        P.geo[i] = make_geo(1, (int)S, 1, 1, block);
+        P.nb[i] = P.max_nb;
+    }
+    P.tile_coh = coh;
+    return launch_tile_cohesion(P, (uint32_t)(B * H), (hipStream_t)stream, name);
+}
+
+extern "C" int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg, int64_t D,
+                                 const int32_t* tiles_host, int n_tiles, float* tile_coh, float* score,
+                                 int32_t* choice, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_select_tiling";
+    BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
+    const int64_t S = (int64_t)T * Hg * Wg;
+    CohParams P;
+    int rc = fill_common(P, q, dtype, B, H, S, D, name);
+    if (rc) return rc;
+    rc = check_tiles(T, Hg, Wg, tiles_host, n_tiles);
+    if (rc) return rc;
+    BSA_REQUIRE(tile_coh != nullptr && score != nullptr && choice != nullptr, "%s: NULL output", name);
+    P.Hg = (uint32_t)Hg;
+    P.Wg = (uint32_t)Wg;
+    P.n_tiles = (uint32_t)n_tiles;
+    P.max_nb = 0;
+    for (int i = 0; i < BSA_MAX_TILINGS; ++i) {
+        const int j = i < n_tiles ? i : 0;
+        const int a = tiles_host[3 * j], b = tiles_host[3 * j + 1], c = tiles_host[3 * j + 2];
+        P.geo[i] = make_geo(Hg, Wg, a, b, c);
+        P.nb[i] = (uint32_t)(S / ((int64_t)a * b * c));
+        if (i < n_tiles && P.nb[i] > P.max_nb) P.max_nb = P.nb[i];
+    }
+    P.tile_coh = tile_coh;
+    hipStream_t st = (hipStream_t)stream;
+    rc = launch_tile_cohesion(P, (uint32_t)(B * H), st, name);
+    if (rc) return rc;
+    SelParams Q;
+    Q.tile_coh = tile_coh;
+    Q.n_tiles = P.n_tiles;
+    Q.max_nb = P.max_nb;
+    for (int i = 0; i < BSA_MAX_TILINGS; ++i) Q.nb[i] = P.nb[i];
+    Q.score = score;
+    Q.choice = choice;
+    select_kernel<<<(unsigned)(B * H), 64, 0, st>>>(Q);
+    return check_launch(name);
+}

@@ -1,0 +1,149 @@
+// Internal helpers shared by the libbsa sources: status reporting, argument
+// checks, fast integer division and bf16 conversions.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "bsa.h"
+
+namespace bsa {
+
+// ---------------------------------------------------------------- status ---
+
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define BSA_FAIL(code, ...)            \
+    do {                               \
+        ::bsa::set_error(__VA_ARGS__); \
+        return (code);                 \
+    } while (0)
+
+#define BSA_REQUIRE(cond, ...)                                \
+    do {                                                      \
+        if (!(cond)) BSA_FAIL(BSA_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+// Status of the most recent launch on this thread.
+int check_launch(const char* what);
+
+inline int elem_size(int dtype) { return dtype == BSA_BF16 ? 2 : (dtype == BSA_F32 ? 4 : 0); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------ fast division -----
+// Division by a run-time invariant divisor d >= 1 for dividends n < 2^31,
+// by multiply-high and shift (Granlund & Montgomery, "Division by invariant
+// integers using multiplication", 1994).
+struct FastDiv {
+    uint32_t d, magic, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.shift = s;
+    const uint64_t one = 1;
+    f.magic = (uint32_t)(((one << 32) * ((one << s) - d)) / d + 1);
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+    uint32_t t = __umulhi(n, f.magic);
+    return (t + n) >> f.shift;
+}
+
+__device__ __forceinline__ void fdivmod(uint32_t n, const FastDiv& f, uint32_t& q, uint32_t& r) {
+    q = fdiv(n, f);
+    r = n - q * f.d;
+}
+
+// -------------------------------------------------------- conversions -----
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Round to nearest, ties to even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------- tilings -------
+// One candidate tiling (a, b, c) of a T x Hg x Wg grid.  Tiles are numbered
+// T-major over the (T/a) x (Hg/b) x (Wg/c) tile grid and cells T-major inside
+// a tile, so permuted position p = tile * vol + cell.
+struct TileGeo {
+    uint32_t a, b, c, nty, ntx, vol;
+    FastDiv f_vol, f_ntyx, f_ntx, f_bc, f_c, f_a, f_b;
+};
+
+inline TileGeo make_geo(int Hg, int Wg, int a, int b, int c) {
+    TileGeo g;
+    g.a = a;
+    g.b = b;
+    g.c = c;
+    g.nty = Hg / b;
+    g.ntx = Wg / c;
+    g.vol = a * b * c;
+    g.f_vol = make_fastdiv(g.vol);
+    g.f_ntyx = make_fastdiv(g.nty * g.ntx);
+    g.f_ntx = make_fastdiv(g.ntx);
+    g.f_bc = make_fastdiv(b * c);
+    g.f_c = make_fastdiv(c);
+    g.f_a = make_fastdiv(a);
+    g.f_b = make_fastdiv(b);
+    return g;
+}
+
+// Every candidate must divide the grid ([Adaptive tiling (SPADE), "Deviations
+// and notes": divisible grids only]).
+inline int check_tiles(int T, int Hg, int Wg, const int32_t* tiles, int n_tiles) {
+    BSA_REQUIRE(tiles != nullptr, "tiles is NULL");
+    BSA_REQUIRE(n_tiles >= 1 && n_tiles <= BSA_MAX_TILINGS, "n_tiles=%d must be in [1, %d]", n_tiles,
+                BSA_MAX_TILINGS);
+    for (int i = 0; i < n_tiles; ++i) {
+        const int a = tiles[3 * i], b = tiles[3 * i + 1], c = tiles[3 * i + 2];
+        BSA_REQUIRE(a > 0 && b > 0 && c > 0, "tile %d (%d,%d,%d) must be positive", i, a, b, c);
+        BSA_REQUIRE(T % a == 0 && Hg % b == 0 && Wg % c == 0,
+                    "candidate tile %d (%d,%d,%d) does not divide the grid %dx%dx%d", i, a, b, c, T, Hg, Wg);
+    }
+    return BSA_OK;
+}
+
+// T-major index of the first token of tile `tile`.
+__device__ __forceinline__ uint32_t tile_origin(uint32_t tile, const TileGeo& g, uint32_t Hg, uint32_t Wg) {
+    uint32_t tt, rem, ty, tx;
+    fdivmod(tile, g.f_ntyx, tt, rem);
+    fdivmod(rem, g.f_ntx, ty, tx);
+    return ((tt * g.a) * Hg + ty * g.b) * Wg + tx * g.c;
+}
+
+// T-major offset of cell `cell` (T-major inside the tile) from the tile origin.
+__device__ __forceinline__ uint32_t cell_offset(uint32_t cell, const TileGeo& g, uint32_t Hg, uint32_t Wg) {
+    uint32_t rt, rem, ry, rx;
+    fdivmod(cell, g.f_bc, rt, rem);
+    fdivmod(rem, g.f_c, ry, rx);
+    return (rt * Hg + ry) * Wg + rx;
+}
+
+// Permuted position p -> T-major token s.
+__device__ __forceinline__ uint32_t perm_to_tmajor(uint32_t p, const TileGeo& g, uint32_t Hg, uint32_t Wg) {
+    uint32_t tid, r, tt, rem, ty, tx, rt, rem2, ry, rx;
+    fdivmod(p, g.f_vol, tid, r);
+    fdivmod(tid, g.f_ntyx, tt, rem);
+    fdivmod(rem, g.f_ntx, ty, tx);
+    fdivmod(r, g.f_bc, rt, rem2);
+    fdivmod(rem2, g.f_c, ry, rx);
+    return ((tt * g.a + rt) * Hg + ty * g.b + ry) * Wg + tx * g.c + rx;
+}
+
+}  // namespace bsa

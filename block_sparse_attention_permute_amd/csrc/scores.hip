@@ -1,0 +1,244 @@
+// Min/max block summaries and estimated block scores: bsa_minmax_block_scores.
+//
+// [Adaptive tiling (SPADE), "The idea" step 3]: each block of tile-contiguous
+// queries (keys) is summarised by its elementwise maximum and minimum, and
+// the (query block I, key block J) score is estimated as
+//   max((qmax_I + qmin_I) . kmax_J, (qmax_I + qmin_I) . kmin_J).
+//
+// Design: pass 1 is an HBM-bound reduction, one wave per block, that keeps
+// the summaries in the input dtype (a max or min of bf16 values is a bf16
+// value, so they are exact).  Pass 2 is a small fp32 product per head,
+// Nb x Nb outputs over D, tiled 64 x 64 per workgroup through LDS, with the
+// two dot products of a score sharing their query operand.
+#include "common.h"
+
+namespace bsa {
+namespace {
+
+constexpr int kWaves = 4;
+
+struct SumParams {
+    const char* q;
+    const char* k;
+    char* summ;  // 4 x (BH, Nb, D) of the input dtype
+    uint32_t block, nb, vecs_per_row, BH;
+};
+
+template <int EPV>
+__device__ __forceinline__ void unpack(const uint4 raw, float (&v)[EPV]) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    if (EPV == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) v[i] = __uint_as_float(w[i]);
+    }
+}
+
+template <int EPV>
+__device__ __forceinline__ uint4 pack(const float (&v)[EPV]) {
+    uint32_t w[4];
+    if (EPV == 8) {
+        // exact: every value is an input bf16 value widened to fp32
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xffff0000u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// blockIdx: x = group of kWaves blocks, y = 0 (q) / 1 (k), z = b*H + h.
+template <int EPV, int LPT>
+__global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumParams P) {
+    constexpr int TPI = 64 / LPT;
+    const int lane = threadIdx.x & 63;
+    const uint32_t blk = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (blk >= P.nb) return;
+    const uint32_t which = blockIdx.y;
+    const uint32_t bh = blockIdx.z;
+    const size_t row_bytes = (size_t)P.vecs_per_row * 16;
+    const char* src = (which == 0 ? P.q : P.k) + ((size_t)bh * P.nb + blk) * P.block * row_bytes;
+    const int sub = lane % LPT;
+    const int slot = lane / LPT;
+    float mx[EPV], mn[EPV];
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) {
+        mx[i] = -__builtin_inff();
+        mn[i] = __builtin_inff();
+    }
+    for (uint32_t t = slot; t < P.block; t += TPI) {
+        float v[EPV];
+        unpack<EPV>(*reinterpret_cast<const uint4*>(src + (size_t)t * row_bytes + (size_t)sub * 16), v);
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) {
+            mx[i] = fmaxf(mx[i], v[i]);
+            mn[i] = fminf(mn[i], v[i]);
+        }
+    }
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) {
+            mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], off));
+            mn[i] = fminf(mn[i], __shfl_xor(mn[i], off));
+        }
+    }
+    if (slot == 0) {
+        const size_t plane = (size_t)P.BH * P.nb * row_bytes;
+        char* dst = P.summ + (size_t)(2 * which) * plane + ((size_t)bh * P.nb + blk) * row_bytes + (size_t)sub * 16;
+        *reinterpret_cast<uint4*>(dst) = pack<EPV>(mx);
+        *reinterpret_cast<uint4*>(dst + plane) = pack<EPV>(mn);
+    }
+}
+
+constexpr int kTile = 64;  // output tile (I x J)
+constexpr int kDC = 32;    // D chunk staged in LDS
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const char* base, size_t idx) {
+    if (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+    return reinterpret_cast<const float*>(base)[idx];
+}
+
+// S[I, J] = max(c_I . kmax_J, c_I . kmin_J), c = qmax + qmin.
+// blockIdx: x = J tile, y = I tile, z = b*H + h.  Thread (ty, tx) owns
+// I = I0 + ty + 16 r and J = J0 + tx + 16 c for r, c < 4.
+template <bool BF16>
+__global__ __launch_bounds__(256) void block_scores_kernel(const char* __restrict__ summ, uint32_t BH, uint32_t nb,
+                                                           uint32_t D, float* __restrict__ scores) {
+    __shared__ float Cs[kDC][kTile + 1];
+    __shared__ float Xs[kDC][kTile + 1];
+    __shared__ float Ns[kDC][kTile + 1];
+    const uint32_t bh = blockIdx.z;
+    const uint32_t I0 = blockIdx.y * kTile, J0 = blockIdx.x * kTile;
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const size_t plane = (size_t)BH * nb * D;
+    const size_t head = (size_t)bh * nb * D;
+    const char* es = summ;
+    const int esz = BF16 ? 2 : 4;
+    const char* qmax = es;
+    const char* qmin = es + plane * esz;
+    const char* kmax = es + 2 * plane * esz;
+    const char* kmin = es + 3 * plane * esz;
+    float ax[4][4], an[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ax[r][c] = an[r][c] = 0.f;
+
+    for (uint32_t d0 = 0; d0 < D; d0 += kDC) {
+        // stage 64 rows x kDC columns of c, kmax and kmin (column-major in LDS)
+#pragma unroll
+        for (int e = tid; e < kTile * kDC; e += 256) {
+            const int row = e / kDC, col = e % kDC;
+            const uint32_t d = d0 + col;
+            float cv = 0.f, xv = 0.f, nv = 0.f;
+            if (d < D) {
+                if (I0 + row < nb) {
+                    const size_t idx = head + (size_t)(I0 + row) * D + d;
+                    cv = load_elem<BF16>(qmax, idx) + load_elem<BF16>(qmin, idx);
+                }
+                if (J0 + row < nb) {
+                    const size_t idx = head + (size_t)(J0 + row) * D + d;
+                    xv = load_elem<BF16>(kmax, idx);
+                    nv = load_elem<BF16>(kmin, idx);
+                }
+            }
+            Cs[col][row] = cv;
+            Xs[col][row] = xv;
+            Ns[col][row] = nv;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int d = 0; d < kDC; ++d) {
+            float a[4], bx[4], bn[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = Cs[d][ty + 16 * r];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                bx[c] = Xs[d][tx + 16 * c];
+                bn[c] = Ns[d][tx + 16 * c];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    ax[r][c] = fmaf(a[r], bx[c], ax[r][c]);
+                    an[r][c] = fmaf(a[r], bn[c], an[r][c]);
+                }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t I = I0 + ty + 16 * r;
+        if (I >= nb) continue;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t J = J0 + tx + 16 * c;
+            if (J < nb) scores[((size_t)bh * nb + I) * nb + J] = fmaxf(ax[r][c], an[r][c]);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H, int64_t S,
+                                       int64_t D, int block, void* summaries, float* scores, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_minmax_block_scores";
+    const int es = elem_size(dtype);
+    BSA_REQUIRE(es != 0, "%s: unknown dtype %d", name, dtype);
+    BSA_REQUIRE(q && k && summaries && scores, "%s: NULL argument", name);
+    BSA_REQUIRE(B >= 1 && H >= 1 && S >= 1 && D >= 1, "%s: sizes must be >= 1", name);
+    BSA_REQUIRE(B * H <= 65535, "%s: B*H too large", name);
+    BSA_REQUIRE(block >= 1 && S % block == 0, "%s: block %d must divide S=%lld", name, block, (long long)S);
+    BSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(summaries), "%s: tensors must be 16-byte aligned", name);
+    const int64_t row_bytes = D * es;
+    BSA_REQUIRE(row_bytes % 16 == 0, "%s: D*elem_size must be a multiple of 16 bytes", name);
+    const int64_t vecs = row_bytes / 16;
+    const int64_t nb = S / block;
+    BSA_REQUIRE(nb <= 65535 * kTile, "%s: too many blocks", name);
+    BSA_REQUIRE(B * H * nb * D < ((int64_t)1 << 40), "%s: too large", name);
+    SumParams P;
+    P.q = static_cast<const char*>(q);
+    P.k = static_cast<const char*>(k);
+    P.summ = static_cast<char*>(summaries);
+    P.block = (uint32_t)block;
+    P.nb = (uint32_t)nb;
+    P.vecs_per_row = (uint32_t)vecs;
+    P.BH = (uint32_t)(B * H);
+    hipStream_t st = (hipStream_t)stream;
+    dim3 g1((unsigned)((nb + kWaves - 1) / kWaves), 2, (unsigned)(B * H));
+#define BSA_MM(EPV, LPT) block_minmax_kernel<EPV, LPT><<<g1, 64 * kWaves, 0, st>>>(P)
+    const bool bf = dtype == BSA_BF16;
+    switch (vecs) {
+        case 1: if (bf) BSA_MM(8, 1); else BSA_MM(4, 1); break;
+        case 2: if (bf) BSA_MM(8, 2); else BSA_MM(4, 2); break;
+        case 4: if (bf) BSA_MM(8, 4); else BSA_MM(4, 4); break;
+        case 8: if (bf) BSA_MM(8, 8); else BSA_MM(4, 8); break;
+        case 16: if (bf) BSA_MM(8, 16); else BSA_MM(4, 16); break;
+        case 32: if (bf) BSA_MM(8, 32); else BSA_MM(4, 32); break;
+        default: BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: D=%lld unsupported", name, (long long)D);
+    }
+#undef BSA_MM
+    int rc = check_launch(name);
+    if (rc) return rc;
+    const unsigned nt = (unsigned)((nb + kTile - 1) / kTile);
+    dim3 g2(nt, nt, (unsigned)(B * H));
+    if (bf)
+        block_scores_kernel<true><<<g2, 256, 0, st>>>(static_cast<const char*>(summaries), P.BH, P.nb, (uint32_t)D, scores);
+    else
+        block_scores_kernel<false><<<g2, 256, 0, st>>>(static_cast<const char*>(summaries), P.BH, P.nb, (uint32_t)D, scores);
+    return check_launch(name);
+}

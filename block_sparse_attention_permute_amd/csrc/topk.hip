@@ -1,0 +1,145 @@
+// Per-row top-k block selection with sink and diagonal blocks: bsa_topk_block_mask.
+//
+// [Adaptive tiling (SPADE), "The idea" step 4]: a fixed budget of k key blocks
+// is kept per query block, and the sink and diagonal blocks are always kept
+// ([Adaptive tiling (SPADE), "Recipe"]: they are ORed into the top-k mask).
+//
+// Design: one wave per row, the row's scores held in registers (element
+// e = i*64 + lane).  Scores map to order-preserving unsigned keys (-0.0 as
+// +0.0, NaN lowest), the k-th largest key is found by a 32-step bitwise
+// search with wave-wide counts, and ties at the threshold are resolved to
+// the lowest indices with ballots.  The kept set comes out in ascending
+// index order as a compact list (what the attention kernel walks) and,
+// optionally, as a byte mask.  Selection is exact: for the same fp32
+// scores it is bit-identical to a sort by (score desc, index asc).
+#include "common.h"
+
+namespace bsa {
+namespace {
+
+struct TopkParams {
+    const float* scores;
+    int32_t* kv_idx;
+    int32_t* kv_cnt;
+    uint8_t* mask;
+    uint32_t nq, nk, k, sink, keep_diag, max_kept;
+    uint64_t rows;
+};
+
+// Larger score -> larger key.  NaN -> 0, and every number maps above 0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    if (f != f) return 0u;
+    if (f == 0.0f) f = 0.0f;  // -0.0 ranks as +0.0
+    const uint32_t b = __float_as_uint(f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
+
+// VPL = values per lane (the row length is at most 64 * VPL).
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t row = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= P.rows) return;
+    const uint32_t I = (uint32_t)(row % P.nq);
+    const float* s = P.scores + row * P.nk;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    uint32_t key[VPL];
+    bool valid[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const uint32_t e = i * 64 + lane;
+        valid[i] = e < P.nk;
+        key[i] = valid[i] ? order_key(s[e]) : 0u;
+    }
+    // k-th largest key T: the largest T with count(key >= T) >= k
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) c += (valid[i] && key[i] >= cand) ? 1u : 0u;
+        if (wave_sum(c) >= P.k) T = cand;
+    }
+    uint32_t gt = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) gt += (valid[i] && key[i] > T) ? 1u : 0u;
+    const uint32_t need = P.k - wave_sum(gt);  // ties at T to take, lowest index first
+
+    bool keep[VPL];
+    uint32_t tie_seen = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const bool tie = valid[i] && key[i] == T;
+        const uint64_t m = __ballot(tie);
+        const uint32_t rank = tie_seen + popc64(m & lt_mask);
+        tie_seen += popc64(m);
+        const uint32_t e = i * 64 + lane;
+        keep[i] = valid[i] && (key[i] > T || (tie && rank < need) || e < P.sink || (P.keep_diag && e == I));
+    }
+    int32_t* out = P.kv_idx + row * P.max_kept;
+    uint32_t pos = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const uint64_t m = __ballot(keep[i]);
+        const uint32_t at = pos + popc64(m & lt_mask);
+        if (keep[i] && at < P.max_kept) out[at] = (int32_t)(i * 64 + lane);
+        pos += popc64(m);
+        if (P.mask != nullptr && valid[i]) P.mask[row * P.nk + i * 64 + lane] = keep[i] ? 1 : 0;
+    }
+    for (uint32_t j = pos + lane; j < P.max_kept; j += 64) out[j] = -1;
+    if (lane == 0) P.kv_cnt[row] = (int32_t)pos;
+}
+
+}  // namespace
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" int bsa_topk_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int Nk, int k, int sink_blocks,
+                                   int keep_diag, int32_t* kv_idx, int32_t* kv_cnt, int max_kept,
+                                   uint8_t* mask_or_null, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_topk_block_mask";
+    BSA_REQUIRE(scores && kv_idx && kv_cnt, "%s: NULL argument", name);
+    BSA_REQUIRE(B >= 1 && H >= 1 && Nq >= 1, "%s: B, H, Nq must be >= 1", name);
+    BSA_REQUIRE(Nk >= 1 && Nk <= 4096, "%s: Nk=%d must be in [1, 4096]", name, Nk);
+    BSA_REQUIRE(k >= 1 && k <= Nk, "%s: k=%d must be in [1, Nk=%d]", name, k, Nk);
+    BSA_REQUIRE(sink_blocks >= 0, "%s: sink_blocks must be >= 0", name);
+    const int64_t widest = std::min<int64_t>(Nk, (int64_t)k + sink_blocks + (keep_diag ? 1 : 0));
+    BSA_REQUIRE(max_kept >= widest, "%s: max_kept=%d < %lld (k + sink + diagonal, at most Nk)", name, max_kept,
+                (long long)widest);
+    TopkParams P;
+    P.scores = scores;
+    P.kv_idx = kv_idx;
+    P.kv_cnt = kv_cnt;
+    P.mask = mask_or_null;
+    P.nq = (uint32_t)Nq;
+    P.nk = (uint32_t)Nk;
+    P.k = (uint32_t)k;
+    P.sink = (uint32_t)std::min(sink_blocks, Nk);
+    P.keep_diag = keep_diag ? 1u : 0u;
+    P.max_kept = (uint32_t)max_kept;
+    P.rows = (uint64_t)B * H * Nq;
+    const uint64_t blocks = (P.rows + 3) / 4;
+    BSA_REQUIRE(blocks < ((uint64_t)1 << 31), "%s: too many rows", name);
+    hipStream_t st = (hipStream_t)stream;
+    const int vpl = (Nk + 63) / 64;
+    if (vpl <= 8)
+        topk_kernel<8><<<(unsigned)blocks, 256, 0, st>>>(P);
+    else if (vpl <= 16)
+        topk_kernel<16><<<(unsigned)blocks, 256, 0, st>>>(P);
+    else if (vpl <= 32)
+        topk_kernel<32><<<(unsigned)blocks, 256, 0, st>>>(P);
+    else
+        topk_kernel<64><<<(unsigned)blocks, 256, 0, st>>>(P);
+    return check_launch(name);
+}

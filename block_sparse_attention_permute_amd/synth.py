@@ -141,22 +141,33 @@ def head_f64(cfg: int, role: int, head: int) -> np.ndarray:
     return g.standard_normal((S, D))
 
 
-def tensor_bits(cfg: int, role: int, heads=None) -> np.ndarray:
+def tensor_bits(cfg: int, role: int, heads=None, workers: int | None = None) -> np.ndarray:
     """A (1, H', S, D) tensor of one role as stored bits.
 
     bf16 workloads return uint16 bit patterns; workload 1 returns float32.
-    ``heads`` selects a subset of heads (default: all).
+    ``heads`` selects a subset of heads (default: all).  Heads are drawn from
+    independent streams, so they are generated in parallel threads with no
+    effect on the values.
     """
+    import concurrent.futures as cf
+    import os
+
     wl = WORKLOADS[cfg]
     heads = list(range(wl.H)) if heads is None else list(heads)
-    if wl.dtype == "f32":
-        out = np.empty((1, len(heads), wl.S, wl.D), dtype=np.float32)
-        for i, h in enumerate(heads):
-            out[0, i] = round_to_f32(head_f64(cfg, role, h))
-        return out
-    out = np.empty((1, len(heads), wl.S, wl.D), dtype=np.uint16)
-    for i, h in enumerate(heads):
-        out[0, i] = round_to_bf16_bits(head_f64(cfg, role, h))
+    f32 = wl.dtype == "f32"
+    out = np.empty((1, len(heads), wl.S, wl.D), dtype=np.float32 if f32 else np.uint16)
+
+    def one(i):
+        x = head_f64(cfg, role, heads[i])
+        out[0, i] = round_to_f32(x) if f32 else round_to_bf16_bits(x)
+
+    n = workers or min(16, os.cpu_count() or 1, len(heads))
+    if n <= 1:
+        for i in range(len(heads)):
+            one(i)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(one, range(len(heads))))
     return out
 
 

@@ -1,0 +1,226 @@
+/*
+ * bsa.h - block-sparse attention over T-major video token sequences, MI355X (gfx950).
+ *
+ * C ABI of libbsa.so.  Every call takes plain pointers and sizes.
+ *
+ * Conventions shared by all calls
+ * -------------------------------
+ *  Tokens.   A video latent of T x Hg x Wg positions is flattened T-major,
+ *            s = (t*Hg + y)*Wg + x  [ADR-0001 "Sparse-attention roadmap for
+ *            video DiTs", shared conventions: token order].  S = T*Hg*Wg.
+ *  Tensors.  q, k, v and outputs are contiguous row-major (B, H, S, D)
+ *            device arrays of one element type (bsa_dtype), 16-byte aligned
+ *            [FastVideo windowed_attention.py, `_validate_qkv`: q, k, v share
+ *            one (B, H, S, D) shape].
+ *  Memory.   The caller owns every buffer and allocates it on the current
+ *            HIP device; "device" below means a device pointer, "host" a
+ *            host pointer.  The library keeps no pointer after a call
+ *            returns.  Device calls are asynchronous on `stream` (0 = the
+ *            null stream) unless marked synchronous.
+ *  Status.   Every call returns a bsa_status.  Bad arguments give
+ *            BSA_ERR_INVALID_ARG and violated invariants BSA_ERR_INVARIANT,
+ *            mirroring the ValueError / RuntimeError split of [ADR-0001,
+ *            shared conventions: validation].  On any error nothing is
+ *            launched and bsa_last_error() returns a message (thread-local).
+ *            Asynchronous calls check their arguments on the host only; they
+ *            trust device-resident indices, which bsa_validate_block_list /
+ *            bsa_validate_indices check on request.
+ *  Masks.    Additive 0 / -inf semantics [ADR-0001, shared conventions: mask
+ *            format]: a key is either seen with its plain score or not at all.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* bsa_stream_t; /* a hipStream_t */
+
+typedef enum {
+    BSA_OK = 0,
+    BSA_ERR_INVALID_ARG = 1, /* bad shape, size or option (a ValueError in Python) */
+    BSA_ERR_INVARIANT = 2,   /* a checked invariant does not hold (a RuntimeError) */
+    BSA_ERR_UNSUPPORTED = 3, /* valid request this build has no kernel for */
+    BSA_ERR_DEVICE = 4       /* a HIP runtime call or launch failed */
+} bsa_status;
+
+typedef enum {
+    BSA_F32 = 0,  /* IEEE binary32 */
+    BSA_BF16 = 1  /* bfloat16 */
+} bsa_dtype;
+
+#define BSA_MAX_TILINGS 8
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* bsa_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int bsa_version(void);
+
+/* ------------------------------------------------------------------------
+ * Host helpers (no GPU involved)
+ * ------------------------------------------------------------------------ */
+
+/* Tile-contiguous order of a T x Hg x Wg grid under tiles of a x b x c.
+ * [Adaptive tiling (SPADE), "Recipe": the order is the argsort of the tile
+ * labels]; tiles are numbered T-major over the tile grid and tokens keep
+ * T-major order inside a tile.  Writes perm_host[p] = source token of
+ * permuted position p, for p < T*Hg*Wg (host array, caller-owned).
+ * INVALID_ARG if a size is <= 0 or the tile does not divide the grid
+ * [Adaptive tiling (SPADE), "Deviations and notes": divisible grids only]. */
+int bsa_tile_permutation(int T, int Hg, int Wg, int a, int b, int c, int32_t* perm_host);
+
+/* inv[perm[p]] = p for p < S (host arrays).  INVALID_ARG unless perm is a
+ * permutation of 0..S-1.  [Adaptive tiling (SPADE), "Recipe": the inverse
+ * order is the argsort of the order.] */
+int bsa_invert_permutation(const int32_t* perm_host, int64_t S, int32_t* inv_host);
+
+/* Key blocks kept per query block: max(1, floor(frac * n_blocks)), with the
+ * product formed in double precision.  [Adaptive tiling (SPADE), "The idea"
+ * step 4 (a fixed budget, 17% on Wan 2.1, 10% on HunyuanVideo) and "Recipe"
+ * (floored, at least one).]  Returns k >= 1, or -1 if frac is not in (0, 1]
+ * or n_blocks < 1. */
+int bsa_budget(double frac, int n_blocks);
+
+/* Sliding-tile block lists over an nt x nh x nw grid of tiles (tiles
+ * numbered T-major): query tile I keeps key tile J when their tile
+ * coordinates differ by at most (rt, rh, rw) on each axis; neighbours
+ * outside the grid do not exist [ADR-0001, "Décision" step 1,
+ * sliding_tile_block_mask, read as a clipped 3x3x3 neighbourhood for radius
+ * 1].  Writes kv_idx_host[I*max_kept + i] (ascending, -1 padded) and
+ * kv_cnt_host[I].  INVALID_ARG on sizes <= 0, radii < 0, or max_kept smaller
+ * than the largest row. */
+int bsa_sliding_tile_block_list(int nt, int nh, int nw, int rt, int rh, int rw,
+                                int32_t* kv_idx_host, int32_t* kv_cnt_host, int max_kept);
+
+/* ------------------------------------------------------------------------
+ * Device calls
+ * ------------------------------------------------------------------------ */
+
+/* Permute tokens so every tile is contiguous:
+ *   y[b,h,p,:] = x[b,h,perm_c[p],:],  c = head_choice[b*H + h] (0 if NULL),
+ * where perm_c is bsa_tile_permutation of the grid under candidate tile c
+ * [Adaptive tiling (SPADE), "The idea" step 2 and "Recipe"].  tiles_host is
+ * a host array of n_tiles (a, b, c) triples, 1 <= n_tiles <= BSA_MAX_TILINGS,
+ * each dividing the grid.  head_choice: device int32[B*H] or NULL; values
+ * must lie in [0, n_tiles) (trusted; see bsa_validate_indices).
+ * x and y: device (B, H, S, D) of `dtype`, S = T*Hg*Wg, must not overlap.
+ * The index math is done in-kernel; no permutation table is read. */
+int bsa_tile_permute(const void* x, void* y, int dtype, int64_t B, int64_t H,
+                     int T, int Hg, int Wg, int64_t D, const int32_t* tiles_host, int n_tiles,
+                     const int32_t* head_choice, bsa_stream_t stream);
+
+/* Inverse of bsa_tile_permute: x[b,h,perm_c[p],:] = y[b,h,p,:] (back to
+ * T-major order) [Adaptive tiling (SPADE), "Recipe": outputs are taken back
+ * with the inverse order].  Same arguments, with y the input and x the output. */
+int bsa_invert_permute(const void* y, void* x, int dtype, int64_t B, int64_t H,
+                       int T, int Hg, int Wg, int64_t D, const int32_t* tiles_host, int n_tiles,
+                       const int32_t* head_choice, bsa_stream_t stream);
+
+/* Cohesion (SICS) of every run of `block` consecutive tokens:
+ *   coh[b,h,i] = mean over ordered pairs u != w of non-zero-norm tokens of
+ *                cos(x_u, x_w), NaN when the run has fewer than two such tokens.
+ * [Adaptive tiling (SPADE), "The idea" step 1 (mean pairwise cosine of the
+ * queries in a tile) and "Deviations and notes" (zero-norm tokens excluded).]
+ * Computed in fp32 from the normalised sum, (|sum u/|u||^2 - n) / (n(n-1)).
+ * x: device (B, H, S, D); coh: device float[B*H*(S/block)].
+ * INVALID_ARG unless block divides S. */
+int bsa_block_cohesion(const void* x, int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                       int block, float* coh, bsa_stream_t stream);
+
+/* Choose a tiling per (b, h): the candidate whose tiles have the highest mean
+ * cohesion, ties to the lowest candidate index [Adaptive tiling (SPADE), "The
+ * idea" step 1; "Deviations and notes": the average of per-tile mean
+ * cosines, tiles without a pair left out, -inf if no tile has one].
+ * q: device (B, H, S, D), S = T*Hg*Wg.  tiles_host: host (a, b, c) triples.
+ * tile_coh: device float[B*H*n_tiles*maxNb] workspace that receives the
+ * per-tile cohesion (maxNb = max over candidates of S/(a*b*c)); score:
+ * device float[B*H*n_tiles]; choice: device int32[B*H].
+ * INVALID_ARG if a candidate does not divide the grid or n_tiles is out of range. */
+int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
+                      int64_t D, const int32_t* tiles_host, int n_tiles, float* tile_coh,
+                      float* score, int32_t* choice, bsa_stream_t stream);
+
+/* Min/max block summaries and estimated block scores of tile-contiguous q, k:
+ *   qmax_I = elementwise max over block I of q, qmin_I the min (and kmax, kmin),
+ *   scores[b,h,I,J] = max((qmax_I + qmin_I) . kmax_J, (qmax_I + qmin_I) . kmin_J)
+ * [Adaptive tiling (SPADE), "The idea" step 3].  Summaries are exact (each is
+ * an input value); the sum and dot products are fp32.  Inputs must be finite.
+ * q, k: device (B, H, S, D).  summaries: device, 4*B*H*Nb*D elements of
+ * `dtype` in the order qmax, qmin, kmax, kmin, each (B, H, Nb, D); it is
+ * written.  scores: device float (B, H, Nb, Nb).  Nb = S/block.
+ * INVALID_ARG unless block divides S. */
+int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
+                            int64_t S, int64_t D, int block, void* summaries, float* scores,
+                            bsa_stream_t stream);
+
+/* Per-row block selection: keep the k best key blocks of each (b, h, I) row,
+ * ranked by score (higher first) and then by index (lower first), then add
+ * key blocks 0 .. sink_blocks-1 and, if keep_diag, block J = I (when I < Nk)
+ * [Adaptive tiling (SPADE), "The idea" step 4 and "Recipe": top-k budget,
+ * sink and diagonal blocks ORed into the mask].  -0.0 ranks as +0.0 and NaN
+ * below every number.
+ * scores: device float (B, H, Nq, Nk).  kv_idx: device int32
+ * (B, H, Nq, max_kept): kept indices ascending, then -1.  kv_cnt: device int32
+ * (B, H, Nq).  mask_or_null: device uint8 (B, H, Nq, Nk), 1 = kept, or NULL.
+ * INVALID_ARG unless 1 <= k <= Nk, 1 <= Nk <= 4096, sink_blocks >= 0 and
+ * max_kept >= min(Nk, k + sink_blocks + (keep_diag != 0)). */
+int bsa_topk_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int Nk, int k,
+                        int sink_blocks, int keep_diag, int32_t* kv_idx, int32_t* kv_cnt,
+                        int max_kept, uint8_t* mask_or_null, bsa_stream_t stream);
+
+/* Block-sparse attention: for every query block I of `block` tokens,
+ *   out_I = softmax(scale * q_I k_K^T) v_K,  K = the tokens of the key blocks
+ *           kv_idx[b,h,I,0..kv_cnt[b,h,I])
+ * which equals dense attention under the additive mask expanded from the
+ * block mask [Adaptive tiling (SPADE), "Recipe": expand the block mask to
+ * tokens and run dense attention; "Dense by design": a block-sparse kernel
+ * skips the masked blocks instead].  scale NaN means D^-1/2
+ * [FastVideo windowed_attention.py, `_default_scale`].
+ * q, k, v, out: device (B, H, S, D) in the tile-contiguous order the blocks
+ * refer to; out has q's dtype.  kv_idx: device int32 (B, H, S/block,
+ * max_kept), ascending without repeats; kv_cnt: device int32 (B, H, S/block)
+ * in [1, max_kept] (both trusted; see bsa_validate_block_list).
+ * bf16: D in {64, 128} and block in {32, 64} run on MFMA; other bf16 / fp32
+ * shapes with D <= 128 use a scalar kernel.  Accumulation and softmax are
+ * fp32; bf16 outputs are rounded to nearest even once.
+ * INVALID_ARG unless block divides S and max_kept >= 1. */
+int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void* out, int dtype,
+                               int64_t B, int64_t H, int64_t S, int64_t D, int block,
+                               const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
+                               float scale, bsa_stream_t stream);
+
+/* Symmetric sliding-window attention with sinks: query i sees key j when
+ * abs(i - j) <= window/2 (integer division) or j < sink
+ * [FastVideo windowed_attention.py, module docstring "Window policy" and
+ * `windowed_attention`].  The kernel visits only the key tiles of the local
+ * slice and the sinks.  `chunk` is the query chunk of the page's loop; it
+ * does not change the result (0 = the default min(window, 512)).  The policy
+ * is applied at every window size (no unmasked shortcut when window >= S).
+ * q, k, v, out: device (B, H, S, D) in T-major order.  scale NaN means D^-1/2.
+ * INVALID_ARG unless window >= 1, 0 <= sink <= S and chunk >= 0 (argument
+ * checks as on the page). */
+int bsa_windowed_attention(const void* q, const void* k, const void* v, void* out, int dtype,
+                           int64_t B, int64_t H, int64_t S, int64_t D, int window, int sink,
+                           float scale, int chunk, bsa_stream_t stream);
+
+/* Synchronous check of device-resident block lists: every count in
+ * [1, max_kept] and every row ascending, without repeats, inside [0, Nk).
+ * An empty row is the "no visible key" case [FastVideo windowed_attention.py,
+ * `windowed_attention`: RuntimeError for a query block without keys].
+ * Returns BSA_ERR_INVARIANT on the first violation found. */
+int bsa_validate_block_list(const int32_t* kv_idx, const int32_t* kv_cnt, int64_t B, int64_t H,
+                            int Nq, int Nk, int max_kept, bsa_stream_t stream);
+
+/* Synchronous check that every device int32 v[0..n) lies in [lo, hi).
+ * Returns BSA_ERR_INVARIANT otherwise. */
+int bsa_validate_indices(const int32_t* v, int64_t n, int lo, int hi, bsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

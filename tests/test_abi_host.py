@@ -1,0 +1,157 @@
+"""libbsa on the CPU: exported symbols, host helpers against the oracle, and
+argument validation of the device calls (rejected before any launch).
+
+No compute kernel is launched here.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import blocks as OB
+from oracle import tiling as OT
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+bsa = pytest.importorskip("block_sparse_attention_permute_amd.bsa")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bsa.LIB_PATH):
+        pytest.fail("libbsa.so is not built (run __graft_entry__.build())")
+    return bsa.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int)\s+(bsa_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(bsa.EXPORTED) == names
+
+
+def test_version_and_empty_error(L):
+    assert bsa.bsa_version() >> 16 == 1
+    assert isinstance(L.bsa_last_error(), bytes)
+
+
+@pytest.mark.parametrize("grid,tile", [((2, 4, 4), (1, 2, 2)), ((8, 16, 16), (2, 4, 4)), ((20, 32, 48), (1, 8, 8)),
+                                       ((20, 32, 48), (4, 4, 4)), ((32, 48, 80), (4, 4, 4)), ((3, 5, 7), (3, 1, 7)),
+                                       ((1, 1, 9), (1, 1, 1))])
+def test_tile_permutation_bit_exact(L, grid, tile):
+    got = bsa.bsa_tile_permutation(*grid, tile)
+    assert got.dtype == np.int32
+    assert np.array_equal(got, OT.tile_permutation(grid, tile))
+    assert np.array_equal(bsa.bsa_invert_permutation(got), OT.invert_permutation(got))
+
+
+def test_tile_permutation_rejects(L):
+    with pytest.raises(ValueError, match="does not divide"):
+        bsa.bsa_tile_permutation(20, 32, 48, (16, 2, 2))
+    with pytest.raises(ValueError):
+        bsa.bsa_tile_permutation(0, 4, 4, (1, 1, 1))
+    with pytest.raises(ValueError):
+        bsa.bsa_invert_permutation(np.array([0, 2, 2], np.int32))
+    with pytest.raises(ValueError):
+        bsa.bsa_invert_permutation(np.array([0, 3, 1], np.int32))
+
+
+def test_budget_matches_oracle(L):
+    rng = np.random.default_rng(0)
+    cases = [(0.17, 480), (0.10, 1920), (0.01, 10), (1.0, 7), (0.5, 1)]
+    cases += [(float(rng.uniform(1e-4, 1.0)), int(rng.integers(1, 5000))) for _ in range(300)]
+    for frac, n in cases:
+        assert bsa.bsa_budget(frac, n) == OB.budget(frac, n), (frac, n)
+    for bad in (0.0, -1.0, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            bsa.bsa_budget(bad, 10)
+    with pytest.raises(ValueError):
+        bsa.bsa_budget(0.5, 0)
+
+
+@pytest.mark.parametrize("tg,rad", [((4, 4, 4), (1, 1, 1)), ((3, 5, 2), (1, 2, 0)), ((1, 1, 1), (1, 1, 1)),
+                                    ((10, 16, 12), (1, 1, 1))])
+def test_sliding_tile_lists_bit_exact(L, tg, rad):
+    idx, cnt = bsa.bsa_sliding_tile_block_list(tg, rad)
+    keep = OT.sliding_tile_keep(tg, rad)
+    lists, ocnt = OB.keep_to_lists(keep)
+    assert np.array_equal(cnt, ocnt)
+    for i, li in enumerate(lists):
+        assert np.array_equal(idx[i, :cnt[i]], li)
+        assert np.all(idx[i, cnt[i]:] == -1)
+    with pytest.raises(ValueError):
+        bsa.bsa_sliding_tile_block_list(tg, rad, max_kept=int(cnt.max()) - 1)
+
+
+# --- argument validation of device calls: all rejected on the host --------
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every case below fails validation first
+TILES = (ctypes.c_int32 * 6)(1, 8, 8, 4, 4, 4)
+BAD_TILES = (ctypes.c_int32 * 3)(16, 2, 2)
+
+
+def _rc(L, name, *args):
+    rc = getattr(L, name)(*args)
+    return rc, L.bsa_last_error().decode()
+
+
+def test_device_calls_reject_bad_arguments(L):
+    F, BF = bsa.BSA_F32, bsa.BSA_BF16
+    cases = [
+        ("bsa_tile_permute", (FAKE, ctypes.c_void_p(1 << 20), BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, None, None),
+         "does not divide"),
+        ("bsa_tile_permute", (FAKE, ctypes.c_void_p(1 << 20), BF, 1, 40, 20, 32, 48, 128, TILES, 0, None, None),
+         "n_tiles"),
+        ("bsa_tile_permute", (FAKE, FAKE, BF, 1, 1, 8, 8, 8, 8, TILES, 1, None, None), "overlap"),
+        ("bsa_invert_permute", (FAKE, ctypes.c_void_p(1 << 20), 7, 1, 1, 20, 32, 48, 128, TILES, 2, None, None),
+         "dtype"),
+        ("bsa_block_cohesion", (FAKE, BF, 1, 2, 100, 64, 64, FAKE, None), "divide"),
+        ("bsa_select_tiling", (FAKE, BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, FAKE, FAKE, FAKE, None), "divide"),
+        ("bsa_minmax_block_scores", (FAKE, FAKE, BF, 1, 2, 100, 128, 64, FAKE, FAKE, None), "divide"),
+        ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 0, 1, 1, FAKE, FAKE, 83, None, None), "k=0"),
+        ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 481, 1, 1, FAKE, FAKE, 483, None, None), "k=481"),
+        ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 81, 1, 1, FAKE, FAKE, 82, None, None), "max_kept"),
+        ("bsa_topk_block_mask", (FAKE, 1, 1, 4, 5000, 81, 1, 1, FAKE, FAKE, 83, None, None), "Nk"),
+        ("bsa_block_sparse_attention",
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 100, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None), "divide"),
+        ("bsa_block_sparse_attention",
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 0, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None), "> 0"),
+        ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 0, 2, ctypes.c_float(0.25), 8, None),
+         "window"),
+        ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, -1, ctypes.c_float(0.25), 8, None),
+         "sink"),
+        ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, 33, ctypes.c_float(0.25), 8, None),
+         "exceed"),
+        ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, 2, ctypes.c_float(0.25), -1, None),
+         "chunk"),
+        ("bsa_windowed_attention", (None, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, 2, ctypes.c_float(0.25), 8, None),
+         "NULL"),
+        ("bsa_validate_block_list", (FAKE, FAKE, 1, 1, 0, 4, 4, None), ">= 1"),
+        ("bsa_validate_indices", (None, 4, 0, 3, None), "NULL"),
+    ]
+    for name, args, needle in cases:
+        rc, msg = _rc(L, name, *args)
+        assert rc == bsa.BSA_ERR_INVALID_ARG, (name, rc, msg)
+        assert needle in msg, (name, msg)
+
+
+def test_unaligned_tensors_rejected(L):
+    rc, msg = _rc(L, "bsa_windowed_attention", ctypes.c_void_p(4098), FAKE, FAKE, FAKE, bsa.BSA_F32, 1, 1, 32, 16, 8,
+                  2, ctypes.c_float(0.25), 8, None)
+    assert rc == bsa.BSA_ERR_INVALID_ARG and "aligned" in msg
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(bsa, "_lib", None)
+    monkeypatch.setattr(bsa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        bsa.bsa_budget(0.5, 10)

@@ -1,0 +1,158 @@
+"""Cohesion, tiling choice, min/max block scores and top-k against the oracle."""
+import numpy as np
+import pytest
+
+from block_sparse_attention_permute_amd import bsa, synth
+from oracle import blocks as OB
+from oracle import tiling as OT
+from tests.gpu_helpers import TOPK_REL, bits, f64, gpu, torch_gpu
+
+WAN_GRID, WAN_TILES = (20, 32, 48), [(1, 8, 8), (4, 4, 4)]
+
+
+# ------------------------------------------------------------- cohesion ---
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,D,block", [("bf16", 64, 16), ("bf16", 128, 64), ("f32", 16, 8), ("bf16", 8, 5)])
+def test_block_cohesion(dtype, D, block):
+    torch_gpu()
+    S = block * 24
+    x = synth.normal_bits((1, 3, S, D), seed=D + block, dtype=dtype)
+    if dtype == "bf16":
+        x[0, 0, :block] = 0                         # empty block -> NaN
+        x[0, 0, block + 1:2 * block] = 0            # one non-zero token -> NaN
+        x[0, 1, 3 * block:3 * block + 2] = 0        # two zero tokens are left out
+    got = bsa.bsa_block_cohesion(gpu(x), block).cpu().numpy().astype(np.float64)
+    xf = synth.stored_to_f64(x)
+    for h in range(3):
+        want = OT.block_self_similarity(xf[0, h], block)
+        assert np.array_equal(np.isnan(got[0, h]), np.isnan(want))
+        ok = ~np.isnan(want)
+        assert np.max(np.abs(got[0, h][ok] - want[ok])) < 2e-5
+
+
+@pytest.mark.gpu
+def test_select_tiling_wan_shape_against_oracle():
+    """Full Wan 2.1 grid; a sample of heads is checked against the oracle."""
+    torch = torch_gpu()
+    heads = [0, 1, 2, 3, 17, 39]
+    q = synth.tensor_bits(4, synth.ROLE_Q, heads=heads)
+    choice, score, _ = bsa.bsa_select_tiling(gpu(q), WAN_GRID, WAN_TILES)
+    torch.cuda.synchronize()
+    ochoice, oscore = OT.select_tiling(synth.stored_to_f64(q), WAN_GRID, WAN_TILES)
+    s = score.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(s - oscore)) < 1e-5
+    c = choice.cpu().numpy()
+    for h in range(len(heads)):
+        if c[0, h] != ochoice[0, h]:
+            a, b = oscore[0, h, c[0, h]], oscore[0, h, ochoice[0, h]]
+            assert abs(a - b) < TOPK_REL * abs(b), (h, a, b)
+    assert len(set(ochoice[0].tolist())) >= 1
+
+
+@pytest.mark.gpu
+def test_select_tiling_ties_and_constructed_choice():
+    torch = torch_gpu()
+    grid = (2, 4, 4)
+    tiles = [(2, 1, 1), (1, 2, 2), (1, 1, 4), (1, 2, 2)]
+    rng = np.random.default_rng(3)
+    vecs = rng.standard_normal((8, 32))
+    lab = OT.tile_labels(grid, (1, 2, 2))
+    q = np.empty((1, 2, 32, 32))
+    q[0, 0] = vecs[lab]
+    q[0, 1] = vecs[OT.tile_labels(grid, (1, 1, 4))]
+    qb = synth.round_to_bf16_bits(q)
+    choice, score, _ = bsa.bsa_select_tiling(gpu(qb), grid, tiles)
+    c = choice.cpu().numpy()
+    assert c[0, 0] == 1 and c[0, 1] == 2                # exact ties go to the lower index
+    ochoice, oscore = OT.select_tiling(synth.stored_to_f64(qb), grid, tiles)
+    assert np.array_equal(c, ochoice)
+    assert np.max(np.abs(score.cpu().numpy() - oscore)) < 1e-5
+
+
+# ----------------------------------------------------------- block scores ---
+
+def _score_bound(qp, kp, block):
+    """|c| . max(|kmax|, |kmin|) per (I, J): scale of the rounding error of a score."""
+    qmax, qmin = OB.block_minmax(qp, block)
+    kmax, kmin = OB.block_minmax(kp, block)
+    c = np.abs(qmax + qmin)
+    return c @ np.maximum(np.abs(kmax), np.abs(kmin)).T
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,S,D,block", [("bf16", 30720, 128, 64), ("bf16", 2048, 64, 32), ("f32", 96, 16, 8),
+                                             ("bf16", 200, 128, 5)])
+def test_minmax_block_scores(dtype, S, D, block):
+    torch_gpu()
+    H = 2
+    if S == 30720:
+        grid = WAN_GRID
+        q = synth.tensor_bits(4, synth.ROLE_Q, heads=[0, 5])
+        k = synth.tensor_bits(4, synth.ROLE_K, heads=[0, 5])
+        perm = OT.tile_permutation(grid, (4, 4, 4))
+        q, k = q[:, :, perm], k[:, :, perm]
+    else:
+        q = synth.normal_bits((1, H, S, D), seed=11 + S, dtype=dtype)
+        k = synth.normal_bits((1, H, S, D), seed=12 + S, dtype=dtype)
+    scores, summ = bsa.bsa_minmax_block_scores(gpu(q), gpu(k), block)
+    sc = scores.cpu().numpy().astype(np.float64)
+    sm = synth.stored_to_f64(bits(summ))
+    qf, kf = synth.stored_to_f64(q), synth.stored_to_f64(k)
+    for h in range(H):
+        qmax, qmin = OB.block_minmax(qf[0, h], block)
+        kmax, kmin = OB.block_minmax(kf[0, h], block)
+        for got, want in zip(sm[:, 0, h], (qmax, qmin, kmax, kmin)):
+            assert np.array_equal(got, want)                # summaries are exact
+        want = OB.minmax_block_scores(qf[0, h], kf[0, h], block)
+        err = np.abs(sc[0, h] - want)
+        # fp32 dot products of length D: |error| <= (D + 2) u sum|c_d k_d|, u = 2^-24
+        assert np.all(err <= (D + 2) * 2.0 ** -24 * _score_bound(qf[0, h], kf[0, h], block) + 1e-30)
+
+
+# ------------------------------------------------------------------ top-k ---
+
+def _check_topk(scores_np, k, sink, diag, max_kept=None):
+    torch = torch_gpu()
+    s = torch.from_numpy(scores_np.astype(np.float32)).cuda()
+    kv_idx, kv_cnt, mask = bsa.bsa_topk_block_mask(s, k, sink, diag, max_kept=max_kept, return_mask=True)
+    idx, cnt, m = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), mask.cpu().numpy().astype(bool)
+    B, H, Nq, Nk = scores_np.shape
+    for b in range(B):
+        for h in range(H):
+            keep = OB.topk_block_mask(scores_np[b, h].astype(np.float32).astype(np.float64), k, sink, diag)
+            assert np.array_equal(m[b, h], keep), (b, h)
+            for I in range(Nq):
+                li = np.flatnonzero(keep[I])
+                assert cnt[b, h, I] == li.size
+                assert np.array_equal(idx[b, h, I, :li.size], li)
+                assert np.all(idx[b, h, I, li.size:] == -1)
+    return idx, cnt
+
+
+@pytest.mark.gpu
+def test_topk_random_and_tie_heavy_rows():
+    rng = np.random.default_rng(0)
+    _check_topk(rng.standard_normal((1, 3, 37, 100)), 17, 1, True)
+    _check_topk(rng.integers(-3, 4, (2, 2, 20, 70)).astype(np.float64), 9, 1, True)   # many exact ties
+    _check_topk(rng.integers(0, 2, (1, 1, 8, 64)).astype(np.float64), 20, 0, False)
+    _check_topk(rng.standard_normal((1, 2, 16, 16)), 16, 1, True)                    # k = Nk keeps all
+
+
+@pytest.mark.gpu
+def test_topk_special_values():
+    s = np.array([[[[np.nan, -0.0, 0.0, -np.inf, np.inf, 1.0, np.nan, -1.0, 0.0, 2.0]]]])
+    for k in range(1, 11):
+        _check_topk(np.broadcast_to(s, (1, 1, 3, 10)).copy(), k, 0, False)
+        _check_topk(np.broadcast_to(s, (1, 1, 3, 10)).copy(), k, 2, True)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("Nq,Nk,k,sink", [(480, 480, 81, 1), (64, 1920, 192, 1), (8, 4096, 1, 3), (70, 33, 5, 1),
+                                          (33, 70, 70, 0)])
+def test_topk_workload_widths(Nq, Nk, k, sink):
+    rng = np.random.default_rng(Nk)
+    s = rng.standard_normal((1, 2, Nq, Nk)) * 100
+    s[..., ::7] = np.round(s[..., ::7])                      # sprinkle exact ties
+    idx, cnt = _check_topk(s, k, sink, True)
+    assert cnt.min() >= k and cnt.max() <= min(Nk, k + sink + 1)
