@@ -230,12 +230,15 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
             const bool full = (j0 + BLK - 1 < P.sink) ||
                               (q0 + BLK - 1 - j0 <= P.half && j0 + BLK - 1 - q0 <= P.half && j0 + BLK <= (int)P.S);
             if (!full) {
+                // branch-free selects: a short-circuit form of this test was
+                // miscompiled (the store for v = 0 was dropped)
+                const float neg_inf = -__builtin_inff();
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int j = kbase + 8 * (v / 4) + (v % 4);
                     const int d = my_row - j;
-                    const bool vis = (j < (int)P.S) && ((d <= P.half && -d <= P.half) || j < P.sink);
-                    if (!vis) x[v] = -__builtin_inff();
+                    const bool vis = (j < (int)P.S) & (((d <= P.half) & (-d <= P.half)) | (j < P.sink));
+                    x[v] = vis ? x[v] : neg_inf;
                 }
             }
         }
