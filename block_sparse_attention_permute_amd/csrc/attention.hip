@@ -66,79 +66,73 @@ struct AttnParams {
 template <int D, int BLK>
 struct Cfg {
     static constexpr int NWR = BLK / 32, NWK = BLK / 32, NW = NWR * NWK, NT = 64 * NW;
-    static constexpr int KS = D + 8;    // K row stride in LDS (bf16), 16-byte pad
-    static constexpr int VS = BLK + 4;  // V^T row stride in LDS (bf16), 8-byte pad
-    static constexpr int K_BYTES = BLK * KS * 2;
-    static constexpr int V_BYTES = D * VS * 2;
-    static constexpr int STAGE = K_BYTES + V_BYTES;
-    static constexpr int CK = BLK * D / 8 / NT;         // 16-byte K chunks per thread
-    static constexpr int CV = (BLK / 2) * (D / 8) / NT; // V key-pair chunks per thread
+    static constexpr int NCH = D / 8;             // 16-byte chunks per row
+    static constexpr int TILE = BLK * D * 2;      // one K or V tile in LDS (swizzled, unpadded)
+    static constexpr int STAGE = 2 * TILE;        // K then V
+    static constexpr int CH = BLK * NCH / NT;     // 16-byte chunks per thread per tensor
     static constexpr int MERGE = (NW - NWR) * 64 * (D / 2 + 2) * 4;
     static constexpr int SMEM = (2 * STAGE > MERGE) ? 2 * STAGE : MERGE;
-    static_assert(CK >= 1 && CV >= 1, "tile too small for the workgroup");
-    static_assert(BLK * D / 8 % NT == 0 && (BLK / 2) * (D / 8) % NT == 0, "uneven staging");
+    static_assert(CH >= 1 && (BLK * NCH) % NT == 0, "uneven staging");
 };
 
-__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// LDS rows are stored unpadded with their 16-byte chunks XOR-swizzled by an
+// even, row-dependent amount.  This keeps the 128-bit K reads (16 rows, one
+// chunk) and the transposing V reads (4 rows x 2 chunks) free of bank
+// conflicts.
+template <int NCH>
+__device__ __forceinline__ int swz(int row) { return (2 * row) & (NCH - 1); }
+
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+    return row * (D * 2) + ((chunk ^ swz<D / 8>(row)) << 4);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Registers holding one K/V tile on its way from global memory to LDS.
 template <int D, int BLK>
 struct Staging {
-    u32x4 k[Cfg<D, BLK>::CK];
-    u32x4 v0[Cfg<D, BLK>::CV], v1[Cfg<D, BLK>::CV];
+    u32x4 k[Cfg<D, BLK>::CH], v[Cfg<D, BLK>::CH];
 };
 
-// Load key tile rows [j0, j0 + BLK) of one head (rows >= S read as zero).
+// Buffer loads of key rows [j0, j0 + BLK): the tile offset is a scalar, the
+// per-thread offset a loop invariant, and rows past the end read as zero.
 template <int D, int BLK>
-__device__ __forceinline__ void stage_load(Staging<D, BLK>& st, const uint16_t* kh, const uint16_t* vh, int j0,
-                                           uint32_t S, int tid) {
+__device__ __forceinline__ void stage_load(Staging<D, BLK>& st, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                           int j0, int tid) {
     using C = Cfg<D, BLK>;
+    const int soff = j0 * (D * 2);
 #pragma unroll
-    for (int j = 0; j < C::CK; ++j) {
+    for (int j = 0; j < C::CH; ++j) {
         const int c = tid + C::NT * j;
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        const uint32_t key = j0 + row;
-        st.k[j] = key < S ? ldg16(kh + (size_t)key * D + col8 * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < C::CV; ++j) {
-        const int c = tid + C::NT * j;
-        const int p = c % (BLK / 2), col8 = c / (BLK / 2);
-        const uint32_t key = j0 + 2 * p;
-        st.v0[j] = key < S ? ldg16(vh + (size_t)key * D + col8 * 8) : u32x4{0, 0, 0, 0};
-        st.v1[j] = key + 1 < S ? ldg16(vh + (size_t)(key + 1) * D + col8 * 8) : u32x4{0, 0, 0, 0};
+        const int voff = (c / C::NCH) * (D * 2) + (c % C::NCH) * 16;
+        st.k[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, voff, soff, 0);
+        st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, soff, 0);
     }
 }
 
-// Write staged registers to one LDS stage: K row-major, V transposed.
 template <int D, int BLK>
 __device__ __forceinline__ void stage_store(const Staging<D, BLK>& st, char* stage, int tid) {
     using C = Cfg<D, BLK>;
-    uint16_t* ks = reinterpret_cast<uint16_t*>(stage);
-    uint32_t* vt = reinterpret_cast<uint32_t*>(stage + C::K_BYTES);
 #pragma unroll
-    for (int j = 0; j < C::CK; ++j) {
+    for (int j = 0; j < C::CH; ++j) {
         const int c = tid + C::NT * j;
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        *reinterpret_cast<u32x4*>(ks + row * C::KS + col8 * 8) = st.k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < C::CV; ++j) {
-        const int c = tid + C::NT * j;
-        const int p = c % (BLK / 2), col8 = c / (BLK / 2);
-        // Vt[d][2p .. 2p+1] = (V[2p][d], V[2p+1][d]) for d = 8*col8 .. +7
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t a = st.v0[j][w], b = st.v1[j][w];
-            const int d = col8 * 8 + 2 * w;
-            vt[(d * C::VS) / 2 + p] = (a & 0xffffu) | (b << 16);
-            vt[((d + 1) * C::VS) / 2 + p] = (a >> 16) | (b & 0xffff0000u);
-        }
+        const int off = lds_off<D>(c / C::NCH, c % C::NCH);
+        *reinterpret_cast<u32x4*>(stage + off) = st.k[j];
+        *reinterpret_cast<u32x4*>(stage + C::TILE + off) = st.v[j];
     }
 }
 
-template <int D, int BLK, int MODE>
-__global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)) void attn_mfma_kernel(const AttnParams P) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// POS: the softmax scale is positive, so the row max of the raw scores gives
+// the max of the scaled ones and exp2(s * c - m) is one FMA and one exp.
+template <int D, int BLK, int MODE, bool POS>
+__global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)) void attn_mfma_kernel(
+    const AttnParams P) {
     using C = Cfg<D, BLK>;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
     const int tid = threadIdx.x;
@@ -150,9 +144,10 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
     if (P.xcd_remap) wg = (wg & 7u) * (P.n_wg >> 3) + (wg >> 3);
     const uint32_t bh = wg / P.nq, I = wg % P.nq;
     const size_t head = (size_t)bh * P.S * D;
-    const uint16_t* qh = P.q + head;
-    const uint16_t* kh = P.k + head;
-    const uint16_t* vh = P.v + head;
+    const uint32_t head_bytes = P.S * D * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(P.q + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(P.k + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(P.v + head, head_bytes);
     const int q0 = (int)I * BLK;
 
     // ---- key tiles to visit
@@ -171,20 +166,19 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         local_first = max(t_lo, n_sink_tiles);
         n_iter = n_sink_tiles + max(0, t_hi - local_first + 1);
     }
+    // tile index of iteration `it` (wave-uniform: it feeds scalar buffer offsets)
     auto tile_at = [&](int it) -> int {
-        if (MODE == kBlockList) return list[it];
+        if (MODE == kBlockList) return __builtin_amdgcn_readfirstlane(list[it]);
         return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
     };
 
     // ---- Q fragment (B operand): row q0 + 32*wr + col, D cols 16*s + 8*half_id + 0..7
     bf16x8 qf[D / 16];
     {
-        const int qrow = q0 + 32 * wr + col;
+        const int voff = (q0 + 32 * wr + col) * (D * 2) + half_id * 16;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            u32x4 raw = qrow < (int)P.S ? ldg16(qh + (size_t)qrow * D + 16 * s + 8 * half_id) : u32x4{0, 0, 0, 0};
-            qf[s] = __builtin_bit_cast(bf16x8, raw);
-        }
+        for (int s = 0; s < D / 16; ++s)
+            qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, voff + 32 * s, 0, 0));
     }
 
     f32x16 o[D / 32];
@@ -194,38 +188,50 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         for (int v = 0; v < 16; ++v) o[t][v] = 0.f;
     float m_used = -1e30f, l_part = 0.f;
     const int my_row = q0 + 32 * wr + col;
+    const float c_scale = POS ? P.scale_log2 : 1.0f;
+
+    // loop-invariant LDS byte offsets of this lane's operands
+    int k_off[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) k_off[s] = lds_off<D>(32 * wk + col, 2 * s + half_id);
+    // transposing V reads: lane (g = lane/16, r = lane%16) addresses key
+    // 32*wk + 16*m + 8*part + 4*(g/2) + r/4, column 32*t + 16*(g%2) + 4*(r%4)
+    const int g16 = lane >> 4, r16 = lane & 15;
+    const int v_key0 = 32 * wk + 4 * (g16 >> 1) + (r16 >> 2);
+    const int v_col0 = 16 * (g16 & 1) + 4 * (r16 & 3);
 
     Staging<D, BLK> st;
     if (n_iter > 0) {
-        stage_load<D, BLK>(st, kh, vh, tile_at(0) * BLK, P.S, tid);
+        stage_load<D, BLK>(st, kr, vr, tile_at(0) * BLK, tid);
         stage_store<D, BLK>(st, smem, tid);
     }
+    // Drain every load (the Q fragment included) before the loop, so that the
+    // loop's only outstanding loads are the next tile's: otherwise the
+    // compiler's wait tracking makes each tile's QK^T wait for the prefetch.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int it = 0; it < n_iter; ++it) {
         const bool more = it + 1 < n_iter;
-        if (more) stage_load<D, BLK>(st, kh, vh, tile_at(it + 1) * BLK, P.S, tid);
+        if (more) stage_load<D, BLK>(st, kr, vr, tile_at(it + 1) * BLK, tid);
         const char* stage = smem + (it & 1) * C::STAGE;
-        const uint16_t* ks = reinterpret_cast<const uint16_t*>(stage);
-        const uint16_t* vt = reinterpret_cast<const uint16_t*>(stage + C::K_BYTES);
-        const int j0 = tile_at(it) * BLK;
 
         // S^T (32 keys x 32 query rows) = K Q^T over D
         f32x16 sacc;
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-        const uint16_t* krow = ks + (32 * wk + col) * C::KS + 8 * half_id;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * s));
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + k_off[s]));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
         }
-
-        // scores in log2 units; value v of this lane is key 8*(v/4) + 4*half_id + v%4 of the wave's half
-        float x[16];
+        if (!POS) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) x[v] = sacc[v] * P.scale_log2;
+            for (int v = 0; v < 16; ++v) sacc[v] *= P.scale_log2;
+        }
+        // value v of this lane is key 8*(v/4) + 4*half_id + v%4 of the wave's half
         if (MODE == kWindow) {
+            const int j0 = tile_at(it) * BLK;
             const int kbase = j0 + 32 * wk + 4 * half_id;
             const bool full = (j0 + BLK - 1 < P.sink) ||
                               (q0 + BLK - 1 - j0 <= P.half && j0 + BLK - 1 - q0 <= P.half && j0 + BLK <= (int)P.S);
@@ -238,18 +244,20 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
                     const int j = kbase + 8 * (v / 4) + (v % 4);
                     const int d = my_row - j;
                     const bool vis = (j < (int)P.S) & (((d <= P.half) & (-d <= P.half)) | (j < P.sink));
-                    x[v] = vis ? x[v] : neg_inf;
+                    sacc[v] = vis ? sacc[v] : neg_inf;
                 }
             }
         }
-        float mloc = x[0];
+        float smax = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
-        for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, x[v]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        for (int v = 3; v < 15; v += 2) smax = fmaxf(fmaxf(smax, sacc[v]), sacc[v + 1]);
+        smax = fmaxf(smax, sacc[15]);
+        smax = fmaxf(smax, __shfl_xor(smax, 32));
+        const float mloc = smax * c_scale;
         const bool grow = mloc > m_used + kRescaleSlack;
         if (__ballot(grow)) {
             const float m_new = grow ? mloc : m_used;
-            const float alpha = exp2f(m_used - m_new);
+            const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
             m_used = m_new;
             l_part *= alpha;
 #pragma unroll
@@ -259,24 +267,30 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         }
         bf16x8 pb[2];
         float psum = 0.f;
+        const float neg_m = -m_used;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const float p = exp2f(x[v] - m_used);
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], c_scale, neg_m));
             psum += p;
             pb[v / 8][v % 8] = (__bf16)p;
         }
         l_part += psum;
 
-        // O^T (D x 32 rows) += V^T P^T; slot jj of MFMA m is key 16m + 8*(jj/4) + 4*half_id + jj%4
+        // O^T (D x 32 rows) += V^T P^T; slot jj of MFMA m is key 16m + 8*(jj/4) + 4*half_id + jj%4,
+        // delivered by two transposing reads (jj < 4, jj >= 4)
+        const char* vs = stage + C::TILE;
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-            const uint16_t* vrow = vt + (32 * t + col) * C::VS + 32 * wk + 4 * half_id;
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * m);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * m + 8);
-                const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
-                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), pb[m], o[t], 0, 0, 0);
+                const int key = v_key0 + 16 * m;
+                const int colv = 32 * t + v_col0;
+                const int off0 = lds_off<D>(key, colv >> 3) + (colv & 7) * 2;
+                const int off1 = lds_off<D>(key + 8, colv >> 3) + (colv & 7) * 2;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + off0));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + off1));
+                const s16x4 a8[2] = {lo, hi};
+                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[m], o[t], 0, 0, 0);
             }
         }
 
@@ -419,7 +433,10 @@ int launch_scalar(const ScalarParams& P, int dtype, int64_t D, hipStream_t st, c
 
 template <int D, int BLK, int MODE>
 void launch_mfma(const AttnParams& P, hipStream_t st) {
-    attn_mfma_kernel<D, BLK, MODE><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P);
+    if (P.scale_log2 > 0.f)
+        attn_mfma_kernel<D, BLK, MODE, true><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P);
+    else
+        attn_mfma_kernel<D, BLK, MODE, false><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P);
 }
 
 int common_checks(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B, int64_t H, int64_t S,
@@ -430,6 +447,7 @@ int common_checks(const void* q, const void* k, const void* v, void* out, int dt
     BSA_REQUIRE(S >= 1, "%s: sequence length must be > 0", name);
     BSA_REQUIRE(D >= 1, "%s: head dim must be > 0", name);
     BSA_REQUIRE(S < ((int64_t)1 << 30), "%s: S too large", name);
+    BSA_REQUIRE(S * D * elem_size(dtype) < ((int64_t)1 << 31), "%s: one head must stay under 2 GiB", name);
     BSA_REQUIRE(B * H * S * D < ((int64_t)1 << 40), "%s: tensor too large", name);
     BSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), "%s: tensors must be 16-byte aligned",
                 name);
