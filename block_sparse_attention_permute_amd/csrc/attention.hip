@@ -34,6 +34,8 @@
 // A scalar fp32 kernel covers fp32 inputs and the other shapes.
 #include "common.h"
 
+#include <type_traits>
+
 namespace bsa {
 namespace {
 
@@ -75,16 +77,21 @@ struct Cfg {
     static_assert(CH >= 1 && (BLK * NCH) % NT == 0, "uneven staging");
 };
 
-// LDS rows are stored unpadded with their 16-byte chunks XOR-swizzled by an
-// even, row-dependent amount.  This keeps the 128-bit K reads (16 rows, one
-// chunk) and the transposing V reads (4 rows x 2 chunks) free of bank
-// conflicts.
-template <int NCH>
-__device__ __forceinline__ int swz(int row) { return (2 * row) & (NCH - 1); }
-
+// LDS rows are stored unpadded with their 16-byte chunks XOR-swizzled per
+// row, with a different swizzle for each tile so that both readers are free
+// of bank conflicts:
+//  * K, chunk ^ (row % 8): a 128-bit K read has 8 consecutive rows reading
+//    one chunk, which then land on 8 different 4-bank groups;
+//  * V, chunk ^ 2*(row % 4): a transposing read has 4 consecutive rows
+//    reading an aligned chunk pair, which then land on 4 different 8-bank
+//    groups.
 template <int D>
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * (D * 2) + ((chunk ^ swz<D / 8>(row)) << 4);
+__device__ __forceinline__ int k_lds(int row, int chunk) {
+    return row * (D * 2) + ((chunk ^ (row & 7)) << 4);
+}
+template <int D>
+__device__ __forceinline__ int v_lds(int row, int chunk) {
+    return row * (D * 2) + ((chunk ^ ((row & 3) << 1)) << 4);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -118,9 +125,9 @@ __device__ __forceinline__ void stage_store(const Staging<D, BLK>& st, char* sta
 #pragma unroll
     for (int j = 0; j < C::CH; ++j) {
         const int c = tid + C::NT * j;
-        const int off = lds_off<D>(c / C::NCH, c % C::NCH);
-        *reinterpret_cast<u32x4*>(stage + off) = st.k[j];
-        *reinterpret_cast<u32x4*>(stage + C::TILE + off) = st.v[j];
+        const int row = c / C::NCH, chunk = c % C::NCH;
+        *reinterpret_cast<u32x4*>(stage + k_lds<D>(row, chunk)) = st.k[j];
+        *reinterpret_cast<u32x4*>(stage + C::TILE + v_lds<D>(row, chunk)) = st.v[j];
     }
 }
 
@@ -128,11 +135,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+template <int N>
+using ic = std::integral_constant<int, N>;
+
 // POS: the softmax scale is positive, so the row max of the raw scores gives
 // the max of the scaled ones and exp2(s * c - m) is one FMA and one exp.
+// kv_idx / kv_cnt are separate restrict arguments so their uniform reads
+// become scalar loads.
 template <int D, int BLK, int MODE, bool POS>
 __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)) void attn_mfma_kernel(
-    const AttnParams P) {
+    const AttnParams P, const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt) {
     using C = Cfg<D, BLK>;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
     const int tid = threadIdx.x;
@@ -156,8 +168,8 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
     int n_sink_tiles = 0, local_first = 0;
     if (MODE == kBlockList) {
         const size_t row = (size_t)bh * P.nq + I;
-        n_iter = min(P.kv_cnt[row], (int)P.max_kept);
-        list = P.kv_idx + row * P.max_kept;
+        n_iter = min(kv_cnt[row], (int)P.max_kept);
+        list = kv_idx + row * P.max_kept;
     } else {
         n_sink_tiles = (P.sink + BLK - 1) / BLK;
         const int lo = max(0, q0 - P.half);
@@ -190,15 +202,22 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
     const int my_row = q0 + 32 * wr + col;
     const float c_scale = POS ? P.scale_log2 : 1.0f;
 
-    // loop-invariant LDS byte offsets of this lane's operands
-    int k_off[D / 16];
+    // loop-invariant LDS byte offsets of this lane's operands (stage 0)
+    int k_addr[D / 16];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) k_off[s] = lds_off<D>(32 * wk + col, 2 * s + half_id);
+    for (int s = 0; s < D / 16; ++s) k_addr[s] = k_lds<D>(32 * wk + col, 2 * s + half_id);
     // transposing V reads: lane (g = lane/16, r = lane%16) addresses key
-    // 32*wk + 16*m + 8*part + 4*(g/2) + r/4, column 32*t + 16*(g%2) + 4*(r%4)
+    // 32*wk + 16*m + 8*part + 4*(g/2) + r/4, column 32*t + 16*(g%2) + 4*(r%4);
+    // the key offset 16*m + 8*part keeps row % 4, hence the swizzle
     const int g16 = lane >> 4, r16 = lane & 15;
     const int v_key0 = 32 * wk + 4 * (g16 >> 1) + (r16 >> 2);
     const int v_col0 = 16 * (g16 & 1) + 4 * (r16 & 3);
+    int v_addr[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+        const int colv = 32 * t + v_col0;
+        v_addr[t] = C::TILE + v_lds<D>(v_key0, colv >> 3) + (colv & 7) * 2;
+    }
 
     Staging<D, BLK> st;
     if (n_iter > 0) {
@@ -211,10 +230,14 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int it = 0; it < n_iter; ++it) {
+    // One key tile.  CUR (0 or 1) is the LDS stage holding tile `it`; it is a
+    // compile-time constant so every LDS address is a register plus an
+    // immediate offset.
+    auto body = [&](auto cur_c, int it) {
+        constexpr int CUR = decltype(cur_c)::value;
         const bool more = it + 1 < n_iter;
         if (more) stage_load<D, BLK>(st, kr, vr, tile_at(it + 1) * BLK, tid);
-        const char* stage = smem + (it & 1) * C::STAGE;
+        const char* stage = smem + CUR * C::STAGE;
 
         // S^T (32 keys x 32 query rows) = K Q^T over D
         f32x16 sacc;
@@ -222,7 +245,7 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + k_off[s]));
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + k_addr[s]));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
         }
         if (!POS) {
@@ -266,37 +289,39 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
                 for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
         }
         bf16x8 pb[2];
-        float psum = 0.f;
+        float psum;
         const float neg_m = -m_used;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], c_scale, neg_m));
-            psum += p;
+            psum = v == 0 ? p : psum + p;
             pb[v / 8][v % 8] = (__bf16)p;
         }
         l_part += psum;
 
         // O^T (D x 32 rows) += V^T P^T; slot jj of MFMA m is key 16m + 8*(jj/4) + 4*half_id + jj%4,
         // delivered by two transposing reads (jj < 4, jj >= 4)
-        const char* vs = stage + C::TILE;
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const int key = v_key0 + 16 * m;
-                const int colv = 32 * t + v_col0;
-                const int off0 = lds_off<D>(key, colv >> 3) + (colv & 7) * 2;
-                const int off1 = lds_off<D>(key + 8, colv >> 3) + (colv & 7) * 2;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + off0));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + off1));
+                const char* va = stage + v_addr[t] + (16 * m) * (D * 2);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)va);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(va + 8 * (D * 2)));
                 const s16x4 a8[2] = {lo, hi};
                 o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[m], o[t], 0, 0, 0);
             }
         }
 
-        if (more) stage_store<D, BLK>(st, smem + ((it + 1) & 1) * C::STAGE, tid);
+        if (more) stage_store<D, BLK>(st, smem + (1 - CUR) * C::STAGE, tid);
         __syncthreads();
+    };
+    int it = 0;
+    for (; it + 1 < n_iter; it += 2) {
+        body(ic<0>{}, it);
+        body(ic<1>{}, it + 1);
     }
+    if (it < n_iter) body(ic<0>{}, it);
 
     // ---- merge the key halves of each row and write out
     float l_row = l_part + __shfl_xor(l_part, 32);
@@ -333,10 +358,13 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            // values 4g .. 4g+3 are d = 32t + 8g + 4*half_id + 0..3
-            uint32_t w0 = f32_to_bf16(o[t][4 * g + 0] * inv) | ((uint32_t)f32_to_bf16(o[t][4 * g + 1] * inv) << 16);
-            uint32_t w1 = f32_to_bf16(o[t][4 * g + 2] * inv) | ((uint32_t)f32_to_bf16(o[t][4 * g + 3] * inv) << 16);
-            *reinterpret_cast<u32x2*>(orow + 32 * t + 8 * g + 4 * half_id) = u32x2{w0, w1};
+            // values 4g .. 4g+3 are d = 32t + 8g + 4*half_id + 0..3; the hardware
+            // conversion rounds to nearest even
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[t][4 * g + e] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half_id) = w;
         }
 }
 
@@ -434,9 +462,9 @@ int launch_scalar(const ScalarParams& P, int dtype, int64_t D, hipStream_t st, c
 template <int D, int BLK, int MODE>
 void launch_mfma(const AttnParams& P, hipStream_t st) {
     if (P.scale_log2 > 0.f)
-        attn_mfma_kernel<D, BLK, MODE, true><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P);
+        attn_mfma_kernel<D, BLK, MODE, true><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P, P.kv_idx, P.kv_cnt);
     else
-        attn_mfma_kernel<D, BLK, MODE, false><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P);
+        attn_mfma_kernel<D, BLK, MODE, false><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P, P.kv_idx, P.kv_cnt);
 }
 
 int common_checks(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B, int64_t H, int64_t S,
