@@ -219,24 +219,30 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         v_addr[t] = C::TILE + v_lds<D>(v_key0, colv >> 3) + (colv & 7) * 2;
     }
 
-    Staging<D, BLK> st;
+    // Tiles are prefetched two iterations ahead into two register sets, so a
+    // tile's global loads have two iterations to land before it is written to
+    // LDS; LDS is double-buffered (tile it in stage it % 2).
+    Staging<D, BLK> st[2];
     if (n_iter > 0) {
-        stage_load<D, BLK>(st, kr, vr, tile_at(0) * BLK, tid);
-        stage_store<D, BLK>(st, smem, tid);
+        stage_load<D, BLK>(st[0], kr, vr, tile_at(0) * BLK, tid);
+        stage_store<D, BLK>(st[0], smem, tid);
     }
     // Drain every load (the Q fragment included) before the loop, so that the
-    // loop's only outstanding loads are the next tile's: otherwise the
+    // loop's only outstanding loads are the prefetched tiles': otherwise the
     // compiler's wait tracking makes each tile's QK^T wait for the prefetch.
     __builtin_amdgcn_s_waitcnt(0);
+    if (n_iter > 0) stage_load<D, BLK>(st[1], kr, vr, tile_at(min(1, n_iter - 1)) * BLK, tid);
     __syncthreads();
 
-    // One key tile.  CUR (0 or 1) is the LDS stage holding tile `it`; it is a
-    // compile-time constant so every LDS address is a register plus an
-    // immediate offset.
+    // One key tile.  CUR (0 or 1) is the LDS stage holding tile `it` and the
+    // register set that receives tile it + 2; it is a compile-time constant so
+    // every LDS address is a register plus an immediate offset.
     auto body = [&](auto cur_c, int it) {
         constexpr int CUR = decltype(cur_c)::value;
-        const bool more = it + 1 < n_iter;
-        if (more) stage_load<D, BLK>(st, kr, vr, tile_at(it + 1) * BLK, tid);
+        // always issued (the last tile again past the end): a conditional load
+        // would make the compiler's wait counts assume it was skipped and wait
+        // for every outstanding load before the LDS store below
+        stage_load<D, BLK>(st[CUR], kr, vr, tile_at(min(it + 2, n_iter - 1)) * BLK, tid);
         const char* stage = smem + CUR * C::STAGE;
 
         // S^T (32 keys x 32 query rows) = K Q^T over D
@@ -313,7 +319,7 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
             }
         }
 
-        if (more) stage_store<D, BLK>(st, smem + (1 - CUR) * C::STAGE, tid);
+        if (it + 1 < n_iter) stage_store<D, BLK>(st[1 - CUR], smem + (1 - CUR) * C::STAGE, tid);
         __syncthreads();
     };
     int it = 0;
