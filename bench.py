@@ -100,12 +100,85 @@ def cpu_baseline(q, k, v, wl, block, kk, budget_s=12.0):
     }
 
 
+def _time(torch, fn, steps, warmup):
+    """Average ms of fn() over `steps` calls, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def sweep(args, torch, np, bsa, synth):
+    """Kernel timings on the sliding-tile, windowed and long-sequence workloads."""
+    dev = torch.device("cuda:0")
+    steps, warmup = max(args.steps // 5, 5), max(args.warmup, 2)
+
+    # sliding tile: grid 8x16x16, tiles 2x4x4 (block 32), 3x3x3 neighbourhood, D=64, H=8
+    wl = synth.WORKLOADS[2]
+    q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(2))
+    tile = [(2, 4, 4)]
+    idx, cnt = bsa.bsa_sliding_tile_block_list((4, 4, 4))
+    kv_idx = torch.from_numpy(np.broadcast_to(idx, (1, wl.H) + idx.shape).copy()).to(dev)
+    kv_cnt = torch.from_numpy(np.broadcast_to(cnt, (1, wl.H, 64)).copy()).to(dev)
+    qp, kp, vp = (bsa.bsa_tile_permute(x, wl.grid, tile) for x in (q, k, v))
+    out = torch.empty_like(qp)
+    ms = _time(torch, lambda: bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 32, out=out), steps, warmup)
+    fl = int(kv_cnt.sum().item()) * 4 * 32 * 32 * wl.D
+
+    def step2():
+        for x, y in ((q, qp), (k, kp), (v, vp)):
+            bsa.bsa_tile_permute(x, wl.grid, tile, out=y)
+        bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 32, out=out)
+        bsa.bsa_invert_permute(out, wl.grid, tile)
+    ms_step = _time(torch, step2, steps, warmup)
+    print(json.dumps({"workload": wl.name, "attention_ms": round(ms, 4), "attention_tflops": round(fl / ms / 1e9, 2),
+                      "step_ms": round(ms_step, 4), "kept_block_flops": fl}), flush=True)
+
+    # windowed: S=16384, window 2048 (half 1024), sink 64, D=128, H=24
+    wl = synth.WORKLOADS[3]
+    q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(3))
+    out = torch.empty_like(q)
+    ms = _time(torch, lambda: bsa.bsa_windowed_attention(q, k, v, 2048, 64, 128 ** -0.5, 512, out=out), steps, warmup)
+    S, half, sink = wl.S, 1024, 64
+    i = np.arange(S)
+    local = np.minimum(S - 1, i + half) - np.maximum(0, i - half) + 1
+    extra = np.maximum(0, np.minimum(sink, np.maximum(0, i - half)))      # sinks left of the window
+    pairs = int((local + extra).sum())
+    fl_tok = pairs * 4 * wl.D * wl.H
+    print(json.dumps({"workload": wl.name, "attention_ms": round(ms, 4),
+                      "attention_tflops_token_exact": round(fl_tok / ms / 1e9, 2), "visible_pairs_per_head": pairs}),
+          flush=True)
+
+    # long sequence: grid 32x48x80 (S=122880), tiles 4x4x4, 10% budget, D=128, H=24
+    wl = synth.WORKLOADS[5]
+    q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(5))
+    pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, [(4, 4, 4)], 0.10, q.dtype, dev)
+    out = torch.empty_like(q)
+    ms_step = _time(torch, lambda: pipe(q, k, v, out=out), max(steps // 2, 3), warmup)
+    kv_idx, kv_cnt = pipe.kv
+    ms = _time(torch, lambda: bsa.bsa_block_sparse_attention(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, 64,
+                                                             out=pipe.op), max(steps // 2, 3), warmup)
+    fl = int(kv_cnt.sum().item()) * 4 * 64 * 64 * wl.D
+    print(json.dumps({"workload": wl.name, "attention_ms": round(ms, 4), "attention_tflops": round(fl / ms / 1e9, 2),
+                      "step_ms": round(ms_step, 4), "step_tflops": round(fl / ms_step / 1e9, 2),
+                      "kept_block_flops": fl}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line, time the hot-path kernels on the other workloads "
+                         "(sliding tile, windowed, long sequence) and print one JSON line per workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -130,6 +203,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30, "calls": 5}))
+        return
+
+    if args.sweep:
+        sweep(args, torch, np, bsa, synth)
         return
 
     wl = synth.WORKLOADS[CFG]
