@@ -374,6 +374,267 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         }
 }
 
+// ------------------------------------------------------------- one wave ---
+// 64-token blocks, D = 128: one single-wave workgroup per query block.  The
+// wave owns all 64 query rows (two 32-row tiles) and all 64 keys of each key
+// tile (two 32-key halves):
+//  * K goes straight from global memory into MFMA A-operand registers (16
+//    buffer loads per tile, issued one tile ahead); Q stays in registers;
+//  * S^T = K Q^T is four independent 8-MFMA chains (key half x row tile), so
+//    every K fragment feeds two MFMAs;
+//  * V is staged through the wave's own LDS (no barrier: one wave) and read
+//    back transposed; each V^T fragment feeds the two row tiles' MFMAs;
+//  * nothing is shared between waves, so there are no barriers at all and
+//    waves of different query blocks drift freely.
+struct SoloCfg {
+    static constexpr int D = 128, BLK = 64, NT = 64, NCH = D / 8;
+    static constexpr int TILE = BLK * D * 2;  // one V tile in LDS
+};
+
+template <int MODE, bool POS>
+__global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, const int32_t* __restrict__ kv_idx,
+                                                          const int32_t* __restrict__ kv_cnt) {
+    using C = SoloCfg;
+    constexpr int D = C::D, BLK = C::BLK;
+    // Q (64 rows) and one V tile live in the wave's LDS (32 KB: four waves per CU)
+    __shared__ __attribute__((aligned(16))) char qlds[C::TILE];
+    __shared__ __attribute__((aligned(16))) char vlds[C::TILE];
+    const int lane = threadIdx.x;
+    const int half_id = lane >> 5, col = lane & 31;
+
+    uint32_t wg = blockIdx.x;
+    if (P.xcd_remap) wg = (wg & 7u) * (P.n_wg >> 3) + (wg >> 3);
+    const uint32_t bh = wg / P.nq, I = wg % P.nq;
+    const size_t head = (size_t)bh * P.S * D;
+    const uint32_t head_bytes = P.S * D * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(P.q + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(P.k + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(P.v + head, head_bytes);
+    const int q0 = (int)I * BLK;
+
+    int n_iter;
+    const int32_t* list = nullptr;
+    int n_sink_tiles = 0, local_first = 0;
+    if (MODE == kBlockList) {
+        const size_t row = (size_t)bh * P.nq + I;
+        n_iter = min(kv_cnt[row], (int)P.max_kept);
+        list = kv_idx + row * P.max_kept;
+    } else {
+        n_sink_tiles = (P.sink + BLK - 1) / BLK;
+        const int lo = max(0, q0 - P.half);
+        const int hi = min((int)P.S, q0 + BLK - 1 + P.half + 1);  // exclusive
+        const int t_lo = lo / BLK, t_hi = (hi - 1) / BLK;
+        local_first = max(t_lo, n_sink_tiles);
+        n_iter = n_sink_tiles + max(0, t_hi - local_first + 1);
+    }
+    auto tile_at = [&](int it) -> int {
+        if (MODE == kBlockList) return __builtin_amdgcn_readfirstlane(list[it]);
+        return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
+    };
+
+    // fragments: row (or key) 32*x + col, D cols 16*s + 8*half_id + 0..7
+    const int frag_off = col * (D * 2) + half_id * 16;
+    // Q rows into LDS once (K swizzle: 8-row 128-bit reads are conflict-free)
+#pragma unroll
+    for (int j = 0; j < BLK * C::NCH / 64; ++j) {
+        const int c = lane + 64 * j;
+        const int row = c / C::NCH, chunk = c % C::NCH;
+        *reinterpret_cast<u32x4*>(qlds + k_lds<D>(row, chunk)) =
+            __builtin_amdgcn_raw_buffer_load_b128(qr, (q0 + row) * (D * 2) + chunk * 16, 0, 0);
+    }
+    int q_addr[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) q_addr[s] = k_lds<D>(col, 2 * s + half_id);
+
+    auto load_k = [&](bf16x8 (&kf)[2][D / 16], int j0) {
+        const int soff = j0 * (D * 2);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+                kf[c][s] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, frag_off + 32 * c * (D * 2) + 32 * s, soff, 0));
+    };
+    // V tile straight into LDS (buffer loads with the LDS destination): wave
+    // instruction q fills LDS bytes [1024q, 1024q + 1024), i.e. rows 4q..4q+3,
+    // lane l landing on physical chunk l % 16 of row 4q + l / 16, which holds
+    // logical chunk (l % 16) ^ 2(row % 4) (the V swizzle); row % 4 = l / 16.
+    const int vdma_off = (lane >> 4) * (D * 2) + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
+    auto dma_v = [&](char* buf, int j0) {
+#pragma unroll
+        for (int q = 0; q < C::TILE / 1024; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(buf + 1024 * q), 16,
+                                                     vdma_off, j0 * (D * 2) + 1024 * q, 0, 0);
+    };
+
+    f32x16 o[2][D / 32];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[r][t][v] = 0.f;
+    float m_used[2] = {-1e30f, -1e30f}, l_part[2] = {0.f, 0.f};
+    const float c_scale = POS ? P.scale_log2 : 1.0f;
+
+    const int g16 = lane >> 4, r16 = lane & 15;
+    const int v_key0 = 4 * (g16 >> 1) + (r16 >> 2);
+    const int v_col0 = 16 * (g16 & 1) + 4 * (r16 & 3);
+    int v_addr[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+        const int colv = 32 * t + v_col0;
+        v_addr[t] = v_lds<D>(v_key0, colv >> 3) + (colv & 7) * 2;
+    }
+
+    bf16x8 kf[2][D / 16];
+    if (n_iter > 0) load_k(kf, tile_at(0) * BLK);
+    __builtin_amdgcn_s_waitcnt(0);
+
+    for (int it = 0; it < n_iter; ++it) {
+        const int nxt = tile_at(min(it + 1, n_iter - 1)) * BLK;
+        // this tile's V into LDS (the previous tile's V reads have completed)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        dma_v(vlds, tile_at(it) * BLK);
+
+        // S^T of (key half c, row tile r) = K_c Q_r^T: four independent chains
+        f32x16 sacc[2][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sacc[c][r][v] = 0.f;
+            }
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qlds + q_addr[s]));
+            const bf16x8 qb =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qlds + q_addr[s] + 32 * (D * 2)));
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                sacc[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][s], qa, sacc[c][0], 0, 0, 0);
+                sacc[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][s], qb, sacc[c][1], 0, 0, 0);
+            }
+        }
+        // K registers are free: fetch the next tile's K (the last tile again past
+        // the end).  The scheduling barriers keep the loads after the MFMAs that
+        // read the old fragments, so old and new K share registers.
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(kf, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // softmax of both row tiles (32 values of one row per lane and tile)
+        if (!POS) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sacc[c][r][v] *= P.scale_log2;
+        }
+        if (MODE == kWindow) {
+            const int j0 = tile_at(it) * BLK;
+            const bool full = (j0 + BLK - 1 < P.sink) ||
+                              (q0 + BLK - 1 - j0 <= P.half && j0 + BLK - 1 - q0 <= P.half && j0 + BLK <= (int)P.S);
+            if (!full) {
+                const float neg_inf = -__builtin_inff();
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const int my_row = q0 + 32 * r + col;
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int j = j0 + 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4);
+                            const int d = my_row - j;
+                            const bool vis = (j < (int)P.S) & (((d <= P.half) & (-d <= P.half)) | (j < P.sink));
+                            sacc[c][r][v] = vis ? sacc[c][r][v] : neg_inf;
+                        }
+                    }
+            }
+        }
+        float mloc[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            float smax = fmaxf(sacc[0][r][0], sacc[1][r][0]);
+#pragma unroll
+            for (int v = 1; v < 16; ++v) smax = fmaxf(fmaxf(smax, sacc[0][r][v]), sacc[1][r][v]);
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+            mloc[r] = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * c_scale;
+        }
+        const bool grow0 = mloc[0] > m_used[0] + kRescaleSlack;
+        const bool grow1 = mloc[1] > m_used[1] + kRescaleSlack;
+        if (__ballot(grow0 | grow1)) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const bool grow = r == 0 ? grow0 : grow1;
+                const float m_new = grow ? mloc[r] : m_used[r];
+                const float alpha = __builtin_amdgcn_exp2f(m_used[r] - m_new);
+                m_used[r] = m_new;
+                l_part[r] *= alpha;
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[r][t][v] *= alpha;
+            }
+        }
+        // P as bf16 B operands: pb[r][m] covers keys 16m..16m+15 of the tile
+        bf16x8 pb[2][4];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float neg_m = -m_used[r];
+            float psum = 0.f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v], c_scale, neg_m));
+                    psum += p;
+                    pb[r][2 * c + v / 8][v % 8] = (__bf16)p;
+                }
+            l_part[r] += psum;
+        }
+
+        // O^T += V^T P^T once this tile's V has landed (only the next tile's 16 K
+        // loads were issued after it)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 16);  // vmcnt(16)
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const char* va = vlds + v_addr[t] + (16 * m) * (D * 2);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)va);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(va + 8 * (D * 2)));
+                const s16x4 a8[2] = {lo, hi};
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, a8);
+                o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[0][m], o[0][t], 0, 0, 0);
+                o[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[1][m], o[1][t], 0, 0, 0);
+            }
+    }
+
+    // ---- write out (each lane pair holds one row; their partial sums add up)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[r]), __float_as_uint(l_part[r]), false,
+                                                         false);
+        const float inv = 1.0f / (__uint_as_float(pr[0]) + __uint_as_float(pr[1]));
+        const int my_row = q0 + 32 * r + col;
+        if (my_row >= (int)P.S) continue;
+        uint16_t* orow = P.out + head + (size_t)my_row * D;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                bf16x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[r][t][4 * g + e] * inv);
+                *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half_id) = w;
+            }
+    }
+}
+
 // ----------------------------------------------------------------- scalar ---
 // One thread per query row, fp32 math, exact online softmax.  For fp32
 // tensors and shapes the MFMA kernel does not cover.
@@ -465,6 +726,14 @@ int launch_scalar(const ScalarParams& P, int dtype, int64_t D, hipStream_t st, c
     return check_launch(name);
 }
 
+template <int MODE>
+void launch_solo(const AttnParams& P, hipStream_t st) {
+    if (P.scale_log2 > 0.f)
+        attn_solo_kernel<MODE, true><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt);
+    else
+        attn_solo_kernel<MODE, false><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt);
+}
+
 template <int D, int BLK, int MODE>
 void launch_mfma(const AttnParams& P, hipStream_t st) {
     if (P.scale_log2 > 0.f)
@@ -528,7 +797,7 @@ extern "C" int bsa_block_sparse_attention(const void* q, const void* k, const vo
         P.kv_idx = kv_idx;
         P.kv_cnt = kv_cnt;
         P.max_kept = (uint32_t)max_kept;
-        if (D == 128 && block == 64) launch_mfma<128, 64, kBlockList>(P, st);
+        if (D == 128 && block == 64) launch_solo<kBlockList>(P, st);
         else if (D == 128 && block == 32) launch_mfma<128, 32, kBlockList>(P, st);
         else if (D == 64 && block == 64) launch_mfma<64, 64, kBlockList>(P, st);
         else launch_mfma<64, 32, kBlockList>(P, st);
@@ -582,7 +851,7 @@ extern "C" int bsa_windowed_attention(const void* q, const void* k, const void* 
         P.scale_log2 = sl2;
         P.half = half;
         P.sink = sink;
-        if (D == 128) launch_mfma<128, BLK, kWindow>(P, st);
+        if (D == 128) launch_solo<kWindow>(P, st);
         else launch_mfma<64, BLK, kWindow>(P, st);
         return check_launch(name);
     }
