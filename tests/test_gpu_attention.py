@@ -64,6 +64,30 @@ def test_block_sparse_random_lists(dtype, D, block, S, H):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("nb", [200, 260])
+def test_block_sparse_long_lists(nb):
+    """Lists longer than 64, 128 and 192 entries (and past 256, where another
+    kernel takes over), checked on the rows of the longest-list blocks."""
+    torch_gpu()
+    block, D, H = 64, 128, 1
+    S = nb * block
+    rng = np.random.default_rng(nb)
+    keep = rng.random((1, H, nb, nb)) < 0.8
+    keep[..., np.arange(nb), np.arange(nb)] = True
+    keep[:, :, 0] = True                                     # nb entries
+    keep[:, :, 1] = False
+    keep[:, :, 1, [0, 63, 64, 127, 128, 191, nb - 1]] = True  # the chunk edges
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=300 + i + nb) for i in range(3))
+    kv_idx, kv_cnt = _keep_to_gpu_lists(keep)
+    out = f64(bsa.bsa_block_sparse_attention(gpu(q), gpu(k), gpu(v), kv_idx, kv_cnt, block))
+    qf, kf, vf = (synth.stored_to_f64(x)[0, 0] for x in (q, k, v))
+    for qb in [0, 1, 2, nb // 2, nb - 1]:
+        rows = np.arange(qb * block, (qb + 1) * block)
+        want = OA.block_sparse_rows(qf, kf, vf, keep[0, 0], block, rows, D ** -0.5)
+        assert max_abs(out[0, 0, rows], want) <= BF16_ATOL, qb
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("dtype,D,block", [("bf16", 128, 64), ("bf16", 64, 32), ("f32", 16, 32)])
 def test_block_sparse_all_kept_equals_dense(dtype, D, block):
     torch_gpu()
