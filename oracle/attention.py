@@ -176,3 +176,26 @@ def window_rows(q_head, k_head, v_head, rows, window: int, sink: int, scale: flo
 def kept_block_flops(kv_cnt, block_q: int, block_k: int, D: int) -> int:
     """Algorithmic FLOPs of block-sparse attention: 4 * Bq * Bk * D per kept block."""
     return int(np.asarray(kv_cnt, dtype=np.int64).sum()) * 4 * block_q * block_k * D
+
+
+def spatial_only_mask(grid) -> np.ndarray:
+    """Additive (S, S) mask: token i sees token j exactly when both are in one frame.
+
+    [ADR-0001, "Décision" step 1] names spatial_only_mask; the pages give no
+    definition.  Reading: spatial-only attention stays inside a frame,
+    t(i) == t(j), T-major tokens s = (t * Hg + y) * Wg + x.
+    """
+    T, Hg, Wg = (int(g) for g in grid)
+    t = np.arange(T * Hg * Wg) // (Hg * Wg)
+    return np.where(t[:, None] == t[None, :], 0.0, NEG_INF)
+
+
+def temporal_only_mask(grid) -> np.ndarray:
+    """Additive (S, S) mask: token i sees token j exactly when both sit at one (y, x).
+
+    [ADR-0001, "Décision" step 1] names temporal_only_mask; reading:
+    temporal-only attention links the same spatial position across frames.
+    """
+    T, Hg, Wg = (int(g) for g in grid)
+    pos = np.arange(T * Hg * Wg) % (Hg * Wg)
+    return np.where(pos[:, None] == pos[None, :], 0.0, NEG_INF)

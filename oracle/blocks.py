@@ -34,6 +34,34 @@ def minmax_block_scores(qp, kp, block: int):
     return np.maximum(c @ kmax.T, c @ kmin.T)
 
 
+def block_minmax_valid(x, valid, block: int):
+    """block_minmax over the valid tokens of each block only (padding left out).
+
+    Used on padded grids ([Adaptive tiling (SPADE), "Deviations and notes":
+    pad with zero tokens]); reading: a partial edge tile is summarised by its
+    real tokens, as SPADE's kernel treats partial tiles.  Every block must
+    hold at least one valid token.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    valid = np.asarray(valid, dtype=bool)
+    s, d = x.shape
+    if block <= 0 or s % block:
+        raise ValueError(f"block {block} must divide S={s}")
+    xb = x.reshape(s // block, block, d)
+    vb = valid.reshape(s // block, block)[:, :, None]
+    if not vb.any(axis=1).all():
+        raise ValueError("a block holds no valid token")
+    return np.where(vb, xb, -np.inf).max(axis=1), np.where(vb, xb, np.inf).min(axis=1)
+
+
+def minmax_block_scores_valid(qp, kp, valid, block: int):
+    """minmax_block_scores with the summaries taken over valid tokens only."""
+    qmax, qmin = block_minmax_valid(qp, valid, block)
+    kmax, kmin = block_minmax_valid(kp, valid, block)
+    c = qmax + qmin
+    return np.maximum(c @ kmax.T, c @ kmin.T)
+
+
 def budget(frac: float, n_blocks: int) -> int:
     """Kept key blocks per query block: max(1, floor(frac * n)).
 
@@ -63,25 +91,71 @@ def topk_row(scores_row, k: int) -> np.ndarray:
     return np.sort(order[:k])
 
 
-def topk_block_mask(scores, k: int, sink_blocks: int = 1, keep_diag: bool = True) -> np.ndarray:
+def static_blocks(nq: int, nk: int, sink_blocks: int = 1, diag_width: int = 1) -> np.ndarray:
+    """Blocks every row keeps whatever the scores: sinks and a diagonal band.
+
+    [Adaptive tiling (SPADE), "Recipe" note]: SPADE always keeps a few sink
+    key blocks and a diagonal band (its Wan configurations use widths 5 and
+    40) and these are ORed into the estimated mask.  Readings: the sinks are
+    key blocks 0 .. sink_blocks-1; a band of width w keeps J with
+    abs(I - J) <= w // 2, the same rule as the windowed-attention policy
+    ([FastVideo windowed_attention, "Window policy"]), so width 1 is the
+    diagonal alone and width 0 keeps no band.
+    """
+    if sink_blocks < 0 or diag_width < 0:
+        raise ValueError("sink_blocks and diag_width must be >= 0")
+    i = np.arange(nq)[:, None]
+    j = np.arange(nk)[None, :]
+    keep = j < sink_blocks
+    if diag_width >= 1:
+        keep = keep | (np.abs(i - j) <= diag_width // 2)
+    return np.broadcast_to(keep, (nq, nk)).copy()
+
+
+def topk_block_mask(scores, k: int, sink_blocks: int = 1, keep_diag=True) -> np.ndarray:
     """Boolean (Nq, Nk) block mask: top-k per row, OR the sink and diagonal blocks.
 
     [Adaptive tiling (SPADE), "The idea" step 4 and "Recipe"]: a fixed top-k
     budget per query block, and the sink key blocks and the diagonal are
-    always kept, ORed in after the top-k (so a row keeps between k and
-    k + sink_blocks + 1 blocks).  Reading: sink blocks are key blocks
-    0 .. sink_blocks-1 and the diagonal is key block J = I.
+    always kept, ORed in after the top-k.  ``keep_diag`` is a diagonal band
+    width (True = 1, the diagonal alone; False = 0); see ``static_blocks``.
     """
     scores = np.asarray(scores, dtype=np.float64)
     nq, nk = scores.shape
-    if sink_blocks < 0:
-        raise ValueError("sink_blocks must be >= 0")
-    keep = np.zeros((nq, nk), dtype=bool)
+    keep = static_blocks(nq, nk, sink_blocks, int(keep_diag))
     for i in range(nq):
         keep[i, topk_row(scores[i], k)] = True
-        keep[i, :min(sink_blocks, nk)] = True
-        if keep_diag and i < nk:
-            keep[i, i] = True
+    return keep
+
+
+def top_p_count(scores_row, p: float, scale: float = 1.0) -> int:
+    """Smallest number of best-ranked blocks whose softmax mass reaches p.
+
+    The pages name top_p_block_mask without defining it ([Adaptive tiling
+    (SPADE), "What mlx-arsenal ships"]).  Reading (the nucleus rule): the
+    row's block probabilities are softmax(scale * S_I.) over all key blocks;
+    blocks are ranked (score desc, index asc) and the shortest prefix with
+    cumulative probability >= p is kept (at least one block).  p in (0, 1].
+    """
+    if not (0.0 < p <= 1.0):
+        raise ValueError(f"p must be in (0, 1], got {p}")
+    s = np.asarray(scores_row, dtype=np.float64) * float(scale)
+    n = s.shape[0]
+    order = np.lexsort((np.arange(n), -s))
+    z = s[order]
+    w = np.exp(z - z[0])
+    cum = np.cumsum(w) / w.sum()
+    m = int(np.searchsorted(cum, p, side="left")) + 1
+    return min(max(m, 1), n)
+
+
+def top_p_block_mask(scores, p: float, sink_blocks: int = 1, diag_width: int = 1, scale: float = 1.0):
+    """Boolean (Nq, Nk) block mask: per row the top-p prefix, OR the static blocks."""
+    scores = np.asarray(scores, dtype=np.float64)
+    nq, nk = scores.shape
+    keep = static_blocks(nq, nk, sink_blocks, diag_width)
+    for i in range(nq):
+        keep[i, topk_row(scores[i], top_p_count(scores[i], p, scale))] = True
     return keep
 
 

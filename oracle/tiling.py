@@ -41,6 +41,48 @@ def tile_permutation(grid, tile) -> np.ndarray:
     return np.argsort(tile_labels(grid, tile), kind="stable").astype(np.int64)
 
 
+def padded_grid(grid, tile):
+    """The grid rounded up, axis by axis, to a multiple of the tile.
+
+    [Adaptive tiling (SPADE), "Deviations and notes"]: a grid the tile does not
+    divide is padded to a multiple of the tile with zero tokens.
+    """
+    T, Hg, Wg = (int(g) for g in grid)
+    a, b, c = (int(t) for t in tile)
+    if min(T, Hg, Wg) <= 0 or min(a, b, c) <= 0:
+        raise ValueError(f"grid {grid} and tile {tile} must be positive")
+    return -(-T // a) * a, -(-Hg // b) * b, -(-Wg // c) * c
+
+
+def pad_tokens(x, grid, tile):
+    """Zero tokens appended along every axis: (..., T*Hg*Wg, D) -> (..., T'*H'*W', D), T-major."""
+    x = np.asarray(x)
+    T, Hg, Wg = grid
+    Tp, Hp, Wp = padded_grid(grid, tile)
+    lead, d = x.shape[:-2], x.shape[-1]
+    g = x.reshape(*lead, T, Hg, Wg, d)
+    out = np.zeros((*lead, Tp, Hp, Wp, d), dtype=x.dtype)
+    out[..., :T, :Hg, :Wg, :] = g
+    return out.reshape(*lead, Tp * Hp * Wp, d)
+
+
+def padded_tile_permutation(grid, tile) -> np.ndarray:
+    """Tile order over the padded grid, as indices into the real tokens (-1 = padding).
+
+    The padded grid is labelled and stably sorted exactly like a dividing
+    grid (tile_permutation of the padded grid); each position is then mapped
+    back to its T-major index in the unpadded grid, or -1 if it is padding.
+    """
+    T, Hg, Wg = (int(g) for g in grid)
+    pg = padded_grid(grid, tile)
+    pperm = tile_permutation(pg, tile)
+    _, Hp, Wp = pg
+    t, rem = np.divmod(pperm, Hp * Wp)
+    y, x = np.divmod(rem, Wp)
+    real = (t < T) & (y < Hg) & (x < Wg)
+    return np.where(real, (t * Hg + y) * Wg + x, -1).astype(np.int64)
+
+
 def invert_permutation(perm) -> np.ndarray:
     """inv with inv[perm[p]] = p; ValueError unless perm is a bijection of 0..S-1.
 
@@ -113,12 +155,53 @@ def tiling_score(q_head, grid, tile) -> float:
     return float(coh.mean()) if coh.size else float("-inf")
 
 
-def select_tiling(q, grid, tiles):
+def tiling_score_padded(q_head, grid, tile) -> float:
+    """tiling_score on the zero-padded grid (padding has zero norm, so it is left out)."""
+    pg = padded_grid(grid, tile)
+    return tiling_score(pad_tokens(q_head, grid, tile), pg, tile)
+
+
+def pooled_tiling_score(q_head, grid, tile, pad: bool = False) -> float:
+    """SPADE engine's pooled statistic: sum of pair cosines over sum of pairs.
+
+    [Adaptive tiling (SPADE), "Deviations and notes", selection statistic]:
+    SPADE's cossim kernel pools the pairwise similarities over the whole
+    tiling (sum of pair similarities / number of pairs) and counts every
+    token, zero-norm ones included.  Readings: a pair with a zero-norm token
+    has similarity 0; on a padded grid the padding positions are not tokens
+    and are not counted (tiles then differ in size).  Brute force over the
+    ordered pairs i != j of every tile.
+    """
+    q = np.asarray(q_head, dtype=np.float64)
+    if pad:
+        perm = padded_tile_permutation(grid, tile)
+    else:
+        perm = tile_permutation(grid, tile)
+    a, b, c = tile
+    vol = a * b * c
+    num, den = 0.0, 0
+    for start in range(0, perm.shape[0], vol):
+        idx = perm[start:start + vol]
+        idx = idx[idx >= 0]
+        x = q[idx]
+        n = x.shape[0]
+        norms = np.sqrt((x * x).sum(axis=1))
+        unit = np.divide(x, norms[:, None], out=np.zeros_like(x), where=norms[:, None] > 0)
+        cos = unit @ unit.T
+        num += float(cos.sum() - np.trace(cos))
+        den += n * (n - 1)
+    return num / den if den else float("-inf")
+
+
+def select_tiling(q, grid, tiles, statistic: str = "mean", pad: bool = False):
     """Per (b, h): index of the most cohesive candidate tiling, and all scores.
 
     [Adaptive tiling (SPADE), "The idea" step 1; "What mlx-arsenal ships",
     select_tiling].  Ties go to the lowest candidate index (np.argmax takes
-    the first maximum).  Returns (choice int64 (B, H), score float64 (B, H, n)).
+    the first maximum).  statistic "mean" averages per-tile SICS (the
+    library's rule); "pooled" is SPADE's engine rule (pooled_tiling_score).
+    pad=True accepts candidates that do not divide the grid and scores them
+    on the zero-padded grid.  Returns (choice int64 (B, H), score float64 (B, H, n)).
     """
     q = np.asarray(q, dtype=np.float64)
     B, H, S, _ = q.shape
@@ -127,13 +210,23 @@ def select_tiling(q, grid, tiles):
         raise ValueError(f"grid {grid} does not match S={S}")
     if len(tiles) < 1:
         raise ValueError("need at least one candidate tiling")
+    if statistic not in ("mean", "pooled"):
+        raise ValueError(f"unknown statistic {statistic!r}")
     for t in tiles:
-        check_tile(grid, t)
+        if pad:
+            padded_grid(grid, t)
+        else:
+            check_tile(grid, t)
     score = np.empty((B, H, len(tiles)))
     for bi in range(B):
         for hi in range(H):
             for ci, t in enumerate(tiles):
-                score[bi, hi, ci] = tiling_score(q[bi, hi], grid, t)
+                if statistic == "pooled":
+                    score[bi, hi, ci] = pooled_tiling_score(q[bi, hi], grid, t, pad)
+                elif pad:
+                    score[bi, hi, ci] = tiling_score_padded(q[bi, hi], grid, t)
+                else:
+                    score[bi, hi, ci] = tiling_score(q[bi, hi], grid, t)
     return np.argmax(score, axis=-1), score
 
 
