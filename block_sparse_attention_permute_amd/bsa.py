@@ -28,7 +28,8 @@ BSA_MAX_TILINGS = 8
 EXPORTED = (
     "bsa_last_error", "bsa_version", "bsa_tile_permutation", "bsa_invert_permutation", "bsa_budget",
     "bsa_sliding_tile_block_list", "bsa_tile_permute", "bsa_invert_permute", "bsa_block_cohesion",
-    "bsa_select_tiling", "bsa_minmax_block_scores", "bsa_topk_block_mask", "bsa_block_sparse_attention",
+    "bsa_select_tiling", "bsa_minmax_block_scores", "bsa_topk_block_mask", "bsa_top_p_block_mask",
+    "bsa_block_sparse_attention",
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices",
 )
 
@@ -53,6 +54,7 @@ _SIGS = {
     "bsa_select_tiling": (_I, [_P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P]),
     "bsa_minmax_block_scores": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P]),
     "bsa_topk_block_mask": (_I, [_P, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
+    "bsa_top_p_block_mask": (_I, [_P, _I64, _I64, _I, _I, _F, _F, _I, _I, _P, _P, _I, _P, _P]),
     "bsa_block_sparse_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _F, _P]),
     "bsa_windowed_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _P]),
     "bsa_validate_block_list": (_I, [_P, _P, _I64, _I64, _I, _I, _I, _P]),
@@ -258,24 +260,60 @@ def bsa_minmax_block_scores(q, k, block: int, out=None):
     return scores, summ
 
 
-def bsa_topk_block_mask(scores, k: int, sink_blocks: int = 1, keep_diag: bool = True,
-                        max_kept: int | None = None, return_mask: bool = False, out=None):
-    """-> (kv_idx int32 (B, H, Nq, max_kept), kv_cnt int32 (B, H, Nq)[, mask uint8 (B, H, Nq, Nk)])."""
+def _band(diag_width) -> int:
+    """Diagonal band width: True/False mean 1/0 (the diagonal alone / none)."""
+    w = int(diag_width)
+    if w < 0:
+        raise ValueError(f"diag_width must be >= 0, got {diag_width}")
+    return w
+
+
+def _band_blocks(w: int) -> int:
+    return 2 * (w // 2) + 1 if w >= 1 else 0
+
+
+def _select_out(scores, max_kept, return_mask, out):
     torch = _torch()
-    if scores.dim() != 4 or scores.dtype != torch.float32:
-        raise ValueError("scores must be float32 (B, H, Nq, Nk)")
     B, H, Nq, Nk = (int(s) for s in scores.shape)
-    if max_kept is None:
-        max_kept = min(Nk, int(k) + int(sink_blocks) + (1 if keep_diag else 0))
     if out is None:
         kv_idx = torch.empty((B, H, Nq, max_kept), dtype=torch.int32, device=scores.device)
         kv_cnt = torch.empty((B, H, Nq), dtype=torch.int32, device=scores.device)
         mask = torch.empty((B, H, Nq, Nk), dtype=torch.uint8, device=scores.device) if return_mask else None
-    else:
-        kv_idx, kv_cnt, mask = out
-    _check(lib().bsa_topk_block_mask(_dev(scores, "scores"), B, H, Nq, Nk, int(k), int(sink_blocks),
-                                     1 if keep_diag else 0, _dev(kv_idx), _dev(kv_cnt), int(max_kept),
+        return kv_idx, kv_cnt, mask
+    return out
+
+
+def bsa_topk_block_mask(scores, k: int, sink_blocks: int = 1, keep_diag=True,
+                        max_kept: int | None = None, return_mask: bool = False, out=None):
+    """-> (kv_idx int32 (B, H, Nq, max_kept), kv_cnt int32 (B, H, Nq)[, mask uint8 (B, H, Nq, Nk)]).
+
+    ``keep_diag`` is the diagonal band width (True = 1, the diagonal alone)."""
+    torch = _torch()
+    if scores.dim() != 4 or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 (B, H, Nq, Nk)")
+    B, H, Nq, Nk = (int(s) for s in scores.shape)
+    w = _band(keep_diag)
+    if max_kept is None:
+        max_kept = min(Nk, int(k) + int(sink_blocks) + _band_blocks(w))
+    kv_idx, kv_cnt, mask = _select_out(scores, max_kept, return_mask, out)
+    _check(lib().bsa_topk_block_mask(_dev(scores, "scores"), B, H, Nq, Nk, int(k), int(sink_blocks), w,
+                                     _dev(kv_idx), _dev(kv_cnt), int(max_kept),
                                      None if mask is None else _dev(mask), _stream(scores)))
+    return (kv_idx, kv_cnt, mask) if return_mask else (kv_idx, kv_cnt)
+
+
+def bsa_top_p_block_mask(scores, p: float, scale: float = 1.0, sink_blocks: int = 1, diag_width=1,
+                         return_mask: bool = False, out=None):
+    """Top-p (nucleus) block selection -> (kv_idx (B, H, Nq, Nk), kv_cnt[, mask])."""
+    torch = _torch()
+    if scores.dim() != 4 or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 (B, H, Nq, Nk)")
+    B, H, Nq, Nk = (int(s) for s in scores.shape)
+    kv_idx, kv_cnt, mask = _select_out(scores, Nk, return_mask, out)
+    _check(lib().bsa_top_p_block_mask(_dev(scores, "scores"), B, H, Nq, Nk, float(p), float(scale),
+                                      int(sink_blocks), _band(diag_width), _dev(kv_idx), _dev(kv_cnt),
+                                      int(kv_idx.shape[-1]), None if mask is None else _dev(mask),
+                                      _stream(scores)))
     return (kv_idx, kv_cnt, mask) if return_mask else (kv_idx, kv_cnt)
 
 
@@ -341,9 +379,13 @@ class AdaptiveBlockSparse:
     select tiling -> permute q, k, v -> min/max scores -> top-k (+sink, +diag)
     -> block-sparse attention -> inverse permute.  Buffers are allocated once
     (torch) and reused, so a call allocates nothing and never synchronises.
+    ``keep_diag`` is the diagonal band width (True = the diagonal alone);
+    ``top_p`` replaces the top-k budget with the top-p rule (softmax of
+    ``p_scale`` * scores).
     """
 
-    def __init__(self, B, H, grid, D, tiles, frac, dtype, device, sink_blocks=1, keep_diag=True, scale=None):
+    def __init__(self, B, H, grid, D, tiles, frac, dtype, device, sink_blocks=1, keep_diag=True, scale=None,
+                 top_p=None, p_scale=1.0):
         torch = _torch()
         self.grid = tuple(int(g) for g in grid)
         self.tiles = [tuple(int(v) for v in t) for t in tiles]
@@ -355,8 +397,12 @@ class AdaptiveBlockSparse:
         self.S = T * Hg * Wg
         self.nb = self.S // self.block
         self.k = bsa_budget(frac, self.nb)
-        self.sink_blocks, self.keep_diag, self.scale = int(sink_blocks), bool(keep_diag), scale
-        self.max_kept = min(self.nb, self.k + self.sink_blocks + (1 if keep_diag else 0))
+        self.sink_blocks, self.keep_diag, self.scale = int(sink_blocks), _band(keep_diag), scale
+        self.top_p, self.p_scale = top_p, float(p_scale)
+        if top_p is None:
+            self.max_kept = min(self.nb, self.k + self.sink_blocks + _band_blocks(self.keep_diag))
+        else:
+            self.max_kept = self.nb
         f = dict(device=device)
         n = len(self.tiles)
         self.ws_select = (torch.empty((B, H, n, self.nb), dtype=torch.float32, **f),
@@ -381,8 +427,12 @@ class AdaptiveBlockSparse:
         for src, dst in ((q, self.qp), (k, self.kp), (v, self.vp)):
             bsa_tile_permute(src, self.grid, self.tiles, head_choice=choice, out=dst)
         scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores)
-        kv_idx, kv_cnt, _ = bsa_topk_block_mask(scores, self.k, self.sink_blocks, self.keep_diag,
-                                                max_kept=self.max_kept, return_mask=True, out=self.ws_topk)
+        if self.top_p is None:
+            kv_idx, kv_cnt, _ = bsa_topk_block_mask(scores, self.k, self.sink_blocks, self.keep_diag,
+                                                    max_kept=self.max_kept, return_mask=True, out=self.ws_topk)
+        else:
+            kv_idx, kv_cnt, _ = bsa_top_p_block_mask(scores, self.top_p, self.p_scale, self.sink_blocks,
+                                                     self.keep_diag, return_mask=True, out=self.ws_topk)
         if attention_hook is not None:
             attention_hook(True)
         bsa_block_sparse_attention(self.qp, self.kp, self.vp, kv_idx, kv_cnt, self.block, self.scale, out=self.op)

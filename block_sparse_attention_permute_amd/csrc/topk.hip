@@ -1,18 +1,29 @@
-// Per-row top-k block selection with sink and diagonal blocks: bsa_topk_block_mask.
+// Per-row block selection with sink and diagonal blocks: bsa_topk_block_mask
+// (a fixed budget) and bsa_top_p_block_mask (a probability-mass budget).
 //
 // [Adaptive tiling (SPADE), "The idea" step 4]: a fixed budget of k key blocks
-// is kept per query block, and the sink and diagonal blocks are always kept
-// ([Adaptive tiling (SPADE), "Recipe"]: they are ORed into the top-k mask).
+// is kept per query block, and the sink blocks and a diagonal band are always
+// kept ([Adaptive tiling (SPADE), "Recipe"]: they are ORed into the top-k
+// mask; SPADE's Wan configurations use a sink width of 5 and a band width of
+// 40).  A band of width w keeps key blocks J with abs(I - J) <= w / 2, so
+// width 1 is the diagonal alone.  The top-p variant (named among the
+// library's block masks on the same page) keeps the shortest best-ranked
+// prefix whose softmax probability mass reaches p.
 //
 // Design: one wave per row, the row's scores held in registers (element
 // e = i*64 + lane).  Scores map to order-preserving unsigned keys (-0.0 as
-// +0.0, NaN lowest), the k-th largest key is found by a 32-step bitwise
-// search with wave-wide counts, and ties at the threshold are resolved to
-// the lowest indices with ballots.  The kept set comes out in ascending
-// index order as a compact list (what the attention kernel walks) and,
-// optionally, as a byte mask.  Selection is exact: for the same fp32
-// scores it is bit-identical to a sort by (score desc, index asc).
+// +0.0, NaN lowest), the threshold key is found by a 32-step bitwise search
+// with wave-wide counts (top-k) or wave-wide probability mass (top-p), and
+// ties at the threshold are resolved to the lowest indices with ballots.
+// The kept set comes out in ascending index order as a compact list (what
+// the attention kernel walks) and, optionally, as a byte mask.  Top-k
+// selection is exact: for the same fp32 scores it is bit-identical to a sort
+// by (score desc, index asc).  Top-p sums fp32 weights (the butterfly sums
+// are identical in every lane), so its cut can differ from a float64 one
+// only where the cumulative mass lies within rounding of p.
 #include "common.h"
+
+#include <cmath>
 
 namespace bsa {
 namespace {
@@ -22,7 +33,9 @@ struct TopkParams {
     int32_t* kv_idx;
     int32_t* kv_cnt;
     uint8_t* mask;
-    uint32_t nq, nk, k, sink, keep_diag, max_kept;
+    uint32_t nq, nk, k, sink, max_kept;
+    int32_t diag_half;  // band half-width; -1: no band
+    float p, scale_log2;  // top-p only
     uint64_t rows;
 };
 
@@ -40,10 +53,23 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return v;
 }
 
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
-// VPL = values per lane (the row length is at most 64 * VPL).
-template <int VPL>
+// VPL = values per lane (the row length is at most 64 * VPL).  TOPP selects
+// by probability mass instead of by count.
+template <int VPL, bool TOPP>
 __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
     const int lane = threadIdx.x & 63;
     const uint64_t row = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -60,19 +86,60 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
         valid[i] = e < P.nk;
         key[i] = valid[i] ? order_key(s[e]) : 0u;
     }
-    // k-th largest key T: the largest T with count(key >= T) >= k
+    // TOPP: softmax weights w = exp(scale * (s - max)); NaN and -inf weigh 0
+    float w[VPL];
+    float target = (float)P.k;
+    if (TOPP) {
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (valid[i] && key[i] != 0u) m = fmaxf(m, s[i * 64 + lane]);
+        m = wave_max_f(m);
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const float x = valid[i] ? s[i * 64 + lane] : 0.f;
+            w[i] = (!valid[i] || key[i] == 0u) ? 0.f : (x == m ? 1.f : __builtin_amdgcn_exp2f((x - m) * P.scale_log2));
+            z += w[i];
+        }
+        target = P.p * wave_sum_f(z);
+    }
+    // threshold key T: the largest T with count (or mass) of keys >= T reaching the target
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = T | (1u << bit);
-        uint32_t c = 0;
+        if (TOPP) {
+            float c = 0.f;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) c += (valid[i] && key[i] >= cand) ? 1u : 0u;
-        if (wave_sum(c) >= P.k) T = cand;
+            for (int i = 0; i < VPL; ++i) c += (valid[i] && key[i] >= cand) ? w[i] : 0.f;
+            if (wave_sum_f(c) >= target) T = cand;
+        } else {
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) c += (valid[i] && key[i] >= cand) ? 1u : 0u;
+            if (wave_sum(c) >= P.k) T = cand;
+        }
     }
-    uint32_t gt = 0;
+    uint32_t need;  // ties at T to take, lowest index first
+    if (TOPP) {
+        float gt = 0.f, wt = 0.f;
+        uint32_t nt = 0;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) gt += (valid[i] && key[i] > T) ? 1u : 0u;
-    const uint32_t need = P.k - wave_sum(gt);  // ties at T to take, lowest index first
+        for (int i = 0; i < VPL; ++i) {
+            gt += (valid[i] && key[i] > T) ? w[i] : 0.f;
+            if (valid[i] && key[i] == T) { wt = w[i]; ++nt; }
+        }
+        gt = wave_sum_f(gt);
+        wt = wave_max_f(wt);
+        nt = wave_sum(nt);
+        const float t = wt > 0.f ? ceilf((target - gt) / wt) : 1.f;
+        need = (uint32_t)fminf(fmaxf(t, 1.f), (float)nt);
+    } else {
+        uint32_t gt = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) gt += (valid[i] && key[i] > T) ? 1u : 0u;
+        need = P.k - wave_sum(gt);
+    }
 
     bool keep[VPL];
     uint32_t tie_seen = 0;
@@ -83,7 +150,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
         const uint32_t rank = tie_seen + popc64(m & lt_mask);
         tie_seen += popc64(m);
         const uint32_t e = i * 64 + lane;
-        keep[i] = valid[i] && (key[i] > T || (tie && rank < need) || e < P.sink || (P.keep_diag && e == I));
+        const int d = (int)e - (int)I;
+        keep[i] = valid[i] &&
+                  (key[i] > T || (tie && rank < need) || e < P.sink || (d <= P.diag_half && -d <= P.diag_half));
     }
     int32_t* out = P.kv_idx + row * P.max_kept;
     uint32_t pos = 0;
@@ -104,8 +173,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
 
 using namespace bsa;
 
+namespace bsa {
+namespace {
+
+int band_width(int diag_width) { return diag_width >= 1 ? 2 * (diag_width / 2) + 1 : 0; }
+
+template <bool TOPP>
+int launch_select(TopkParams& P, hipStream_t st, const char* name) {
+    const uint64_t blocks = (P.rows + 3) / 4;
+    BSA_REQUIRE(blocks < ((uint64_t)1 << 31), "%s: too many rows", name);
+    const int vpl = ((int)P.nk + 63) / 64;
+    if (vpl <= 8)
+        topk_kernel<8, TOPP><<<(unsigned)blocks, 256, 0, st>>>(P);
+    else if (vpl <= 16)
+        topk_kernel<16, TOPP><<<(unsigned)blocks, 256, 0, st>>>(P);
+    else if (vpl <= 32)
+        topk_kernel<32, TOPP><<<(unsigned)blocks, 256, 0, st>>>(P);
+    else
+        topk_kernel<64, TOPP><<<(unsigned)blocks, 256, 0, st>>>(P);
+    return check_launch(name);
+}
+
+}  // namespace
+}  // namespace bsa
+
 extern "C" int bsa_topk_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int Nk, int k, int sink_blocks,
-                                   int keep_diag, int32_t* kv_idx, int32_t* kv_cnt, int max_kept,
+                                   int diag_width, int32_t* kv_idx, int32_t* kv_cnt, int max_kept,
                                    uint8_t* mask_or_null, bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_topk_block_mask";
@@ -114,10 +207,11 @@ extern "C" int bsa_topk_block_mask(const float* scores, int64_t B, int64_t H, in
     BSA_REQUIRE(Nk >= 1 && Nk <= 4096, "%s: Nk=%d must be in [1, 4096]", name, Nk);
     BSA_REQUIRE(k >= 1 && k <= Nk, "%s: k=%d must be in [1, Nk=%d]", name, k, Nk);
     BSA_REQUIRE(sink_blocks >= 0, "%s: sink_blocks must be >= 0", name);
-    const int64_t widest = std::min<int64_t>(Nk, (int64_t)k + sink_blocks + (keep_diag ? 1 : 0));
-    BSA_REQUIRE(max_kept >= widest, "%s: max_kept=%d < %lld (k + sink + diagonal, at most Nk)", name, max_kept,
+    BSA_REQUIRE(diag_width >= 0, "%s: diag_width must be >= 0", name);
+    const int64_t widest = std::min<int64_t>(Nk, (int64_t)k + sink_blocks + band_width(diag_width));
+    BSA_REQUIRE(max_kept >= widest, "%s: max_kept=%d < %lld (k + sink + band, at most Nk)", name, max_kept,
                 (long long)widest);
-    TopkParams P;
+    TopkParams P{};
     P.scores = scores;
     P.kv_idx = kv_idx;
     P.kv_cnt = kv_cnt;
@@ -126,20 +220,38 @@ extern "C" int bsa_topk_block_mask(const float* scores, int64_t B, int64_t H, in
     P.nk = (uint32_t)Nk;
     P.k = (uint32_t)k;
     P.sink = (uint32_t)std::min(sink_blocks, Nk);
-    P.keep_diag = keep_diag ? 1u : 0u;
+    P.diag_half = diag_width >= 1 ? diag_width / 2 : -1;
     P.max_kept = (uint32_t)max_kept;
     P.rows = (uint64_t)B * H * Nq;
-    const uint64_t blocks = (P.rows + 3) / 4;
-    BSA_REQUIRE(blocks < ((uint64_t)1 << 31), "%s: too many rows", name);
-    hipStream_t st = (hipStream_t)stream;
-    const int vpl = (Nk + 63) / 64;
-    if (vpl <= 8)
-        topk_kernel<8><<<(unsigned)blocks, 256, 0, st>>>(P);
-    else if (vpl <= 16)
-        topk_kernel<16><<<(unsigned)blocks, 256, 0, st>>>(P);
-    else if (vpl <= 32)
-        topk_kernel<32><<<(unsigned)blocks, 256, 0, st>>>(P);
-    else
-        topk_kernel<64><<<(unsigned)blocks, 256, 0, st>>>(P);
-    return check_launch(name);
+    return launch_select<false>(P, (hipStream_t)stream, name);
+}
+
+extern "C" int bsa_top_p_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int Nk, float p, float scale,
+                                    int sink_blocks, int diag_width, int32_t* kv_idx, int32_t* kv_cnt, int max_kept,
+                                    uint8_t* mask_or_null, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_top_p_block_mask";
+    BSA_REQUIRE(scores && kv_idx && kv_cnt, "%s: NULL argument", name);
+    BSA_REQUIRE(B >= 1 && H >= 1 && Nq >= 1, "%s: B, H, Nq must be >= 1", name);
+    BSA_REQUIRE(Nk >= 1 && Nk <= 4096, "%s: Nk=%d must be in [1, 4096]", name, Nk);
+    BSA_REQUIRE(p > 0.f && p <= 1.f, "%s: p=%g must be in (0, 1]", name, (double)p);
+    BSA_REQUIRE(scale > 0.f && std::isfinite(scale), "%s: scale must be positive and finite", name);
+    BSA_REQUIRE(sink_blocks >= 0, "%s: sink_blocks must be >= 0", name);
+    BSA_REQUIRE(diag_width >= 0, "%s: diag_width must be >= 0", name);
+    BSA_REQUIRE(max_kept >= Nk, "%s: max_kept=%d must be >= Nk=%d (top-p can keep every block)", name, max_kept, Nk);
+    TopkParams P{};
+    P.scores = scores;
+    P.kv_idx = kv_idx;
+    P.kv_cnt = kv_cnt;
+    P.mask = mask_or_null;
+    P.nq = (uint32_t)Nq;
+    P.nk = (uint32_t)Nk;
+    P.k = 1;
+    P.sink = (uint32_t)std::min(sink_blocks, Nk);
+    P.diag_half = diag_width >= 1 ? diag_width / 2 : -1;
+    P.max_kept = (uint32_t)max_kept;
+    P.p = p;
+    P.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    P.rows = (uint64_t)B * H * Nq;
+    return launch_select<true>(P, (hipStream_t)stream, name);
 }

@@ -159,18 +159,35 @@ int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, 
 
 /* Per-row block selection: keep the k best key blocks of each (b, h, I) row,
  * ranked by score (higher first) and then by index (lower first), then add
- * key blocks 0 .. sink_blocks-1 and, if keep_diag, block J = I (when I < Nk)
+ * key blocks 0 .. sink_blocks-1 and the diagonal band abs(J - I) <= diag_width/2
+ * (integer division; diag_width 1 = block J = I alone, 0 = no band)
  * [Adaptive tiling (SPADE), "The idea" step 4 and "Recipe": top-k budget,
- * sink and diagonal blocks ORed into the mask].  -0.0 ranks as +0.0 and NaN
- * below every number.
+ * sink blocks and a diagonal band ORed into the mask; SPADE's Wan widths are
+ * 5 and 40].  -0.0 ranks as +0.0 and NaN below every number.
  * scores: device float (B, H, Nq, Nk).  kv_idx: device int32
  * (B, H, Nq, max_kept): kept indices ascending, then -1.  kv_cnt: device int32
  * (B, H, Nq).  mask_or_null: device uint8 (B, H, Nq, Nk), 1 = kept, or NULL.
- * INVALID_ARG unless 1 <= k <= Nk, 1 <= Nk <= 4096, sink_blocks >= 0 and
- * max_kept >= min(Nk, k + sink_blocks + (keep_diag != 0)). */
+ * INVALID_ARG unless 1 <= k <= Nk, 1 <= Nk <= 4096, sink_blocks >= 0,
+ * diag_width >= 0 and max_kept >= min(Nk, k + sink_blocks + band), where
+ * band = 2*(diag_width/2) + 1 (0 when diag_width = 0). */
 int bsa_topk_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int Nk, int k,
-                        int sink_blocks, int keep_diag, int32_t* kv_idx, int32_t* kv_cnt,
+                        int sink_blocks, int diag_width, int32_t* kv_idx, int32_t* kv_cnt,
                         int max_kept, uint8_t* mask_or_null, bsa_stream_t stream);
+
+/* Per-row block selection by probability mass (top-p; the pages name
+ * top_p_block_mask among the block masks [Adaptive tiling (SPADE), "What
+ * mlx-arsenal ships"] without defining it; the nucleus rule is used): the
+ * row's block probabilities are softmax(scale * scores[b,h,I,:]); blocks are
+ * ranked as in bsa_topk_block_mask and the shortest prefix whose cumulative
+ * probability reaches p is kept (at least one block), then the sink blocks
+ * and the diagonal band are added.  Weights and sums are fp32; NaN scores
+ * weigh 0.  Arguments and outputs as bsa_topk_block_mask.
+ * INVALID_ARG unless 0 < p <= 1, scale > 0, 1 <= Nk <= 4096, sink_blocks >= 0,
+ * diag_width >= 0 and max_kept >= Nk. */
+int bsa_top_p_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int Nk, float p,
+                         float scale, int sink_blocks, int diag_width, int32_t* kv_idx,
+                         int32_t* kv_cnt, int max_kept, uint8_t* mask_or_null,
+                         bsa_stream_t stream);
 
 /* Block-sparse attention: for every query block I of `block` tokens,
  *   out_I = softmax(scale * q_I k_K^T) v_K,  K = the tokens of the key blocks

@@ -136,6 +136,7 @@ def top_p_count(scores_row, p: float, scale: float = 1.0) -> int:
     row's block probabilities are softmax(scale * S_I.) over all key blocks;
     blocks are ranked (score desc, index asc) and the shortest prefix with
     cumulative probability >= p is kept (at least one block).  p in (0, 1].
+    NaN scores rank last (as in topk_row) and carry no probability.
     """
     if not (0.0 < p <= 1.0):
         raise ValueError(f"p must be in (0, 1], got {p}")
@@ -144,6 +145,7 @@ def top_p_count(scores_row, p: float, scale: float = 1.0) -> int:
     order = np.lexsort((np.arange(n), -s))
     z = s[order]
     w = np.exp(z - z[0])
+    w = np.where(np.isnan(z), 0.0, w)   # NaN scores rank last and weigh nothing
     cum = np.cumsum(w) / w.sum()
     m = int(np.searchsorted(cum, p, side="left")) + 1
     return min(max(m, 1), n)

@@ -31,3 +31,28 @@ def bits(t):
 
 def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+TOPP_REL = 1e-5    # relative distance of the cumulative mass from p under which a top-p cut may differ
+
+
+def top_p_row_ok(gpu_row, scores_row, p, scale, static_row, rel=TOPP_REL):
+    """True if the GPU's kept row equals the oracle's top-p row, or differs
+    only by moving the cut where the oracle's cumulative mass is within
+    ``rel`` of p.  gpu_row, static_row: bool (Nk,); scores_row: float64."""
+    from oracle import blocks as OB
+    nk = scores_row.shape[0]
+    want = OB.top_p_block_mask(scores_row[None, :], p, 0, 0, scale)[0] | static_row
+    if np.array_equal(gpu_row, want):
+        return True
+    row = scores_row * scale
+    order = np.lexsort((np.arange(nk), -row))
+    w = np.exp(row[order] - row[order][0])
+    w = np.where(np.isnan(row[order]), 0.0, w)
+    cum = np.cumsum(w) / w.sum()
+    cuts = [c for c in range(1, nk + 1) if np.array_equal(np.isin(np.arange(nk), order[:c]) | static_row, gpu_row)]
+    if not cuts:
+        return False
+    mo = OB.top_p_count(scores_row, p, scale)
+    c = min(cuts, key=lambda x: abs(x - mo))
+    return abs(cum[min(c, mo) - 1] - p) <= rel * p

@@ -121,6 +121,16 @@ def test_device_calls_reject_bad_arguments(L):
         ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 481, 1, 1, FAKE, FAKE, 483, None, None), "k=481"),
         ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 81, 1, 1, FAKE, FAKE, 82, None, None), "max_kept"),
         ("bsa_topk_block_mask", (FAKE, 1, 1, 4, 5000, 81, 1, 1, FAKE, FAKE, 83, None, None), "Nk"),
+        ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 81, 5, 40, FAKE, FAKE, 126, None, None), "max_kept"),
+        ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 81, 1, -1, FAKE, FAKE, 83, None, None), "diag_width"),
+        ("bsa_top_p_block_mask", (FAKE, 1, 1, 480, 480, ctypes.c_float(0.0), ctypes.c_float(1.0), 1, 1, FAKE, FAKE,
+                                  480, None, None), "p="),
+        ("bsa_top_p_block_mask", (FAKE, 1, 1, 480, 480, ctypes.c_float(1.5), ctypes.c_float(1.0), 1, 1, FAKE, FAKE,
+                                  480, None, None), "p="),
+        ("bsa_top_p_block_mask", (FAKE, 1, 1, 480, 480, ctypes.c_float(0.5), ctypes.c_float(0.0), 1, 1, FAKE, FAKE,
+                                  480, None, None), "scale"),
+        ("bsa_top_p_block_mask", (FAKE, 1, 1, 480, 480, ctypes.c_float(0.5), ctypes.c_float(1.0), 1, 1, FAKE, FAKE,
+                                  479, None, None), "max_kept"),
         ("bsa_block_sparse_attention",
          (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 100, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None), "divide"),
         ("bsa_block_sparse_attention",

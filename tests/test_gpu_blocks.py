@@ -5,7 +5,7 @@ import pytest
 from block_sparse_attention_permute_amd import bsa, synth
 from oracle import blocks as OB
 from oracle import tiling as OT
-from tests.gpu_helpers import TOPK_REL, bits, f64, gpu, torch_gpu
+from tests.gpu_helpers import TOPK_REL, bits, f64, gpu, top_p_row_ok, torch_gpu
 
 WAN_GRID, WAN_TILES = (20, 32, 48), [(1, 8, 8), (4, 4, 4)]
 
@@ -156,3 +156,68 @@ def test_topk_workload_widths(Nq, Nk, k, sink):
     s[..., ::7] = np.round(s[..., ::7])                      # sprinkle exact ties
     idx, cnt = _check_topk(s, k, sink, True)
     assert cnt.min() >= k and cnt.max() <= min(Nk, k + sink + 1)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("sink,width", [(5, 40), (0, 0), (2, 2), (1, 3), (0, 1000)])
+def test_topk_sink_and_band_widths(sink, width):
+    """SPADE's static widths (sink 5, band 40 at the Wan shape) and edge widths, bit-exact."""
+    rng = np.random.default_rng(width + 7)
+    s = rng.standard_normal((1, 2, 480, 480)) * 50
+    idx, cnt = _check_topk(s, 81, sink, width)
+    band = 2 * (width // 2) + 1 if width else 0
+    assert cnt.max() <= min(480, 81 + sink + band)
+
+
+# ------------------------------------------------------------------ top-p ---
+
+def _check_top_p(scores_np, p, scale, sink, width):
+    """GPU top-p against the oracle, row by row (tests.gpu_helpers.top_p_row_ok)."""
+    torch = torch_gpu()
+    s32 = scores_np.astype(np.float32)
+    s = torch.from_numpy(s32).cuda()
+    kv_idx, kv_cnt, mask = bsa.bsa_top_p_block_mask(s, p, scale, sink, width, return_mask=True)
+    idx, cnt, m = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), mask.cpu().numpy().astype(bool)
+    B, H, Nq, Nk = scores_np.shape
+    for b in range(B):
+        for h in range(H):
+            sf = s32[b, h].astype(np.float64)
+            static = OB.static_blocks(Nq, Nk, sink, width)
+            for I in range(Nq):
+                li = np.flatnonzero(m[b, h, I])
+                assert cnt[b, h, I] == li.size and np.array_equal(idx[b, h, I, :li.size], li)
+                assert np.all(idx[b, h, I, li.size:] == -1)
+                assert top_p_row_ok(m[b, h, I], sf[I], p, scale, static[I]), (b, h, I)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("p,scale", [(0.5, 1.0), (0.9, 1.0), (0.99, 0.3), (0.2, 3.0)])
+def test_top_p_random_rows(p, scale):
+    rng = np.random.default_rng(int(p * 100))
+    s = rng.standard_normal((1, 2, 40, 200)) * 3
+    _check_top_p(s, p, scale, 1, 1)
+
+
+@pytest.mark.gpu
+def test_top_p_ties_uniform_and_special_values():
+    rng = np.random.default_rng(11)
+    _check_top_p(rng.integers(-2, 3, (1, 1, 30, 64)).astype(np.float64), 0.6, 1.0, 0, 0)   # many exact ties
+    _check_top_p(np.zeros((1, 1, 4, 10)), 0.35, 1.0, 0, 0)                               # uniform: ceil(p n)
+    _check_top_p(np.zeros((1, 1, 4, 10)), 1.0, 1.0, 0, 0)                                # p = 1 keeps all
+    s = np.array([[[[np.nan, 0.5, -np.inf, 2.0, 2.0, -1.0, np.nan, 0.0]]]])
+    for p in (0.1, 0.5, 0.8, 0.999):
+        _check_top_p(np.broadcast_to(s, (1, 1, 3, 8)).copy(), p, 1.0, 1, 1)
+
+
+@pytest.mark.gpu
+def test_top_p_wan_shape_scores():
+    """Min/max scores of the Wan-shape inputs (a sample of heads) under the
+    softmax scale: counts vary per row and include the static blocks."""
+    torch = torch_gpu()
+    heads = [0, 5]
+    q = synth.tensor_bits(4, synth.ROLE_Q, heads=heads)
+    k = synth.tensor_bits(4, synth.ROLE_K, heads=heads)
+    qp, kp = (bsa.bsa_tile_permute(gpu(x), WAN_GRID, [(4, 4, 4)]) for x in (q, k))
+    scores, _ = bsa.bsa_minmax_block_scores(qp, kp, 64)
+    s = scores.cpu().numpy().astype(np.float64)
+    _check_top_p(s[:, :, :48], 0.9, 128 ** -0.5, 5, 40)

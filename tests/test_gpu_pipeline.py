@@ -12,7 +12,7 @@ from oracle import attention as OA
 from oracle import blocks as OB
 from oracle import pipeline as OP
 from oracle import tiling as OT
-from tests.gpu_helpers import BF16_ATOL, TOPK_REL, f64, gpu, max_abs, torch_gpu
+from tests.gpu_helpers import BF16_ATOL, TOPK_REL, f64, gpu, max_abs, top_p_row_ok, torch_gpu
 
 SETUPS = {
     4: dict(tiles=[(1, 8, 8), (4, 4, 4)], frac=0.17, heads=[0, 7, 22, 39]),
@@ -30,13 +30,15 @@ def _sample_rows(cnt_row, nb, block, rng):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("cfg", [4, 5])
-def test_adaptive_pipeline_full_size(cfg):
+@pytest.mark.parametrize("cfg,sink,width", [(4, 1, 1), (5, 1, 1), (4, 5, 40)])
+def test_adaptive_pipeline_full_size(cfg, sink, width):
+    """(4, 5, 40): SPADE's static widths for Wan (sink 5, diagonal band 40)."""
     torch = torch_gpu()
     wl, st = synth.WORKLOADS[cfg], SETUPS[cfg]
     q, k, v = synth.qkv(cfg)
     qg, kg, vg = gpu(q), gpu(k), gpu(v)
-    pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, st["tiles"], st["frac"], qg.dtype, qg.device)
+    pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, st["tiles"], st["frac"], qg.dtype, qg.device,
+                                   sink_blocks=sink, keep_diag=width)
     out = pipe(qg, kg, vg)
     torch.cuda.synchronize()
     kv_idx, kv_cnt = pipe.kv
@@ -44,7 +46,8 @@ def test_adaptive_pipeline_full_size(cfg):
     choice = pipe.choice.cpu().numpy()
     idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
     assert pipe.k == OB.budget(st["frac"], pipe.nb) == (81 if cfg == 4 else 192)
-    assert cnt.min() >= pipe.k and cnt.max() <= pipe.k + 2
+    band = 2 * (width // 2) + 1
+    assert cnt.min() >= pipe.k and cnt.max() <= pipe.k + sink + band
     outf = None
     rng = np.random.default_rng(cfg)
     scale = wl.D ** -0.5
@@ -60,12 +63,13 @@ def test_adaptive_pipeline_full_size(cfg):
         qp, kp, vp = (OT.permute_tokens(x, perm) for x in (qf, kf, vf))
         # kept lists: oracle top-k on oracle scores, differences only at near ties
         scores = OB.minmax_block_scores(qp, kp, pipe.block)
-        okeep = OB.topk_block_mask(scores, pipe.k, 1, True)
+        okeep = OB.topk_block_mask(scores, pipe.k, sink, width)
+        static = OB.static_blocks(pipe.nb, pipe.nb, sink, width)
         gkeep = np.zeros_like(okeep)
         for I in range(pipe.nb):
             gkeep[I, idx[0, h, I, :cnt[0, h, I]]] = True
         for I, J in zip(*np.nonzero(okeep != gkeep)):
-            assert J != 0 and J != I
+            assert not static[I, J]
             assert OB.near_tie_ok(scores[I], pipe.k, J, TOPK_REL), (h, I, J)
         # sampled rows of the output (T-major), attended over the GPU's kept lists
         rows_p = _sample_rows(cnt[0, h], pipe.nb, pipe.block, rng)
@@ -100,3 +104,37 @@ def test_adaptive_pipeline_small_grid_every_output():
             gkeep[I, idx[0, h, I, :cnt[0, h, I]]] = True
         if np.array_equal(gkeep, ref["keep"][0, h]):
             assert max_abs(out[0, h], ref["out"][0, h]) <= BF16_ATOL, h
+
+
+@pytest.mark.gpu
+def test_adaptive_pipeline_top_p_small_grid():
+    """Top-p instead of top-k (p = 0.9 of the softmax of scores / sqrt(D)),
+    with SPADE-style static blocks, on a grid the oracle runs whole."""
+    torch = torch_gpu()
+    grid, tiles = (4, 16, 16), [(1, 8, 8), (4, 4, 4)]
+    H, D, p = 3, 128, 0.9
+    q, k, v = (synth.normal_bits((1, H, 1024, D), seed=600 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    pipe = bsa.AdaptiveBlockSparse(1, H, grid, D, tiles, 0.25, qg.dtype, qg.device, sink_blocks=2, keep_diag=3,
+                                   top_p=p, p_scale=D ** -0.5)
+    out = f64(pipe(qg, kg, vg))
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (q, k, v))
+    ref = OP.adaptive_block_sparse(qf, kf, vf, grid, tiles, 0.25, sink_blocks=2, keep_diag=3, top_p=p,
+                                   p_scale=D ** -0.5)
+    choice = pipe.choice.cpu().numpy()
+    kv_idx, kv_cnt = pipe.kv
+    idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    static = OB.static_blocks(16, 16, 2, 3)
+    for h in range(H):
+        assert choice[0, h] == ref["choice"][0, h]
+        gkeep = np.zeros((16, 16), bool)
+        for I in range(16):
+            gkeep[I, idx[0, h, I, :cnt[0, h, I]]] = True
+        # GPU scores (fp32) against the oracle's: the kept rows agree up to the cut tolerance
+        for I in range(16):
+            assert top_p_row_ok(gkeep[I], ref["scores"][0, h, I], p, D ** -0.5, static[I]), (h, I)
+        perm = ref["perm"][0, h]
+        qp, kp, vp = (OT.permute_tokens(x[0, h], perm) for x in (qf, kf, vf))
+        want = OT.unpermute_tokens(OA.block_sparse_attention(qp[None, None], kp[None, None], vp[None, None],
+                                                             gkeep[None, None], 64, D ** -0.5)[0, 0], perm)
+        assert max_abs(out[0, h], want) <= BF16_ATOL, h
