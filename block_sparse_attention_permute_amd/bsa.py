@@ -23,13 +23,16 @@ LIB_PATH = os.path.join(_HERE, "libbsa.so")
 
 BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_INVARIANT, BSA_ERR_UNSUPPORTED, BSA_ERR_DEVICE = range(5)
 BSA_F32, BSA_BF16 = 0, 1
+BSA_STAT_MEAN, BSA_STAT_POOLED = 0, 1
 BSA_MAX_TILINGS = 8
 
 EXPORTED = (
     "bsa_last_error", "bsa_version", "bsa_tile_permutation", "bsa_invert_permutation", "bsa_budget",
     "bsa_sliding_tile_block_list", "bsa_tile_permute", "bsa_invert_permute", "bsa_block_cohesion",
     "bsa_select_tiling", "bsa_minmax_block_scores", "bsa_topk_block_mask", "bsa_top_p_block_mask",
-    "bsa_block_sparse_attention",
+    "bsa_block_sparse_attention", "bsa_padded_length", "bsa_tile_permutation_padded", "bsa_label_block_list",
+    "bsa_tile_permute_padded", "bsa_invert_permute_padded", "bsa_select_tiling_ex",
+    "bsa_minmax_block_scores_masked", "bsa_topk_block_mask_tiled", "bsa_block_sparse_attention_labels",
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices",
 )
 
@@ -59,6 +62,16 @@ _SIGS = {
     "bsa_windowed_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _P]),
     "bsa_validate_block_list": (_I, [_P, _P, _I64, _I64, _I, _I, _I, _P]),
     "bsa_validate_indices": (_I, [_P, _I64, _I, _I, _P]),
+    "bsa_padded_length": (_I64, [_I, _I, _I, _I, _I, _I]),
+    "bsa_tile_permutation_padded": (_I, [_I, _I, _I, _I, _I, _I, _P]),
+    "bsa_label_block_list": (_I, [_P, _I64, _I, _P, _P, _I]),
+    "bsa_tile_permute_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _I64, _P, _P]),
+    "bsa_invert_permute_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _I64, _P]),
+    "bsa_select_tiling_ex": (_I, [_P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "bsa_minmax_block_scores_masked": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P]),
+    "bsa_topk_block_mask_tiled": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _P]),
+    "bsa_block_sparse_attention_labels": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _P,
+                                               _I64, _F, _P]),
 }
 
 
@@ -179,6 +192,39 @@ def bsa_sliding_tile_block_list(tile_grid, radius=(1, 1, 1), max_kept: int | Non
     return idx, cnt
 
 
+def bsa_padded_length(T: int, Hg: int, Wg: int, tile) -> int:
+    """Host: length of the grid padded up to a multiple of the tile."""
+    a, b, c = (int(v) for v in tile)
+    n = int(lib().bsa_padded_length(int(T), int(Hg), int(Wg), a, b, c))
+    if n < 0:
+        raise ValueError(lib().bsa_last_error().decode())
+    return n
+
+
+def bsa_tile_permutation_padded(T: int, Hg: int, Wg: int, tile) -> np.ndarray:
+    """Host: tile order of the padded grid, the real token of each position or -1."""
+    a, b, c = (int(v) for v in tile)
+    out = np.empty(max(bsa_padded_length(T, Hg, Wg, tile), 1), dtype=np.int32)
+    _check(lib().bsa_tile_permutation_padded(int(T), int(Hg), int(Wg), a, b, c, out.ctypes.data))
+    return out
+
+
+def bsa_label_block_list(labels, block: int, max_kept: int | None = None):
+    """Host: (kv_idx int32 (Nb, max_kept), kv_cnt int32 (Nb,)) keeping blocks that share a label."""
+    lab = np.ascontiguousarray(labels, dtype=np.int32).ravel()
+    S = lab.size
+    if block < 1 or S % block:
+        raise ValueError(f"block {block} must divide S={S}")
+    nb = S // block
+    mk = nb if max_kept is None else int(max_kept)
+    idx = np.empty((nb, max(mk, 1)), dtype=np.int32)
+    cnt = np.empty(nb, dtype=np.int32)
+    _check(lib().bsa_label_block_list(lab.ctypes.data, S, int(block), idx.ctypes.data, cnt.ctypes.data, mk))
+    if max_kept is None:
+        idx = np.ascontiguousarray(idx[:, :max(int(cnt.max()), 1)])
+    return idx, cnt
+
+
 # ---------------------------------------------------------- device calls ---
 
 def _permute(fn, x, grid, tiles, head_choice, out):
@@ -210,6 +256,55 @@ def bsa_invert_permute(y, grid, tiles, head_choice=None, out=None):
     return _permute(lib().bsa_invert_permute, y, grid, tiles, head_choice, out)
 
 
+def padded_rows(grid, tiles) -> int:
+    """Rows per head of a padded permutation covering every candidate."""
+    T, Hg, Wg = (int(g) for g in grid)
+    return max(bsa_padded_length(T, Hg, Wg, t) for t in tiles)
+
+
+def bsa_tile_permute_padded(x, grid, tiles, head_choice=None, Sp=None, out=None, labels=True):
+    """Padded tile order -> (y (B, H, Sp, D) with zero padding rows, labels int32 (B, H, Sp) or None)."""
+    torch = _torch()
+    B, H, S, D = _bhsd(x, "x")
+    T, Hg, Wg = (int(g) for g in grid)
+    if T * Hg * Wg != S:
+        raise ValueError(f"grid {tuple(grid)} does not match S={S}")
+    arr, n = _tiles_arr(tiles)
+    Sp = padded_rows(grid, tiles) if Sp is None else int(Sp)
+    if out is None:
+        y = torch.empty((B, H, Sp, D), dtype=x.dtype, device=x.device)
+        lab = torch.empty((B, H, Sp), dtype=torch.int32, device=x.device) if labels else None
+    else:
+        y, lab = out
+    if tuple(y.shape) != (B, H, Sp, D) or y.dtype != x.dtype:
+        raise ValueError("out must be (B, H, Sp, D) of x's dtype")
+    hc = None
+    if head_choice is not None:
+        if head_choice.dtype != torch.int32 or head_choice.numel() != B * H:
+            raise ValueError("head_choice must be int32 with B*H entries")
+        hc = _dev(head_choice, "head_choice")
+    _check(lib().bsa_tile_permute_padded(_dev(x, "x"), _dev(y, "out"), _dtype_code(x), B, H, T, Hg, Wg, D, arr, n,
+                                         hc, Sp, None if lab is None else _dev(lab, "labels"), _stream(x)))
+    return y, lab
+
+
+def bsa_invert_permute_padded(y, grid, tiles, head_choice=None, out=None):
+    """Back to T-major order, padding rows dropped -> (B, H, S, D)."""
+    torch = _torch()
+    B, H, Sp, D = _bhsd(y, "y")
+    T, Hg, Wg = (int(g) for g in grid)
+    arr, n = _tiles_arr(tiles)
+    x = torch.empty((B, H, T * Hg * Wg, D), dtype=y.dtype, device=y.device) if out is None else out
+    hc = None
+    if head_choice is not None:
+        if head_choice.dtype != torch.int32 or head_choice.numel() != B * H:
+            raise ValueError("head_choice must be int32 with B*H entries")
+        hc = _dev(head_choice, "head_choice")
+    _check(lib().bsa_invert_permute_padded(_dev(y, "y"), _dev(x, "out"), _dtype_code(y), B, H, T, Hg, Wg, D, arr, n,
+                                           hc, Sp, _stream(y)))
+    return x
+
+
 def bsa_block_cohesion(x, block: int):
     """Cohesion of each run of `block` tokens -> float32 (B, H, S // block)."""
     torch = _torch()
@@ -221,28 +316,42 @@ def bsa_block_cohesion(x, block: int):
     return coh
 
 
-def bsa_select_tiling(q, grid, tiles, workspace=None):
-    """Per-head tiling choice -> (choice int32 (B, H), score float32 (B, H, n), tile_coh)."""
+def bsa_select_tiling(q, grid, tiles, workspace=None, statistic: str = "mean", pad: bool = False):
+    """Per-head tiling choice -> (choice int32 (B, H), score float32 (B, H, n), tile_coh).
+
+    statistic "mean" (per-tile cohesion averaged) or "pooled" (SPADE's engine
+    rule); pad=True scores candidates that do not divide the grid on the
+    zero-padded grid."""
     torch = _torch()
     B, H, S, D = _bhsd(q, "q")
     T, Hg, Wg = (int(g) for g in grid)
     if T * Hg * Wg != S:
         raise ValueError(f"grid {tuple(grid)} does not match S={S}")
+    if statistic not in ("mean", "pooled"):
+        raise ValueError(f"unknown statistic {statistic!r}")
     arr, n = _tiles_arr(tiles)
-    max_nb = max(S // max(a * b * c, 1) for a, b, c in tiles)
+    if pad:
+        max_nb = max(bsa_padded_length(T, Hg, Wg, t) // max(t[0] * t[1] * t[2], 1) for t in tiles)
+    else:
+        max_nb = max(S // max(a * b * c, 1) for a, b, c in tiles)
     if workspace is None:
         tile_coh = torch.empty((B, H, n, max_nb), dtype=torch.float32, device=q.device)
         score = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
         choice = torch.empty((B, H), dtype=torch.int32, device=q.device)
     else:
         tile_coh, score, choice = workspace
-    _check(lib().bsa_select_tiling(_dev(q, "q"), _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, _dev(tile_coh),
-                                   _dev(score), _dev(choice), _stream(q)))
+        if tile_coh.numel() < B * H * n * max_nb:
+            raise ValueError("tile_coh workspace too small")
+    stat = BSA_STAT_POOLED if statistic == "pooled" else BSA_STAT_MEAN
+    _check(lib().bsa_select_tiling_ex(_dev(q, "q"), _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, stat, int(bool(pad)),
+                                      _dev(tile_coh), _dev(score), _dev(choice), _stream(q)))
     return choice, score, tile_coh
 
 
-def bsa_minmax_block_scores(q, k, block: int, out=None):
-    """-> (scores float32 (B, H, Nb, Nb), summaries (4, B, H, Nb, D): qmax, qmin, kmax, kmin)."""
+def bsa_minmax_block_scores(q, k, block: int, out=None, labels=None):
+    """-> (scores float32 (B, H, Nb, Nb), summaries (4, B, H, Nb, D): qmax, qmin, kmax, kmin).
+
+    labels: int32 (B, H, S) or None; tokens labelled < 0 are left out."""
     torch = _torch()
     B, H, S, D = _bhsd(q, "q")
     if _bhsd(k, "k") != (B, H, S, D) or k.dtype != q.dtype:
@@ -255,8 +364,15 @@ def bsa_minmax_block_scores(q, k, block: int, out=None):
         summ = torch.empty((4, B, H, nb, D), dtype=q.dtype, device=q.device)
     else:
         scores, summ = out
-    _check(lib().bsa_minmax_block_scores(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, S, D, int(block),
-                                         _dev(summ), _dev(scores), _stream(q)))
+    if labels is None:
+        _check(lib().bsa_minmax_block_scores(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, S, D, int(block),
+                                             _dev(summ), _dev(scores), _stream(q)))
+    else:
+        if labels.dtype != torch.int32 or tuple(labels.shape) != (B, H, S):
+            raise ValueError("labels must be int32 (B, H, S)")
+        _check(lib().bsa_minmax_block_scores_masked(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, S, D,
+                                                    int(block), _dev(labels, "labels"), _dev(summ), _dev(scores),
+                                                    _stream(q)))
     return scores, summ
 
 
@@ -317,6 +433,30 @@ def bsa_top_p_block_mask(scores, p: float, scale: float = 1.0, sink_blocks: int 
     return (kv_idx, kv_cnt, mask) if return_mask else (kv_idx, kv_cnt)
 
 
+def bsa_topk_block_mask_tiled(scores, head_choice, k_table, nk_table, sink_blocks: int = 1, diag_width=1,
+                              max_kept: int | None = None, return_mask: bool = False, out=None):
+    """Top-k with a per-head budget k_table[c] over the head's nk_table[c] blocks, c = head_choice[b, h]."""
+    torch = _torch()
+    if scores.dim() != 4 or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 (B, H, Nq, Nk)")
+    B, H, Nq, Nk = (int(s) for s in scores.shape)
+    if head_choice.dtype != torch.int32 or head_choice.numel() != B * H:
+        raise ValueError("head_choice must be int32 with B*H entries")
+    kt = np.ascontiguousarray(k_table, dtype=np.int32)
+    nt = np.ascontiguousarray(nk_table, dtype=np.int32)
+    if kt.shape != nt.shape or kt.ndim != 1:
+        raise ValueError("k_table and nk_table must be 1-D of equal length")
+    w = _band(diag_width)
+    if max_kept is None:
+        max_kept = int(max(min(int(n), int(k) + int(sink_blocks) + _band_blocks(w)) for k, n in zip(kt, nt)))
+    kv_idx, kv_cnt, mask = _select_out(scores, max_kept, return_mask, out)
+    _check(lib().bsa_topk_block_mask_tiled(_dev(scores, "scores"), B, H, Nq, Nk, _dev(head_choice, "head_choice"),
+                                           kt.ctypes.data, nt.ctypes.data, int(kt.size), int(sink_blocks), w,
+                                           _dev(kv_idx), _dev(kv_cnt), int(kv_idx.shape[-1]),
+                                           None if mask is None else _dev(mask), _stream(scores)))
+    return (kv_idx, kv_cnt, mask) if return_mask else (kv_idx, kv_cnt)
+
+
 def _qkv(q, k, v):
     shp = _bhsd(q, "q")
     if _bhsd(k, "k") != shp or _bhsd(v, "v") != shp:
@@ -341,6 +481,34 @@ def bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block: int, scale=None, 
     _check(lib().bsa_block_sparse_attention(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
                                             _dtype_code(q), B, H, S, D, int(block), _dev(kv_idx), _dev(kv_cnt),
                                             int(kv_idx.shape[3]), _scale(scale), _stream(q)))
+    return o
+
+
+def bsa_block_sparse_attention_labels(q, k, v, kv_idx, kv_cnt, block: int, labels, scale=None, out=None):
+    """Block-sparse attention with the token rule labels[i] == labels[j] inside kept blocks.
+
+    labels: int32 (S,) shared by every head, or (B, H, S)."""
+    torch = _torch()
+    B, H, S, D = _qkv(q, k, v)
+    if kv_idx.dtype != torch.int32 or kv_cnt.dtype != torch.int32 or kv_idx.dim() != 4:
+        raise ValueError("kv_idx must be int32 (B, H, Nq, max_kept) and kv_cnt int32 (B, H, Nq)")
+    if block < 1 or S % block:
+        raise ValueError(f"block {block} must divide S={S}")
+    if tuple(kv_idx.shape[:3]) != (B, H, S // block) or tuple(kv_cnt.shape) != (B, H, S // block):
+        raise ValueError("block lists do not match (B, H, S // block)")
+    if labels.dtype != torch.int32:
+        raise ValueError("labels must be int32")
+    if tuple(labels.shape) == (S,):
+        stride = 0
+    elif tuple(labels.shape) == (B, H, S):
+        stride = S
+    else:
+        raise ValueError("labels must be (S,) or (B, H, S)")
+    o = torch.empty_like(q) if out is None else out
+    _check(lib().bsa_block_sparse_attention_labels(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+                                                   _dtype_code(q), B, H, S, D, int(block), _dev(kv_idx),
+                                                   _dev(kv_cnt), int(kv_idx.shape[3]), _dev(labels, "labels"), stride,
+                                                   _scale(scale), _stream(q)))
     return o
 
 
@@ -381,11 +549,16 @@ class AdaptiveBlockSparse:
     (torch) and reused, so a call allocates nothing and never synchronises.
     ``keep_diag`` is the diagonal band width (True = the diagonal alone);
     ``top_p`` replaces the top-k budget with the top-p rule (softmax of
-    ``p_scale`` * scores).
+    ``p_scale`` * scores); ``statistic`` is the tiling-choice rule ("mean" or
+    SPADE's "pooled").  ``pad=True`` accepts candidates that do not divide
+    the grid: every head works on the zero-padded grid of its own choice
+    (padding left out of the cohesion and the summaries, masked as keys,
+    dropped from the output), with the budget floor(frac * that grid's block
+    count).
     """
 
     def __init__(self, B, H, grid, D, tiles, frac, dtype, device, sink_blocks=1, keep_diag=True, scale=None,
-                 top_p=None, p_scale=1.0):
+                 top_p=None, p_scale=1.0, statistic="mean", pad=False):
         torch = _torch()
         self.grid = tuple(int(g) for g in grid)
         self.tiles = [tuple(int(v) for v in t) for t in tiles]
@@ -395,20 +568,32 @@ class AdaptiveBlockSparse:
         self.block = vols.pop()
         T, Hg, Wg = self.grid
         self.S = T * Hg * Wg
-        self.nb = self.S // self.block
-        self.k = bsa_budget(frac, self.nb)
+        self.pad, self.statistic = bool(pad), statistic
+        if self.pad and top_p is not None:
+            raise ValueError("top_p is not supported together with pad")
+        self.Sp = padded_rows(self.grid, self.tiles) if self.pad else self.S
+        self.nb = self.Sp // self.block
         self.sink_blocks, self.keep_diag, self.scale = int(sink_blocks), _band(keep_diag), scale
         self.top_p, self.p_scale = top_p, float(p_scale)
-        if top_p is None:
-            self.max_kept = min(self.nb, self.k + self.sink_blocks + _band_blocks(self.keep_diag))
+        if self.pad:
+            self.nk_table = [bsa_padded_length(T, Hg, Wg, t) // self.block for t in self.tiles]
+            self.k_table = [bsa_budget(frac, n) for n in self.nk_table]
+            self.k = max(self.k_table)
+            self.max_kept = max(min(n, k + self.sink_blocks + _band_blocks(self.keep_diag))
+                                for k, n in zip(self.k_table, self.nk_table))
         else:
-            self.max_kept = self.nb
+            self.k = bsa_budget(frac, self.nb)
+            if top_p is None:
+                self.max_kept = min(self.nb, self.k + self.sink_blocks + _band_blocks(self.keep_diag))
+            else:
+                self.max_kept = self.nb
         f = dict(device=device)
         n = len(self.tiles)
         self.ws_select = (torch.empty((B, H, n, self.nb), dtype=torch.float32, **f),
                           torch.empty((B, H, n), dtype=torch.float32, **f),
                           torch.empty((B, H), dtype=torch.int32, **f))
-        self.qp, self.kp, self.vp, self.op = (torch.empty((B, H, self.S, D), dtype=dtype, **f) for _ in range(4))
+        self.qp, self.kp, self.vp, self.op = (torch.empty((B, H, self.Sp, D), dtype=dtype, **f) for _ in range(4))
+        self.labels = torch.empty((B, H, self.Sp), dtype=torch.int32, **f) if self.pad else None
         self.ws_scores = (torch.empty((B, H, self.nb, self.nb), dtype=torch.float32, **f),
                           torch.empty((4, B, H, self.nb, D), dtype=dtype, **f))
         self.ws_topk = (torch.empty((B, H, self.nb, self.max_kept), dtype=torch.int32, **f),
@@ -423,19 +608,69 @@ class AdaptiveBlockSparse:
         return self.ws_topk[0], self.ws_topk[1]
 
     def __call__(self, q, k, v, out=None, attention_hook=None):
-        choice, _, _ = bsa_select_tiling(q, self.grid, self.tiles, workspace=self.ws_select)
-        for src, dst in ((q, self.qp), (k, self.kp), (v, self.vp)):
-            bsa_tile_permute(src, self.grid, self.tiles, head_choice=choice, out=dst)
-        scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores)
-        if self.top_p is None:
-            kv_idx, kv_cnt, _ = bsa_topk_block_mask(scores, self.k, self.sink_blocks, self.keep_diag,
-                                                    max_kept=self.max_kept, return_mask=True, out=self.ws_topk)
+        choice, _, _ = bsa_select_tiling(q, self.grid, self.tiles, workspace=self.ws_select, statistic=self.statistic,
+                                         pad=self.pad)
+        if self.pad:
+            for src, dst, lab in ((q, self.qp, self.labels), (k, self.kp, None), (v, self.vp, None)):
+                bsa_tile_permute_padded(src, self.grid, self.tiles, head_choice=choice, Sp=self.Sp, out=(dst, lab))
+            scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores, labels=self.labels)
+            kv_idx, kv_cnt = bsa_topk_block_mask_tiled(scores, choice, self.k_table, self.nk_table, self.sink_blocks,
+                                                       self.keep_diag, max_kept=self.max_kept, out=self.ws_topk)
         else:
-            kv_idx, kv_cnt, _ = bsa_top_p_block_mask(scores, self.top_p, self.p_scale, self.sink_blocks,
-                                                     self.keep_diag, return_mask=True, out=self.ws_topk)
+            for src, dst in ((q, self.qp), (k, self.kp), (v, self.vp)):
+                bsa_tile_permute(src, self.grid, self.tiles, head_choice=choice, out=dst)
+            scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores)
+            if self.top_p is None:
+                kv_idx, kv_cnt, _ = bsa_topk_block_mask(scores, self.k, self.sink_blocks, self.keep_diag,
+                                                        max_kept=self.max_kept, return_mask=True, out=self.ws_topk)
+            else:
+                kv_idx, kv_cnt, _ = bsa_top_p_block_mask(scores, self.top_p, self.p_scale, self.sink_blocks,
+                                                         self.keep_diag, return_mask=True, out=self.ws_topk)
         if attention_hook is not None:
             attention_hook(True)
-        bsa_block_sparse_attention(self.qp, self.kp, self.vp, kv_idx, kv_cnt, self.block, self.scale, out=self.op)
+        if self.pad:
+            bsa_block_sparse_attention_labels(self.qp, self.kp, self.vp, kv_idx, kv_cnt, self.block, self.labels,
+                                              self.scale, out=self.op)
+        else:
+            bsa_block_sparse_attention(self.qp, self.kp, self.vp, kv_idx, kv_cnt, self.block, self.scale,
+                                       out=self.op)
         if attention_hook is not None:
             attention_hook(False)
+        if self.pad:
+            return bsa_invert_permute_padded(self.op, self.grid, self.tiles, head_choice=choice, out=out)
         return bsa_invert_permute(self.op, self.grid, self.tiles, head_choice=choice, out=out)
+
+
+def video_label_attention(q, k, v, grid, kind: str, block: int = 64, scale=None):
+    """Spatial-only or temporal-only attention of T-major q, k, v as block lists plus labels.
+
+    kind "spatial": a token sees the tokens of its frame (labels = frame
+    index, T-major order, block lists of the frames' blocks).  kind
+    "temporal": a token sees the tokens at its (y, x) in every frame; the
+    tokens are permuted with tiles (T, 1, 1) so that each position's frames
+    are contiguous, labelled by position, attended, and permuted back.
+    [ADR-0001, "Décision" step 1: spatial_only_mask, temporal_only_mask.]
+    """
+    torch = _torch()
+    B, H, S, D = _qkv(q, k, v)
+    T, Hg, Wg = (int(g) for g in grid)
+    if T * Hg * Wg != S:
+        raise ValueError(f"grid {tuple(grid)} does not match S={S}")
+    if kind == "spatial":
+        lab = np.arange(S, dtype=np.int32) // (Hg * Wg)
+        tiles = None
+    elif kind == "temporal":
+        tiles = [(T, 1, 1)]
+        lab = (bsa_tile_permutation(T, Hg, Wg, (T, 1, 1)) % (Hg * Wg)).astype(np.int32)
+    else:
+        raise ValueError(f"kind must be 'spatial' or 'temporal', got {kind!r}")
+    idx, cnt = bsa_label_block_list(lab, block)
+    nb = S // block
+    kv_idx = torch.from_numpy(np.broadcast_to(idx, (B, H) + idx.shape).copy()).to(q.device)
+    kv_cnt = torch.from_numpy(np.broadcast_to(cnt, (B, H, nb)).copy()).to(q.device)
+    labels = torch.from_numpy(lab).to(q.device)
+    if tiles is None:
+        return bsa_block_sparse_attention_labels(q, k, v, kv_idx, kv_cnt, block, labels, scale)
+    qp, kp, vp = (bsa_tile_permute(x, grid, tiles) for x in (q, k, v))
+    op = bsa_block_sparse_attention_labels(qp, kp, vp, kv_idx, kv_cnt, block, labels, scale)
+    return bsa_invert_permute(op, grid, tiles)

@@ -46,7 +46,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P may grow to 2^8 before a rescale
 
-enum Mode { kBlockList = 0, kWindow = 1 };
+// kLabels: a block list plus the token rule labels[i] == labels[j] inside
+// the kept blocks (padding of a padded tiling, spatial-only and
+// temporal-only attention).
+enum Mode { kBlockList = 0, kWindow = 1, kLabels = 2 };
 
 struct AttnParams {
     const uint16_t* q;
@@ -63,6 +66,9 @@ struct AttnParams {
     uint32_t max_kept;
     // window
     int32_t half, sink;
+    // labels
+    const int32_t* labels;
+    uint64_t label_stride;  // elements between heads (0: one row for all heads)
 };
 
 template <int D, int BLK>
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     int n_iter;
     const int32_t* list = nullptr;
     int n_sink_tiles = 0, local_first = 0;
-    if (MODE == kBlockList) {
+    if (MODE != kWindow) {
         const size_t row = (size_t)bh * P.nq + I;
         n_iter = min(kv_cnt[row], (int)P.max_kept);
         list = kv_idx + row * P.max_kept;
@@ -428,7 +434,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         n_iter = n_sink_tiles + max(0, t_hi - local_first + 1);
     }
     auto tile_at = [&](int it) -> int {
-        if (MODE == kBlockList) return __builtin_amdgcn_readfirstlane(list[it]);
+        if (MODE != kWindow) return __builtin_amdgcn_readfirstlane(list[it]);
         return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
     };
 
@@ -487,8 +493,25 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         v_addr[t] = v_lds<D>(v_key0, colv >> 3) + (colv & 7) * 2;
     }
 
+    // label rule: this lane's two row labels, whether the whole query block
+    // shares one label, and the key labels of the next tile (lane l holds
+    // key l), fetched with that tile's K
+    int qlab[2] = {0, 0}, q_uni = 0, klab = 0, klab_next = 0;
+    bool q_uniform = true;
+    const int32_t* labs = nullptr;
+    if (MODE == kLabels) {
+        labs = P.labels + (size_t)bh * P.label_stride;
+        qlab[0] = labs[q0 + col];
+        qlab[1] = labs[q0 + 32 + col];
+        q_uni = __builtin_amdgcn_readfirstlane(qlab[0]);
+        q_uniform = __ballot((qlab[0] != q_uni) | (qlab[1] != q_uni)) == 0;
+    }
+
     bf16x8 kf[2][D / 16];
-    if (n_iter > 0) load_k(kf, tile_at(0) * BLK);
+    if (n_iter > 0) {
+        load_k(kf, tile_at(0) * BLK);
+        if (MODE == kLabels) klab_next = labs[tile_at(0) * BLK + lane];
+    }
     __builtin_amdgcn_s_waitcnt(0);
 
     for (int it = 0; it < n_iter; ++it) {
@@ -521,7 +544,9 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         // the end).  The scheduling barriers keep the loads after the MFMAs that
         // read the old fragments, so old and new K share registers.
         __builtin_amdgcn_sched_barrier(0);
+        if (MODE == kLabels) klab = klab_next;
         load_k(kf, nxt);
+        if (MODE == kLabels) klab_next = labs[nxt + lane];
         __builtin_amdgcn_sched_barrier(0);
 
         // softmax of both row tiles (32 values of one row per lane and tile)
@@ -551,6 +576,20 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                             const bool vis = (j < (int)P.S) & (((d <= P.half) & (-d <= P.half)) | (j < P.sink));
                             sacc[c][r][v] = vis ? sacc[c][r][v] : neg_inf;
                         }
+                    }
+            }
+        }
+        if (MODE == kLabels) {
+            // a tile whose keys all carry the query block's single label needs no mask
+            if (!q_uniform || __ballot(klab != q_uni) != 0) {
+                const float neg_inf = -__builtin_inff();
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int kl = __shfl(klab, 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4));
+#pragma unroll
+                        for (int r = 0; r < 2; ++r) sacc[c][r][v] = kl == qlab[r] ? sacc[c][r][v] : neg_inf;
                     }
             }
         }
@@ -618,7 +657,8 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     for (int r = 0; r < 2; ++r) {
         const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[r]), __float_as_uint(l_part[r]), false,
                                                          false);
-        const float inv = 1.0f / (__uint_as_float(pr[0]) + __uint_as_float(pr[1]));
+        const float l = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        const float inv = l > 0.f ? 1.0f / l : 0.f;  // a row that saw no key is written as zeros
         const int my_row = q0 + 32 * r + col;
         if (my_row >= (int)P.S) continue;
         uint16_t* orow = P.out + head + (size_t)my_row * D;
@@ -650,6 +690,8 @@ struct ScalarParams {
     const int32_t* kv_cnt;
     uint32_t max_kept, nq;
     int32_t half, sink;
+    const int32_t* labels;
+    uint64_t label_stride;
 };
 
 template <bool BF16>
@@ -683,13 +725,16 @@ __global__ __launch_bounds__(64) void attn_scalar_kernel(const ScalarParams P) {
         for (int d = 0; d < D; ++d) acc[d] = fmaf(p, ld<BF16>(P.v, head + (size_t)j * D + d), acc[d] * a);
         m = mn;
     };
-    if (MODE == kBlockList) {
+    if (MODE != kWindow) {
         const size_t row = (size_t)bh * P.nq + i / P.block;
         const int cnt = min(P.kv_cnt[row], (int)P.max_kept);
+        const int32_t* labs = MODE == kLabels ? P.labels + (size_t)bh * P.label_stride : nullptr;
+        const int32_t my_label = MODE == kLabels ? labs[i] : 0;
         for (int t = 0; t < cnt; ++t) {
             const uint32_t J = (uint32_t)P.kv_idx[row * P.max_kept + t];
             if (J >= P.nq) continue;  // invalid lists are reported by bsa_validate_block_list
-            for (uint32_t j = J * P.block; j < (J + 1) * P.block; ++j) visit(j);
+            for (uint32_t j = J * P.block; j < (J + 1) * P.block; ++j)
+                if (MODE != kLabels || labs[j] == my_label) visit(j);
         }
     } else {
         const uint32_t sink = (uint32_t)P.sink;
@@ -698,7 +743,7 @@ __global__ __launch_bounds__(64) void attn_scalar_kernel(const ScalarParams P) {
         const int64_t hi = min((int64_t)P.S - 1, (int64_t)i + P.half);
         for (int64_t j = lo; j <= hi; ++j) visit((uint32_t)j);
     }
-    const float inv = 1.0f / l;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;  // a row that saw no key is written as zeros
     for (int d = 0; d < D; ++d) {
         const float r = acc[d] * inv;
         if (BF16)
@@ -866,4 +911,59 @@ extern "C" int bsa_windowed_attention(const void* q, const void* k, const void* 
     P.half = half;
     P.sink = sink;
     return launch_scalar<kWindow>(P, dtype, D, st, name);
+}
+
+extern "C" int bsa_block_sparse_attention_labels(const void* q, const void* k, const void* v, void* out, int dtype,
+                                                 int64_t B, int64_t H, int64_t S, int64_t D, int block,
+                                                 const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
+                                                 const int32_t* labels, int64_t label_head_stride, float scale,
+                                                 bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_block_sparse_attention_labels";
+    int rc = common_checks(q, k, v, out, dtype, B, H, S, D, name);
+    if (rc) return rc;
+    BSA_REQUIRE(kv_idx && kv_cnt && labels, "%s: NULL block list or labels", name);
+    BSA_REQUIRE(block >= 1 && S % block == 0, "%s: block %d must divide S=%lld", name, block, (long long)S);
+    BSA_REQUIRE(max_kept >= 1, "%s: max_kept must be >= 1", name);
+    BSA_REQUIRE(label_head_stride == 0 || label_head_stride >= S, "%s: label_head_stride must be 0 or >= S", name);
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t nq = S / block;
+    const float sl2 = resolve_scale_log2(scale, D);
+    if (dtype == BSA_BF16 && D == 128 && block == 64) {
+        const int64_t nwg = B * H * nq;
+        BSA_REQUIRE(nwg < ((int64_t)1 << 31), "%s: too many blocks", name);
+        AttnParams P{};
+        P.q = static_cast<const uint16_t*>(q);
+        P.k = static_cast<const uint16_t*>(k);
+        P.v = static_cast<const uint16_t*>(v);
+        P.out = static_cast<uint16_t*>(out);
+        P.S = (uint32_t)S;
+        P.nq = (uint32_t)nq;
+        P.n_wg = (uint32_t)nwg;
+        P.xcd_remap = (nwg % 8 == 0) ? 1u : 0u;
+        P.scale_log2 = sl2;
+        P.kv_idx = kv_idx;
+        P.kv_cnt = kv_cnt;
+        P.max_kept = (uint32_t)max_kept;
+        P.labels = labels;
+        P.label_stride = (uint64_t)label_head_stride;
+        launch_solo<kLabels>(P, st);
+        return check_launch(name);
+    }
+    ScalarParams P{};
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.out = out;
+    P.S = (uint32_t)S;
+    P.BH = (uint32_t)(B * H);
+    P.block = (uint32_t)block;
+    P.scale_log2 = sl2;
+    P.kv_idx = kv_idx;
+    P.kv_cnt = kv_cnt;
+    P.max_kept = (uint32_t)max_kept;
+    P.nq = (uint32_t)nq;
+    P.labels = labels;
+    P.label_stride = (uint64_t)label_head_stride;
+    return launch_scalar<kLabels>(P, dtype, D, st, name);
 }

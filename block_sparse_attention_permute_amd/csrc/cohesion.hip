@@ -14,6 +14,17 @@
 // geometry, so no candidate tiling is ever materialised.  Per-tile values go
 // to a caller-provided buffer and a second small kernel averages them per
 // (b, h, candidate) in double in a fixed order, so results are deterministic.
+//
+// bsa_select_tiling_ex adds two variants of the same passes:
+//  * padded candidates ([Adaptive tiling (SPADE), "Deviations and notes": pad
+//    the grid to a multiple of the tile with zero tokens, left out of the
+//    cohesion]): tiles run over the padded tile grid and only their real
+//    cells are read, which is the same as reading zero padding and leaving
+//    zero-norm tokens out;
+//  * SPADE's pooled statistic ([same section, "Selection statistic"]: sum of
+//    pair similarities over the number of pairs across the whole tiling,
+//    zero-norm tokens counted): a tile contributes |sum u/|u||^2 - n_nonzero
+//    to the numerator and n(n - 1) (n = its real tokens) to the denominator.
 #include "common.h"
 
 namespace bsa {
@@ -24,7 +35,8 @@ constexpr int kWaves = 4;
 struct CohParams {
     const char* x;
     int dtype;
-    uint32_t S, Hg, Wg, D;
+    uint32_t S, T, Hg, Wg, D;
+    uint32_t pad, pooled;
     uint32_t vecs_per_row;  // 16-byte vectors per token row
     uint32_t n_tiles, max_nb;
     uint32_t nb[BSA_MAX_TILINGS];
@@ -49,7 +61,7 @@ __device__ __forceinline__ void load_vec(const char* p, float (&v)[EPV]) {
 }
 
 // LPT lanes cooperate on one token (16 bytes each); 64/LPT tokens per step.
-template <int EPV, int LPT>
+template <int EPV, int LPT, bool PAD>
 __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohParams P) {
     constexpr int TPI = 64 / LPT;
     const int lane = threadIdx.x & 63;
@@ -58,7 +70,16 @@ __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohPar
     const uint32_t bh = blockIdx.z;
     if (tile >= P.nb[cand]) return;
     const TileGeo& g = P.geo[cand];
-    const uint32_t origin = tile_origin(tile, g, P.Hg, P.Wg);
+    const uint32_t origin = PAD ? 0u : tile_origin(tile, g, P.Hg, P.Wg);
+    uint32_t t0 = 0, y0 = 0, x0 = 0;
+    if (PAD) {
+        uint32_t tt, rem, ty, tx;
+        fdivmod(tile, g.f_ntyx, tt, rem);
+        fdivmod(rem, g.f_ntx, ty, tx);
+        t0 = tt * g.a;
+        y0 = ty * g.b;
+        x0 = tx * g.c;
+    }
     const size_t row_bytes = (size_t)P.vecs_per_row * 16;
     const char* head = P.x + (size_t)bh * P.S * row_bytes;
     const int sub = lane % LPT;   // which 16-byte slice of the row
@@ -72,8 +93,18 @@ __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohPar
         const uint32_t cell = base + slot;
         float v[EPV];
         float ss = 0.f;
-        if (cell < g.vol) {
-            const uint32_t s = origin + cell_offset(cell, g, P.Hg, P.Wg);
+        bool real = cell < g.vol;
+        uint32_t s = 0;
+        if (PAD && real) {
+            uint32_t rt, rem, ry, rx;
+            fdivmod(cell, g.f_bc, rt, rem);
+            fdivmod(rem, g.f_c, ry, rx);
+            real = t0 + rt < P.T && y0 + ry < P.Hg && x0 + rx < P.Wg;
+            s = ((t0 + rt) * P.Hg + y0 + ry) * P.Wg + x0 + rx;
+        } else if (real) {
+            s = origin + cell_offset(cell, g, P.Hg, P.Wg);
+        }
+        if (real) {
             load_vec<EPV>(head + (size_t)s * row_bytes + (size_t)sub * 16, v);
 #pragma unroll
             for (int i = 0; i < EPV; ++i) ss = fmaf(v[i], v[i], ss);
@@ -106,7 +137,7 @@ __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohPar
         // after the slot reduction n is the number of non-zero tokens
         const float cnt = n;
         const float sics = cnt >= 2.f ? (uu - cnt) / (cnt * (cnt - 1.f)) : __builtin_nanf("");
-        P.tile_coh[((size_t)bh * P.n_tiles + cand) * P.max_nb + tile] = sics;
+        P.tile_coh[((size_t)bh * P.n_tiles + cand) * P.max_nb + tile] = P.pooled ? uu - cnt : sics;
     }
 }
 
@@ -116,9 +147,21 @@ struct SelParams {
     uint32_t nb[BSA_MAX_TILINGS];
     float* score;
     int32_t* choice;
+    uint32_t pooled, T, Hg, Wg;
+    TileGeo geo[BSA_MAX_TILINGS];  // pooled: tile extents (padded geometry)
 };
 
-// One wave per (b, h): mean over tiles of each candidate, then the argmax.
+// Real tokens of a (possibly clipped) tile.
+__device__ __forceinline__ double tile_tokens(uint32_t tile, const TileGeo& g, const SelParams& P) {
+    uint32_t tt, rem, ty, tx;
+    fdivmod(tile, g.f_ntyx, tt, rem);
+    fdivmod(rem, g.f_ntx, ty, tx);
+    const uint32_t at = min(g.a, P.T - tt * g.a), bt = min(g.b, P.Hg - ty * g.b), ct = min(g.c, P.Wg - tx * g.c);
+    return (double)at * bt * ct;
+}
+
+// One wave per (b, h): per candidate the mean over tiles (or the pooled
+// ratio), then the argmax.
 __global__ __launch_bounds__(64) void select_kernel(const SelParams P) {
     const uint32_t bh = blockIdx.x;
     const int lane = threadIdx.x;
@@ -130,7 +173,11 @@ __global__ __launch_bounds__(64) void select_kernel(const SelParams P) {
         double cnt = 0.0;
         for (uint32_t t = lane; t < P.nb[c]; t += 64) {
             const float v = row[t];
-            if (v == v) {
+            if (P.pooled) {
+                const double n = tile_tokens(t, P.geo[c], P);
+                sum += (double)v;
+                cnt += n * (n - 1.0);
+            } else if (v == v) {
                 sum += (double)v;
                 cnt += 1.0;
             }
@@ -153,7 +200,9 @@ __global__ __launch_bounds__(64) void select_kernel(const SelParams P) {
 int launch_tile_cohesion(const CohParams& P, uint32_t BH, hipStream_t stream, const char* name) {
     dim3 grid((P.max_nb + kWaves - 1) / kWaves, P.n_tiles, BH);
     const int lpt = (int)P.vecs_per_row;
-#define BSA_COH(EPV, LPT) tile_cohesion_kernel<EPV, LPT><<<grid, 64 * kWaves, 0, stream>>>(P)
+#define BSA_COH(EPV, LPT)                                                                \
+    (P.pad ? tile_cohesion_kernel<EPV, LPT, true><<<grid, 64 * kWaves, 0, stream>>>(P) \
+           : tile_cohesion_kernel<EPV, LPT, false><<<grid, 64 * kWaves, 0, stream>>>(P))
     if (P.dtype == BSA_BF16) {
         switch (lpt) {
             case 1: BSA_COH(8, 1); break;
@@ -217,6 +266,9 @@ extern "C" int bsa_block_cohesion(const void* x, int dtype, int64_t B, int64_t H
     BSA_REQUIRE(coh != nullptr, "%s: NULL output", name);
     BSA_REQUIRE(block >= 1 && S % block == 0, "%s: block %d must divide S=%lld", name, block, (long long)S);
     // consecutive runs = tiles (1, 1, block) of a 1 x 1 x S grid
+    P.T = 1;
+    P.pad = 0;
+    P.pooled = 0;
     P.Hg = 1;
     P.Wg = (uint32_t)S;
     P.n_tiles = 1;
@@ -229,28 +281,34 @@ extern "C" int bsa_block_cohesion(const void* x, int dtype, int64_t B, int64_t H
     return launch_tile_cohesion(P, (uint32_t)(B * H), (hipStream_t)stream, name);
 }
 
-extern "C" int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg, int64_t D,
-                                 const int32_t* tiles_host, int n_tiles, float* tile_coh, float* score,
-                                 int32_t* choice, bsa_stream_t stream) {
+extern "C" int bsa_select_tiling_ex(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
+                                    int64_t D, const int32_t* tiles_host, int n_tiles, int statistic, int pad,
+                                    float* tile_coh, float* score, int32_t* choice, bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_select_tiling";
     BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
+    BSA_REQUIRE(statistic == BSA_STAT_MEAN || statistic == BSA_STAT_POOLED, "%s: unknown statistic %d", name,
+                statistic);
+    BSA_REQUIRE(pad == 0 || pad == 1, "%s: pad must be 0 or 1", name);
     const int64_t S = (int64_t)T * Hg * Wg;
     CohParams P;
     int rc = fill_common(P, q, dtype, B, H, S, D, name);
     if (rc) return rc;
-    rc = check_tiles(T, Hg, Wg, tiles_host, n_tiles);
+    rc = pad ? check_tiles_padded(T, Hg, Wg, tiles_host, n_tiles) : check_tiles(T, Hg, Wg, tiles_host, n_tiles);
     if (rc) return rc;
     BSA_REQUIRE(tile_coh != nullptr && score != nullptr && choice != nullptr, "%s: NULL output", name);
+    P.T = (uint32_t)T;
     P.Hg = (uint32_t)Hg;
     P.Wg = (uint32_t)Wg;
+    P.pad = (uint32_t)pad;
+    P.pooled = statistic == BSA_STAT_POOLED ? 1u : 0u;
     P.n_tiles = (uint32_t)n_tiles;
     P.max_nb = 0;
     for (int i = 0; i < BSA_MAX_TILINGS; ++i) {
         const int j = i < n_tiles ? i : 0;
         const int a = tiles_host[3 * j], b = tiles_host[3 * j + 1], c = tiles_host[3 * j + 2];
-        P.geo[i] = make_geo(Hg, Wg, a, b, c);
-        P.nb[i] = (uint32_t)(S / ((int64_t)a * b * c));
+        P.geo[i] = make_geo_padded(Hg, Wg, a, b, c);  // equals make_geo when the tile divides the grid
+        P.nb[i] = (uint32_t)(padded_length(T, Hg, Wg, a, b, c) / ((int64_t)a * b * c));
         if (i < n_tiles && P.nb[i] > P.max_nb) P.max_nb = P.nb[i];
     }
     P.tile_coh = tile_coh;
@@ -261,9 +319,23 @@ extern "C" int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H,
     Q.tile_coh = tile_coh;
     Q.n_tiles = P.n_tiles;
     Q.max_nb = P.max_nb;
-    for (int i = 0; i < BSA_MAX_TILINGS; ++i) Q.nb[i] = P.nb[i];
+    for (int i = 0; i < BSA_MAX_TILINGS; ++i) {
+        Q.nb[i] = P.nb[i];
+        Q.geo[i] = P.geo[i];
+    }
     Q.score = score;
     Q.choice = choice;
+    Q.pooled = P.pooled;
+    Q.T = P.T;
+    Q.Hg = P.Hg;
+    Q.Wg = P.Wg;
     select_kernel<<<(unsigned)(B * H), 64, 0, st>>>(Q);
     return check_launch(name);
+}
+
+extern "C" int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg, int64_t D,
+                                 const int32_t* tiles_host, int n_tiles, float* tile_coh, float* score,
+                                 int32_t* choice, bsa_stream_t stream) {
+    return bsa_select_tiling_ex(q, dtype, B, H, T, Hg, Wg, D, tiles_host, n_tiles, BSA_STAT_MEAN, 0, tile_coh, score,
+                                choice, stream);
 }

@@ -106,6 +106,38 @@ inline TileGeo make_geo(int Hg, int Wg, int a, int b, int c) {
 
 // Every candidate must divide the grid ([Adaptive tiling (SPADE), "Deviations
 // and notes": divisible grids only]).
+// The same tiling on the grid padded up to a multiple of the tile along every
+// axis ([Adaptive tiling (SPADE), "Deviations and notes": pad with zero
+// tokens]): the tile grid is ceil(T/a) x ceil(Hg/b) x ceil(Wg/c) and cells
+// outside T x Hg x Wg are padding.
+inline TileGeo make_geo_padded(int Hg, int Wg, int a, int b, int c) {
+    TileGeo g = make_geo(Hg, Wg, a, b, c);
+    g.nty = (Hg + b - 1) / b;
+    g.ntx = (Wg + c - 1) / c;
+    g.f_ntyx = make_fastdiv(g.nty * g.ntx);
+    g.f_ntx = make_fastdiv(g.ntx);
+    return g;
+}
+
+// Padded length T' * Hg' * Wg' of a tiling, or -1 for bad arguments.
+inline int64_t padded_length(int T, int Hg, int Wg, int a, int b, int c) {
+    if (T <= 0 || Hg <= 0 || Wg <= 0 || a <= 0 || b <= 0 || c <= 0) return -1;
+    return (int64_t)((T + a - 1) / a * a) * ((Hg + b - 1) / b * b) * ((Wg + c - 1) / c * c);
+}
+
+// Candidates of a padded tiling only need positive extents.
+inline int check_tiles_padded(int T, int Hg, int Wg, const int32_t* tiles, int n_tiles) {
+    BSA_REQUIRE(tiles != nullptr, "tiles is NULL");
+    BSA_REQUIRE(n_tiles >= 1 && n_tiles <= BSA_MAX_TILINGS, "n_tiles=%d must be in [1, %d]", n_tiles,
+                BSA_MAX_TILINGS);
+    BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "grid must be positive");
+    for (int i = 0; i < n_tiles; ++i) {
+        const int a = tiles[3 * i], b = tiles[3 * i + 1], c = tiles[3 * i + 2];
+        BSA_REQUIRE(a > 0 && b > 0 && c > 0, "tile %d (%d,%d,%d) must be positive", i, a, b, c);
+    }
+    return BSA_OK;
+}
+
 inline int check_tiles(int T, int Hg, int Wg, const int32_t* tiles, int n_tiles) {
     BSA_REQUIRE(tiles != nullptr, "tiles is NULL");
     BSA_REQUIRE(n_tiles >= 1 && n_tiles <= BSA_MAX_TILINGS, "n_tiles=%d must be in [1, %d]", n_tiles,
@@ -144,6 +176,21 @@ __device__ __forceinline__ uint32_t perm_to_tmajor(uint32_t p, const TileGeo& g,
     fdivmod(r, g.f_bc, rt, rem2);
     fdivmod(rem2, g.f_c, ry, rx);
     return ((tt * g.a + rt) * Hg + ty * g.b + ry) * Wg + tx * g.c + rx;
+}
+
+// Padded permuted position p -> T-major token of the unpadded grid, or -1
+// for a padding cell (g from make_geo_padded).
+__device__ __forceinline__ int32_t perm_to_tmajor_padded(uint32_t p, const TileGeo& g, uint32_t T, uint32_t Hg,
+                                                         uint32_t Wg) {
+    uint32_t tid, r, tt, rem, ty, tx, rt, rem2, ry, rx;
+    fdivmod(p, g.f_vol, tid, r);
+    fdivmod(tid, g.f_ntyx, tt, rem);
+    fdivmod(rem, g.f_ntx, ty, tx);
+    fdivmod(r, g.f_bc, rt, rem2);
+    fdivmod(rem2, g.f_c, ry, rx);
+    const uint32_t t = tt * g.a + rt, y = ty * g.b + ry, x = tx * g.c + rx;
+    if (t >= T || y >= Hg || x >= Wg) return -1;
+    return (int32_t)((t * Hg + y) * Wg + x);
 }
 
 }  // namespace bsa

@@ -1,11 +1,14 @@
-// Host-side entry points of libbsa: error reporting, the tile permutation and
-// its inverse, the top-k budget and the sliding-tile block lists.
+// Host-side entry points of libbsa: error reporting, the tile permutation
+// (plain and padded) and its inverse, the top-k budget, and the sliding-tile
+// and same-label block lists.
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -56,6 +59,72 @@ extern "C" int bsa_tile_permutation(int T, int Hg, int Wg, int a, int b, int c, 
                     for (int ry = 0; ry < b; ++ry)
                         for (int rx = 0; rx < c; ++rx)
                             perm[p++] = (int32_t)(((int64_t)(tt * a + rt) * Hg + ty * b + ry) * Wg + tx * c + rx);
+    return BSA_OK;
+}
+
+extern "C" int64_t bsa_padded_length(int T, int Hg, int Wg, int a, int b, int c) {
+    clear_error();
+    const int64_t n = padded_length(T, Hg, Wg, a, b, c);
+    if (n < 0) set_error("grid %dx%dx%d and tile %dx%dx%d must be positive", T, Hg, Wg, a, b, c);
+    return n;
+}
+
+extern "C" int bsa_tile_permutation_padded(int T, int Hg, int Wg, int a, int b, int c, int32_t* perm) {
+    clear_error();
+    const int64_t n = padded_length(T, Hg, Wg, a, b, c);
+    BSA_REQUIRE(n > 0, "grid %dx%dx%d and tile %dx%dx%d must be positive", T, Hg, Wg, a, b, c);
+    BSA_REQUIRE(n <= INT32_MAX, "grid too large");
+    BSA_REQUIRE(perm != nullptr, "perm is NULL");
+    const int nt = (T + a - 1) / a, ny = (Hg + b - 1) / b, nx = (Wg + c - 1) / c;
+    int64_t p = 0;
+    for (int tt = 0; tt < nt; ++tt)
+        for (int ty = 0; ty < ny; ++ty)
+            for (int tx = 0; tx < nx; ++tx)
+                for (int rt = 0; rt < a; ++rt)
+                    for (int ry = 0; ry < b; ++ry)
+                        for (int rx = 0; rx < c; ++rx) {
+                            const int t = tt * a + rt, y = ty * b + ry, x = tx * c + rx;
+                            perm[p++] = (t < T && y < Hg && x < Wg)
+                                            ? (int32_t)(((int64_t)t * Hg + y) * Wg + x)
+                                            : -1;
+                        }
+    return BSA_OK;
+}
+
+extern "C" int bsa_label_block_list(const int32_t* labels, int64_t S, int block, int32_t* kv_idx, int32_t* kv_cnt,
+                                    int max_kept) {
+    clear_error();
+    BSA_REQUIRE(labels != nullptr && kv_idx != nullptr && kv_cnt != nullptr, "NULL argument");
+    BSA_REQUIRE(S > 0 && block >= 1 && S % block == 0, "block %d must divide S=%lld", block, (long long)S);
+    BSA_REQUIRE(max_kept >= 1, "max_kept must be >= 1");
+    const int64_t nb = S / block;
+    BSA_REQUIRE(nb <= 16384, "too many blocks (%lld)", (long long)nb);
+    // (label, block) pairs sorted by label: every run of one label links all its blocks
+    std::vector<std::pair<int32_t, int32_t>> lb;
+    lb.reserve((size_t)S);
+    for (int64_t s = 0; s < S; ++s)
+        if (labels[s] >= 0) lb.emplace_back(labels[s], (int32_t)(s / block));
+    std::sort(lb.begin(), lb.end());
+    lb.erase(std::unique(lb.begin(), lb.end()), lb.end());
+    std::vector<uint8_t> keep((size_t)(nb * nb), 0);
+    for (size_t i = 0; i < lb.size();) {
+        size_t j = i;
+        while (j < lb.size() && lb[j].first == lb[i].first) ++j;
+        for (size_t u = i; u < j; ++u)
+            for (size_t w = i; w < j; ++w) keep[(size_t)lb[u].second * nb + lb[w].second] = 1;
+        i = j;
+    }
+    for (int64_t I = 0; I < nb; ++I) {
+        int cnt = 0;
+        for (int64_t J = 0; J < nb; ++J)
+            if (keep[(size_t)(I * nb + J)]) {
+                BSA_REQUIRE(cnt < max_kept, "query block %lld keeps more than max_kept=%d blocks", (long long)I,
+                            max_kept);
+                kv_idx[I * max_kept + cnt++] = (int32_t)J;
+            }
+        for (int i = cnt; i < max_kept; ++i) kv_idx[I * max_kept + i] = -1;
+        kv_cnt[I] = cnt;
+    }
     return BSA_OK;
 }
 

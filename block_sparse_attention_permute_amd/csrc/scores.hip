@@ -5,6 +5,11 @@
 // the (query block I, key block J) score is estimated as
 //   max((qmax_I + qmin_I) . kmax_J, (qmax_I + qmin_I) . kmin_J).
 //
+// bsa_minmax_block_scores_masked leaves out tokens labelled < 0 (the padding
+// of a padded tiling, [Adaptive tiling (SPADE), "Deviations and notes"]):
+// a partial block is summarised by its real tokens, and a block with none
+// scores -inf in its row and its column.
+//
 // Design: pass 1 is an HBM-bound reduction, one wave per block, that keeps
 // the summaries in the input dtype (a max or min of bf16 values is a bf16
 // value, so they are exact).  Pass 2 is a small fp32 product per head,
@@ -22,6 +27,7 @@ struct SumParams {
     const char* k;
     char* summ;  // 4 x (BH, Nb, D) of the input dtype
     uint32_t block, nb, vecs_per_row, BH;
+    const int32_t* labels;  // (BH, S) or null; tokens labelled < 0 are left out
 };
 
 template <int EPV>
@@ -72,7 +78,9 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
         mx[i] = -__builtin_inff();
         mn[i] = __builtin_inff();
     }
+    const int32_t* lab = P.labels != nullptr ? P.labels + ((size_t)bh * P.nb + blk) * P.block : nullptr;
     for (uint32_t t = slot; t < P.block; t += TPI) {
+        if (lab != nullptr && lab[t] < 0) continue;
         float v[EPV];
         unpack<EPV>(*reinterpret_cast<const uint4*>(src + (size_t)t * row_bytes + (size_t)sub * 16), v);
 #pragma unroll
@@ -176,6 +184,14 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const char* __restric
         }
         __syncthreads();
     }
+    // a block without tokens has max = -inf (inputs are finite otherwise)
+    bool ok_i[4], ok_j[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t I = I0 + ty + 16 * r, J = J0 + tx + 16 * r;
+        ok_i[r] = I < nb && load_elem<BF16>(qmax, head + (size_t)I * D) != -__builtin_inff();
+        ok_j[r] = J < nb && load_elem<BF16>(kmax, head + (size_t)J * D) != -__builtin_inff();
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const uint32_t I = I0 + ty + 16 * r;
@@ -183,7 +199,9 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const char* __restric
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint32_t J = J0 + tx + 16 * c;
-            if (J < nb) scores[((size_t)bh * nb + I) * nb + J] = fmaxf(ax[r][c], an[r][c]);
+            if (J < nb)
+                scores[((size_t)bh * nb + I) * nb + J] =
+                    (ok_i[r] && ok_j[c]) ? fmaxf(ax[r][c], an[r][c]) : -__builtin_inff();
         }
     }
 }
@@ -193,8 +211,9 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const char* __restric
 
 using namespace bsa;
 
-extern "C" int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H, int64_t S,
-                                       int64_t D, int block, void* summaries, float* scores, bsa_stream_t stream) {
+extern "C" int bsa_minmax_block_scores_masked(const void* q, const void* k, int dtype, int64_t B, int64_t H,
+                                              int64_t S, int64_t D, int block, const int32_t* labels_or_null,
+                                              void* summaries, float* scores, bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_minmax_block_scores";
     const int es = elem_size(dtype);
@@ -218,6 +237,7 @@ extern "C" int bsa_minmax_block_scores(const void* q, const void* k, int dtype, 
     P.nb = (uint32_t)nb;
     P.vecs_per_row = (uint32_t)vecs;
     P.BH = (uint32_t)(B * H);
+    P.labels = labels_or_null;
     hipStream_t st = (hipStream_t)stream;
     dim3 g1((unsigned)((nb + kWaves - 1) / kWaves), 2, (unsigned)(B * H));
 #define BSA_MM(EPV, LPT) block_minmax_kernel<EPV, LPT><<<g1, 64 * kWaves, 0, st>>>(P)
@@ -241,4 +261,9 @@ extern "C" int bsa_minmax_block_scores(const void* q, const void* k, int dtype, 
     else
         block_scores_kernel<false><<<g2, 256, 0, st>>>(static_cast<const char*>(summaries), P.BH, P.nb, (uint32_t)D, scores);
     return check_launch(name);
+}
+
+extern "C" int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H, int64_t S,
+                                       int64_t D, int block, void* summaries, float* scores, bsa_stream_t stream) {
+    return bsa_minmax_block_scores_masked(q, k, dtype, B, H, S, D, block, nullptr, summaries, scores, stream);
 }

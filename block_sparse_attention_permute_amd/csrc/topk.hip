@@ -37,6 +37,11 @@ struct TopkParams {
     int32_t diag_half;  // band half-width; -1: no band
     float p, scale_log2;  // top-p only
     uint64_t rows;
+    // per-head budget (bsa_topk_block_mask_tiled): k and the head's block
+    // count come from the tables at the head's tiling choice
+    const int32_t* head_choice;
+    uint32_t n_table;
+    uint32_t k_table[BSA_MAX_TILINGS], nk_table[BSA_MAX_TILINGS];
 };
 
 // Larger score -> larger key.  NaN -> 0, and every number maps above 0.
@@ -77,13 +82,21 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
     const uint32_t I = (uint32_t)(row % P.nq);
     const float* s = P.scores + row * P.nk;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t k_row = P.k, nk_row = P.nk;
+    if (P.head_choice != nullptr) {
+        uint32_t c = (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[row / P.nq]);
+        if (c >= P.n_table) c = 0;  // out-of-range choices are caught by bsa_validate_indices
+        k_row = P.k_table[c];
+        nk_row = P.nk_table[c];
+    }
+    const bool row_exists = P.head_choice == nullptr || I < nk_row;
 
     uint32_t key[VPL];
     bool valid[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const uint32_t e = i * 64 + lane;
-        valid[i] = e < P.nk;
+        valid[i] = row_exists && e < nk_row;
         key[i] = valid[i] ? order_key(s[e]) : 0u;
     }
     // TOPP: softmax weights w = exp(scale * (s - max)); NaN and -inf weigh 0
@@ -117,7 +130,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
             uint32_t c = 0;
 #pragma unroll
             for (int i = 0; i < VPL; ++i) c += (valid[i] && key[i] >= cand) ? 1u : 0u;
-            if (wave_sum(c) >= P.k) T = cand;
+            if (wave_sum(c) >= k_row) T = cand;
         }
     }
     uint32_t need;  // ties at T to take, lowest index first
@@ -138,7 +151,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
         uint32_t gt = 0;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) gt += (valid[i] && key[i] > T) ? 1u : 0u;
-        need = P.k - wave_sum(gt);
+        need = row_exists ? k_row - wave_sum(gt) : 0u;
     }
 
     bool keep[VPL];
@@ -162,7 +175,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
         const uint32_t at = pos + popc64(m & lt_mask);
         if (keep[i] && at < P.max_kept) out[at] = (int32_t)(i * 64 + lane);
         pos += popc64(m);
-        if (P.mask != nullptr && valid[i]) P.mask[row * P.nk + i * 64 + lane] = keep[i] ? 1 : 0;
+        if (P.mask != nullptr && i * 64 + lane < P.nk) P.mask[row * P.nk + i * 64 + lane] = keep[i] ? 1 : 0;
     }
     for (uint32_t j = pos + lane; j < P.max_kept; j += 64) out[j] = -1;
     if (lane == 0) P.kv_cnt[row] = (int32_t)pos;
@@ -254,4 +267,47 @@ extern "C" int bsa_top_p_block_mask(const float* scores, int64_t B, int64_t H, i
     P.scale_log2 = (float)((double)scale * 1.4426950408889634);
     P.rows = (uint64_t)B * H * Nq;
     return launch_select<true>(P, (hipStream_t)stream, name);
+}
+
+extern "C" int bsa_topk_block_mask_tiled(const float* scores, int64_t B, int64_t H, int Nq, int Nk,
+                                         const int32_t* head_choice, const int32_t* k_table, const int32_t* nk_table,
+                                         int n_table, int sink_blocks, int diag_width, int32_t* kv_idx,
+                                         int32_t* kv_cnt, int max_kept, uint8_t* mask_or_null, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_topk_block_mask_tiled";
+    BSA_REQUIRE(scores && kv_idx && kv_cnt && head_choice && k_table && nk_table, "%s: NULL argument", name);
+    BSA_REQUIRE(B >= 1 && H >= 1 && Nq >= 1, "%s: B, H, Nq must be >= 1", name);
+    BSA_REQUIRE(Nk >= 1 && Nk <= 4096, "%s: Nk=%d must be in [1, 4096]", name, Nk);
+    BSA_REQUIRE(n_table >= 1 && n_table <= BSA_MAX_TILINGS, "%s: n_table=%d must be in [1, %d]", name, n_table,
+                BSA_MAX_TILINGS);
+    BSA_REQUIRE(sink_blocks >= 0, "%s: sink_blocks must be >= 0", name);
+    BSA_REQUIRE(diag_width >= 0, "%s: diag_width must be >= 0", name);
+    TopkParams P{};
+    int64_t widest = 0;
+    for (int c = 0; c < n_table; ++c) {
+        BSA_REQUIRE(nk_table[c] >= 1 && nk_table[c] <= Nk, "%s: nk_table[%d]=%d must be in [1, Nk=%d]", name, c,
+                    nk_table[c], Nk);
+        BSA_REQUIRE(k_table[c] >= 1 && k_table[c] <= nk_table[c], "%s: k_table[%d]=%d must be in [1, %d]", name, c,
+                    k_table[c], nk_table[c]);
+        widest = std::max<int64_t>(widest, std::min<int64_t>(nk_table[c], (int64_t)k_table[c] + sink_blocks +
+                                                                              band_width(diag_width)));
+        P.k_table[c] = (uint32_t)k_table[c];
+        P.nk_table[c] = (uint32_t)nk_table[c];
+    }
+    BSA_REQUIRE(max_kept >= widest, "%s: max_kept=%d < %lld (k + sink + band, at most nk)", name, max_kept,
+                (long long)widest);
+    P.scores = scores;
+    P.kv_idx = kv_idx;
+    P.kv_cnt = kv_cnt;
+    P.mask = mask_or_null;
+    P.nq = (uint32_t)Nq;
+    P.nk = (uint32_t)Nk;
+    P.k = 1;
+    P.sink = (uint32_t)std::min(sink_blocks, Nk);
+    P.diag_half = diag_width >= 1 ? diag_width / 2 : -1;
+    P.max_kept = (uint32_t)max_kept;
+    P.rows = (uint64_t)B * H * Nq;
+    P.head_choice = head_choice;
+    P.n_table = (uint32_t)n_table;
+    return launch_select<false>(P, (hipStream_t)stream, name);
 }

@@ -52,6 +52,11 @@ typedef enum {
     BSA_BF16 = 1  /* bfloat16 */
 } bsa_dtype;
 
+typedef enum {
+    BSA_STAT_MEAN = 0,   /* mean over tiles of the per-tile cohesion */
+    BSA_STAT_POOLED = 1  /* sum of pair similarities over the number of pairs */
+} bsa_statistic;
+
 #define BSA_MAX_TILINGS 8
 
 /* Message of the last failed call on this thread ("" if none). */
@@ -96,6 +101,32 @@ int bsa_budget(double frac, int n_blocks);
 int bsa_sliding_tile_block_list(int nt, int nh, int nw, int rt, int rh, int rw,
                                 int32_t* kv_idx_host, int32_t* kv_cnt_host, int max_kept);
 
+/* Length T'*Hg'*Wg' of the grid padded up to a multiple of the tile along
+ * every axis [Adaptive tiling (SPADE), "Deviations and notes": a grid the
+ * candidate tiles do not divide is padded with zero tokens].  Returns -1 if
+ * a size is <= 0. */
+int64_t bsa_padded_length(int T, int Hg, int Wg, int a, int b, int c);
+
+/* Tile order of the padded grid: writes perm_host[p] for p < the padded
+ * length, the T-major index (in the unpadded grid) of the token at padded
+ * permuted position p, or -1 for padding.  Tiles are numbered T-major over
+ * the padded tile grid, cells T-major inside a tile (so a dividing tile
+ * gives bsa_tile_permutation).  INVALID_ARG if a size is <= 0. */
+int bsa_tile_permutation_padded(int T, int Hg, int Wg, int a, int b, int c, int32_t* perm_host);
+
+/* Block lists of the "same label" rule: key block J is kept for query block
+ * I when some token of I and some token of J carry the same label (labels
+ * < 0 never match).  With the frame index as label this is the block
+ * structure of spatial-only attention, with the spatial position (in an
+ * order that groups positions, e.g. tiles (T, 1, 1)) that of temporal-only
+ * attention [ADR-0001, "Décision" step 1: spatial_only_mask,
+ * temporal_only_mask].  labels_host: S int32 (host); block divides S.
+ * Writes kv_idx_host[I*max_kept + i] (ascending, -1 padded) and
+ * kv_cnt_host[I] for I < S/block.  INVALID_ARG on bad sizes or if a row does
+ * not fit in max_kept. */
+int bsa_label_block_list(const int32_t* labels_host, int64_t S, int block, int32_t* kv_idx_host,
+                         int32_t* kv_cnt_host, int max_kept);
+
 /* ------------------------------------------------------------------------
  * Device calls
  * ------------------------------------------------------------------------ */
@@ -119,6 +150,26 @@ int bsa_tile_permute(const void* x, void* y, int dtype, int64_t B, int64_t H,
 int bsa_invert_permute(const void* y, void* x, int dtype, int64_t B, int64_t H,
                        int T, int Hg, int Wg, int64_t D, const int32_t* tiles_host, int n_tiles,
                        const int32_t* head_choice, bsa_stream_t stream);
+
+/* bsa_tile_permute over padded tilings (candidates need not divide the
+ * grid): y is device (B, H, Sp, D) with Sp >= bsa_padded_length of every
+ * candidate; y[b,h,p,:] = x[b,h,perm_c[p],:] with perm_c from
+ * bsa_tile_permutation_padded, and zero rows where perm_c[p] = -1 or p is
+ * past the padded length of candidate c [Adaptive tiling (SPADE),
+ * "Deviations and notes": pad with zero tokens].  labels_or_null: device
+ * int32 (B, H, Sp), written 0 for real rows and -1 for padding (the labels
+ * of bsa_minmax_block_scores_masked and bsa_block_sparse_attention_labels),
+ * or NULL.  INVALID_ARG if a tile extent is <= 0 or Sp is too short. */
+int bsa_tile_permute_padded(const void* x, void* y, int dtype, int64_t B, int64_t H, int T, int Hg,
+                            int Wg, int64_t D, const int32_t* tiles_host, int n_tiles,
+                            const int32_t* head_choice, int64_t Sp, int32_t* labels_or_null,
+                            bsa_stream_t stream);
+
+/* Inverse of bsa_tile_permute_padded: x[b,h,perm_c[p],:] = y[b,h,p,:] for
+ * the real rows (padding rows are dropped); y (B, H, Sp, D), x (B, H, S, D). */
+int bsa_invert_permute_padded(const void* y, void* x, int dtype, int64_t B, int64_t H, int T, int Hg,
+                              int Wg, int64_t D, const int32_t* tiles_host, int n_tiles,
+                              const int32_t* head_choice, int64_t Sp, bsa_stream_t stream);
 
 /* Cohesion (SICS) of every run of `block` consecutive tokens:
  *   coh[b,h,i] = mean over ordered pairs u != w of non-zero-norm tokens of
@@ -144,6 +195,23 @@ int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H, int T, int
                       int64_t D, const int32_t* tiles_host, int n_tiles, float* tile_coh,
                       float* score, int32_t* choice, bsa_stream_t stream);
 
+/* bsa_select_tiling with a choice of statistic and padded candidates.
+ * statistic BSA_STAT_MEAN is bsa_select_tiling's rule; BSA_STAT_POOLED is
+ * SPADE's engine rule [Adaptive tiling (SPADE), "Deviations and notes",
+ * selection statistic]: per candidate, the sum over tiles of the sum over
+ * ordered pairs i != j of cos(q_i, q_j) divided by the number of such pairs,
+ * every token counted (a pair with a zero-norm token has similarity 0).
+ * pad = 1 accepts candidates that do not divide the grid and scores them on
+ * the zero-padded grid: padding is left out of the mean rule and is not
+ * counted by the pooled rule; pad = 0 rejects them like bsa_select_tiling.
+ * tile_coh: device float[B*H*n_tiles*maxNb], maxNb = max over candidates of
+ * bsa_padded_length/(a*b*c) (per-tile values: the cohesion, or for the
+ * pooled rule its numerator).  INVALID_ARG on an unknown statistic, pad not
+ * in {0, 1}, or a bad candidate. */
+int bsa_select_tiling_ex(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
+                         int64_t D, const int32_t* tiles_host, int n_tiles, int statistic, int pad,
+                         float* tile_coh, float* score, int32_t* choice, bsa_stream_t stream);
+
 /* Min/max block summaries and estimated block scores of tile-contiguous q, k:
  *   qmax_I = elementwise max over block I of q, qmin_I the min (and kmax, kmin),
  *   scores[b,h,I,J] = max((qmax_I + qmin_I) . kmax_J, (qmax_I + qmin_I) . kmin_J)
@@ -156,6 +224,16 @@ int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H, int T, int
 int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
                             int64_t S, int64_t D, int block, void* summaries, float* scores,
                             bsa_stream_t stream);
+
+/* bsa_minmax_block_scores over labelled tokens only: tokens with
+ * labels[b,h,s] < 0 (padding) are left out of the summaries, so a partial
+ * block is summarised by its real tokens [Adaptive tiling (SPADE),
+ * "Deviations and notes": padded grids].  A block with no such token scores
+ * -inf in its whole row and column.  labels_or_null: device int32 (B, H, S)
+ * (NULL: every token counts). */
+int bsa_minmax_block_scores_masked(const void* q, const void* k, int dtype, int64_t B, int64_t H,
+                                   int64_t S, int64_t D, int block, const int32_t* labels_or_null,
+                                   void* summaries, float* scores, bsa_stream_t stream);
 
 /* Per-row block selection: keep the k best key blocks of each (b, h, I) row,
  * ranked by score (higher first) and then by index (lower first), then add
@@ -189,6 +267,21 @@ int bsa_top_p_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int 
                          int32_t* kv_cnt, int max_kept, uint8_t* mask_or_null,
                          bsa_stream_t stream);
 
+/* bsa_topk_block_mask with a per-head budget and block count: head (b, h)
+ * uses k = k_table[c] and nk = nk_table[c], c = head_choice[b*H + h]
+ * (device int32, trusted to lie in [0, n_table)).  Only key blocks J < nk
+ * exist for the head (the sink blocks and the band are clipped to them) and
+ * query rows I >= nk keep nothing (count 0).  This is the padded recipe,
+ * where every candidate tiling has its own padded block count and the
+ * budget is floor(frac * that count) [Adaptive tiling (SPADE), "Recipe" and
+ * "Deviations and notes"].  k_table, nk_table: host int32[n_table],
+ * 1 <= k <= nk <= Nk.  max_kept >= min(max nk, max k + sink + band). */
+int bsa_topk_block_mask_tiled(const float* scores, int64_t B, int64_t H, int Nq, int Nk,
+                              const int32_t* head_choice, const int32_t* k_table_host,
+                              const int32_t* nk_table_host, int n_table, int sink_blocks,
+                              int diag_width, int32_t* kv_idx, int32_t* kv_cnt, int max_kept,
+                              uint8_t* mask_or_null, bsa_stream_t stream);
+
 /* Block-sparse attention: for every query block I of `block` tokens,
  *   out_I = softmax(scale * q_I k_K^T) v_K,  K = the tokens of the key blocks
  *           kv_idx[b,h,I,0..kv_cnt[b,h,I])
@@ -209,6 +302,24 @@ int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void
                                int64_t B, int64_t H, int64_t S, int64_t D, int block,
                                const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
                                float scale, bsa_stream_t stream);
+
+/* bsa_block_sparse_attention with a token label rule inside the kept
+ * blocks: query i sees key j when j's block is kept for i's block AND
+ * labels[i] == labels[j].  Padding of a padded tiling is labelled -1 and
+ * real tokens 0, so padded keys are masked out of every real row
+ * [Adaptive tiling (SPADE), "Deviations and notes": mask the padded keys];
+ * frame indices give spatial-only and spatial positions temporal-only
+ * attention [ADR-0001, "Décision" step 1].  labels: device int32 with
+ * element (b, h, s) at labels[(b*H + h)*label_head_stride + s]
+ * (label_head_stride 0: one row shared by every head, else >= S).  A query
+ * row that sees no key is written as zeros.  Other arguments as
+ * bsa_block_sparse_attention (kv_cnt may be 0 for rows that keep nothing). */
+int bsa_block_sparse_attention_labels(const void* q, const void* k, const void* v, void* out,
+                                      int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                                      int block, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                      int max_kept, const int32_t* labels,
+                                      int64_t label_head_stride, float scale,
+                                      bsa_stream_t stream);
 
 /* Symmetric sliding-window attention with sinks: query i sees key j when
  * abs(i - j) <= window/2 (integer division) or j < sink

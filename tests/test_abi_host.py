@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import blocks as OB
+from oracle import pipeline as OP
 from oracle import tiling as OT
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -28,7 +29,7 @@ def L():
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const char\*|int)\s+(bsa_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int64_t|int)\s+(bsa_\w+)\s*\(", text, re.M)))
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -92,11 +93,52 @@ def test_sliding_tile_lists_bit_exact(L, tg, rad):
         bsa.bsa_sliding_tile_block_list(tg, rad, max_kept=int(cnt.max()) - 1)
 
 
+@pytest.mark.parametrize("grid,tile", [((20, 32, 48), (16, 2, 2)), ((16, 45, 80), (1, 8, 8)), ((3, 5, 6), (2, 2, 4)),
+                                       ((4, 8, 8), (2, 4, 4)), ((1, 1, 5), (2, 2, 2))])
+def test_padded_permutation_bit_exact(L, grid, tile):
+    got = bsa.bsa_tile_permutation_padded(*grid, tile)
+    want = OT.padded_tile_permutation(grid, tile)
+    assert bsa.bsa_padded_length(*grid, tile) == want.size == int(np.prod(OT.padded_grid(grid, tile)))
+    assert np.array_equal(got, want)
+    with pytest.raises(ValueError):
+        bsa.bsa_padded_length(0, 4, 4, tile)
+
+
+@pytest.mark.parametrize("grid,block,kind", [((5, 4, 4), 16, "temporal"), ((3, 4, 4), 8, "spatial"),
+                                             ((20, 32, 48), 64, "temporal"), ((20, 32, 48), 64, "spatial"),
+                                             ((3, 6, 5), 8, "padded")])
+def test_label_block_lists_bit_exact(L, grid, block, kind):
+    T, Hg, Wg = grid
+    if kind == "spatial":
+        lab = np.arange(T * Hg * Wg) // (Hg * Wg)
+    elif kind == "temporal":
+        lab = OT.tile_permutation(grid, (T, 1, 1)) % (Hg * Wg)
+    else:   # padding labelled -1 never matches
+        perm = OT.padded_tile_permutation(grid, (2, 2, 2))
+        lab = np.where(perm >= 0, 0, -1)
+    idx, cnt = bsa.bsa_label_block_list(lab, block)
+    if lab.size <= 4096:
+        keep = OP.label_block_keep(lab, block)
+    else:   # the oracle's brute force over 480^2 block pairs, on the structure it must have
+        nb = lab.size // block
+        sets = [set(lab[i * block:(i + 1) * block].tolist()) for i in range(nb)]
+        keep = np.array([[bool(sets[i] & sets[j]) for j in range(nb)] for i in range(nb)])
+    lists, ocnt = OB.keep_to_lists(keep)
+    assert np.array_equal(cnt, ocnt)
+    for i, li in enumerate(lists):
+        assert np.array_equal(idx[i, :cnt[i]], li)
+    with pytest.raises(ValueError):
+        bsa.bsa_label_block_list(lab, block, max_kept=int(cnt.max()) - 1)
+
+
 # --- argument validation of device calls: all rejected on the host --------
 
 FAKE = ctypes.c_void_p(4096)  # never dereferenced: every case below fails validation first
 TILES = (ctypes.c_int32 * 6)(1, 8, 8, 4, 4, 4)
 BAD_TILES = (ctypes.c_int32 * 3)(16, 2, 2)
+K_TAB = (ctypes.c_int32 * 2)(81, 130)
+NK_TAB = (ctypes.c_int32 * 2)(480, 768)
+NK_BAD = (ctypes.c_int32 * 2)(480, 769)
 
 
 def _rc(L, name, *args):
@@ -146,6 +188,28 @@ def test_device_calls_reject_bad_arguments(L):
         ("bsa_windowed_attention", (None, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, 2, ctypes.c_float(0.25), 8, None),
          "NULL"),
         ("bsa_validate_block_list", (FAKE, FAKE, 1, 1, 0, 4, 4, None), ">= 1"),
+        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, TILES, 2, 7, 0, FAKE, FAKE, FAKE, None),
+         "statistic"),
+        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, 0, 0, FAKE, FAKE, FAKE, None),
+         "divide"),
+        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, TILES, 2, 0, 2, FAKE, FAKE, FAKE, None), "pad"),
+        ("bsa_tile_permute_padded", (FAKE, ctypes.c_void_p(1 << 30), BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, None,
+                                     30720, None, None), "shorter"),
+        ("bsa_tile_permute_padded", (FAKE, ctypes.c_void_p(1 << 30), BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, None,
+                                     0, None, None), "Sp"),
+        ("bsa_invert_permute_padded", (FAKE, ctypes.c_void_p(1 << 30), BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1,
+                                       None, 40000, None), "shorter"),
+        ("bsa_minmax_block_scores_masked", (FAKE, FAKE, BF, 1, 2, 100, 128, 64, FAKE, FAKE, FAKE, None), "divide"),
+        ("bsa_topk_block_mask_tiled", (FAKE, 1, 1, 768, 768, FAKE, K_TAB, NK_BAD, 2, 1, 1, FAKE, FAKE, 140, None,
+                                       None), "nk_table"),
+        ("bsa_topk_block_mask_tiled", (FAKE, 1, 1, 768, 768, FAKE, K_TAB, NK_TAB, 2, 1, 1, FAKE, FAKE, 100, None,
+                                       None), "max_kept"),
+        ("bsa_block_sparse_attention_labels",
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 128, 128, 64, FAKE, FAKE, 2, FAKE, 5, ctypes.c_float(0.1), None),
+         "stride"),
+        ("bsa_block_sparse_attention_labels",
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 128, 128, 64, FAKE, FAKE, 2, None, 0, ctypes.c_float(0.1), None),
+         "NULL"),
         ("bsa_validate_indices", (None, 4, 0, 3, None), "NULL"),
     ]
     for name, args, needle in cases:

@@ -1,0 +1,322 @@
+"""Padded grids, the pooled statistic, per-head budgets, label-masked
+attention and the spatial-only / temporal-only masks, against the oracle."""
+import numpy as np
+import pytest
+
+from block_sparse_attention_permute_amd import bsa, synth
+from oracle import attention as OA
+from oracle import blocks as OB
+from oracle import pipeline as OP
+from oracle import tiling as OT
+from tests.gpu_helpers import BF16_ATOL, F32_ATOL, TOPK_REL, f64, gpu, max_abs, torch_gpu
+
+WAN_GRID = (20, 32, 48)
+
+
+def _gather_padded(x_head, perm):
+    valid = perm >= 0
+    return np.where(valid[:, None], x_head[np.where(valid, perm, 0)], 0.0)
+
+
+# --------------------------------------------------------------- permutes ---
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,grid,tiles", [("bf16", (3, 5, 6), [(2, 2, 4), (1, 4, 8)]),
+                                              ("f32", (5, 3, 7), [(2, 2, 2), (4, 1, 3), (5, 3, 7)]),
+                                              ("bf16", (20, 32, 48), [(16, 2, 2), (1, 8, 8)])])
+def test_padded_permute_roundtrip(dtype, grid, tiles):
+    torch = torch_gpu()
+    T, Hg, Wg = grid
+    S, H = T * Hg * Wg, 4
+    D = 128 if S > 10000 else 16
+    x = synth.normal_bits((1, H, S, D), seed=S + D, dtype=dtype)
+    choice = torch.tensor([[h % len(tiles) for h in range(H)]], dtype=torch.int32).cuda()
+    y, lab = bsa.bsa_tile_permute_padded(gpu(x), grid, tiles, head_choice=choice)
+    Sp = max(int(np.prod(OT.padded_grid(grid, t))) for t in tiles)
+    assert tuple(y.shape) == (1, H, Sp, D)
+    yb, lb = f64(y), lab.cpu().numpy()
+    xf = synth.stored_to_f64(x)
+    for h in range(H):
+        perm = OT.padded_tile_permutation(grid, tiles[h % len(tiles)])
+        perm = np.concatenate([perm, -np.ones(Sp - perm.size, np.int64)])
+        assert np.array_equal(yb[0, h], _gather_padded(xf[0, h], perm))
+        assert np.array_equal(lb[0, h], np.where(perm >= 0, 0, -1))
+    back = bsa.bsa_invert_permute_padded(y, grid, tiles, head_choice=choice)
+    assert np.array_equal(synth.from_torch(back), x)
+
+
+# ------------------------------------------------------ tiling selection ---
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("statistic,pad", [("pooled", False), ("mean", True), ("pooled", True)])
+def test_select_tiling_pooled_and_padded(statistic, pad):
+    torch = torch_gpu()
+    grid = (4, 8, 8) if not pad else (5, 9, 10)
+    tiles = [(1, 4, 8), (4, 2, 4), (2, 4, 4)]
+    S = int(np.prod(grid))
+    q = synth.normal_bits((1, 4, S, 64), seed=700 + int(pad))
+    q[0, 1, :40] = 0                                        # zero-norm tokens: counted by pooled, not by mean
+    choice, score, _ = bsa.bsa_select_tiling(gpu(q), grid, tiles, statistic=statistic, pad=pad)
+    oc, osc = OT.select_tiling(synth.stored_to_f64(q), grid, tiles, statistic=statistic, pad=pad)
+    got = score.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - osc)) < 2e-5
+    ch = choice.cpu().numpy()
+    for h in range(4):
+        if ch[0, h] != oc[0, h]:
+            a, b = osc[0, h, ch[0, h]], osc[0, h, oc[0, h]]
+            assert abs(a - b) < TOPK_REL * abs(b)
+
+
+@pytest.mark.gpu
+def test_select_tiling_wan_shape_with_padded_candidate():
+    """Wan 2.1 grid with all three SPADE candidates; (16, 2, 2) scored on the padded grid."""
+    torch = torch_gpu()
+    heads = [0, 3, 9, 21]
+    tiles = [(1, 8, 8), (4, 4, 4), (16, 2, 2)]
+    q = synth.tensor_bits(4, synth.ROLE_Q, heads=heads)
+    for statistic in ("mean", "pooled"):
+        choice, score, _ = bsa.bsa_select_tiling(gpu(q), WAN_GRID, tiles, statistic=statistic, pad=True)
+        oc, osc = OT.select_tiling(synth.stored_to_f64(q), WAN_GRID, tiles, statistic=statistic, pad=True)
+        assert np.max(np.abs(score.cpu().numpy() - osc)) < 2e-5
+        ch = choice.cpu().numpy()
+        for h in range(len(heads)):
+            if ch[0, h] != oc[0, h]:
+                a, b = osc[0, h, ch[0, h]], osc[0, h, oc[0, h]]
+                assert abs(a - b) < TOPK_REL * abs(b)
+
+
+# ------------------------------------------------------- masked summaries ---
+
+@pytest.mark.gpu
+def test_minmax_scores_masked():
+    torch = torch_gpu()
+    S, D, block = 640, 128, 64
+    q, k = (synth.normal_bits((1, 2, S, D), seed=710 + i) for i in range(2))
+    rng = np.random.default_rng(3)
+    lab = np.where(rng.random((1, 2, S)) < 0.2, -1, 0).astype(np.int32)
+    lab[0, 0, 128:192] = -1                                   # a block with no real token
+    scores, summ = bsa.bsa_minmax_block_scores(gpu(q), gpu(k), block, labels=torch.from_numpy(lab).cuda())
+    got = scores.cpu().numpy().astype(np.float64)[0]
+    qf, kf = synth.stored_to_f64(q), synth.stored_to_f64(k)
+    for h in range(2):
+        valid = lab[0, h] >= 0
+        nb = S // block
+        ok = np.array([valid[i * block:(i + 1) * block].any() for i in range(nb)])
+        want = np.full((nb, nb), -np.inf)
+        vq = np.where(ok.repeat(block), valid, True)        # the oracle needs a token per block
+        sub = OB.minmax_block_scores_valid(qf[0, h], kf[0, h], vq, block)
+        want[np.ix_(ok, ok)] = sub[np.ix_(ok, ok)]
+        assert np.array_equal(np.isinf(got[h]), np.isinf(want))
+        fin = np.isfinite(want)
+        # fp32 dot products of length D: error <= (D + 2) u sum_d |c_d| max(|kmax_d|, |kmin_d|)
+        qmax, qmin = OB.block_minmax_valid(qf[0, h], vq, block)
+        kmax, kmin = OB.block_minmax_valid(kf[0, h], vq, block)
+        bound = np.abs(qmax + qmin) @ np.maximum(np.abs(kmax), np.abs(kmin)).T
+        err = np.abs(got[h] - np.where(fin, want, 0.0))
+        assert np.all(err[fin] <= (D + 2) * 2.0 ** -24 * bound[fin] + 1e-30)
+
+
+# ------------------------------------------------------- per-head budgets ---
+
+@pytest.mark.gpu
+def test_topk_tiled_per_head_budgets():
+    torch = torch_gpu()
+    rng = np.random.default_rng(5)
+    B, H, N = 1, 4, 300
+    s = (rng.standard_normal((B, H, N, N)) * 10).astype(np.float32)
+    choice = np.array([[0, 1, 2, 1]], np.int32)
+    k_tab, nk_tab = [40, 12, 70], [300, 100, 250]
+    kv_idx, kv_cnt, mask = bsa.bsa_topk_block_mask_tiled(torch.from_numpy(s).cuda(), torch.from_numpy(choice).cuda(),
+                                                         k_tab, nk_tab, 5, 40, return_mask=True)
+    idx, cnt, m = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), mask.cpu().numpy().astype(bool)
+    for h in range(H):
+        c = choice[0, h]
+        nk, k = nk_tab[c], k_tab[c]
+        keep = OB.topk_block_mask(s[0, h, :nk, :nk].astype(np.float64), k, 5, 40)
+        assert np.array_equal(m[0, h, :nk, :nk], keep)
+        assert not m[0, h, :, nk:].any() and not m[0, h, nk:].any()
+        assert np.all(cnt[0, h, nk:] == 0)
+        for I in range(nk):
+            li = np.flatnonzero(keep[I])
+            assert cnt[0, h, I] == li.size and np.array_equal(idx[0, h, I, :li.size], li)
+
+
+# ------------------------------------------------- label-masked attention ---
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,D,block,shared", [("bf16", 128, 64, True), ("bf16", 128, 64, False),
+                                                  ("bf16", 64, 32, False), ("f32", 16, 16, True)])
+def test_block_sparse_attention_labels(dtype, D, block, shared):
+    torch = torch_gpu()
+    S, H = 512, 2
+    rng = np.random.default_rng(D + block)
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=720 + i, dtype=dtype) for i in range(3))
+    nb = S // block
+    keep = rng.random((1, H, nb, nb)) < 0.5
+    keep[..., np.arange(nb), np.arange(nb)] = True
+    lab = rng.integers(0, 3, (1, H, S)).astype(np.int32)
+    lab[:, :, 5] = -1                                   # a padding token
+    lab[:, :, 7] = 9                                    # a label found nowhere else: its row sees only itself
+    if shared:
+        lab[:, 1] = lab[:, 0]
+    cnt = keep.sum(-1).astype(np.int32)
+    idx = np.full((1, H, nb, nb), -1, np.int32)
+    for h in range(H):
+        for I in range(nb):
+            li = np.flatnonzero(keep[0, h, I])
+            idx[0, h, I, :li.size] = li
+    lt = torch.from_numpy(lab[0, 0] if shared else lab).cuda()
+    out = bsa.bsa_block_sparse_attention_labels(gpu(q), gpu(k), gpu(v), torch.from_numpy(idx).cuda(),
+                                                torch.from_numpy(cnt).cuda(), block, lt)
+    got = f64(out)
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (q, k, v))
+    tol = BF16_ATOL if dtype == "bf16" else F32_ATOL
+    for h in range(H):
+        want = OP.label_equal_attention(qf[0, h], kf[0, h], vf[0, h], lab[0, h], D ** -0.5, keep[0, h], block)
+        assert max_abs(got[0, h], want) <= tol, h
+
+
+@pytest.mark.gpu
+def test_labels_row_without_keys_is_zero():
+    torch = torch_gpu()
+    S, D = 128, 128
+    q, k, v = (synth.normal_bits((1, 1, S, D), seed=730 + i) for i in range(3))
+    lab = np.zeros(S, np.int32)
+    lab[:64] = 1                       # block 0 only keeps block 1, whose keys carry label 0
+    idx = torch.tensor([[[[1, -1], [0, 1]]]], dtype=torch.int32).cuda()
+    cnt = torch.tensor([[[1, 2]]], dtype=torch.int32).cuda()
+    out = f64(bsa.bsa_block_sparse_attention_labels(gpu(q), gpu(k), gpu(v), idx, cnt, 64, torch.from_numpy(lab).cuda()))
+    assert np.all(out[0, 0, :64] == 0.0)
+    qf, kf, vf = (synth.stored_to_f64(x)[0, 0] for x in (q, k, v))
+    rows = np.arange(64, 128)
+    allowed = lab[rows][:, None] == lab[None, :]          # block 1 keeps blocks 0 and 1
+    want = OA.masked_attention_rows(qf[rows], kf, vf, np.where(allowed, 0.0, -np.inf), D ** -0.5)
+    assert max_abs(out[0, 0, rows], want) <= BF16_ATOL
+
+
+# ------------------------------------------------ spatial / temporal masks ---
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kind,D", [("spatial", 128), ("temporal", 128), ("spatial", 64), ("temporal", 64)])
+def test_spatial_temporal_attention_small(kind, D):
+    torch_gpu()
+    grid = (4, 8, 16)
+    S = 512
+    q, k, v = (synth.normal_bits((1, 2, S, D), seed=740 + i) for i in range(3))
+    out = f64(bsa.video_label_attention(gpu(q), gpu(k), gpu(v), grid, kind))
+    mask = OA.spatial_only_mask(grid) if kind == "spatial" else OA.temporal_only_mask(grid)
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (q, k, v))
+    for h in range(2):
+        want = OA.masked_attention(qf[0, h], kf[0, h], vf[0, h], mask, D ** -0.5)
+        assert max_abs(out[0, h], want) <= BF16_ATOL, h
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kind", ["spatial", "temporal"])
+def test_spatial_temporal_attention_wan_shape(kind):
+    """Wan 2.1 grid (S = 30720), two heads; sampled rows against the dense definition."""
+    torch = torch_gpu()
+    heads = [0, 1]
+    q, k, v = (synth.tensor_bits(4, role, heads=heads) for role in (synth.ROLE_Q, synth.ROLE_K, synth.ROLE_V))
+    out = bsa.video_label_attention(gpu(q), gpu(k), gpu(v), WAN_GRID, kind)
+    T, Hg, Wg = WAN_GRID
+    S = T * Hg * Wg
+    rng = np.random.default_rng(1)
+    rows = np.concatenate([[0, 1535, 1536, S - 1], rng.integers(0, S, 12)])
+    got = f64(out[:, :, torch.from_numpy(rows).cuda()])
+    j = np.arange(S)
+    for h in range(2):
+        qf, kf, vf = (synth.stored_to_f64(x[0, h]) for x in (q, k, v))
+        if kind == "spatial":
+            allowed = (rows[:, None] // (Hg * Wg)) == (j[None, :] // (Hg * Wg))
+        else:
+            allowed = (rows[:, None] % (Hg * Wg)) == (j[None, :] % (Hg * Wg))
+        want = OA.masked_attention_rows(qf[rows], kf, vf, np.where(allowed, 0.0, -np.inf), 128 ** -0.5)
+        assert max_abs(got[0, h], want) <= BF16_ATOL, h
+
+
+# ---------------------------------------------------------- padded recipe ---
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("statistic", ["mean", "pooled"])
+def test_padded_pipeline_small_grid_every_output(statistic):
+    """The recipe on a grid no candidate divides; every output against the oracle."""
+    torch = torch_gpu()
+    grid, tiles = (5, 10, 12), [(4, 4, 4), (1, 8, 8)]
+    H, D = 3, 128
+    S = 600
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=750 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    pipe = bsa.AdaptiveBlockSparse(1, H, grid, D, tiles, 0.3, qg.dtype, qg.device, sink_blocks=1, keep_diag=3,
+                                   statistic=statistic, pad=True)
+    out = f64(pipe(qg, kg, vg))
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (q, k, v))
+    ref = OP.padded_adaptive_block_sparse(qf, kf, vf, grid, tiles, 0.3, sink_blocks=1, keep_diag=3,
+                                          statistic=statistic)
+    choice = pipe.choice.cpu().numpy()
+    kv_idx, kv_cnt = pipe.kv
+    idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    checked = 0
+    for h in range(H):
+        if choice[0, h] != ref["choice"][0, h]:
+            a, b = ref["tiling_score"][0, h, choice[0, h]], ref["tiling_score"][0, h, ref["choice"][0, h]]
+            assert abs(a - b) < TOPK_REL * abs(b)
+            continue
+        keep = ref["keep"][h]
+        nb = keep.shape[0]
+        gkeep = np.zeros_like(keep)
+        for I in range(nb):
+            gkeep[I, idx[0, h, I, :cnt[0, h, I]]] = True
+        for I, J in zip(*np.nonzero(gkeep != keep)):
+            assert OB.near_tie_ok(ref["scores"][h][I], ref["k"][h], J, TOPK_REL), (h, I, J)
+        if np.array_equal(gkeep, keep):
+            assert max_abs(out[0, h], ref["out"][0, h]) <= BF16_ATOL, h
+            checked += 1
+    assert checked >= 1
+
+
+@pytest.mark.gpu
+def test_padded_pipeline_wan_shape_with_16_2_2():
+    """Wan 2.1 grid with all three SPADE candidates, (16, 2, 2) padded to T = 32.
+    Sampled heads: choice, kept lists (near ties aside) and sampled output rows."""
+    torch = torch_gpu()
+    wl = synth.WORKLOADS[4]
+    tiles = [(1, 8, 8), (4, 4, 4), (16, 2, 2)]
+    q, k, v = synth.qkv(4)
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, tiles, 0.17, qg.dtype, qg.device, pad=True)
+    out = pipe(qg, kg, vg)
+    torch.cuda.synchronize()
+    assert pipe.k_table == [81, 81, 130] and pipe.Sp == 49152
+    choice = pipe.choice.cpu().numpy()
+    kv_idx, kv_cnt = pipe.kv
+    idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    rng = np.random.default_rng(4)
+    heads = [0, 11, 25, 38]
+    qs = synth.stored_to_f64(q[:, heads])
+    oc, osc = OT.select_tiling(qs, wl.grid, tiles, pad=True)
+    for n, h in enumerate(heads):
+        c = int(choice[0, h])
+        if c != oc[0, n]:
+            a, b = osc[0, n, c], osc[0, n, oc[0, n]]
+            assert abs(a - b) < TOPK_REL * abs(b)
+        perm = OT.padded_tile_permutation(wl.grid, tiles[c])
+        valid = perm >= 0
+        qp, kp, vp = (_gather_padded(synth.stored_to_f64(x[0, h]), perm) for x in (q, k, v))
+        nb = perm.size // 64
+        scores = OB.minmax_block_scores_valid(qp, kp, valid, 64)
+        kk = OB.budget(0.17, nb)
+        okeep = OB.topk_block_mask(scores, kk, 1, True)
+        gkeep = np.zeros((nb, nb), bool)
+        for I in range(nb):
+            gkeep[I, idx[0, h, I, :cnt[0, h, I]]] = True
+        for I, J in zip(*np.nonzero(okeep != gkeep)):
+            assert J != 0 and J != I
+            assert OB.near_tie_ok(scores[I], kk, J, TOPK_REL), (h, I, J)
+        # sampled real rows, attended over the GPU's lists with padded keys masked
+        real_pos = np.flatnonzero(valid)
+        rows_p = np.sort(rng.choice(real_pos, 12, replace=False))
+        allowed = gkeep[rows_p // 64][:, np.arange(perm.size) // 64] & valid[None, :]
+        want = OA.masked_attention_rows(qp[rows_p], kp, vp, np.where(allowed, 0.0, -np.inf), 128 ** -0.5)
+        got = f64(out[0, h, torch.from_numpy(perm[rows_p]).cuda()])
+        assert max_abs(got, want) <= BF16_ATOL, h
