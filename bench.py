@@ -155,6 +155,41 @@ def sweep(args, torch, np, bsa, synth):
                       "attention_tflops_token_exact": round(fl_tok / ms / 1e9, 2), "visible_pairs_per_head": pairs}),
           flush=True)
 
+    # Wan shape variants: SPADE's static widths, top-p, the pooled statistic, padded (16, 2, 2),
+    # spatial-only and temporal-only attention
+    wl = synth.WORKLOADS[4]
+    q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(4))
+    variants = [
+        ("wan sink 5 + band 40", dict(tiles=[(1, 8, 8), (4, 4, 4)], sink_blocks=5, keep_diag=40)),
+        ("wan top-p 0.9 (scores / sqrt(D))", dict(tiles=[(1, 8, 8), (4, 4, 4)], top_p=0.9, p_scale=wl.D ** -0.5)),
+        ("wan pooled statistic", dict(tiles=[(1, 8, 8), (4, 4, 4)], statistic="pooled")),
+        ("wan padded, candidates (1,8,8) (4,4,4) (16,2,2)", dict(tiles=[(1, 8, 8), (4, 4, 4), (16, 2, 2)], pad=True)),
+    ]
+    out = torch.empty_like(q)
+    for name, kw in variants:
+        tiles = kw.pop("tiles")
+        pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, tiles, 0.17, q.dtype, dev, **kw)
+        ms_step = _time(torch, lambda: pipe(q, k, v, out=out), max(steps // 2, 3), warmup)
+        kv_idx, kv_cnt = pipe.kv
+        fn = (bsa.bsa_block_sparse_attention_labels if pipe.pad else bsa.bsa_block_sparse_attention)
+        extra = (pipe.labels,) if pipe.pad else ()
+        ms = _time(torch, lambda: fn(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, 64, *extra, out=pipe.op),
+                   max(steps // 2, 3), warmup)
+        kept = int(kv_cnt.sum().item())
+        fl = kept * 4 * 64 * 64 * wl.D
+        choice = np.bincount(pipe.choice.cpu().numpy().ravel(), minlength=len(tiles)).tolist()
+        print(json.dumps({"workload": name, "attention_ms": round(ms, 4), "attention_tflops": round(fl / ms / 1e9, 2),
+                          "step_ms": round(ms_step, 4), "step_tflops": round(fl / ms_step / 1e9, 2),
+                          "kept_blocks": kept, "heads_per_candidate": choice}), flush=True)
+    S, HW = wl.S, wl.grid[1] * wl.grid[2]
+    for kind, pairs in (("spatial", S * HW), ("temporal", S * wl.grid[0])):
+        att = bsa.VideoLabelAttention(1, wl.H, wl.grid, kind, dev)
+        ms = _time(torch, lambda: att(q, k, v, out=out), max(steps // 2, 3), warmup)
+        fl_tok = pairs * 4 * wl.D * wl.H
+        print(json.dumps({"workload": f"wan {kind}-only attention (permute + label attention + inverse)",
+                          "ms": round(ms, 4), "tflops_token_exact": round(fl_tok / ms / 1e9, 2),
+                          "visible_pairs_per_head": pairs}), flush=True)
+
     # long sequence: grid 32x48x80 (S=122880), tiles 4x4x4, 10% budget, D=128, H=24
     wl = synth.WORKLOADS[5]
     q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(5))

@@ -641,36 +641,51 @@ class AdaptiveBlockSparse:
         return bsa_invert_permute(self.op, self.grid, self.tiles, head_choice=choice, out=out)
 
 
-def video_label_attention(q, k, v, grid, kind: str, block: int = 64, scale=None):
-    """Spatial-only or temporal-only attention of T-major q, k, v as block lists plus labels.
+class VideoLabelAttention:
+    """Spatial-only or temporal-only attention of T-major (B, H, S, D) tensors.
 
-    kind "spatial": a token sees the tokens of its frame (labels = frame
+    kind "spatial": a token sees the tokens of its own frame (labels = frame
     index, T-major order, block lists of the frames' blocks).  kind
-    "temporal": a token sees the tokens at its (y, x) in every frame; the
+    "temporal": a token sees the tokens at its own (y, x) in every frame; the
     tokens are permuted with tiles (T, 1, 1) so that each position's frames
     are contiguous, labelled by position, attended, and permuted back.
     [ADR-0001, "Décision" step 1: spatial_only_mask, temporal_only_mask.]
+    Block lists and labels are built once (host, then copied to the device);
+    a call is a sequence of libbsa launches on the current stream.
     """
-    torch = _torch()
-    B, H, S, D = _qkv(q, k, v)
-    T, Hg, Wg = (int(g) for g in grid)
-    if T * Hg * Wg != S:
-        raise ValueError(f"grid {tuple(grid)} does not match S={S}")
-    if kind == "spatial":
-        lab = np.arange(S, dtype=np.int32) // (Hg * Wg)
-        tiles = None
-    elif kind == "temporal":
-        tiles = [(T, 1, 1)]
-        lab = (bsa_tile_permutation(T, Hg, Wg, (T, 1, 1)) % (Hg * Wg)).astype(np.int32)
-    else:
-        raise ValueError(f"kind must be 'spatial' or 'temporal', got {kind!r}")
-    idx, cnt = bsa_label_block_list(lab, block)
-    nb = S // block
-    kv_idx = torch.from_numpy(np.broadcast_to(idx, (B, H) + idx.shape).copy()).to(q.device)
-    kv_cnt = torch.from_numpy(np.broadcast_to(cnt, (B, H, nb)).copy()).to(q.device)
-    labels = torch.from_numpy(lab).to(q.device)
-    if tiles is None:
-        return bsa_block_sparse_attention_labels(q, k, v, kv_idx, kv_cnt, block, labels, scale)
-    qp, kp, vp = (bsa_tile_permute(x, grid, tiles) for x in (q, k, v))
-    op = bsa_block_sparse_attention_labels(qp, kp, vp, kv_idx, kv_cnt, block, labels, scale)
-    return bsa_invert_permute(op, grid, tiles)
+
+    def __init__(self, B, H, grid, kind: str, device, block: int = 64):
+        torch = _torch()
+        self.grid = tuple(int(g) for g in grid)
+        T, Hg, Wg = self.grid
+        S = T * Hg * Wg
+        if kind == "spatial":
+            lab = np.arange(S, dtype=np.int32) // (Hg * Wg)
+            self.tiles = None
+        elif kind == "temporal":
+            self.tiles = [(T, 1, 1)]
+            lab = (bsa_tile_permutation(T, Hg, Wg, (T, 1, 1)) % (Hg * Wg)).astype(np.int32)
+        else:
+            raise ValueError(f"kind must be 'spatial' or 'temporal', got {kind!r}")
+        if S % block:
+            raise ValueError(f"block {block} must divide S={S}")
+        self.kind, self.block, self.S = kind, int(block), S
+        idx, cnt = bsa_label_block_list(lab, self.block)
+        nb = S // self.block
+        self.kv_idx = torch.from_numpy(np.broadcast_to(idx, (B, H) + idx.shape).copy()).to(device)
+        self.kv_cnt = torch.from_numpy(np.broadcast_to(cnt, (B, H, nb)).copy()).to(device)
+        self.labels = torch.from_numpy(lab).to(device)
+
+    def __call__(self, q, k, v, scale=None, out=None):
+        if self.tiles is None:
+            return bsa_block_sparse_attention_labels(q, k, v, self.kv_idx, self.kv_cnt, self.block, self.labels, scale,
+                                                     out=out)
+        qp, kp, vp = (bsa_tile_permute(x, self.grid, self.tiles) for x in (q, k, v))
+        op = bsa_block_sparse_attention_labels(qp, kp, vp, self.kv_idx, self.kv_cnt, self.block, self.labels, scale)
+        return bsa_invert_permute(op, self.grid, self.tiles, out=out)
+
+
+def video_label_attention(q, k, v, grid, kind: str, block: int = 64, scale=None, out=None):
+    """One-shot VideoLabelAttention (builds the block lists on every call)."""
+    B, H, _, _ = _bhsd(q, "q")
+    return VideoLabelAttention(B, H, grid, kind, q.device, block)(q, k, v, scale, out)
