@@ -1,9 +1,13 @@
 """Benchmark: adaptive-tiling block-sparse attention at the Wan 2.1 latent shape.
 
 One step = the whole hot path over one batch already resident in HBM:
-  select tiling (cohesion of q under (1,8,8) and (4,4,4)) -> permute q, k, v
-  -> min/max block scores -> top-k (81 of 480, + sink + diagonal)
-  -> block-sparse attention -> inverse permute of the output.
+  select tiling (cohesion of q under (1,8,8) and (4,4,4)) -> min/max block
+  scores of the tiles -> top-k (81 of 480, + sink + diagonal) -> block-sparse
+  attention over the kept tiles -> output in T-major order.
+The tile permutation is applied on load (scores and attention read q, k, v
+in place through the tile geometry and the attention writes its rows back
+in T-major order); the same step with permuted copies and the inverse pass
+is timed beside it (`unfused_step_ms`) and must give identical bits.
 Workload: B=1, H=40, grid 20x32x48 (S=30720), D=128, bf16, seeded synthetic
 inputs (the Fourier-feature q/k recipe, v ~ N(0, 1)).
 
@@ -100,6 +104,19 @@ def cpu_baseline(q, k, v, wl, block, kk, budget_s=12.0):
     }
 
 
+def attention_call(bsa, pipe, q, k, v, out):
+    """The pipeline's attention launch alone, on its current block lists."""
+    kv_idx, kv_cnt = pipe.kv
+    if pipe.fused:
+        return lambda: bsa.bsa_block_sparse_attention_tiled(q, k, v, pipe.grid, pipe.tiles, kv_idx, kv_cnt,
+                                                            head_choice=pipe.choice, scale=pipe.scale, out=out)
+    if pipe.pad:
+        return lambda: bsa.bsa_block_sparse_attention_labels(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, pipe.block,
+                                                             pipe.labels, pipe.scale, out=pipe.op)
+    return lambda: bsa.bsa_block_sparse_attention(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, pipe.block, pipe.scale,
+                                                  out=pipe.op)
+
+
 def _time(torch, fn, steps, warmup):
     """Average ms of fn() over `steps` calls, HIP events on the current stream."""
     for _ in range(warmup):
@@ -171,10 +188,7 @@ def sweep(args, torch, np, bsa, synth):
         pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, tiles, 0.17, q.dtype, dev, **kw)
         ms_step = _time(torch, lambda: pipe(q, k, v, out=out), max(steps // 2, 3), warmup)
         kv_idx, kv_cnt = pipe.kv
-        fn = (bsa.bsa_block_sparse_attention_labels if pipe.pad else bsa.bsa_block_sparse_attention)
-        extra = (pipe.labels,) if pipe.pad else ()
-        ms = _time(torch, lambda: fn(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, 64, *extra, out=pipe.op),
-                   max(steps // 2, 3), warmup)
+        ms = _time(torch, attention_call(bsa, pipe, q, k, v, out), max(steps // 2, 3), warmup)
         kept = int(kv_cnt.sum().item())
         fl = kept * 4 * 64 * 64 * wl.D
         choice = np.bincount(pipe.choice.cpu().numpy().ravel(), minlength=len(tiles)).tolist()
@@ -197,8 +211,7 @@ def sweep(args, torch, np, bsa, synth):
     out = torch.empty_like(q)
     ms_step = _time(torch, lambda: pipe(q, k, v, out=out), max(steps // 2, 3), warmup)
     kv_idx, kv_cnt = pipe.kv
-    ms = _time(torch, lambda: bsa.bsa_block_sparse_attention(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, 64,
-                                                             out=pipe.op), max(steps // 2, 3), warmup)
+    ms = _time(torch, attention_call(bsa, pipe, q, k, v, out), max(steps // 2, 3), warmup)
     fl = int(kv_cnt.sum().item()) * 4 * 64 * 64 * wl.D
     print(json.dumps({"workload": wl.name, "attention_ms": round(ms, 4), "attention_tflops": round(fl / ms / 1e9, 2),
                       "step_ms": round(ms_step, 4), "step_tflops": round(fl / ms_step / 1e9, 2),
@@ -296,31 +309,33 @@ def main():
         mark("start")
         choice, _, _ = bsa.bsa_select_tiling(qg, wl.grid, TILES, workspace=pipe.ws_select)
         mark("select_tiling")
-        for src, dst in ((qg, pipe.qp), (kg, pipe.kp), (vg, pipe.vp)):
-            bsa.bsa_tile_permute(src, wl.grid, TILES, head_choice=choice, out=dst)
-        mark("tile_permute_qkv")
-        scores, _ = bsa.bsa_minmax_block_scores(pipe.qp, pipe.kp, block, out=pipe.ws_scores)
-        mark("minmax_block_scores")
+        scores, _ = bsa.bsa_minmax_block_scores_tiled(qg, kg, wl.grid, TILES, head_choice=choice, out=pipe.ws_scores)
+        mark("minmax_block_scores (gather on load)")
         kv_idx, kv_cnt2 = bsa.bsa_topk_block_mask(scores, pipe.k, 1, True, max_kept=pipe.max_kept,
                                                   out=pipe.ws_topk)[:2]
         mark("topk_block_mask")
-        bsa.bsa_block_sparse_attention(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt2, block, out=pipe.op)
-        mark("block_sparse_attention")
-        bsa.bsa_invert_permute(pipe.op, wl.grid, TILES, head_choice=choice, out=out)
-        mark("invert_permute")
+        bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, wl.grid, TILES, kv_idx, kv_cnt2, head_choice=choice, out=out)
+        mark("block_sparse_attention (gather on load, T-major out)")
         torch.cuda.synchronize()
         for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
             stages.setdefault(name, []).append(a.elapsed_time(b))
     stage_ms = {n: round(float(np.median(t)), 4) for n, t in stages.items()}
 
+    # the same step with permuted copies (permute q, k, v -> scores -> top-k -> attention -> inverse)
+    unfused = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, TILES, FRAC, qg.dtype, dev, fused=False)
+    ms_unfused = _time(torch, lambda: unfused(qg, kg, vg, out=out), max(args.steps // 2, 5), 3)
+    same = bool(torch.equal(unfused(qg, kg, vg), pipe(qg, kg, vg)))
+    del unfused
+
     # cold attention: a 512 MB write between calls evicts q, k, v from L2 and MALL
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    attn = attention_call(bsa, pipe, qg, kg, vg, out)
     cold = []
     for _ in range(max(5, min(args.steps, 20))):
         flush.fill_(1)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        bsa.bsa_block_sparse_attention(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt2, block, out=pipe.op)
+        attn()
         b.record()
         b.synchronize()
         cold.append(a.elapsed_time(b))
@@ -347,12 +362,15 @@ def main():
             "tiles": [list(t) for t in TILES], "tiles_dropped_not_dividing": [list(t) for t in DROPPED_TILES],
             "budget_frac": FRAC, "k": pipe.k, "sink_blocks": 1, "diagonal": True,
             "kept_blocks_per_step": kept, "kept_fraction": round(kept / (wl.H * pipe.nb * pipe.nb), 4),
+            "fused": pipe.fused,
         },
+        "unfused_step_ms": round(ms_unfused, 4),
+        "fused_equals_unfused": same,
         "attention": {
             "ms_per_call": round(attn_ms_avg, 4),
             "tflops": round(achieved, 2),
             "frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "kernel": "attn_solo_kernel<block list, positive scale>",
+            "kernel": "attn_solo_kernel<block list, positive scale, gather on load>",
             "cold_ms_per_call": round(cold_ms, 4),
             "cold_tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2),
         },

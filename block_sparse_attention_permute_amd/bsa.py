@@ -33,6 +33,7 @@ EXPORTED = (
     "bsa_block_sparse_attention", "bsa_padded_length", "bsa_tile_permutation_padded", "bsa_label_block_list",
     "bsa_tile_permute_padded", "bsa_invert_permute_padded", "bsa_select_tiling_ex",
     "bsa_minmax_block_scores_masked", "bsa_topk_block_mask_tiled", "bsa_block_sparse_attention_labels",
+    "bsa_minmax_block_scores_tiled", "bsa_block_sparse_attention_tiled",
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices",
 )
 
@@ -72,6 +73,9 @@ _SIGS = {
     "bsa_topk_block_mask_tiled": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _P]),
     "bsa_block_sparse_attention_labels": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _P,
                                                _I64, _F, _P]),
+    "bsa_minmax_block_scores_tiled": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P]),
+    "bsa_block_sparse_attention_tiled": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
+                                              _I, _F, _P]),
 }
 
 
@@ -376,6 +380,29 @@ def bsa_minmax_block_scores(q, k, block: int, out=None, labels=None):
     return scores, summ
 
 
+def bsa_minmax_block_scores_tiled(q, k, grid, tiles, head_choice=None, out=None):
+    """Min/max block scores of T-major q, k, block J = tile J of each head's tiling."""
+    torch = _torch()
+    B, H, S, D = _bhsd(q, "q")
+    if _bhsd(k, "k") != (B, H, S, D) or k.dtype != q.dtype:
+        raise ValueError("q and k must match")
+    T, Hg, Wg = (int(g) for g in grid)
+    if T * Hg * Wg != S:
+        raise ValueError(f"grid {tuple(grid)} does not match S={S}")
+    arr, n = _tiles_arr(tiles)
+    block = tiles[0][0] * tiles[0][1] * tiles[0][2]
+    nb = S // block
+    if out is None:
+        scores = torch.empty((B, H, nb, nb), dtype=torch.float32, device=q.device)
+        summ = torch.empty((4, B, H, nb, D), dtype=q.dtype, device=q.device)
+    else:
+        scores, summ = out
+    hc = None if head_choice is None else _dev(head_choice, "head_choice")
+    _check(lib().bsa_minmax_block_scores_tiled(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, T, Hg, Wg, D, arr,
+                                               n, hc, _dev(summ), _dev(scores), _stream(q)))
+    return scores, summ
+
+
 def _band(diag_width) -> int:
     """Diagonal band width: True/False mean 1/0 (the diagonal alone / none)."""
     w = int(diag_width)
@@ -484,6 +511,33 @@ def bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block: int, scale=None, 
     return o
 
 
+def tiled_attention_supported(dtype, D, tiles) -> bool:
+    """Whether bsa_block_sparse_attention_tiled has a kernel for these tilings."""
+    torch = _torch()
+    return (dtype == torch.bfloat16 and int(D) == 128 and
+            all(a * b * c == 64 and c % 4 == 0 for a, b, c in (tuple(int(v) for v in t) for t in tiles)))
+
+
+def bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_choice=None, scale=None, out=None):
+    """Block-sparse attention of T-major tensors, blocks = tiles (gather on load) -> T-major (B, H, S, D)."""
+    torch = _torch()
+    B, H, S, D = _qkv(q, k, v)
+    T, Hg, Wg = (int(g) for g in grid)
+    if T * Hg * Wg != S:
+        raise ValueError(f"grid {tuple(grid)} does not match S={S}")
+    arr, n = _tiles_arr(tiles)
+    if kv_idx.dtype != torch.int32 or kv_cnt.dtype != torch.int32 or kv_idx.dim() != 4:
+        raise ValueError("kv_idx must be int32 (B, H, Nq, max_kept) and kv_cnt int32 (B, H, Nq)")
+    if tuple(kv_idx.shape[:3]) != (B, H, S // 64) or tuple(kv_cnt.shape) != (B, H, S // 64):
+        raise ValueError("block lists do not match (B, H, S // 64)")
+    o = torch.empty_like(q) if out is None else out
+    hc = None if head_choice is None else _dev(head_choice, "head_choice")
+    _check(lib().bsa_block_sparse_attention_tiled(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+                                                  _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, hc, _dev(kv_idx),
+                                                  _dev(kv_cnt), int(kv_idx.shape[3]), _scale(scale), _stream(q)))
+    return o
+
+
 def bsa_block_sparse_attention_labels(q, k, v, kv_idx, kv_cnt, block: int, labels, scale=None, out=None):
     """Block-sparse attention with the token rule labels[i] == labels[j] inside kept blocks.
 
@@ -554,11 +608,15 @@ class AdaptiveBlockSparse:
     the grid: every head works on the zero-padded grid of its own choice
     (padding left out of the cohesion and the summaries, masked as keys,
     dropped from the output), with the budget floor(frac * that grid's block
-    count).
+    count).  ``fused`` (default: whenever the kernels cover the tilings,
+    bf16 D = 128 tiles of 64 tokens with an x extent that is a multiple of 4,
+    and no padding) reads q, k, v in place through the tile geometry for the
+    scores and the attention and writes the output in T-major order, so no
+    permuted copy is formed.
     """
 
     def __init__(self, B, H, grid, D, tiles, frac, dtype, device, sink_blocks=1, keep_diag=True, scale=None,
-                 top_p=None, p_scale=1.0, statistic="mean", pad=False):
+                 top_p=None, p_scale=1.0, statistic="mean", pad=False, fused=None):
         torch = _torch()
         self.grid = tuple(int(g) for g in grid)
         self.tiles = [tuple(int(v) for v in t) for t in tiles]
@@ -575,6 +633,10 @@ class AdaptiveBlockSparse:
         self.nb = self.Sp // self.block
         self.sink_blocks, self.keep_diag, self.scale = int(sink_blocks), _band(keep_diag), scale
         self.top_p, self.p_scale = top_p, float(p_scale)
+        can_fuse = not self.pad and tiled_attention_supported(dtype, D, self.tiles)
+        if fused and not can_fuse:
+            raise ValueError("the fused path needs bf16, D = 128, tiles of 64 tokens with x extent % 4 == 0, no pad")
+        self.fused = can_fuse if fused is None else bool(fused)
         if self.pad:
             self.nk_table = [bsa_padded_length(T, Hg, Wg, t) // self.block for t in self.tiles]
             self.k_table = [bsa_budget(frac, n) for n in self.nk_table]
@@ -592,7 +654,11 @@ class AdaptiveBlockSparse:
         self.ws_select = (torch.empty((B, H, n, self.nb), dtype=torch.float32, **f),
                           torch.empty((B, H, n), dtype=torch.float32, **f),
                           torch.empty((B, H), dtype=torch.int32, **f))
-        self.qp, self.kp, self.vp, self.op = (torch.empty((B, H, self.Sp, D), dtype=dtype, **f) for _ in range(4))
+        if self.fused:
+            self.qp = self.kp = self.vp = self.op = None
+        else:
+            self.qp, self.kp, self.vp, self.op = (torch.empty((B, H, self.Sp, D), dtype=dtype, **f)
+                                                  for _ in range(4))
         self.labels = torch.empty((B, H, self.Sp), dtype=torch.int32, **f) if self.pad else None
         self.ws_scores = (torch.empty((B, H, self.nb, self.nb), dtype=torch.float32, **f),
                           torch.empty((4, B, H, self.nb, D), dtype=dtype, **f))
@@ -617,15 +683,27 @@ class AdaptiveBlockSparse:
             kv_idx, kv_cnt = bsa_topk_block_mask_tiled(scores, choice, self.k_table, self.nk_table, self.sink_blocks,
                                                        self.keep_diag, max_kept=self.max_kept, out=self.ws_topk)
         else:
-            for src, dst in ((q, self.qp), (k, self.kp), (v, self.vp)):
-                bsa_tile_permute(src, self.grid, self.tiles, head_choice=choice, out=dst)
-            scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores)
+            if self.fused:
+                scores, _ = bsa_minmax_block_scores_tiled(q, k, self.grid, self.tiles, head_choice=choice,
+                                                          out=self.ws_scores)
+            else:
+                for src, dst in ((q, self.qp), (k, self.kp), (v, self.vp)):
+                    bsa_tile_permute(src, self.grid, self.tiles, head_choice=choice, out=dst)
+                scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores)
             if self.top_p is None:
                 kv_idx, kv_cnt, _ = bsa_topk_block_mask(scores, self.k, self.sink_blocks, self.keep_diag,
                                                         max_kept=self.max_kept, return_mask=True, out=self.ws_topk)
             else:
                 kv_idx, kv_cnt, _ = bsa_top_p_block_mask(scores, self.top_p, self.p_scale, self.sink_blocks,
                                                          self.keep_diag, return_mask=True, out=self.ws_topk)
+        if self.fused:
+            if attention_hook is not None:
+                attention_hook(True)
+            o = bsa_block_sparse_attention_tiled(q, k, v, self.grid, self.tiles, kv_idx, kv_cnt, head_choice=choice,
+                                                 scale=self.scale, out=out)
+            if attention_hook is not None:
+                attention_hook(False)
+            return o
         if attention_hook is not None:
             attention_hook(True)
         if self.pad:

@@ -69,6 +69,12 @@ struct AttnParams {
     // labels
     const int32_t* labels;
     uint64_t label_stride;  // elements between heads (0: one row for all heads)
+    // tiled (gather on load): q, k, v, out stay in T-major order and block J
+    // of a head is tile J of the head's tiling
+    const int32_t* head_choice;
+    uint32_t n_tiles, Hg, Wg;
+    TileGeo geo[BSA_MAX_TILINGS];
+    int32_t voff[BSA_MAX_TILINGS][16];  // byte offset of cells 4q..4q+3 from the tile origin
 };
 
 template <int D, int BLK>
@@ -397,7 +403,7 @@ struct SoloCfg {
     static constexpr int TILE = BLK * D * 2;  // one V tile in LDS
 };
 
-template <int MODE, bool POS>
+template <int MODE, bool POS, bool TILED>
 __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, const int32_t* __restrict__ kv_idx,
                                                           const int32_t* __restrict__ kv_cnt) {
     using C = SoloCfg;
@@ -417,6 +423,21 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(P.k + head, head_bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(P.v + head, head_bytes);
     const int q0 = (int)I * BLK;
+    // TILED: the head's tiling, the query tile's T-major origin, and each
+    // lane's two cells (32c + col) as T-major offsets from a tile origin
+    uint32_t tc = 0;
+    if (TILED && P.head_choice != nullptr) {
+        tc = (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[bh]);
+        if (tc >= P.n_tiles) tc = 0;  // out-of-range choices are caught by bsa_validate_indices
+    }
+    const TileGeo& geo = P.geo[tc];
+    const uint32_t q_origin = TILED ? tile_origin(I, geo, P.Hg, P.Wg) : (uint32_t)q0;
+    int kcell[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) kcell[c] = TILED ? (int)cell_offset(32 * c + col, geo, P.Hg, P.Wg) : 32 * c + col;
+    auto tile_soff = [&](int t) -> int {  // byte offset of key tile t's first row
+        return TILED ? (int)tile_origin((uint32_t)t, geo, P.Hg, P.Wg) * (D * 2) : t * BLK * (D * 2);
+    };
 
     int n_iter;
     const int32_t* list = nullptr;
@@ -439,38 +460,41 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     };
 
     // fragments: row (or key) 32*x + col, D cols 16*s + 8*half_id + 0..7
-    const int frag_off = col * (D * 2) + half_id * 16;
+    int koff[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) koff[c] = kcell[c] * (D * 2) + half_id * 16;
     // Q rows into LDS once (K swizzle: 8-row 128-bit reads are conflict-free)
 #pragma unroll
     for (int j = 0; j < BLK * C::NCH / 64; ++j) {
         const int c = lane + 64 * j;
         const int row = c / C::NCH, chunk = c % C::NCH;
+        const int src_row = TILED ? (int)(q_origin + cell_offset(row, geo, P.Hg, P.Wg)) : q0 + row;
         *reinterpret_cast<u32x4*>(qlds + k_lds<D>(row, chunk)) =
-            __builtin_amdgcn_raw_buffer_load_b128(qr, (q0 + row) * (D * 2) + chunk * 16, 0, 0);
+            __builtin_amdgcn_raw_buffer_load_b128(qr, src_row * (D * 2) + chunk * 16, 0, 0);
     }
     int q_addr[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) q_addr[s] = k_lds<D>(col, 2 * s + half_id);
 
-    auto load_k = [&](bf16x8 (&kf)[2][D / 16], int j0) {
-        const int soff = j0 * (D * 2);
+    auto load_k = [&](bf16x8 (&kf)[2][D / 16], int soff) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int s = 0; s < D / 16; ++s)
-                kf[c][s] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, frag_off + 32 * c * (D * 2) + 32 * s, soff, 0));
+                kf[c][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[c] + 32 * s, soff, 0));
     };
     // V tile straight into LDS (buffer loads with the LDS destination): wave
     // instruction q fills LDS bytes [1024q, 1024q + 1024), i.e. rows 4q..4q+3,
     // lane l landing on physical chunk l % 16 of row 4q + l / 16, which holds
     // logical chunk (l % 16) ^ 2(row % 4) (the V swizzle); row % 4 = l / 16.
+    // TILED: cells 4q..4q+3 are 4 consecutive T-major tokens (tiles with an x
+    // extent that is a multiple of 4), P.voff[tc][q] bytes from the origin.
     const int vdma_off = (lane >> 4) * (D * 2) + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
-    auto dma_v = [&](char* buf, int j0) {
+    auto dma_v = [&](char* buf, int soff) {
 #pragma unroll
         for (int q = 0; q < C::TILE / 1024; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(buf + 1024 * q), 16,
-                                                     vdma_off, j0 * (D * 2) + 1024 * q, 0, 0);
+                                                     vdma_off, soff + (TILED ? P.voff[tc][q] : 1024 * q), 0, 0);
     };
 
     f32x16 o[2][D / 32];
@@ -509,16 +533,17 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
 
     bf16x8 kf[2][D / 16];
     if (n_iter > 0) {
-        load_k(kf, tile_at(0) * BLK);
+        load_k(kf, tile_soff(tile_at(0)));
         if (MODE == kLabels) klab_next = labs[tile_at(0) * BLK + lane];
     }
     __builtin_amdgcn_s_waitcnt(0);
 
     for (int it = 0; it < n_iter; ++it) {
-        const int nxt = tile_at(min(it + 1, n_iter - 1)) * BLK;
+        const int nxt_tile = tile_at(min(it + 1, n_iter - 1));
+        const int nxt = nxt_tile * BLK;
         // this tile's V into LDS (the previous tile's V reads have completed)
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        dma_v(vlds, tile_at(it) * BLK);
+        dma_v(vlds, tile_soff(tile_at(it)));
 
         // S^T of (key half c, row tile r) = K_c Q_r^T: four independent chains
         f32x16 sacc[2][2];
@@ -545,7 +570,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         // read the old fragments, so old and new K share registers.
         __builtin_amdgcn_sched_barrier(0);
         if (MODE == kLabels) klab = klab_next;
-        load_k(kf, nxt);
+        load_k(kf, tile_soff(nxt_tile));
         if (MODE == kLabels) klab_next = labs[nxt + lane];
         __builtin_amdgcn_sched_barrier(0);
 
@@ -659,7 +684,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                                                          false);
         const float l = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
         const float inv = l > 0.f ? 1.0f / l : 0.f;  // a row that saw no key is written as zeros
-        const int my_row = q0 + 32 * r + col;
+        const int my_row = TILED ? (int)q_origin + kcell[r] : q0 + 32 * r + col;
         if (my_row >= (int)P.S) continue;
         uint16_t* orow = P.out + head + (size_t)my_row * D;
 #pragma unroll
@@ -771,12 +796,12 @@ int launch_scalar(const ScalarParams& P, int dtype, int64_t D, hipStream_t st, c
     return check_launch(name);
 }
 
-template <int MODE>
+template <int MODE, bool TILED = false>
 void launch_solo(const AttnParams& P, hipStream_t st) {
     if (P.scale_log2 > 0.f)
-        attn_solo_kernel<MODE, true><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt);
+        attn_solo_kernel<MODE, true, TILED><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt);
     else
-        attn_solo_kernel<MODE, false><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt);
+        attn_solo_kernel<MODE, false, TILED><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt);
 }
 
 template <int D, int BLK, int MODE>
@@ -966,4 +991,59 @@ extern "C" int bsa_block_sparse_attention_labels(const void* q, const void* k, c
     P.labels = labels;
     P.label_stride = (uint64_t)label_head_stride;
     return launch_scalar<kLabels>(P, dtype, D, st, name);
+}
+
+extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, const void* v, void* out, int dtype,
+                                                int64_t B, int64_t H, int T, int Hg, int Wg, int64_t D,
+                                                const int32_t* tiles_host, int n_tiles, const int32_t* head_choice,
+                                                const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
+                                                float scale, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_block_sparse_attention_tiled";
+    BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
+    const int64_t S = (int64_t)T * Hg * Wg;
+    int rc = common_checks(q, k, v, out, dtype, B, H, S, D, name);
+    if (rc) return rc;
+    rc = check_tiles(T, Hg, Wg, tiles_host, n_tiles);
+    if (rc) return rc;
+    BSA_REQUIRE(kv_idx && kv_cnt, "%s: NULL block list", name);
+    BSA_REQUIRE(max_kept >= 1, "%s: max_kept must be >= 1", name);
+    if (!(dtype == BSA_BF16 && D == 128))
+        BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: bf16 with D = 128 only (permute and use bsa_block_sparse_attention)",
+                 name);
+    AttnParams P{};
+    for (int i = 0; i < BSA_MAX_TILINGS; ++i) {
+        const int j = i < n_tiles ? i : 0;
+        const int a = tiles_host[3 * j], b = tiles_host[3 * j + 1], c = tiles_host[3 * j + 2];
+        if (a * b * c != 64 || c % 4 != 0)
+            BSA_FAIL(BSA_ERR_UNSUPPORTED,
+                     "%s: tiles of 64 tokens with an x extent that is a multiple of 4 only (tile %d is %dx%dx%d)",
+                     name, j, a, b, c);
+        P.geo[i] = make_geo(Hg, Wg, a, b, c);
+        for (int qq = 0; qq < 16; ++qq) {
+            const int cell = 4 * qq, rt = cell / (b * c), ry = (cell % (b * c)) / c, rx = cell % c;
+            P.voff[i][qq] = (int32_t)((((int64_t)rt * Hg + ry) * Wg + rx) * D * 2);
+        }
+    }
+    const int64_t nq = S / 64;
+    const int64_t nwg = B * H * nq;
+    BSA_REQUIRE(nwg < ((int64_t)1 << 31), "%s: too many blocks", name);
+    P.q = static_cast<const uint16_t*>(q);
+    P.k = static_cast<const uint16_t*>(k);
+    P.v = static_cast<const uint16_t*>(v);
+    P.out = static_cast<uint16_t*>(out);
+    P.S = (uint32_t)S;
+    P.nq = (uint32_t)nq;
+    P.n_wg = (uint32_t)nwg;
+    P.xcd_remap = (nwg % 8 == 0) ? 1u : 0u;
+    P.scale_log2 = resolve_scale_log2(scale, D);
+    P.kv_idx = kv_idx;
+    P.kv_cnt = kv_cnt;
+    P.max_kept = (uint32_t)max_kept;
+    P.head_choice = head_choice;
+    P.n_tiles = (uint32_t)n_tiles;
+    P.Hg = (uint32_t)Hg;
+    P.Wg = (uint32_t)Wg;
+    launch_solo<kBlockList, true>(P, (hipStream_t)stream);
+    return check_launch(name);
 }

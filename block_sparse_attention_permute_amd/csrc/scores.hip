@@ -5,6 +5,10 @@
 // the (query block I, key block J) score is estimated as
 //   max((qmax_I + qmin_I) . kmax_J, (qmax_I + qmin_I) . kmin_J).
 //
+// bsa_minmax_block_scores_tiled reads q and k in T-major order, block J of a
+// head being tile J of the head's chosen tiling (the permuted copies are
+// never formed).
+//
 // bsa_minmax_block_scores_masked leaves out tokens labelled < 0 (the padding
 // of a padded tiling, [Adaptive tiling (SPADE), "Deviations and notes"]):
 // a partial block is summarised by its real tokens, and a block with none
@@ -28,6 +32,10 @@ struct SumParams {
     char* summ;  // 4 x (BH, Nb, D) of the input dtype
     uint32_t block, nb, vecs_per_row, BH;
     const int32_t* labels;  // (BH, S) or null; tokens labelled < 0 are left out
+    // tiled: q, k in T-major order, block = tile of the head's tiling
+    const int32_t* head_choice;
+    uint32_t n_tiles, Hg, Wg;
+    TileGeo geo[BSA_MAX_TILINGS];
 };
 
 template <int EPV>
@@ -60,7 +68,7 @@ __device__ __forceinline__ uint4 pack(const float (&v)[EPV]) {
 }
 
 // blockIdx: x = group of kWaves blocks, y = 0 (q) / 1 (k), z = b*H + h.
-template <int EPV, int LPT>
+template <int EPV, int LPT, bool TILED>
 __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumParams P) {
     constexpr int TPI = 64 / LPT;
     const int lane = threadIdx.x & 63;
@@ -69,7 +77,16 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
     const uint32_t which = blockIdx.y;
     const uint32_t bh = blockIdx.z;
     const size_t row_bytes = (size_t)P.vecs_per_row * 16;
-    const char* src = (which == 0 ? P.q : P.k) + ((size_t)bh * P.nb + blk) * P.block * row_bytes;
+    uint32_t origin = 0;
+    const TileGeo* g = nullptr;
+    if (TILED) {
+        uint32_t c = P.head_choice != nullptr ? (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[bh]) : 0u;
+        if (c >= P.n_tiles) c = 0;  // out-of-range choices are caught by bsa_validate_indices
+        g = &P.geo[c];
+        origin = tile_origin(blk, *g, P.Hg, P.Wg);
+    }
+    const char* src = TILED ? (which == 0 ? P.q : P.k) + ((size_t)bh * P.nb * P.block + origin) * row_bytes
+                            : (which == 0 ? P.q : P.k) + ((size_t)bh * P.nb + blk) * P.block * row_bytes;
     const int sub = lane % LPT;
     const int slot = lane / LPT;
     float mx[EPV], mn[EPV];
@@ -82,7 +99,8 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
     for (uint32_t t = slot; t < P.block; t += TPI) {
         if (lab != nullptr && lab[t] < 0) continue;
         float v[EPV];
-        unpack<EPV>(*reinterpret_cast<const uint4*>(src + (size_t)t * row_bytes + (size_t)sub * 16), v);
+        const uint32_t r = TILED ? cell_offset(t, *g, P.Hg, P.Wg) : t;
+        unpack<EPV>(*reinterpret_cast<const uint4*>(src + (size_t)r * row_bytes + (size_t)sub * 16), v);
 #pragma unroll
         for (int i = 0; i < EPV; ++i) {
             mx[i] = fmaxf(mx[i], v[i]);
@@ -211,11 +229,12 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const char* __restric
 
 using namespace bsa;
 
-extern "C" int bsa_minmax_block_scores_masked(const void* q, const void* k, int dtype, int64_t B, int64_t H,
-                                              int64_t S, int64_t D, int block, const int32_t* labels_or_null,
-                                              void* summaries, float* scores, bsa_stream_t stream) {
-    clear_error();
-    const char* name = "bsa_minmax_block_scores";
+namespace bsa {
+namespace {
+
+int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H, int64_t S, int64_t D, int block,
+                  const int32_t* labels, SumParams& P, bool tiled, void* summaries, float* scores, hipStream_t st,
+                  const char* name) {
     const int es = elem_size(dtype);
     BSA_REQUIRE(es != 0, "%s: unknown dtype %d", name, dtype);
     BSA_REQUIRE(q && k && summaries && scores, "%s: NULL argument", name);
@@ -229,7 +248,6 @@ extern "C" int bsa_minmax_block_scores_masked(const void* q, const void* k, int 
     const int64_t nb = S / block;
     BSA_REQUIRE(nb <= 65535 * kTile, "%s: too many blocks", name);
     BSA_REQUIRE(B * H * nb * D < ((int64_t)1 << 40), "%s: too large", name);
-    SumParams P;
     P.q = static_cast<const char*>(q);
     P.k = static_cast<const char*>(k);
     P.summ = static_cast<char*>(summaries);
@@ -237,10 +255,11 @@ extern "C" int bsa_minmax_block_scores_masked(const void* q, const void* k, int 
     P.nb = (uint32_t)nb;
     P.vecs_per_row = (uint32_t)vecs;
     P.BH = (uint32_t)(B * H);
-    P.labels = labels_or_null;
-    hipStream_t st = (hipStream_t)stream;
+    P.labels = labels;
     dim3 g1((unsigned)((nb + kWaves - 1) / kWaves), 2, (unsigned)(B * H));
-#define BSA_MM(EPV, LPT) block_minmax_kernel<EPV, LPT><<<g1, 64 * kWaves, 0, st>>>(P)
+#define BSA_MM(EPV, LPT)                                                          \
+    (tiled ? block_minmax_kernel<EPV, LPT, true><<<g1, 64 * kWaves, 0, st>>>(P) \
+           : block_minmax_kernel<EPV, LPT, false><<<g1, 64 * kWaves, 0, st>>>(P))
     const bool bf = dtype == BSA_BF16;
     switch (vecs) {
         case 1: if (bf) BSA_MM(8, 1); else BSA_MM(4, 1); break;
@@ -257,10 +276,49 @@ extern "C" int bsa_minmax_block_scores_masked(const void* q, const void* k, int 
     const unsigned nt = (unsigned)((nb + kTile - 1) / kTile);
     dim3 g2(nt, nt, (unsigned)(B * H));
     if (bf)
-        block_scores_kernel<true><<<g2, 256, 0, st>>>(static_cast<const char*>(summaries), P.BH, P.nb, (uint32_t)D, scores);
+        block_scores_kernel<true><<<g2, 256, 0, st>>>(static_cast<const char*>(summaries), P.BH, P.nb, (uint32_t)D,
+                                                      scores);
     else
-        block_scores_kernel<false><<<g2, 256, 0, st>>>(static_cast<const char*>(summaries), P.BH, P.nb, (uint32_t)D, scores);
+        block_scores_kernel<false><<<g2, 256, 0, st>>>(static_cast<const char*>(summaries), P.BH, P.nb, (uint32_t)D,
+                                                       scores);
     return check_launch(name);
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" int bsa_minmax_block_scores_masked(const void* q, const void* k, int dtype, int64_t B, int64_t H,
+                                              int64_t S, int64_t D, int block, const int32_t* labels_or_null,
+                                              void* summaries, float* scores, bsa_stream_t stream) {
+    clear_error();
+    SumParams P{};
+    return minmax_scores(q, k, dtype, B, H, S, D, block, labels_or_null, P, false, summaries, scores,
+                         (hipStream_t)stream, "bsa_minmax_block_scores");
+}
+
+extern "C" int bsa_minmax_block_scores_tiled(const void* q, const void* k, int dtype, int64_t B, int64_t H, int T,
+                                             int Hg, int Wg, int64_t D, const int32_t* tiles_host, int n_tiles,
+                                             const int32_t* head_choice, void* summaries, float* scores,
+                                             bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_minmax_block_scores_tiled";
+    BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
+    int rc = check_tiles(T, Hg, Wg, tiles_host, n_tiles);
+    if (rc) return rc;
+    SumParams P{};
+    const int vol = tiles_host[0] * tiles_host[1] * tiles_host[2];
+    for (int i = 0; i < BSA_MAX_TILINGS; ++i) {
+        const int j = i < n_tiles ? i : 0;
+        const int a = tiles_host[3 * j], b = tiles_host[3 * j + 1], c = tiles_host[3 * j + 2];
+        BSA_REQUIRE(a * b * c == vol, "%s: candidate tiles must share one volume", name);
+        P.geo[i] = make_geo(Hg, Wg, a, b, c);
+    }
+    P.head_choice = head_choice;
+    P.n_tiles = (uint32_t)n_tiles;
+    P.Hg = (uint32_t)Hg;
+    P.Wg = (uint32_t)Wg;
+    return minmax_scores(q, k, dtype, B, H, (int64_t)T * Hg * Wg, D, vol, nullptr, P, true, summaries, scores,
+                         (hipStream_t)stream, name);
 }
 
 extern "C" int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H, int64_t S,

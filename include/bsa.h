@@ -225,6 +225,17 @@ int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, 
                             int64_t S, int64_t D, int block, void* summaries, float* scores,
                             bsa_stream_t stream);
 
+/* bsa_minmax_block_scores on T-major q and k: block J of head (b, h) is tile
+ * J of candidate c = head_choice[b*H + h] (0 if NULL), read in place through
+ * the tile geometry, so the permuted copies of q and k are never formed
+ * (the summaries fused with the permutation [Adaptive tiling (SPADE),
+ * "The idea" steps 2 and 3]).  Candidates must divide the grid and share one
+ * volume, the block size.  Outputs as bsa_minmax_block_scores. */
+int bsa_minmax_block_scores_tiled(const void* q, const void* k, int dtype, int64_t B, int64_t H,
+                                  int T, int Hg, int Wg, int64_t D, const int32_t* tiles_host,
+                                  int n_tiles, const int32_t* head_choice, void* summaries,
+                                  float* scores, bsa_stream_t stream);
+
 /* bsa_minmax_block_scores over labelled tokens only: tokens with
  * labels[b,h,s] < 0 (padding) are left out of the summaries, so a partial
  * block is summarised by its real tokens [Adaptive tiling (SPADE),
@@ -302,6 +313,25 @@ int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void
                                int64_t B, int64_t H, int64_t S, int64_t D, int block,
                                const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
                                float scale, bsa_stream_t stream);
+
+/* Block-sparse attention on T-major q, k, v, out: query/key block J of head
+ * (b, h) is tile J of candidate c = head_choice[b*H + h] (0 if NULL), and the
+ * kernel gathers tile rows on load and scatters output rows on store, so
+ * the result equals bsa_tile_permute -> bsa_block_sparse_attention ->
+ * bsa_invert_permute without the three permuted copies and the inverse pass
+ * [Adaptive tiling (SPADE), "The idea" step 2 and "Recipe": attention in
+ * tile order, results taken back to T-major order].  kv_idx / kv_cnt as in
+ * bsa_block_sparse_attention with S/64 blocks per head.
+ * UNSUPPORTED unless dtype is bf16, D = 128 and every candidate has 64
+ * tokens with an x extent c that is a multiple of 4 (4 consecutive T-major
+ * tokens per LDS-DMA row group); INVALID_ARG if a candidate does not divide
+ * the grid. */
+int bsa_block_sparse_attention_tiled(const void* q, const void* k, const void* v, void* out,
+                                     int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
+                                     int64_t D, const int32_t* tiles_host, int n_tiles,
+                                     const int32_t* head_choice, const int32_t* kv_idx,
+                                     const int32_t* kv_cnt, int max_kept, float scale,
+                                     bsa_stream_t stream);
 
 /* bsa_block_sparse_attention with a token label rule inside the kept
  * blocks: query i sees key j when j's block is kept for i's block AND

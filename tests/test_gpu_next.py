@@ -320,3 +320,68 @@ def test_padded_pipeline_wan_shape_with_16_2_2():
         want = OA.masked_attention_rows(qp[rows_p], kp, vp, np.where(allowed, 0.0, -np.inf), 128 ** -0.5)
         got = f64(out[0, h, torch.from_numpy(perm[rows_p]).cuda()])
         assert max_abs(got, want) <= BF16_ATOL, h
+
+
+# ------------------------------------------------------ gather on load ---
+
+@pytest.mark.gpu
+def test_tiled_scores_and_attention_equal_the_permuted_path():
+    """Reading q, k, v through the tile geometry gives the same bits as the
+    permute -> scores / attention -> inverse permute sequence."""
+    torch = torch_gpu()
+    grid, tiles = (4, 16, 16), [(1, 8, 8), (4, 4, 4), (2, 8, 4)]
+    H, D, S = 5, 128, 1024
+    q, k, v = (gpu(synth.normal_bits((1, H, S, D), seed=760 + i)) for i in range(3))
+    choice = torch.tensor([[0, 1, 2, 1, 0]], dtype=torch.int32).cuda()
+    s_t, _ = bsa.bsa_minmax_block_scores_tiled(q, k, grid, tiles, head_choice=choice)
+    qp, kp, vp = (bsa.bsa_tile_permute(x, grid, tiles, head_choice=choice) for x in (q, k, v))
+    s_p, _ = bsa.bsa_minmax_block_scores(qp, kp, 64)
+    assert torch.equal(s_t, s_p)
+    kv_idx, kv_cnt = bsa.bsa_topk_block_mask(s_p, 4, 1, 3)
+    o_t = bsa.bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_choice=choice)
+    o_p = bsa.bsa_invert_permute(bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 64), grid, tiles,
+                                 head_choice=choice)
+    assert torch.equal(o_t, o_p)
+    # and against the oracle for one head
+    qf, kf, vf = (f64(x)[0, 3] for x in (q, k, v))
+    perm = OT.tile_permutation(grid, tiles[1])
+    keep = np.zeros((16, 16), bool)
+    idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    for I in range(16):
+        keep[I, idx[0, 3, I, :cnt[0, 3, I]]] = True
+    lab = np.empty(S, np.int64)
+    lab[perm] = np.arange(S) // 64
+    want = OP.label_mask_attention(qf, kf, vf, lab, keep, D ** -0.5)
+    assert max_abs(f64(o_t)[0, 3], want) <= BF16_ATOL
+
+
+@pytest.mark.gpu
+def test_tiled_attention_rejects_uncovered_tilings():
+    torch = torch_gpu()
+    q = gpu(synth.normal_bits((1, 1, 1024, 128), seed=770))
+    idx = torch.zeros((1, 1, 16, 1), dtype=torch.int32).cuda()
+    cnt = torch.ones((1, 1, 16), dtype=torch.int32).cuda()
+    with pytest.raises(bsa.UnsupportedError):
+        bsa.bsa_block_sparse_attention_tiled(q, q, q, (4, 16, 16), [(4, 8, 2)], idx, cnt)    # x extent 2
+    with pytest.raises(bsa.UnsupportedError):
+        bsa.bsa_block_sparse_attention_tiled(q, q, q, (4, 16, 16), [(2, 4, 4)], idx, cnt)    # 32 tokens
+    q64 = gpu(synth.normal_bits((1, 1, 1024, 64), seed=771))
+    with pytest.raises(bsa.UnsupportedError):
+        bsa.bsa_block_sparse_attention_tiled(q64, q64, q64, (4, 16, 16), [(1, 8, 8)], idx, cnt)
+    with pytest.raises(ValueError):
+        bsa.bsa_block_sparse_attention_tiled(q, q, q, (4, 16, 16), [(3, 4, 4)], idx, cnt)    # does not divide
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_fused_pipeline_equals_unfused_full_size(cfg):
+    torch = torch_gpu()
+    wl = synth.WORKLOADS[cfg]
+    tiles = [(1, 8, 8), (4, 4, 4)] if cfg == 4 else [(4, 4, 4)]
+    frac = 0.17 if cfg == 4 else 0.10
+    q, k, v = (gpu(x) for x in synth.qkv(cfg))
+    fused = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, tiles, frac, q.dtype, q.device)
+    assert fused.fused
+    a = fused(q, k, v)
+    b = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, tiles, frac, q.dtype, q.device, fused=False)(q, k, v)
+    assert torch.equal(a, b)
