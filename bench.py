@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -46,8 +47,10 @@ def log(msg):
 
 
 def attention_source_hash() -> str:
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (16 hex digits) of the attention source with comments and blank lines removed."""
+    with open(ATTN_SRC, encoding="utf-8") as f:
+        lines = [re.sub(r"//.*$", "", line).rstrip() for line in f.read().splitlines()]
+    return hashlib.sha256("\n".join(line for line in lines if line).encode()).hexdigest()[:16]
 
 
 def measured_traffic():

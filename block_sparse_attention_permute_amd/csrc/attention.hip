@@ -12,26 +12,30 @@
 //    slice and the sink tiles ([FastVideo windowed_attention.py, "Window
 //    policy" and "Implementation note (FLOPs)"]).
 //
-// MFMA path (bf16, D in {64, 128}, block in {32, 64}), one workgroup per
-// query block, (BLK/32) x (BLK/32) waves:
-//  * wave (wr, wk) owns query rows 32*wr..+32 and key columns 32*wk..+32 of
-//    every key block, so all waves share each K/V tile staged in LDS;
-//  * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
-//    (A = K from LDS, B = Q held in registers for the whole kernel): each lane
-//    then holds 16 scores of ONE query row, which is exactly the B-operand
-//    layout of O^T = V^T P^T, so P never leaves registers;
-//  * V is written to LDS transposed (d-major) while staging, so the V^T
-//    operand is two 8-byte LDS reads per MFMA;
+// Kernels:
+//  * attn_solo_kernel (bf16, D = 128, blocks of 64): one single-wave
+//    workgroup per query block; described at its definition.  Modes: block
+//    list, window, labels (a token rule inside kept blocks), and gather on
+//    load (q, k, v, out in T-major order, blocks = tiles of a tiling);
+//  * attn_mfma_kernel (bf16, D in {64, 128}, blocks of 32 or 64; used for
+//    D = 64 and blocks of 32): one workgroup per query block of
+//    (BLK/32) x (BLK/32) waves; wave (wr, wk) owns query rows 32*wr..+32 and
+//    key columns 32*wk..+32 of every key block, all waves share each K/V tile
+//    staged in LDS (double-buffered, one barrier per tile), and the key
+//    halves are merged through LDS at the end;
+//  * attn_scalar_kernel: one thread per query row, fp32 math, for fp32
+//    tensors and every other shape.
+// Common to the MFMA kernels:
+//  * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//    each lane then holds 16 scores of ONE query row, which is exactly the
+//    B-operand layout of O^T = V^T P^T, so P never leaves registers;
+//  * V^T fragments come from LDS with the transposing ds_read_b64_tr_b16;
 //  * online softmax in fp32 with exp2 (log2 e folded into the scale) and a
 //    lazy rescale: the running max is only moved when a row's max grows by
 //    more than 2^8, which skips almost every O rescale;
-//  * K/V tiles are double-buffered (global loads for tile n+1 are in flight
-//    while tile n is multiplied), one barrier per tile;
-//  * the key halves of a block are merged through LDS at the end;
 //  * workgroups are remapped so consecutive query blocks of a head run on
 //    the same XCD and share its L2 (neighbouring query blocks keep many of
 //    the same key blocks).
-// A scalar fp32 kernel covers fp32 inputs and the other shapes.
 #include "common.h"
 
 #include <type_traits>
@@ -391,7 +395,8 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
 // wave owns all 64 query rows (two 32-row tiles) and all 64 keys of each key
 // tile (two 32-key halves):
 //  * K goes straight from global memory into MFMA A-operand registers (16
-//    buffer loads per tile, issued one tile ahead); Q stays in registers;
+//    buffer loads per tile, issued one tile ahead); Q is loaded once into the
+//    wave's LDS;
 //  * S^T = K Q^T is four independent 8-MFMA chains (key half x row tile), so
 //    every K fragment feeds two MFMAs;
 //  * V is staged through the wave's own LDS (no barrier: one wave) and read
