@@ -47,9 +47,11 @@ def log(msg):
 
 
 def attention_source_hash() -> str:
-    """sha256 (16 hex digits) of the attention source with comments and blank lines removed."""
+    """sha256 (16 hex digits) of the attention source, comments and blank lines removed, and its extra flags."""
+    from block_sparse_attention_permute_amd.build import SOURCE_FLAGS
     with open(ATTN_SRC, encoding="utf-8") as f:
         lines = [re.sub(r"//.*$", "", line).rstrip() for line in f.read().splitlines()]
+    lines.append(" ".join(SOURCE_FLAGS.get(os.path.basename(ATTN_SRC), [])))
     return hashlib.sha256("\n".join(line for line in lines if line).encode()).hexdigest()[:16]
 
 

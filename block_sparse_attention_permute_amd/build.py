@@ -37,8 +37,16 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The attention kernels use LLVM's max-ILP machine
+# scheduler, which interleaves their MFMA chains with the softmax arithmetic
+# better than the default (measured: 2-3% faster at the Wan shape).
+SOURCE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(line for line in r.stderr.splitlines() if noise not in line)
