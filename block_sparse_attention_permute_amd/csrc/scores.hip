@@ -16,8 +16,9 @@
 //
 // Design: pass 1 is an HBM-bound reduction, one wave per block, that keeps
 // the summaries in the input dtype (a max or min of bf16 values is a bf16
-// value, so they are exact).  Pass 2 is a small fp32 product per head,
-// Nb x Nb outputs over D, tiled 64 x 64 per workgroup through LDS, with the
+// value, so they are exact).  Pass 2 is a small product per head, Nb x Nb
+// outputs over D: for bf16 on the matrix cores (block_scores_mfma_kernel),
+// otherwise in fp32 FMAs tiled 64 x 64 per workgroup through LDS, with the
 // two dot products of a score sharing their query operand.
 #include "common.h"
 
@@ -224,6 +225,73 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const char* __restric
     }
 }
 
+// bf16 summaries, D a multiple of 16: the same scores on the matrix cores.
+// c = qmax + qmin is formed in fp32 (as above) and split exactly into three
+// bf16 parts, c = c0 + c1 + c2 (8 significant bits each cover fp32's 24), so
+// every product c_d * k_d is exact and the MFMAs accumulate in fp32, as the
+// FMA chain does.  One wave per 32 x 32 tile of (I, J): S^T-free layout,
+// A = parts of c (rows I), B = kmax / kmin (columns J).
+typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
+typedef float f32x16s __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(64) void block_scores_mfma_kernel(const uint16_t* __restrict__ summ, uint32_t BH,
+                                                               uint32_t nb, uint32_t D, float* __restrict__ scores) {
+    const int lane = threadIdx.x;
+    const uint32_t bh = blockIdx.z;
+    const uint32_t I0 = blockIdx.y * 32, J0 = blockIdx.x * 32;
+    const size_t plane = (size_t)BH * nb * D;
+    const size_t head = (size_t)bh * nb * D;
+    const uint16_t* qmax = summ;
+    const uint16_t* qmin = summ + plane;
+    const uint16_t* kmax = summ + 2 * plane;
+    const uint16_t* kmin = summ + 3 * plane;
+    const int r = lane & 31, kg = lane >> 5;
+    const uint32_t I = min(I0 + r, nb - 1), J = min(J0 + r, nb - 1);  // rows past nb are computed and dropped
+    f32x16s sx, sn;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sx[v] = sn[v] = 0.f;
+    for (uint32_t d0 = 0; d0 < D; d0 += 16) {
+        const uint32_t d = d0 + 8 * kg;
+        const uint4 a = *reinterpret_cast<const uint4*>(qmax + head + (size_t)I * D + d);
+        const uint4 b = *reinterpret_cast<const uint4*>(qmin + head + (size_t)I * D + d);
+        const uint4 x = *reinterpret_cast<const uint4*>(kmax + head + (size_t)J * D + d);
+        const uint4 n = *reinterpret_cast<const uint4*>(kmin + head + (size_t)J * D + d);
+        const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+        bf16x8s p0, p1, p2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t ha = (e & 1) ? (wa[e / 2] & 0xffff0000u) : (wa[e / 2] << 16);
+            const uint32_t hb = (e & 1) ? (wb[e / 2] & 0xffff0000u) : (wb[e / 2] << 16);
+            const float c = __uint_as_float(ha) + __uint_as_float(hb);
+            const __bf16 c0 = (__bf16)c;
+            const float r1 = c - (float)c0;
+            const __bf16 c1 = (__bf16)r1;
+            const __bf16 c2 = (__bf16)(r1 - (float)c1);
+            p0[e] = c0;
+            p1[e] = c1;
+            p2[e] = c2;
+        }
+        const bf16x8s bx = __builtin_bit_cast(bf16x8s, x), bn = __builtin_bit_cast(bf16x8s, n);
+        sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, bx, sx, 0, 0, 0);
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, bn, sn, 0, 0, 0);
+        sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, bx, sx, 0, 0, 0);
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, bn, sn, 0, 0, 0);
+        sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2, bx, sx, 0, 0, 0);
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2, bn, sn, 0, 0, 0);
+    }
+    // value v of lane l: row I0 + 8(v/4) + 4(l/32) + v%4, column J0 + l%32
+    const uint32_t Jc = J0 + r;
+    if (Jc >= nb) return;
+    const bool ok_j = bf16_to_f32(kmax[head + (size_t)Jc * D]) != -__builtin_inff();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const uint32_t Ir = I0 + 8 * (v / 4) + 4 * kg + (v % 4);
+        if (Ir >= nb) continue;
+        const bool ok_i = bf16_to_f32(qmax[head + (size_t)Ir * D]) != -__builtin_inff();
+        scores[((size_t)bh * nb + Ir) * nb + Jc] = (ok_i && ok_j) ? fmaxf(sx[v], sn[v]) : -__builtin_inff();
+    }
+}
+
 }  // namespace
 }  // namespace bsa
 
@@ -273,6 +341,13 @@ int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
 #undef BSA_MM
     int rc = check_launch(name);
     if (rc) return rc;
+    if (bf && D % 16 == 0) {
+        const unsigned n32 = (unsigned)((nb + 31) / 32);
+        dim3 g3(n32, n32, (unsigned)(B * H));
+        block_scores_mfma_kernel<<<g3, 64, 0, st>>>(static_cast<const uint16_t*>(summaries), P.BH, P.nb,
+                                                    (uint32_t)D, scores);
+        return check_launch(name);
+    }
     const unsigned nt = (unsigned)((nb + kTile - 1) / kTile);
     dim3 g2(nt, nt, (unsigned)(B * H));
     if (bf)
