@@ -385,3 +385,69 @@ def test_fused_pipeline_equals_unfused_full_size(cfg):
     a = fused(q, k, v)
     b = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, tiles, frac, q.dtype, q.device, fused=False)(q, k, v)
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------- batch > 1 ---
+
+@pytest.mark.gpu
+def test_batch_two_fused_and_padded_pipelines():
+    """B = 2 through the fused pipeline and the padded pipeline, every output
+    against the oracle (rows attended over the GPU's kept lists)."""
+    torch = torch_gpu()
+    H, D = 2, 128
+    for grid, tiles, pad in [((4, 16, 16), [(1, 8, 8), (4, 4, 4)], False), ((5, 10, 12), [(4, 4, 4), (1, 8, 8)], True)]:
+        S = int(np.prod(grid))
+        q, k, v = (synth.normal_bits((2, H, S, D), seed=780 + i + S) for i in range(3))
+        qg, kg, vg = gpu(q), gpu(k), gpu(v)
+        pipe = bsa.AdaptiveBlockSparse(2, H, grid, D, tiles, 0.3, qg.dtype, qg.device, pad=pad)
+        assert pipe.fused == (not pad)
+        out = f64(pipe(qg, kg, vg))
+        choice = pipe.choice.cpu().numpy()
+        kv_idx, kv_cnt = pipe.kv
+        idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+        qf, kf, vf = (synth.stored_to_f64(x) for x in (q, k, v))
+        oc, osc = OT.select_tiling(qf, grid, tiles, pad=pad)
+        for b in range(2):
+            for h in range(H):
+                c = int(choice[b, h])
+                if c != oc[b, h]:
+                    a_, b_ = osc[b, h, c], osc[b, h, oc[b, h]]
+                    assert abs(a_ - b_) < TOPK_REL * abs(b_)
+                perm = (OT.padded_tile_permutation if pad else OT.tile_permutation)(grid, tiles[c])
+                valid = perm >= 0
+                nb = perm.size // 64
+                gkeep = np.zeros((nb, nb), bool)
+                for I in range(nb):
+                    gkeep[I, idx[b, h, I, :cnt[b, h, I]]] = True
+                qp, kp, vp = (_gather_padded(x[b, h], perm) for x in (qf, kf, vf))
+                rows = np.flatnonzero(valid)
+                allowed = gkeep[rows // 64][:, np.arange(perm.size) // 64] & valid[None, :]
+                want = OA.masked_attention_rows(qp[rows], kp, vp, np.where(allowed, 0.0, -np.inf), D ** -0.5)
+                assert max_abs(out[b, h, perm[rows]], want) <= BF16_ATOL, (grid, b, h)
+
+
+@pytest.mark.gpu
+def test_padded_pipeline_scalar_path_fp32():
+    """fp32 and D = 64 take the scalar label kernel on the padded path."""
+    torch = torch_gpu()
+    grid, tiles = (3, 5, 6), [(2, 2, 4), (1, 4, 4)]
+    H = 2
+    for dtype, D in (("f32", 16), ("bf16", 64)):
+        S = 90
+        q, k, v = (synth.normal_bits((1, H, S, D), seed=790 + i, dtype=dtype) for i in range(3))
+        qg, kg, vg = gpu(q), gpu(k), gpu(v)
+        pipe = bsa.AdaptiveBlockSparse(1, H, grid, D, tiles, 0.5, qg.dtype, qg.device, pad=True)
+        out = f64(pipe(qg, kg, vg))
+        ref = OP.padded_adaptive_block_sparse(*(synth.stored_to_f64(x) for x in (q, k, v)), grid, tiles, 0.5)
+        choice = pipe.choice.cpu().numpy()
+        kv_idx, kv_cnt = pipe.kv
+        idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+        tol = BF16_ATOL if dtype == "bf16" else F32_ATOL
+        for h in range(H):
+            assert choice[0, h] == ref["choice"][0, h]
+            keep = ref["keep"][h]
+            gkeep = np.zeros_like(keep)
+            for I in range(keep.shape[0]):
+                gkeep[I, idx[0, h, I, :cnt[0, h, I]]] = True
+            if np.array_equal(gkeep, keep):
+                assert max_abs(out[0, h], ref["out"][0, h]) <= tol, (dtype, h)
