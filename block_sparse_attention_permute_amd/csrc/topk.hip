@@ -127,10 +127,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
             for (int i = 0; i < VPL; ++i) c += (valid[i] && key[i] >= cand) ? w[i] : 0.f;
             if (wave_sum_f(c) >= target) T = cand;
         } else {
+            // wave-wide count from ballots (scalar popcounts, no cross-lane shuffles)
             uint32_t c = 0;
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) c += (valid[i] && key[i] >= cand) ? 1u : 0u;
-            if (wave_sum(c) >= k_row) T = cand;
+            for (int i = 0; i < VPL; ++i) c += popc64(__ballot(valid[i] && key[i] >= cand));
+            if (c >= k_row) T = cand;
         }
     }
     uint32_t need;  // ties at T to take, lowest index first
@@ -150,8 +151,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
     } else {
         uint32_t gt = 0;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) gt += (valid[i] && key[i] > T) ? 1u : 0u;
-        need = row_exists ? k_row - wave_sum(gt) : 0u;
+        for (int i = 0; i < VPL; ++i) gt += popc64(__ballot(valid[i] && key[i] > T));
+        need = row_exists ? k_row - gt : 0u;
     }
 
     bool keep[VPL];
