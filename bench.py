@@ -309,7 +309,9 @@ def main():
         e.record()
         marks.append((name, e))
 
-    for _ in range(3):
+    # the clock ramps up again over the first few calls after the syncs: the
+    # median is taken over the last 5 of 12 passes
+    for _ in range(12):
         marks.clear()
         mark("start")
         choice, _, _ = bsa.bsa_select_tiling(qg, wl.grid, TILES, workspace=pipe.ws_select)
@@ -324,7 +326,7 @@ def main():
         torch.cuda.synchronize()
         for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
             stages.setdefault(name, []).append(a.elapsed_time(b))
-    stage_ms = {n: round(float(np.median(t)), 4) for n, t in stages.items()}
+    stage_ms = {n: round(float(np.median(t[-5:])), 4) for n, t in stages.items()}
 
     # the same step with permuted copies (permute q, k, v -> scores -> top-k -> attention -> inverse)
     unfused = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, TILES, FRAC, qg.dtype, dev, fused=False)

@@ -39,9 +39,11 @@ FLAGS = [
 
 # Per-source additions.  The attention kernels use LLVM's max-ILP machine
 # scheduler, which interleaves their MFMA chains with the softmax arithmetic
-# better than the default (measured: 2-3% faster at the Wan shape).
+# better than the default (measured: 2-3% faster at the Wan shape), and keep
+# MFMA accumulators in ordinary VGPRs, so the softmax reads the scores without
+# accumulator-to-VGPR copies.
 SOURCE_FLAGS = {
-    "attention.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attention.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -48,7 +48,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// row sums add the bf16-rounded P two at a time (v_dot2 with ones): exactly
+// the weights the P V product uses
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P may grow to 2^8 before a rescale
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8; a field at its maximum does not wait)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kVmcnt16 = waitcnt_vm(16);  // all but the 16 most recent vector-memory ops
+constexpr int kLgkmcnt0 = 0xC07F;         // all LDS / scalar-memory ops
+static_assert(kVmcnt16 == 0x4F70, "vmcnt(16) encoding");
 
 // kLabels: a block list plus the token rule labels[i] == labels[j] inside
 // the kept blocks (padding of a padded tiling, spatial-only and
@@ -402,7 +413,14 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
 //  * V is staged through the wave's own LDS (no barrier: one wave) and read
 //    back transposed; each V^T fragment feeds the two row tiles' MFMAs;
 //  * nothing is shared between waves, so there are no barriers at all and
-//    waves of different query blocks drift freely.
+//    waves of different query blocks drift freely;
+//  * one wave per SIMD has no other wave to hide its LDS latency, so the
+//    loop is laid out by hand in steps fenced by scheduling barriers: Q
+//    fragments are read two score steps ahead, the V DMA is spread over the
+//    score steps, and in the P V product the exps of 16-key group m+1 and its
+//    V^T reads are issued beside the MFMAs of group m;
+//  * block-list entries come one tile ahead through buffer loads (vector
+//    memory), so waiting for them never waits on LDS traffic.
 struct SoloCfg {
     static constexpr int D = 128, BLK = 64, NT = 64, NCH = D / 8;
     static constexpr int TILE = BLK * D * 2;  // one V tile in LDS
@@ -463,6 +481,12 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         if (MODE != kWindow) return __builtin_amdgcn_readfirstlane(list[it]);
         return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
     };
+    // entry it of the list as a vector value (a buffer load, read one tile ahead)
+    const __amdgpu_buffer_rsrc_t lr = make_rsrc(list, MODE != kWindow ? 4u * (uint32_t)max(n_iter, 0) : 0u);
+    auto tile_ahead = [&](int it) -> int {
+        if (MODE != kWindow) return __builtin_amdgcn_raw_buffer_load_b32(lr, 4 * it, 0, 0);
+        return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
+    };
 
     // fragments: row (or key) 32*x + col, D cols 16*s + 8*half_id + 0..7
     int koff[2];
@@ -495,11 +519,14 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     // TILED: cells 4q..4q+3 are 4 consecutive T-major tokens (tiles with an x
     // extent that is a multiple of 4), P.voff[tc][q] bytes from the origin.
     const int vdma_off = (lane >> 4) * (D * 2) + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
-    auto dma_v = [&](char* buf, int soff) {
+    int vdoff[C::TILE / 1024];
 #pragma unroll
-        for (int q = 0; q < C::TILE / 1024; ++q)
+    for (int q = 0; q < C::TILE / 1024; ++q) vdoff[q] = vdma_off + (TILED ? P.voff[tc][q] : 1024 * q);
+    auto dma_v = [&](char* buf, int soff, int q_lo, int q_hi) {
+#pragma unroll
+        for (int q = q_lo; q < q_hi; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(buf + 1024 * q), 16,
-                                                     vdma_off, soff + (TILED ? P.voff[tc][q] : 1024 * q), 0, 0);
+                                                     vdoff[q], soff, 0, 0);
     };
 
     f32x16 o[2][D / 32];
@@ -537,18 +564,21 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     }
 
     bf16x8 kf[2][D / 16];
+    int soff_cur = 0, v_nxt = 0;
     if (n_iter > 0) {
-        load_k(kf, tile_soff(tile_at(0)));
-        if (MODE == kLabels) klab_next = labs[tile_at(0) * BLK + lane];
+        const int t0 = tile_at(0);
+        soff_cur = tile_soff(t0);
+        load_k(kf, soff_cur);
+        if (MODE == kLabels) klab_next = labs[t0 * BLK + lane];
+        v_nxt = tile_ahead(min(1, n_iter - 1));
     }
     __builtin_amdgcn_s_waitcnt(0);
 
     for (int it = 0; it < n_iter; ++it) {
-        const int nxt_tile = tile_at(min(it + 1, n_iter - 1));
+        const int nxt_tile = __builtin_amdgcn_readfirstlane(v_nxt);
         const int nxt = nxt_tile * BLK;
         // this tile's V into LDS (the previous tile's V reads have completed)
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        dma_v(vlds, tile_soff(tile_at(it)));
+        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
 
         // S^T of (key half c, row tile r) = K_c Q_r^T: four independent chains
         f32x16 sacc[2][2];
@@ -559,23 +589,33 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
 #pragma unroll
                 for (int v = 0; v < 16; ++v) sacc[c][r][v] = 0.f;
             }
+        // Q fragments of the two row tiles, read two steps ahead (ring of three)
+        bf16x8 qfa[3], qfb[3];
+        auto read_q = [&](int s) {
+            qfa[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qlds + q_addr[s]));
+            qfb[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qlds + q_addr[s] + 32 * (D * 2)));
+        };
+        read_q(0);
+        read_q(1);
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qlds + q_addr[s]));
-            const bf16x8 qb =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qlds + q_addr[s] + 32 * (D * 2)));
+            if (s + 2 < D / 16) read_q(s + 2);
+            dma_v(vlds, soff_cur, 2 * s, 2 * s + 2);  // this tile's V, two rows of 4 per step
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                sacc[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][s], qa, sacc[c][0], 0, 0, 0);
-                sacc[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][s], qb, sacc[c][1], 0, 0, 0);
+                sacc[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][s], qfa[s % 3], sacc[c][0], 0, 0, 0);
+                sacc[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][s], qfb[s % 3], sacc[c][1], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // K registers are free: fetch the next tile's K (the last tile again past
         // the end).  The scheduling barriers keep the loads after the MFMAs that
         // read the old fragments, so old and new K share registers.
         __builtin_amdgcn_sched_barrier(0);
         if (MODE == kLabels) klab = klab_next;
-        load_k(kf, tile_soff(nxt_tile));
+        v_nxt = tile_ahead(min(it + 2, n_iter - 1));
+        const int soff_nxt = tile_soff(nxt_tile);
+        load_k(kf, soff_nxt);
         if (MODE == kLabels) klab_next = labs[nxt + lane];
         __builtin_amdgcn_sched_barrier(0);
 
@@ -648,38 +688,60 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                     for (int v = 0; v < 16; ++v) o[r][t][v] *= alpha;
             }
         }
-        // P as bf16 B operands: pb[r][m] covers keys 16m..16m+15 of the tile
+        // P as bf16 B operands, one 16-key group m at a time (pb[r][m] covers keys
+        // 16m..16m+15); group m+1's exps and V^T reads are issued beside the
+        // MFMAs of group m
         bf16x8 pb[2][4];
+        float psum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+        auto make_p = [&](int m) {
+            const int c = m / 2, v0 = 8 * (m % 2);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const float neg_m = -m_used[r];
-            float psum = 0.f;
+            for (int r = 0; r < 2; ++r) {
+                const float neg_m = -m_used[r];
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v], c_scale, neg_m));
-                    psum += p;
-                    pb[r][2 * c + v / 8][v % 8] = (__bf16)p;
+                for (int v = v0; v < v0 + 8; v += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v], c_scale, neg_m));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v + 1], c_scale, neg_m));
+                    const bf16x2 two = {(__bf16)p0, (__bf16)p1};
+                    psum[r][m % 2] = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, psum[r][m % 2], false);
+                    pb[r][m][v % 8] = two[0];
+                    pb[r][m][v % 8 + 1] = two[1];
                 }
-            l_part[r] += psum;
-        }
-
-        // O^T += V^T P^T once this tile's V has landed (only the next tile's 16 K
-        // loads were issued after it)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 16);  // vmcnt(16)
+            }
+        };
+        bf16x8 vfr[2][D / 32];
+        auto read_v = [&](int m) {
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int t = 0; t < D / 32; ++t) {
                 const char* va = vlds + v_addr[t] + (16 * m) * (D * 2);
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)va);
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(va + 8 * (D * 2)));
                 const s16x4 a8[2] = {lo, hi};
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, a8);
-                o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[0][m], o[0][t], 0, 0, 0);
-                o[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[1][m], o[1][t], 0, 0, 0);
+                vfr[m % 2][t] = __builtin_bit_cast(bf16x8, a8);
             }
+        };
+        make_p(0);
+        // O^T += V^T P^T once this tile's V has landed: only the next tile's 16 K
+        // loads and (block lists) its list entry were issued after it
+        __builtin_amdgcn_s_waitcnt(MODE == kWindow ? kVmcnt16 : waitcnt_vm(17));
+        read_v(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            if (m + 1 < 4) {
+                read_v(m + 1);
+                make_p(m + 1);
+            }
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) {
+                o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m % 2][t], pb[0][m], o[0][t], 0, 0, 0);
+                o[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m % 2][t], pb[1][m], o[1][t], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) l_part[r] += psum[r][0] + psum[r][1];
+        soff_cur = soff_nxt;
     }
 
     // ---- write out (each lane pair holds one row; their partial sums add up)
