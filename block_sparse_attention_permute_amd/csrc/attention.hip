@@ -405,9 +405,12 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
 // 64-token blocks, D = 128: one single-wave workgroup per query block.  The
 // wave owns all 64 query rows (two 32-row tiles) and all 64 keys of each key
 // tile (two 32-key halves):
-//  * K goes straight from global memory into MFMA A-operand registers (16
-//    buffer loads per tile, issued one tile ahead); Q is loaded once into the
-//    wave's LDS;
+//  * Q is loaded once into registers (the B operand of both row tiles);
+//  * K goes global -> LDS with the LDS-destination buffer loads, whole 256-byte
+//    rows per instruction (16 per tile, issued one tile ahead), and is read
+//    back as A-operand fragments two score steps ahead.  Loading the A
+//    fragments straight from global memory instead costs 32 partial cache
+//    lines per instruction in the vector-memory path and was 7% slower;
 //  * S^T = K Q^T is four independent 8-MFMA chains (key half x row tile), so
 //    every K fragment feeds two MFMAs;
 //  * V is staged through the wave's own LDS (no barrier: one wave) and read
@@ -415,7 +418,7 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
 //  * nothing is shared between waves, so there are no barriers at all and
 //    waves of different query blocks drift freely;
 //  * one wave per SIMD has no other wave to hide its LDS latency, so the
-//    loop is laid out by hand in steps fenced by scheduling barriers: Q
+//    loop is laid out by hand in steps fenced by scheduling barriers: K
 //    fragments are read two score steps ahead, the V DMA is spread over the
 //    score steps, and in the P V product the exps of 16-key group m+1 and its
 //    V^T reads are issued beside the MFMAs of group m;
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     using C = SoloCfg;
     constexpr int D = C::D, BLK = C::BLK;
     // Q (64 rows) and one V tile live in the wave's LDS (32 KB: four waves per CU)
-    __shared__ __attribute__((aligned(16))) char qlds[C::TILE];
+    __shared__ __attribute__((aligned(16))) char klds[C::TILE];
     __shared__ __attribute__((aligned(16))) char vlds[C::TILE];
     const int lane = threadIdx.x;
     const int half_id = lane >> 5, col = lane & 31;
@@ -488,29 +491,35 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
     };
 
-    // fragments: row (or key) 32*x + col, D cols 16*s + 8*half_id + 0..7
+    // fragments: row (or key) 32*x + col, D cols 16*s + 8*half_id + 0..7;
+    // koff[x] is that row's byte offset from its tile's origin
     int koff[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) koff[c] = kcell[c] * (D * 2) + half_id * 16;
-    // Q rows into LDS once (K swizzle: 8-row 128-bit reads are conflict-free)
+    // Q stays in registers as the B operand of both row tiles
+    bf16x8 qf[2][D / 16];
 #pragma unroll
-    for (int j = 0; j < BLK * C::NCH / 64; ++j) {
-        const int c = lane + 64 * j;
-        const int row = c / C::NCH, chunk = c % C::NCH;
-        const int src_row = TILED ? (int)(q_origin + cell_offset(row, geo, P.Hg, P.Wg)) : q0 + row;
-        *reinterpret_cast<u32x4*>(qlds + k_lds<D>(row, chunk)) =
-            __builtin_amdgcn_raw_buffer_load_b128(qr, src_row * (D * 2) + chunk * 16, 0, 0);
-    }
-    int q_addr[D / 16];
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) q_addr[s] = k_lds<D>(col, 2 * s + half_id);
-
-    auto load_k = [&](bf16x8 (&kf)[2][D / 16], int soff) {
+        for (int s = 0; s < D / 16; ++s)
+            qf[r][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, koff[r] + 32 * s, TILED ? (int)q_origin * (D * 2) : q0 * (D * 2), 0));
+    // LDS address of K fragment (key half 0, step s); key half 1 is 32 rows on
+    int k_addr[D / 16];
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+    for (int s = 0; s < D / 16; ++s) k_addr[s] = k_lds<D>(col, 2 * s + half_id);
+    // K tile straight into LDS with the K swizzle: instruction q fills rows
+    // 4q..4q+3, lane l physical chunk l % 16 of row 4q + l / 16, which holds
+    // logical chunk (l % 16) ^ (row % 8), row % 8 = 4(q % 2) + l / 16
+    int kdoff[C::TILE / 1024];
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s)
-                kf[c][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[c] + 32 * s, soff, 0));
+    for (int q = 0; q < C::TILE / 1024; ++q)
+        kdoff[q] = (lane >> 4) * (D * 2) + (((lane & 15) ^ (4 * (q & 1) + (lane >> 4))) << 4) +
+                   (TILED ? P.voff[tc][q] : 1024 * q);
+    auto dma_k = [&](int soff) {
+#pragma unroll
+        for (int q = 0; q < C::TILE / 1024; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(klds + 1024 * q), 16,
+                                                     kdoff[q], soff, 0, 0);
     };
     // V tile straight into LDS (buffer loads with the LDS destination): wave
     // instruction q fills LDS bytes [1024q, 1024q + 1024), i.e. rows 4q..4q+3,
@@ -563,12 +572,11 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         q_uniform = __ballot((qlab[0] != q_uni) | (qlab[1] != q_uni)) == 0;
     }
 
-    bf16x8 kf[2][D / 16];
     int soff_cur = 0, v_nxt = 0;
     if (n_iter > 0) {
         const int t0 = tile_at(0);
         soff_cur = tile_soff(t0);
-        load_k(kf, soff_cur);
+        dma_k(soff_cur);
         if (MODE == kLabels) klab_next = labs[t0 * BLK + lane];
         v_nxt = tile_ahead(min(1, n_iter - 1));
     }
@@ -577,8 +585,9 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     for (int it = 0; it < n_iter; ++it) {
         const int nxt_tile = __builtin_amdgcn_readfirstlane(v_nxt);
         const int nxt = nxt_tile * BLK;
-        // this tile's V into LDS (the previous tile's V reads have completed)
-        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+        // this tile's K has landed in LDS (nothing later was issued) and the
+        // previous tile's V reads have completed
+        __builtin_amdgcn_s_waitcnt(0);
 
         // S^T of (key half c, row tile r) = K_c Q_r^T: four independent chains
         f32x16 sacc[2][2];
@@ -589,33 +598,33 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
 #pragma unroll
                 for (int v = 0; v < 16; ++v) sacc[c][r][v] = 0.f;
             }
-        // Q fragments of the two row tiles, read two steps ahead (ring of three)
-        bf16x8 qfa[3], qfb[3];
-        auto read_q = [&](int s) {
-            qfa[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qlds + q_addr[s]));
-            qfb[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qlds + q_addr[s] + 32 * (D * 2)));
+        // K fragments of the two key halves, read two steps ahead (ring of three)
+        bf16x8 kfa[3], kfb[3];
+        auto read_k = [&](int s) {
+            kfa[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(klds + k_addr[s]));
+            kfb[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(klds + k_addr[s] + 32 * (D * 2)));
         };
-        read_q(0);
-        read_q(1);
+        read_k(0);
+        read_k(1);
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            if (s + 2 < D / 16) read_q(s + 2);
+            if (s + 2 < D / 16) read_k(s + 2);
             dma_v(vlds, soff_cur, 2 * s, 2 * s + 2);  // this tile's V, two rows of 4 per step
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                sacc[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][s], qfa[s % 3], sacc[c][0], 0, 0, 0);
-                sacc[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][s], qfb[s % 3], sacc[c][1], 0, 0, 0);
+                const bf16x8 kc = c == 0 ? kfa[s % 3] : kfb[s % 3];
+                sacc[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[0][s], sacc[c][0], 0, 0, 0);
+                sacc[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[1][s], sacc[c][1], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // K registers are free: fetch the next tile's K (the last tile again past
-        // the end).  The scheduling barriers keep the loads after the MFMAs that
-        // read the old fragments, so old and new K share registers.
-        __builtin_amdgcn_sched_barrier(0);
+        // this tile's K is read: the next tile's K goes into its LDS (the last tile
+        // again past the end), with the list entry of the tile after it
         if (MODE == kLabels) klab = klab_next;
         v_nxt = tile_ahead(min(it + 2, n_iter - 1));
         const int soff_nxt = tile_soff(nxt_tile);
-        load_k(kf, soff_nxt);
+        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);  // this tile's K reads are complete
+        dma_k(soff_nxt);
         if (MODE == kLabels) klab_next = labs[nxt + lane];
         __builtin_amdgcn_sched_barrier(0);
 
