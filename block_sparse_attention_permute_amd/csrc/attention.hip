@@ -606,16 +606,21 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         };
         read_k(0);
         read_k(1);
+        // (one MFMA per fenced region, with one V DMA or the K reads of step s+2
+        // beside it)
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
+            const bf16x8 ka = kfa[s % 3], kb = kfb[s % 3];
+            sacc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][s], sacc[0][0], 0, 0, 0);
+            dma_v(vlds, soff_cur, 2 * s, 2 * s + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][s], sacc[0][1], 0, 0, 0);
+            dma_v(vlds, soff_cur, 2 * s + 1, 2 * s + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[0][s], sacc[1][0], 0, 0, 0);
             if (s + 2 < D / 16) read_k(s + 2);
-            dma_v(vlds, soff_cur, 2 * s, 2 * s + 2);  // this tile's V, two rows of 4 per step
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const bf16x8 kc = c == 0 ? kfa[s % 3] : kfb[s % 3];
-                sacc[c][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[0][s], sacc[c][0], 0, 0, 0);
-                sacc[c][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[1][s], sacc[c][1], 0, 0, 0);
-            }
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[1][s], sacc[1][1], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         // this tile's K is read: the next tile's K goes into its LDS (the last tile
@@ -702,51 +707,60 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         // MFMAs of group m
         bf16x8 pb[2][4];
         float psum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-        auto make_p = [&](int m) {
-            const int c = m / 2, v0 = 8 * (m % 2);
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const float neg_m = -m_used[r];
-#pragma unroll
-                for (int v = v0; v < v0 + 8; v += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v], c_scale, neg_m));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v + 1], c_scale, neg_m));
-                    const bf16x2 two = {(__bf16)p0, (__bf16)p1};
-                    psum[r][m % 2] = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, psum[r][m % 2], false);
-                    pb[r][m][v % 8] = two[0];
-                    pb[r][m][v % 8 + 1] = two[1];
-                }
-            }
+        // piece j (0..3) of group m for row tile r: accumulator values
+        // 8(m % 2) + 2j and + 1 of key half m / 2, i.e. two of this lane's share
+        // of keys 16m..16m+15
+        auto p_piece = [&](int m, int r, int j) {
+            const int c = m / 2, v = 8 * (m % 2) + 2 * j;
+            const float neg_m = -m_used[r];
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v], c_scale, neg_m));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v + 1], c_scale, neg_m));
+            const bf16x2 two = {(__bf16)p0, (__bf16)p1};
+            psum[r][m % 2] = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, psum[r][m % 2], false);
+            pb[r][m][v % 8] = two[0];
+            pb[r][m][v % 8 + 1] = two[1];
         };
+        // V^T fragment t of group m (keys 16m..16m+15) in two transposing reads of
+        // 8 keys each; vfr[m % 2] holds a group's four fragments
         bf16x8 vfr[2][D / 32];
-        auto read_v = [&](int m) {
-#pragma unroll
-            for (int t = 0; t < D / 32; ++t) {
-                const char* va = vlds + v_addr[t] + (16 * m) * (D * 2);
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)va);
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(va + 8 * (D * 2)));
-                const s16x4 a8[2] = {lo, hi};
+        s16x4 vlo[D / 32];
+        auto v_half = [&](int m, int t, int h) {
+            const char* va = vlds + v_addr[t] + (16 * m + 8 * h) * (D * 2);
+            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)va);
+            if (h == 0) {
+                vlo[t] = x;
+            } else {
+                const s16x4 a8[2] = {vlo[t], x};
                 vfr[m % 2][t] = __builtin_bit_cast(bf16x8, a8);
             }
         };
-        make_p(0);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p_piece(0, r, j);
         // O^T += V^T P^T once this tile's V has landed: only the next tile's 16 K
         // loads and (block lists) its list entry were issued after it
         __builtin_amdgcn_s_waitcnt(MODE == kWindow ? kVmcnt16 : waitcnt_vm(17));
-        read_v(0);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+            v_half(0, t, 0);
+            v_half(0, t, 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
+        // (one MFMA per fenced region; beside each, one piece of group m+1: two
+        // exps of one row tile and half of one V^T fragment)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            if (m + 1 < 4) {
-                read_v(m + 1);
-                make_p(m + 1);
-            }
 #pragma unroll
-            for (int t = 0; t < D / 32; ++t) {
-                o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m % 2][t], pb[0][m], o[0][t], 0, 0, 0);
-                o[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m % 2][t], pb[1][m], o[1][t], 0, 0, 0);
+            for (int i = 0; i < 2 * (D / 32); ++i) {
+                const int t = i / 2, r = i % 2;
+                o[r][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m % 2][t], pb[r][m], o[r][t], 0, 0, 0);
+                if (m + 1 < 4) {
+                    p_piece(m + 1, i / 4, i % 4);
+                    v_half(m + 1, t, i % 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int r = 0; r < 2; ++r) l_part[r] += psum[r][0] + psum[r][1];
