@@ -234,6 +234,38 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const char* __restric
 typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
 typedef float f32x16s __attribute__((ext_vector_type(16)));
 
+// c = qmax + qmin over eight dims (a, b: eight bf16 values each), split
+// exactly into three bf16 parts c = p0 + p1 + p2, and the six MFMAs of one
+// 16-dim step: S_max += c kmax^T, S_min += c kmin^T over the three parts
+__device__ __forceinline__ void score_step(const uint4 a, const uint4 b, const uint4 x, const uint4 n, f32x16s& sx,
+                                           f32x16s& sn) {
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    bf16x8s p0, p1, p2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t ha = (e & 1) ? (wa[e / 2] & 0xffff0000u) : (wa[e / 2] << 16);
+        const uint32_t hb = (e & 1) ? (wb[e / 2] & 0xffff0000u) : (wb[e / 2] << 16);
+        const float c = __uint_as_float(ha) + __uint_as_float(hb);
+        const __bf16 c0 = (__bf16)c;
+        const float r1 = c - (float)c0;
+        const __bf16 c1 = (__bf16)r1;
+        p0[e] = c0;
+        p1[e] = c1;
+        p2[e] = (__bf16)(r1 - (float)c1);
+    }
+    const bf16x8s bx = __builtin_bit_cast(bf16x8s, x), bn = __builtin_bit_cast(bf16x8s, n);
+    sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, bx, sx, 0, 0, 0);
+    sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, bn, sn, 0, 0, 0);
+    sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, bx, sx, 0, 0, 0);
+    sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, bn, sn, 0, 0, 0);
+    sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2, bx, sx, 0, 0, 0);
+    sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2, bn, sn, 0, 0, 0);
+}
+
+// ND > 0: D = 16 * ND and every step's operands are loaded before the first
+// MFMA (one memory latency per tile instead of one per step); ND = 0: any D,
+// one step at a time.
+template <int ND>
 __global__ __launch_bounds__(64) void block_scores_mfma_kernel(const uint16_t* __restrict__ summ, uint32_t BH,
                                                                uint32_t nb, uint32_t D, float* __restrict__ scores) {
     const int lane = threadIdx.x;
@@ -250,34 +282,26 @@ __global__ __launch_bounds__(64) void block_scores_mfma_kernel(const uint16_t* _
     f32x16s sx, sn;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sx[v] = sn[v] = 0.f;
-    for (uint32_t d0 = 0; d0 < D; d0 += 16) {
-        const uint32_t d = d0 + 8 * kg;
-        const uint4 a = *reinterpret_cast<const uint4*>(qmax + head + (size_t)I * D + d);
-        const uint4 b = *reinterpret_cast<const uint4*>(qmin + head + (size_t)I * D + d);
-        const uint4 x = *reinterpret_cast<const uint4*>(kmax + head + (size_t)J * D + d);
-        const uint4 n = *reinterpret_cast<const uint4*>(kmin + head + (size_t)J * D + d);
-        const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-        bf16x8s p0, p1, p2;
+    auto ld = [&](const uint16_t* base, uint32_t row, uint32_t d) {
+        return *reinterpret_cast<const uint4*>(base + head + (size_t)row * D + d);
+    };
+    if (ND > 0) {
+        uint4 a[ND > 0 ? ND : 1], b[ND > 0 ? ND : 1], x[ND > 0 ? ND : 1], n[ND > 0 ? ND : 1];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t ha = (e & 1) ? (wa[e / 2] & 0xffff0000u) : (wa[e / 2] << 16);
-            const uint32_t hb = (e & 1) ? (wb[e / 2] & 0xffff0000u) : (wb[e / 2] << 16);
-            const float c = __uint_as_float(ha) + __uint_as_float(hb);
-            const __bf16 c0 = (__bf16)c;
-            const float r1 = c - (float)c0;
-            const __bf16 c1 = (__bf16)r1;
-            const __bf16 c2 = (__bf16)(r1 - (float)c1);
-            p0[e] = c0;
-            p1[e] = c1;
-            p2[e] = c2;
+        for (int s = 0; s < ND; ++s) {
+            const uint32_t d = 16 * s + 8 * kg;
+            a[s] = ld(qmax, I, d);
+            b[s] = ld(qmin, I, d);
+            x[s] = ld(kmax, J, d);
+            n[s] = ld(kmin, J, d);
         }
-        const bf16x8s bx = __builtin_bit_cast(bf16x8s, x), bn = __builtin_bit_cast(bf16x8s, n);
-        sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, bx, sx, 0, 0, 0);
-        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, bn, sn, 0, 0, 0);
-        sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, bx, sx, 0, 0, 0);
-        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, bn, sn, 0, 0, 0);
-        sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2, bx, sx, 0, 0, 0);
-        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2, bn, sn, 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < ND; ++s) score_step(a[s], b[s], x[s], n[s], sx, sn);
+    } else {
+        for (uint32_t d0 = 0; d0 < D; d0 += 16) {
+            const uint32_t d = d0 + 8 * kg;
+            score_step(ld(qmax, I, d), ld(qmin, I, d), ld(kmax, J, d), ld(kmin, J, d), sx, sn);
+        }
     }
     // value v of lane l: row I0 + 8(v/4) + 4(l/32) + v%4, column J0 + l%32
     const uint32_t Jc = J0 + r;
@@ -344,8 +368,13 @@ int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
     if (bf && D % 16 == 0) {
         const unsigned n32 = (unsigned)((nb + 31) / 32);
         dim3 g3(n32, n32, (unsigned)(B * H));
-        block_scores_mfma_kernel<<<g3, 64, 0, st>>>(static_cast<const uint16_t*>(summaries), P.BH, P.nb,
-                                                    (uint32_t)D, scores);
+        const uint16_t* summ = static_cast<const uint16_t*>(summaries);
+        if (D == 128)
+            block_scores_mfma_kernel<8><<<g3, 64, 0, st>>>(summ, P.BH, P.nb, (uint32_t)D, scores);
+        else if (D == 64)
+            block_scores_mfma_kernel<4><<<g3, 64, 0, st>>>(summ, P.BH, P.nb, (uint32_t)D, scores);
+        else
+            block_scores_mfma_kernel<0><<<g3, 64, 0, st>>>(summ, P.BH, P.nb, (uint32_t)D, scores);
         return check_launch(name);
     }
     const unsigned nt = (unsigned)((nb + kTile - 1) / kTile);
