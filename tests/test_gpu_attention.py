@@ -178,3 +178,42 @@ def test_windowed_workload_sampled_rows():
         qf, kf, vf = (synth.stored_to_f64(x[0, h]) for x in (q, k, v))
         want = OA.window_rows(qf, kf, vf, rows, 2048, 64, 128 ** -0.5)
         assert max_abs(out[0, h, rows], want) <= BF16_ATOL, h
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("tiled", [False, True])
+def test_block_sparse_short_and_empty_lists(tiled):
+    """Lists of 0 to 4 key blocks, on the permuted and the gather-on-load
+    paths: a query block with an empty list is written as zeros, every other
+    row matches the oracle."""
+    torch = torch_gpu()
+    grid, tiles = (4, 16, 16), [(1, 8, 8), (4, 4, 4)]
+    H, D, block = 2, 128, 64
+    S = 4 * 16 * 16
+    nb = S // block
+    rng = np.random.default_rng(31 + tiled)
+    keep = np.zeros((1, H, nb, nb), bool)
+    for h in range(H):
+        for I in range(nb):
+            n = I % 5                                       # 0, 1, 2, 3, 4 blocks
+            keep[0, h, I, rng.choice(nb, size=n, replace=False)] = True
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=520 + i + 10 * tiled) for i in range(3))
+    kv_idx, kv_cnt = _keep_to_gpu_lists(keep)
+    choice = torch.tensor([[0, 1]], dtype=torch.int32).cuda()
+    if tiled:
+        out = f64(bsa.bsa_block_sparse_attention_tiled(gpu(q), gpu(k), gpu(v), grid, tiles, kv_idx, kv_cnt,
+                                                       head_choice=choice))
+    else:
+        out = f64(bsa.bsa_block_sparse_attention(gpu(q), gpu(k), gpu(v), kv_idx, kv_cnt, block))
+    qf, kf, vf = (synth.stored_to_f64(x)[0] for x in (q, k, v))
+    for h in range(H):
+        # rows of the head in block order: the tile order of its tiling (tiled), or T-major
+        perm = OT.tile_permutation(grid, tiles[h]) if tiled else np.arange(S)
+        qh, kh, vh, oh = qf[h][perm], kf[h][perm], vf[h][perm], out[0, h][perm]
+        empty = np.flatnonzero(~keep[0, h].any(-1))
+        assert empty.size > 0
+        for I in empty:
+            assert np.all(oh[I * block:(I + 1) * block] == 0.0), (h, I)
+        rows = np.concatenate([np.arange(I * block, (I + 1) * block) for I in range(nb) if keep[0, h, I].any()])
+        want = OA.block_sparse_rows(qh, kh, vh, keep[0, h], block, rows, D ** -0.5)
+        assert max_abs(oh[rows], want) <= BF16_ATOL, h
