@@ -507,35 +507,36 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     int k_addr[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) k_addr[s] = k_lds<D>(col, 2 * s + half_id);
+    // Row group q (rows 4q..4q+3 of a tile) lies goff[q] bytes from the tile's
+    // first row: the same for every lane, so it goes into the DMA's scalar
+    // offset and only the lane's place within the group stays in a VGPR.
+    // TILED: cells 4q..4q+3 are 4 consecutive T-major tokens (tiles with an x
+    // extent that is a multiple of 4), P.voff[tc][q] bytes from the origin.
+    int goff[C::TILE / 1024];
+#pragma unroll
+    for (int q = 0; q < C::TILE / 1024; ++q) goff[q] = TILED ? P.voff[tc][q] : 1024 * q;
     // K tile straight into LDS with the K swizzle: instruction q fills rows
     // 4q..4q+3, lane l physical chunk l % 16 of row 4q + l / 16, which holds
     // logical chunk (l % 16) ^ (row % 8), row % 8 = 4(q % 2) + l / 16
-    int kdoff[C::TILE / 1024];
+    int klane[2];
 #pragma unroll
-    for (int q = 0; q < C::TILE / 1024; ++q)
-        kdoff[q] = (lane >> 4) * (D * 2) + (((lane & 15) ^ (4 * (q & 1) + (lane >> 4))) << 4) +
-                   (TILED ? P.voff[tc][q] : 1024 * q);
+    for (int p = 0; p < 2; ++p) klane[p] = (lane >> 4) * (D * 2) + (((lane & 15) ^ (4 * p + (lane >> 4))) << 4);
     auto dma_k = [&](int soff) {
 #pragma unroll
         for (int q = 0; q < C::TILE / 1024; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(klds + 1024 * q), 16,
-                                                     kdoff[q], soff, 0, 0);
+                                                     klane[q & 1], soff + goff[q], 0, 0);
     };
     // V tile straight into LDS (buffer loads with the LDS destination): wave
     // instruction q fills LDS bytes [1024q, 1024q + 1024), i.e. rows 4q..4q+3,
     // lane l landing on physical chunk l % 16 of row 4q + l / 16, which holds
     // logical chunk (l % 16) ^ 2(row % 4) (the V swizzle); row % 4 = l / 16.
-    // TILED: cells 4q..4q+3 are 4 consecutive T-major tokens (tiles with an x
-    // extent that is a multiple of 4), P.voff[tc][q] bytes from the origin.
-    const int vdma_off = (lane >> 4) * (D * 2) + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
-    int vdoff[C::TILE / 1024];
-#pragma unroll
-    for (int q = 0; q < C::TILE / 1024; ++q) vdoff[q] = vdma_off + (TILED ? P.voff[tc][q] : 1024 * q);
+    const int vlane = (lane >> 4) * (D * 2) + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
     auto dma_v = [&](char* buf, int soff, int q_lo, int q_hi) {
 #pragma unroll
         for (int q = q_lo; q < q_hi; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(buf + 1024 * q), 16,
-                                                     vdoff[q], soff, 0, 0);
+                                                     vlane, soff + goff[q], 0, 0);
     };
 
     f32x16 o[2][D / 32];
