@@ -114,12 +114,13 @@ def attention_call(bsa, pipe, q, k, v, out):
     kv_idx, kv_cnt = pipe.kv
     if pipe.fused:
         return lambda: bsa.bsa_block_sparse_attention_tiled(q, k, v, pipe.grid, pipe.tiles, kv_idx, kv_cnt,
-                                                            head_choice=pipe.choice, scale=pipe.scale, out=out)
+                                                            head_choice=pipe.choice, scale=pipe.scale, out=out,
+                                                            key_norms=pipe.ws_knorm)
     if pipe.pad:
         return lambda: bsa.bsa_block_sparse_attention_labels(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, pipe.block,
                                                              pipe.labels, pipe.scale, out=pipe.op)
     return lambda: bsa.bsa_block_sparse_attention(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, pipe.block, pipe.scale,
-                                                  out=pipe.op)
+                                                  out=pipe.op, key_norms=pipe.ws_knorm)
 
 
 def _time(torch, fn, steps, warmup):
@@ -316,12 +317,14 @@ def main():
         mark("start")
         choice, _, _ = bsa.bsa_select_tiling(qg, wl.grid, TILES, workspace=pipe.ws_select)
         mark("select_tiling")
-        scores, _ = bsa.bsa_minmax_block_scores_tiled(qg, kg, wl.grid, TILES, head_choice=choice, out=pipe.ws_scores)
+        scores, _ = bsa.bsa_minmax_block_scores_tiled(qg, kg, wl.grid, TILES, head_choice=choice, out=pipe.ws_scores,
+                                                      key_norms=pipe.ws_knorm)
         mark("minmax_block_scores (gather on load)")
         kv_idx, kv_cnt2 = bsa.bsa_topk_block_mask(scores, pipe.k, 1, True, max_kept=pipe.max_kept,
                                                   out=pipe.ws_topk)[:2]
         mark("topk_block_mask")
-        bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, wl.grid, TILES, kv_idx, kv_cnt2, head_choice=choice, out=out)
+        bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, wl.grid, TILES, kv_idx, kv_cnt2, head_choice=choice, out=out,
+                                             key_norms=pipe.ws_knorm)
         mark("block_sparse_attention (gather on load, T-major out)")
         torch.cuda.synchronize()
         for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
@@ -377,7 +380,7 @@ def main():
             "ms_per_call": round(attn_ms_avg, 4),
             "tflops": round(achieved, 2),
             "frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "kernel": "attn_solo_kernel<block list, positive scale, gather on load>",
+            "kernel": "attn_solo_kernel<block list, positive scale, gather on load, key-norm bound>",
             "cold_ms_per_call": round(cold_ms, 4),
             "cold_tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2),
         },

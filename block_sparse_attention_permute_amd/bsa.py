@@ -56,10 +56,10 @@ _SIGS = {
     "bsa_invert_permute": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P]),
     "bsa_block_cohesion": (_I, [_P, _I, _I64, _I64, _I64, _I64, _I, _P, _P]),
     "bsa_select_tiling": (_I, [_P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P]),
-    "bsa_minmax_block_scores": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P]),
+    "bsa_minmax_block_scores": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P]),
     "bsa_topk_block_mask": (_I, [_P, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "bsa_top_p_block_mask": (_I, [_P, _I64, _I64, _I, _I, _F, _F, _I, _I, _P, _P, _I, _P, _P]),
-    "bsa_block_sparse_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _F, _P]),
+    "bsa_block_sparse_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _F, _P, _P]),
     "bsa_windowed_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _P]),
     "bsa_validate_block_list": (_I, [_P, _P, _I64, _I64, _I, _I, _I, _P]),
     "bsa_validate_indices": (_I, [_P, _I64, _I, _I, _P]),
@@ -69,13 +69,13 @@ _SIGS = {
     "bsa_tile_permute_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _I64, _P, _P]),
     "bsa_invert_permute_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _I64, _P]),
     "bsa_select_tiling_ex": (_I, [_P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _I, _I, _P, _P, _P, _P]),
-    "bsa_minmax_block_scores_masked": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P]),
+    "bsa_minmax_block_scores_masked": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P]),
     "bsa_topk_block_mask_tiled": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _P]),
     "bsa_block_sparse_attention_labels": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _P,
                                                _I64, _F, _P]),
-    "bsa_minmax_block_scores_tiled": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P]),
+    "bsa_minmax_block_scores_tiled": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P, _P]),
     "bsa_block_sparse_attention_tiled": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
-                                              _I, _F, _P]),
+                                              _I, _F, _P, _P]),
 }
 
 
@@ -352,10 +352,24 @@ def bsa_select_tiling(q, grid, tiles, workspace=None, statistic: str = "mean", p
     return choice, score, tile_coh
 
 
-def bsa_minmax_block_scores(q, k, block: int, out=None, labels=None):
+def _norms_out(key_norms, B, H, nb, like):
+    """Pointer of an optional float32 (B, H, nb) key-norm tensor (None: not written / not used)."""
+    if key_norms is None:
+        return None
+    torch = _torch()
+    if key_norms.dtype != torch.float32 or tuple(key_norms.shape) != (B, H, nb):
+        raise ValueError(f"key_norms must be float32 {(B, H, nb)}")
+    if key_norms.device != like.device:
+        raise ValueError("key_norms must be on the tensors' device")
+    return _dev(key_norms, "key_norms")
+
+
+def bsa_minmax_block_scores(q, k, block: int, out=None, labels=None, key_norms=None):
     """-> (scores float32 (B, H, Nb, Nb), summaries (4, B, H, Nb, D): qmax, qmin, kmax, kmin).
 
-    labels: int32 (B, H, S) or None; tokens labelled < 0 are left out."""
+    labels: int32 (B, H, S) or None; tokens labelled < 0 are left out.
+    key_norms: float32 (B, H, Nb) or None; when given it receives each key
+    block's largest row L2 norm (for bsa_block_sparse_attention)."""
     torch = _torch()
     B, H, S, D = _bhsd(q, "q")
     if _bhsd(k, "k") != (B, H, S, D) or k.dtype != q.dtype:
@@ -368,20 +382,22 @@ def bsa_minmax_block_scores(q, k, block: int, out=None, labels=None):
         summ = torch.empty((4, B, H, nb, D), dtype=q.dtype, device=q.device)
     else:
         scores, summ = out
+    kn = _norms_out(key_norms, B, H, nb, q)
     if labels is None:
         _check(lib().bsa_minmax_block_scores(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, S, D, int(block),
-                                             _dev(summ), _dev(scores), _stream(q)))
+                                             _dev(summ), _dev(scores), kn, _stream(q)))
     else:
         if labels.dtype != torch.int32 or tuple(labels.shape) != (B, H, S):
             raise ValueError("labels must be int32 (B, H, S)")
         _check(lib().bsa_minmax_block_scores_masked(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, S, D,
                                                     int(block), _dev(labels, "labels"), _dev(summ), _dev(scores),
-                                                    _stream(q)))
+                                                    kn, _stream(q)))
     return scores, summ
 
 
-def bsa_minmax_block_scores_tiled(q, k, grid, tiles, head_choice=None, out=None):
-    """Min/max block scores of T-major q, k, block J = tile J of each head's tiling."""
+def bsa_minmax_block_scores_tiled(q, k, grid, tiles, head_choice=None, out=None, key_norms=None):
+    """Min/max block scores of T-major q, k, block J = tile J of each head's tiling (key_norms as in
+    bsa_minmax_block_scores)."""
     torch = _torch()
     B, H, S, D = _bhsd(q, "q")
     if _bhsd(k, "k") != (B, H, S, D) or k.dtype != q.dtype:
@@ -398,8 +414,9 @@ def bsa_minmax_block_scores_tiled(q, k, grid, tiles, head_choice=None, out=None)
     else:
         scores, summ = out
     hc = None if head_choice is None else _dev(head_choice, "head_choice")
+    kn = _norms_out(key_norms, B, H, nb, q)
     _check(lib().bsa_minmax_block_scores_tiled(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, T, Hg, Wg, D, arr,
-                                               n, hc, _dev(summ), _dev(scores), _stream(q)))
+                                               n, hc, _dev(summ), _dev(scores), kn, _stream(q)))
     return scores, summ
 
 
@@ -494,8 +511,12 @@ def _qkv(q, k, v):
     return shp
 
 
-def bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block: int, scale=None, out=None):
-    """Attention of every query block over its kept key blocks -> (B, H, S, D) like q."""
+def bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block: int, scale=None, out=None, key_norms=None):
+    """Attention of every query block over its kept key blocks -> (B, H, S, D) like q.
+
+    key_norms: float32 (B, H, S // block) or None, at least each key block's largest row L2 norm (as
+    bsa_minmax_block_scores writes them); it lets the kernel skip the running-max update of key blocks
+    that cannot pass it, which changes the result only by rounding."""
     torch = _torch()
     B, H, S, D = _qkv(q, k, v)
     if kv_idx.dtype != torch.int32 or kv_cnt.dtype != torch.int32 or kv_idx.dim() != 4:
@@ -507,7 +528,8 @@ def bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block: int, scale=None, 
     o = torch.empty_like(q) if out is None else out
     _check(lib().bsa_block_sparse_attention(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
                                             _dtype_code(q), B, H, S, D, int(block), _dev(kv_idx), _dev(kv_cnt),
-                                            int(kv_idx.shape[3]), _scale(scale), _stream(q)))
+                                            int(kv_idx.shape[3]), _scale(scale),
+                                            _norms_out(key_norms, B, H, S // block, q), _stream(q)))
     return o
 
 
@@ -518,8 +540,11 @@ def tiled_attention_supported(dtype, D, tiles) -> bool:
             all(a * b * c == 64 and c % 4 == 0 for a, b, c in (tuple(int(v) for v in t) for t in tiles)))
 
 
-def bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_choice=None, scale=None, out=None):
-    """Block-sparse attention of T-major tensors, blocks = tiles (gather on load) -> T-major (B, H, S, D)."""
+def bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_choice=None, scale=None, out=None,
+                                     key_norms=None):
+    """Block-sparse attention of T-major tensors, blocks = tiles (gather on load) -> T-major (B, H, S, D).
+
+    key_norms: per tile of each head's tiling, as in bsa_block_sparse_attention."""
     torch = _torch()
     B, H, S, D = _qkv(q, k, v)
     T, Hg, Wg = (int(g) for g in grid)
@@ -534,7 +559,8 @@ def bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_
     hc = None if head_choice is None else _dev(head_choice, "head_choice")
     _check(lib().bsa_block_sparse_attention_tiled(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
                                                   _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, hc, _dev(kv_idx),
-                                                  _dev(kv_cnt), int(kv_idx.shape[3]), _scale(scale), _stream(q)))
+                                                  _dev(kv_cnt), int(kv_idx.shape[3]), _scale(scale),
+                                                  _norms_out(key_norms, B, H, S // 64, q), _stream(q)))
     return o
 
 
@@ -664,6 +690,9 @@ class AdaptiveBlockSparse:
                           torch.empty((4, B, H, self.nb, D), dtype=dtype, **f))
         self.ws_topk = (torch.empty((B, H, self.nb, self.max_kept), dtype=torch.int32, **f),
                         torch.empty((B, H, self.nb), dtype=torch.int32, **f), None)
+        # each key block's largest row norm, written by the scores pass: the attention kernel skips the
+        # running-max update of the key blocks it proves cannot pass it
+        self.ws_knorm = None if self.pad else torch.empty((B, H, self.nb), dtype=torch.float32, **f)
 
     @property
     def choice(self):
@@ -685,11 +714,12 @@ class AdaptiveBlockSparse:
         else:
             if self.fused:
                 scores, _ = bsa_minmax_block_scores_tiled(q, k, self.grid, self.tiles, head_choice=choice,
-                                                          out=self.ws_scores)
+                                                          out=self.ws_scores, key_norms=self.ws_knorm)
             else:
                 for src, dst in ((q, self.qp), (k, self.kp), (v, self.vp)):
                     bsa_tile_permute(src, self.grid, self.tiles, head_choice=choice, out=dst)
-                scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores)
+                scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores,
+                                                    key_norms=self.ws_knorm)
             if self.top_p is None:
                 kv_idx, kv_cnt, _ = bsa_topk_block_mask(scores, self.k, self.sink_blocks, self.keep_diag,
                                                         max_kept=self.max_kept, return_mask=True, out=self.ws_topk)
@@ -700,7 +730,7 @@ class AdaptiveBlockSparse:
             if attention_hook is not None:
                 attention_hook(True)
             o = bsa_block_sparse_attention_tiled(q, k, v, self.grid, self.tiles, kv_idx, kv_cnt, head_choice=choice,
-                                                 scale=self.scale, out=out)
+                                                 scale=self.scale, out=out, key_norms=self.ws_knorm)
             if attention_hook is not None:
                 attention_hook(False)
             return o
@@ -711,7 +741,7 @@ class AdaptiveBlockSparse:
                                               self.scale, out=self.op)
         else:
             bsa_block_sparse_attention(self.qp, self.kp, self.vp, kv_idx, kv_cnt, self.block, self.scale,
-                                       out=self.op)
+                                       out=self.op, key_norms=self.ws_knorm)
         if attention_hook is not None:
             attention_hook(False)
         if self.pad:

@@ -53,6 +53,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // the weights the P V product uses
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P may grow to 2^8 before a rescale
+constexpr float kSkipSlack = 32.0f;    // log2 units: P may reach 2^32 in a tile that skips the max
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
 // 6:4, lgkmcnt in 11:8; a field at its maximum does not wait)
@@ -81,6 +82,8 @@ struct AttnParams {
     uint32_t max_kept;
     // window
     int32_t half, sink;
+    // block lists: per key block, at least the largest L2 norm of its key rows, or null
+    const float* knorm;
     // labels
     const int32_t* labels;
     uint64_t label_stride;  // elements between heads (0: one row for all heads)
@@ -429,9 +432,10 @@ struct SoloCfg {
     static constexpr int TILE = BLK * D * 2;  // one V tile in LDS
 };
 
-template <int MODE, bool POS, bool TILED>
+template <int MODE, bool POS, bool TILED, bool BOUND = false>
 __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, const int32_t* __restrict__ kv_idx,
-                                                          const int32_t* __restrict__ kv_cnt) {
+                                                          const int32_t* __restrict__ kv_cnt,
+                                                          const float* __restrict__ knorm) {
     using C = SoloCfg;
     constexpr int D = C::D, BLK = C::BLK;
     // Q (64 rows) and one V tile live in the wave's LDS (32 KB: four waves per CU)
@@ -548,6 +552,37 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
             for (int v = 0; v < 16; ++v) o[r][t][v] = 0.f;
     float m_used[2] = {-1e30f, -1e30f}, l_part[2] = {0.f, 0.f};
     const float c_scale = POS ? P.scale_log2 : 1.0f;
+    // Key norms given (block lists, positive scale): by Cauchy-Schwarz every
+    // score of this query block against key tile J, times scale * log2(e), is
+    // at most q_lim * knorm[J], q_lim = the largest |q_row| of the block times
+    // scale * log2(e).  When that stays within kSkipSlack of the smallest
+    // running max of the block's rows, m_min, no softmax weight of the tile
+    // can pass 2^kSkipSlack and the tile skips the max.  The test is
+    // knorm[J] <= kn_lim = (m_min + kSkipSlack) / q_lim, on scalars; kn_lim
+    // only moves when a rescale moves the running max.
+    constexpr bool bounded = BOUND && MODE == kBlockList && POS;
+    const float* knorm_head = bounded ? knorm + (size_t)bh * P.nq : nullptr;
+    float q_lim = 0.f, kn_lim = -__builtin_inff(), kn_cur = 0.f;
+    if (bounded) {
+        float n2max = 0.f;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            float n2 = 0.f;
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bf16x2 two = {qf[r][s][2 * e], qf[r][s][2 * e + 1]};
+                    n2 = __builtin_amdgcn_fdot2_f32_bf16(two, two, n2, false);
+                }
+            // lanes l and l ^ 32 hold the two halves of row 32r + l % 32
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(n2), __float_as_uint(n2), false, false);
+            n2max = fmaxf(n2max, __uint_as_float(pr[0]) + __uint_as_float(pr[1]));
+        }
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) n2max = fmaxf(n2max, __shfl_xor(n2max, off));
+        q_lim = sqrtf(__uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(n2max)))) * c_scale;
+    }
 
     const int g16 = lane >> 4, r16 = lane & 15;
     const int v_key0 = 4 * (g16 >> 1) + (r16 >> 2);
@@ -576,6 +611,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     int soff_cur = 0, v_nxt = 0;
     if (n_iter > 0) {
         const int t0 = tile_at(0);
+        if (bounded) kn_cur = knorm_head[t0];
         soff_cur = tile_soff(t0);
         dma_k(soff_cur);
         if (MODE == kLabels) klab_next = labs[t0 * BLK + lane];
@@ -586,6 +622,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     for (int it = 0; it < n_iter; ++it) {
         const int nxt_tile = __builtin_amdgcn_readfirstlane(v_nxt);
         const int nxt = nxt_tile * BLK;
+        const float kn_nxt = bounded ? knorm_head[nxt_tile] : 0.f;
         // this tile's K has landed in LDS (nothing later was issued) and the
         // previous tile's V reads have completed
         __builtin_amdgcn_s_waitcnt(0);
@@ -678,29 +715,43 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                     }
             }
         }
-        float mloc[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            float smax = fmaxf(sacc[0][r][0], sacc[1][r][0]);
-#pragma unroll
-            for (int v = 1; v < 16; ++v) smax = fmaxf(fmaxf(smax, sacc[0][r][v]), sacc[1][r][v]);
-            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
-            mloc[r] = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * c_scale;
-        }
-        const bool grow0 = mloc[0] > m_used[0] + kRescaleSlack;
-        const bool grow1 = mloc[1] > m_used[1] + kRescaleSlack;
-        if (__ballot(grow0 | grow1)) {
+        // (the ballot keeps the test in a VGPR compare; as a plain scalar branch
+        // the compiler allocates the loop's registers far worse)
+        const bool skip = bounded && __ballot(kn_cur <= kn_lim) != 0;
+        kn_cur = kn_nxt;
+        if (__builtin_expect(!skip, !bounded)) {
+            float mloc[2];
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const bool grow = r == 0 ? grow0 : grow1;
-                const float m_new = grow ? mloc[r] : m_used[r];
-                const float alpha = __builtin_amdgcn_exp2f(m_used[r] - m_new);
-                m_used[r] = m_new;
-                l_part[r] *= alpha;
+                float smax = fmaxf(sacc[0][r][0], sacc[1][r][0]);
 #pragma unroll
-                for (int t = 0; t < D / 32; ++t)
+                for (int v = 1; v < 16; ++v) smax = fmaxf(fmaxf(smax, sacc[0][r][v]), sacc[1][r][v]);
+                const auto pr =
+                    __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+                mloc[r] = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * c_scale;
+            }
+            const bool grow0 = mloc[0] > m_used[0] + kRescaleSlack;
+            const bool grow1 = mloc[1] > m_used[1] + kRescaleSlack;
+            if (__ballot(grow0 | grow1)) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) o[r][t][v] *= alpha;
+                for (int r = 0; r < 2; ++r) {
+                    const bool grow = r == 0 ? grow0 : grow1;
+                    const float m_new = grow ? mloc[r] : m_used[r];
+                    const float alpha = __builtin_amdgcn_exp2f(m_used[r] - m_new);
+                    m_used[r] = m_new;
+                    l_part[r] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) o[r][t][v] *= alpha;
+                }
+                if (bounded) {
+                    float mm = fminf(m_used[0], m_used[1]);
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) mm = fminf(mm, __shfl_xor(mm, off));
+                    const float m_min = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(mm)));
+                    kn_lim = (m_min + kSkipSlack) / q_lim;
+                }
             }
         }
         // P as bf16 B operands, one 16-key group m at a time (pb[r][m] covers keys
@@ -889,10 +940,12 @@ int launch_scalar(const ScalarParams& P, int dtype, int64_t D, hipStream_t st, c
 
 template <int MODE, bool TILED = false>
 void launch_solo(const AttnParams& P, hipStream_t st) {
-    if (P.scale_log2 > 0.f)
-        attn_solo_kernel<MODE, true, TILED><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt);
+    if (MODE == kBlockList && P.scale_log2 > 0.f && P.knorm != nullptr)
+        attn_solo_kernel<MODE, true, TILED, true><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, P.knorm);
+    else if (P.scale_log2 > 0.f)
+        attn_solo_kernel<MODE, true, TILED><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
     else
-        attn_solo_kernel<MODE, false, TILED><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt);
+        attn_solo_kernel<MODE, false, TILED><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
 }
 
 template <int D, int BLK, int MODE>
@@ -930,7 +983,8 @@ using namespace bsa;
 
 extern "C" int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B,
                                           int64_t H, int64_t S, int64_t D, int block, const int32_t* kv_idx,
-                                          const int32_t* kv_cnt, int max_kept, float scale, bsa_stream_t stream) {
+                                          const int32_t* kv_cnt, int max_kept, float scale,
+                                          const float* key_norms_or_null, bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_block_sparse_attention";
     int rc = common_checks(q, k, v, out, dtype, B, H, S, D, name);
@@ -958,6 +1012,7 @@ extern "C" int bsa_block_sparse_attention(const void* q, const void* k, const vo
         P.kv_idx = kv_idx;
         P.kv_cnt = kv_cnt;
         P.max_kept = (uint32_t)max_kept;
+        P.knorm = key_norms_or_null;
         if (D == 128 && block == 64) launch_solo<kBlockList>(P, st);
         else if (D == 128 && block == 32) launch_mfma<128, 32, kBlockList>(P, st);
         else if (D == 64 && block == 64) launch_mfma<64, 64, kBlockList>(P, st);
@@ -1088,7 +1143,8 @@ extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, co
                                                 int64_t B, int64_t H, int T, int Hg, int Wg, int64_t D,
                                                 const int32_t* tiles_host, int n_tiles, const int32_t* head_choice,
                                                 const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
-                                                float scale, bsa_stream_t stream) {
+                                                float scale, const float* key_norms_or_null,
+                                                bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_block_sparse_attention_tiled";
     BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
@@ -1131,6 +1187,7 @@ extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, co
     P.kv_idx = kv_idx;
     P.kv_cnt = kv_cnt;
     P.max_kept = (uint32_t)max_kept;
+    P.knorm = key_norms_or_null;
     P.head_choice = head_choice;
     P.n_tiles = (uint32_t)n_tiles;
     P.Hg = (uint32_t)Hg;

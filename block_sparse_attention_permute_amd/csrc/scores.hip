@@ -31,6 +31,7 @@ struct SumParams {
     const char* q;
     const char* k;
     char* summ;  // 4 x (BH, Nb, D) of the input dtype
+    float* knorm;  // (BH, Nb): largest L2 norm of a key row in each block, or null
     uint32_t block, nb, vecs_per_row, BH;
     const int32_t* labels;  // (BH, S) or null; tokens labelled < 0 are left out
     // tiled: q, k in T-major order, block = tile of the head's tiling
@@ -97,6 +98,10 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
         mn[i] = __builtin_inff();
     }
     const int32_t* lab = P.labels != nullptr ? P.labels + ((size_t)bh * P.nb + blk) * P.block : nullptr;
+    // key blocks: also the largest squared row norm (a row's LPT lanes add
+    // their squares; every pass of the loop keeps the same lanes together)
+    const bool norms = which == 1 && P.knorm != nullptr;
+    float n2max = 0.f;
     for (uint32_t t = slot; t < P.block; t += TPI) {
         if (lab != nullptr && lab[t] < 0) continue;
         float v[EPV];
@@ -107,6 +112,19 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
             mx[i] = fmaxf(mx[i], v[i]);
             mn[i] = fminf(mn[i], v[i]);
         }
+        if (norms) {
+            float n2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) n2 = fmaf(v[i], v[i], n2);
+#pragma unroll
+            for (int off = 1; off < LPT; off <<= 1) n2 += __shfl_xor(n2, off);
+            n2max = fmaxf(n2max, n2);
+        }
+    }
+    if (norms) {
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) n2max = fmaxf(n2max, __shfl_xor(n2max, off));
+        if (lane == 0) P.knorm[(size_t)bh * P.nb + blk] = sqrtf(n2max);
     }
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
@@ -325,8 +343,8 @@ namespace bsa {
 namespace {
 
 int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H, int64_t S, int64_t D, int block,
-                  const int32_t* labels, SumParams& P, bool tiled, void* summaries, float* scores, hipStream_t st,
-                  const char* name) {
+                  const int32_t* labels, SumParams& P, bool tiled, void* summaries, float* scores, float* key_norms,
+                  hipStream_t st, const char* name) {
     const int es = elem_size(dtype);
     BSA_REQUIRE(es != 0, "%s: unknown dtype %d", name, dtype);
     BSA_REQUIRE(q && k && summaries && scores, "%s: NULL argument", name);
@@ -348,6 +366,7 @@ int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
     P.vecs_per_row = (uint32_t)vecs;
     P.BH = (uint32_t)(B * H);
     P.labels = labels;
+    P.knorm = key_norms;
     dim3 g1((unsigned)((nb + kWaves - 1) / kWaves), 2, (unsigned)(B * H));
 #define BSA_MM(EPV, LPT)                                                          \
     (tiled ? block_minmax_kernel<EPV, LPT, true><<<g1, 64 * kWaves, 0, st>>>(P) \
@@ -393,17 +412,18 @@ int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
 
 extern "C" int bsa_minmax_block_scores_masked(const void* q, const void* k, int dtype, int64_t B, int64_t H,
                                               int64_t S, int64_t D, int block, const int32_t* labels_or_null,
-                                              void* summaries, float* scores, bsa_stream_t stream) {
+                                              void* summaries, float* scores, float* key_norms_or_null,
+                                              bsa_stream_t stream) {
     clear_error();
     SumParams P{};
     return minmax_scores(q, k, dtype, B, H, S, D, block, labels_or_null, P, false, summaries, scores,
-                         (hipStream_t)stream, "bsa_minmax_block_scores");
+                         key_norms_or_null, (hipStream_t)stream, "bsa_minmax_block_scores");
 }
 
 extern "C" int bsa_minmax_block_scores_tiled(const void* q, const void* k, int dtype, int64_t B, int64_t H, int T,
                                              int Hg, int Wg, int64_t D, const int32_t* tiles_host, int n_tiles,
                                              const int32_t* head_choice, void* summaries, float* scores,
-                                             bsa_stream_t stream) {
+                                             float* key_norms_or_null, bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_minmax_block_scores_tiled";
     BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
@@ -422,10 +442,12 @@ extern "C" int bsa_minmax_block_scores_tiled(const void* q, const void* k, int d
     P.Hg = (uint32_t)Hg;
     P.Wg = (uint32_t)Wg;
     return minmax_scores(q, k, dtype, B, H, (int64_t)T * Hg * Wg, D, vol, nullptr, P, true, summaries, scores,
-                         (hipStream_t)stream, name);
+                         key_norms_or_null, (hipStream_t)stream, name);
 }
 
 extern "C" int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H, int64_t S,
-                                       int64_t D, int block, void* summaries, float* scores, bsa_stream_t stream) {
-    return bsa_minmax_block_scores_masked(q, k, dtype, B, H, S, D, block, nullptr, summaries, scores, stream);
+                                       int64_t D, int block, void* summaries, float* scores, float* key_norms_or_null,
+                                       bsa_stream_t stream) {
+    return bsa_minmax_block_scores_masked(q, k, dtype, B, H, S, D, block, nullptr, summaries, scores,
+                                          key_norms_or_null, stream);
 }

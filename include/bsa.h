@@ -220,10 +220,14 @@ int bsa_select_tiling_ex(const void* q, int dtype, int64_t B, int64_t H, int T, 
  * q, k: device (B, H, S, D).  summaries: device, 4*B*H*Nb*D elements of
  * `dtype` in the order qmax, qmin, kmax, kmin, each (B, H, Nb, D); it is
  * written.  scores: device float (B, H, Nb, Nb).  Nb = S/block.
+ * key_norms_or_null: device float (B, H, Nb) or NULL; when given, entry
+ * (b, h, J) is set to the largest L2 norm of a key row of block J (fp32;
+ * not part of the method: it lets bsa_block_sparse_attention bound a block's
+ * scores by Cauchy-Schwarz).
  * INVALID_ARG unless block divides S. */
 int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
                             int64_t S, int64_t D, int block, void* summaries, float* scores,
-                            bsa_stream_t stream);
+                            float* key_norms_or_null, bsa_stream_t stream);
 
 /* bsa_minmax_block_scores on T-major q and k: block J of head (b, h) is tile
  * J of candidate c = head_choice[b*H + h] (0 if NULL), read in place through
@@ -234,17 +238,18 @@ int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, 
 int bsa_minmax_block_scores_tiled(const void* q, const void* k, int dtype, int64_t B, int64_t H,
                                   int T, int Hg, int Wg, int64_t D, const int32_t* tiles_host,
                                   int n_tiles, const int32_t* head_choice, void* summaries,
-                                  float* scores, bsa_stream_t stream);
+                                  float* scores, float* key_norms_or_null, bsa_stream_t stream);
 
 /* bsa_minmax_block_scores over labelled tokens only: tokens with
  * labels[b,h,s] < 0 (padding) are left out of the summaries, so a partial
  * block is summarised by its real tokens [Adaptive tiling (SPADE),
  * "Deviations and notes": padded grids].  A block with no such token scores
  * -inf in its whole row and column.  labels_or_null: device int32 (B, H, S)
- * (NULL: every token counts). */
+ * (NULL: every token counts); key norms over the labelled key rows. */
 int bsa_minmax_block_scores_masked(const void* q, const void* k, int dtype, int64_t B, int64_t H,
                                    int64_t S, int64_t D, int block, const int32_t* labels_or_null,
-                                   void* summaries, float* scores, bsa_stream_t stream);
+                                   void* summaries, float* scores, float* key_norms_or_null,
+                                   bsa_stream_t stream);
 
 /* Per-row block selection: keep the k best key blocks of each (b, h, I) row,
  * ranked by score (higher first) and then by index (lower first), then add
@@ -308,11 +313,19 @@ int bsa_topk_block_mask_tiled(const float* scores, int64_t B, int64_t H, int Nq,
  * bf16: D in {64, 128} and block in {32, 64} run on MFMA; other bf16 / fp32
  * shapes with D <= 128 use a scalar kernel.  Accumulation and softmax are
  * fp32; bf16 outputs are rounded to nearest even once.
+ * key_norms_or_null: device float (B, H, S/block) or NULL, each at least the
+ * largest L2 norm of a key row of its block (bsa_minmax_block_scores writes
+ * them).  It changes only the work, not the result beyond rounding: for
+ * bf16, D = 128, block 64 and scale > 0, a key block whose scores cannot
+ * pass the running row max by more than 24 in log2 units (|q_i| * norm_J *
+ * scale * log2(e), Cauchy-Schwarz) skips the running-max update, so its
+ * softmax weights are taken relative to an older max (an exact shift of the
+ * softmax; the weights are rounded to bf16 at a different scale).
  * INVALID_ARG unless block divides S and max_kept >= 1. */
 int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void* out, int dtype,
                                int64_t B, int64_t H, int64_t S, int64_t D, int block,
                                const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
-                               float scale, bsa_stream_t stream);
+                               float scale, const float* key_norms_or_null, bsa_stream_t stream);
 
 /* Block-sparse attention on T-major q, k, v, out: query/key block J of head
  * (b, h) is tile J of candidate c = head_choice[b*H + h] (0 if NULL), and the
@@ -320,8 +333,9 @@ int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void
  * the result equals bsa_tile_permute -> bsa_block_sparse_attention ->
  * bsa_invert_permute without the three permuted copies and the inverse pass
  * [Adaptive tiling (SPADE), "The idea" step 2 and "Recipe": attention in
- * tile order, results taken back to T-major order].  kv_idx / kv_cnt as in
- * bsa_block_sparse_attention with S/64 blocks per head.
+ * tile order, results taken back to T-major order].  kv_idx / kv_cnt and
+ * key_norms_or_null (per tile, as bsa_minmax_block_scores_tiled writes them)
+ * as in bsa_block_sparse_attention with S/64 blocks per head.
  * UNSUPPORTED unless dtype is bf16, D = 128 and every candidate has 64
  * tokens with an x extent c that is a multiple of 4 (4 consecutive T-major
  * tokens per LDS-DMA row group); INVALID_ARG if a candidate does not divide
@@ -331,7 +345,7 @@ int bsa_block_sparse_attention_tiled(const void* q, const void* k, const void* v
                                      int64_t D, const int32_t* tiles_host, int n_tiles,
                                      const int32_t* head_choice, const int32_t* kv_idx,
                                      const int32_t* kv_cnt, int max_kept, float scale,
-                                     bsa_stream_t stream);
+                                     const float* key_norms_or_null, bsa_stream_t stream);
 
 /* bsa_block_sparse_attention with a token label rule inside the kept
  * blocks: query i sees key j when j's block is kept for i's block AND

@@ -158,7 +158,7 @@ def test_device_calls_reject_bad_arguments(L):
          "dtype"),
         ("bsa_block_cohesion", (FAKE, BF, 1, 2, 100, 64, 64, FAKE, None), "divide"),
         ("bsa_select_tiling", (FAKE, BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, FAKE, FAKE, FAKE, None), "divide"),
-        ("bsa_minmax_block_scores", (FAKE, FAKE, BF, 1, 2, 100, 128, 64, FAKE, FAKE, None), "divide"),
+        ("bsa_minmax_block_scores", (FAKE, FAKE, BF, 1, 2, 100, 128, 64, FAKE, FAKE, None, None), "divide"),
         ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 0, 1, 1, FAKE, FAKE, 83, None, None), "k=0"),
         ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 481, 1, 1, FAKE, FAKE, 483, None, None), "k=481"),
         ("bsa_topk_block_mask", (FAKE, 1, 1, 480, 480, 81, 1, 1, FAKE, FAKE, 82, None, None), "max_kept"),
@@ -174,9 +174,9 @@ def test_device_calls_reject_bad_arguments(L):
         ("bsa_top_p_block_mask", (FAKE, 1, 1, 480, 480, ctypes.c_float(0.5), ctypes.c_float(1.0), 1, 1, FAKE, FAKE,
                                   479, None, None), "max_kept"),
         ("bsa_block_sparse_attention",
-         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 100, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None), "divide"),
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 100, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None, None), "divide"),
         ("bsa_block_sparse_attention",
-         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 0, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None), "> 0"),
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 0, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None, None), "> 0"),
         ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 0, 2, ctypes.c_float(0.25), 8, None),
          "window"),
         ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, -1, ctypes.c_float(0.25), 8, None),
@@ -199,7 +199,8 @@ def test_device_calls_reject_bad_arguments(L):
                                      0, None, None), "Sp"),
         ("bsa_invert_permute_padded", (FAKE, ctypes.c_void_p(1 << 30), BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1,
                                        None, 40000, None), "shorter"),
-        ("bsa_minmax_block_scores_masked", (FAKE, FAKE, BF, 1, 2, 100, 128, 64, FAKE, FAKE, FAKE, None), "divide"),
+        ("bsa_minmax_block_scores_masked", (FAKE, FAKE, BF, 1, 2, 100, 128, 64, FAKE, FAKE, FAKE, None, None),
+         "divide"),
         ("bsa_topk_block_mask_tiled", (FAKE, 1, 1, 768, 768, FAKE, K_TAB, NK_BAD, 2, 1, 1, FAKE, FAKE, 140, None,
                                        None), "nk_table"),
         ("bsa_topk_block_mask_tiled", (FAKE, 1, 1, 768, 768, FAKE, K_TAB, NK_TAB, 2, 1, 1, FAKE, FAKE, 100, None,
