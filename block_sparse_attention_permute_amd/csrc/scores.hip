@@ -69,6 +69,25 @@ __device__ __forceinline__ uint4 pack(const float (&v)[EPV]) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Sum over the LPT consecutive lanes that share a token row, with DPP lane
+// swaps (VALU, no LDS): pairs, then quads (quad permutations), then the two
+// quads of each 8-lane half (half-row mirror), then the two halves of a
+// 16-lane row (row mirror); across 16-lane rows a shuffle.  Every step reads
+// lanes of the same group only.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int LPT>
+__device__ __forceinline__ float group_sum(float x) {
+    if (LPT >= 2) x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    if (LPT >= 4) x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    if (LPT >= 8) x += dpp_f32<0x141>(x);  // row_half_mirror
+    if (LPT >= 16) x += dpp_f32<0x140>(x); // row_mirror
+    if (LPT >= 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
 // blockIdx: x = group of kWaves blocks, y = 0 (q) / 1 (k), z = b*H + h.
 template <int EPV, int LPT, bool TILED>
 __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumParams P) {
@@ -116,9 +135,7 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
             float n2 = 0.f;
 #pragma unroll
             for (int i = 0; i < EPV; ++i) n2 = fmaf(v[i], v[i], n2);
-#pragma unroll
-            for (int off = 1; off < LPT; off <<= 1) n2 += __shfl_xor(n2, off);
-            n2max = fmaxf(n2max, n2);
+            n2max = fmaxf(n2max, group_sum<LPT>(n2));
         }
     }
     if (norms) {
