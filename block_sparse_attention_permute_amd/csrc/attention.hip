@@ -428,7 +428,7 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
 //  * block-list entries come one tile ahead through buffer loads (vector
 //    memory), so waiting for them never waits on LDS traffic.
 struct SoloCfg {
-    static constexpr int D = 128, BLK = 64, NT = 64, NCH = D / 8;
+    static constexpr int D = 128, BLK = 64;
     static constexpr int TILE = BLK * D * 2;  // one V tile in LDS
 };
 

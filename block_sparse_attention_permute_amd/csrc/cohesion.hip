@@ -31,6 +31,7 @@ namespace bsa {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kBatch = 8;  // tokens loaded per lane before use
 
 struct CohParams {
     const char* x;
@@ -45,8 +46,7 @@ struct CohParams {
 };
 
 template <int EPV>
-__device__ __forceinline__ void load_vec(const char* p, float (&v)[EPV]) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void unpack(const uint4 raw, float (&v)[EPV]) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     if (EPV == 8) {
 #pragma unroll
@@ -89,36 +89,42 @@ __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohPar
 #pragma unroll
     for (int i = 0; i < EPV; ++i) u[i] = 0.f;
     float n = 0.f;
-    for (uint32_t base = 0; base < g.vol; base += TPI) {
-        const uint32_t cell = base + slot;
-        float v[EPV];
-        float ss = 0.f;
-        bool real = cell < g.vol;
-        uint32_t s = 0;
-        if (PAD && real) {
-            uint32_t rt, rem, ry, rx;
-            fdivmod(cell, g.f_bc, rt, rem);
-            fdivmod(rem, g.f_c, ry, rx);
-            real = t0 + rt < P.T && y0 + ry < P.Hg && x0 + rx < P.Wg;
-            s = ((t0 + rt) * P.Hg + y0 + ry) * P.Wg + x0 + rx;
-        } else if (real) {
-            s = origin + cell_offset(cell, g, P.Hg, P.Wg);
+    // kBatch tokens per lane are loaded before any is used, so that many
+    // loads are in flight per wave; a cell outside the tile or the grid loads
+    // the head's first row and is then taken as a zero token.
+    for (uint32_t base = 0; base < g.vol; base += TPI * kBatch) {
+        uint4 raw[kBatch];
+        bool real[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const uint32_t cell = base + j * TPI + slot;
+            real[j] = cell < g.vol;
+            uint32_t s = 0;
+            if (PAD) {
+                uint32_t rt, rem, ry, rx;
+                fdivmod(real[j] ? cell : 0u, g.f_bc, rt, rem);
+                fdivmod(rem, g.f_c, ry, rx);
+                real[j] = real[j] && t0 + rt < P.T && y0 + ry < P.Hg && x0 + rx < P.Wg;
+                s = real[j] ? ((t0 + rt) * P.Hg + y0 + ry) * P.Wg + x0 + rx : 0u;
+            } else {
+                s = real[j] ? origin + cell_offset(cell, g, P.Hg, P.Wg) : 0u;
+            }
+            raw[j] = *reinterpret_cast<const uint4*>(head + (size_t)s * row_bytes + (size_t)sub * 16);
         }
-        if (real) {
-            load_vec<EPV>(head + (size_t)s * row_bytes + (size_t)sub * 16, v);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            float v[EPV];
+            unpack<EPV>(raw[j], v);
+            float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < EPV; ++i) ss = fmaf(v[i], v[i], ss);
-        } else {
+            ss = group_sum<LPT>(ss);
+            if (real[j] && ss > 0.f) {
+                const float inv = 1.0f / sqrtf(ss);
 #pragma unroll
-            for (int i = 0; i < EPV; ++i) v[i] = 0.f;
-        }
-#pragma unroll
-        for (int off = LPT / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-        if (ss > 0.f) {
-            const float inv = 1.0f / sqrtf(ss);
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) u[i] = fmaf(v[i], inv, u[i]);
-            n += 1.f;
+                for (int i = 0; i < EPV; ++i) u[i] = fmaf(v[i], inv, u[i]);
+                n += 1.f;
+            }
         }
     }
     // sum the normalised vectors over token slots (lanes with equal `sub`)

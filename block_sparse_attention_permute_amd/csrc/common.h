@@ -65,6 +65,27 @@ __device__ __forceinline__ void fdivmod(uint32_t n, const FastDiv& f, uint32_t& 
     r = n - q * f.d;
 }
 
+// ------------------------------------------------------ lane groups -----
+
+// Sum over the LPT consecutive lanes that share a token row, with DPP lane
+// swaps (VALU, no LDS): pairs, then quads (quad permutations), then the two
+// quads of each 8-lane half (half-row mirror), then the two halves of a
+// 16-lane row (row mirror); across 16-lane rows a shuffle.  Every step reads
+// lanes of the same group only.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int LPT>
+__device__ __forceinline__ float group_sum(float x) {
+    if (LPT >= 2) x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    if (LPT >= 4) x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    if (LPT >= 8) x += dpp_f32<0x141>(x);  // row_half_mirror
+    if (LPT >= 16) x += dpp_f32<0x140>(x); // row_mirror
+    if (LPT >= 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
 // -------------------------------------------------------- conversions -----
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }

@@ -26,6 +26,7 @@ namespace bsa {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kBatch = 8;  // token rows loaded per lane before use
 
 struct SumParams {
     const char* q;
@@ -69,27 +70,9 @@ __device__ __forceinline__ uint4 pack(const float (&v)[EPV]) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Sum over the LPT consecutive lanes that share a token row, with DPP lane
-// swaps (VALU, no LDS): pairs, then quads (quad permutations), then the two
-// quads of each 8-lane half (half-row mirror), then the two halves of a
-// 16-lane row (row mirror); across 16-lane rows a shuffle.  Every step reads
-// lanes of the same group only.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-template <int LPT>
-__device__ __forceinline__ float group_sum(float x) {
-    if (LPT >= 2) x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-    if (LPT >= 4) x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
-    if (LPT >= 8) x += dpp_f32<0x141>(x);  // row_half_mirror
-    if (LPT >= 16) x += dpp_f32<0x140>(x); // row_mirror
-    if (LPT >= 32) x += __shfl_xor(x, 16);
-    return x;
-}
-
 // blockIdx: x = group of kWaves blocks, y = 0 (q) / 1 (k), z = b*H + h.
-template <int EPV, int LPT, bool TILED>
+// LABELS: P.labels is set (contiguous blocks only).
+template <int EPV, int LPT, bool TILED, bool LABELS>
 __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumParams P) {
     constexpr int TPI = 64 / LPT;
     const int lane = threadIdx.x & 63;
@@ -116,26 +99,47 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
         mx[i] = -__builtin_inff();
         mn[i] = __builtin_inff();
     }
-    const int32_t* lab = P.labels != nullptr ? P.labels + ((size_t)bh * P.nb + blk) * P.block : nullptr;
+    const int32_t* lab = LABELS ? P.labels + ((size_t)bh * P.nb + blk) * P.block : nullptr;
     // key blocks: also the largest squared row norm (a row's LPT lanes add
     // their squares; every pass of the loop keeps the same lanes together)
     const bool norms = which == 1 && P.knorm != nullptr;
     float n2max = 0.f;
-    for (uint32_t t = slot; t < P.block; t += TPI) {
-        if (lab != nullptr && lab[t] < 0) continue;
-        float v[EPV];
-        const uint32_t r = TILED ? cell_offset(t, *g, P.Hg, P.Wg) : t;
-        unpack<EPV>(*reinterpret_cast<const uint4*>(src + (size_t)r * row_bytes + (size_t)sub * 16), v);
+    // kBatch rows per lane are loaded before any is used, so that many loads
+    // are in flight per wave; a row past the block or labelled < 0 loads the
+    // block's first row and is then left out.
+    for (uint32_t t0 = slot; t0 < P.block; t0 += TPI * kBatch) {
+        uint4 raw[kBatch];
+        bool use[kBatch];
+        int32_t lv[kBatch];
 #pragma unroll
-        for (int i = 0; i < EPV; ++i) {
-            mx[i] = fmaxf(mx[i], v[i]);
-            mn[i] = fminf(mn[i], v[i]);
+        for (int j = 0; j < kBatch; ++j) {
+            const uint32_t t = t0 + j * TPI;
+            const uint32_t tc = t < P.block ? t : 0u;
+            if (LABELS) lv[j] = lab[tc];
+            const uint32_t r = TILED ? cell_offset(tc, *g, P.Hg, P.Wg) : tc;
+            raw[j] = *reinterpret_cast<const uint4*>(src + (size_t)r * row_bytes + (size_t)sub * 16);
         }
-        if (norms) {
-            float n2 = 0.f;
 #pragma unroll
-            for (int i = 0; i < EPV; ++i) n2 = fmaf(v[i], v[i], n2);
-            n2max = fmaxf(n2max, group_sum<LPT>(n2));
+        for (int j = 0; j < kBatch; ++j) use[j] = t0 + j * TPI < P.block && (!LABELS || lv[j] >= 0);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            float v[EPV];
+            unpack<EPV>(raw[j], v);
+            if (use[j]) {
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) {
+                    mx[i] = fmaxf(mx[i], v[i]);
+                    mn[i] = fminf(mn[i], v[i]);
+                }
+            }
+            if (norms) {
+                float n2 = 0.f;
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) n2 = fmaf(v[i], v[i], n2);
+                // every lane of the row group takes part in the lane swaps
+                const float row = group_sum<LPT>(n2);
+                if (use[j]) n2max = fmaxf(n2max, row);
+            }
         }
     }
     if (norms) {
@@ -385,9 +389,10 @@ int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
     P.labels = labels;
     P.knorm = key_norms;
     dim3 g1((unsigned)((nb + kWaves - 1) / kWaves), 2, (unsigned)(B * H));
-#define BSA_MM(EPV, LPT)                                                          \
-    (tiled ? block_minmax_kernel<EPV, LPT, true><<<g1, 64 * kWaves, 0, st>>>(P) \
-           : block_minmax_kernel<EPV, LPT, false><<<g1, 64 * kWaves, 0, st>>>(P))
+#define BSA_MM(EPV, LPT)                                                                    \
+    (tiled ? block_minmax_kernel<EPV, LPT, true, false><<<g1, 64 * kWaves, 0, st>>>(P)     \
+     : labels ? block_minmax_kernel<EPV, LPT, false, true><<<g1, 64 * kWaves, 0, st>>>(P) \
+              : block_minmax_kernel<EPV, LPT, false, false><<<g1, 64 * kWaves, 0, st>>>(P))
     const bool bf = dtype == BSA_BF16;
     switch (vecs) {
         case 1: if (bf) BSA_MM(8, 1); else BSA_MM(4, 1); break;
