@@ -68,12 +68,13 @@ _SIGS = {
     "bsa_label_block_list": (_I, [_P, _I64, _I, _P, _P, _I]),
     "bsa_tile_permute_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _I64, _P, _P]),
     "bsa_invert_permute_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _I64, _P]),
-    "bsa_select_tiling_ex": (_I, [_P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "bsa_select_tiling_ex": (_I, [_P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "bsa_minmax_block_scores_masked": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P]),
     "bsa_topk_block_mask_tiled": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _P]),
     "bsa_block_sparse_attention_labels": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _P,
                                                _I64, _F, _P]),
-    "bsa_minmax_block_scores_tiled": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P, _P]),
+    "bsa_minmax_block_scores_tiled": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P, _P,
+                                           _P]),
     "bsa_block_sparse_attention_tiled": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
                                               _I, _F, _P, _P]),
 }
@@ -320,12 +321,15 @@ def bsa_block_cohesion(x, block: int):
     return coh
 
 
-def bsa_select_tiling(q, grid, tiles, workspace=None, statistic: str = "mean", pad: bool = False):
+def bsa_select_tiling(q, grid, tiles, workspace=None, statistic: str = "mean", pad: bool = False,
+                      q_summaries=None):
     """Per-head tiling choice -> (choice int32 (B, H), score float32 (B, H, n), tile_coh).
 
     statistic "mean" (per-tile cohesion averaged) or "pooled" (SPADE's engine
     rule); pad=True scores candidates that do not divide the grid on the
-    zero-padded grid."""
+    zero-padded grid.  q_summaries: None, or a (n, 2, B, H, S // volume, D)
+    tensor of q's dtype that receives every candidate's block max and min of
+    q (candidates of one volume, pad=False), for bsa_minmax_block_scores_tiled."""
     torch = _torch()
     B, H, S, D = _bhsd(q, "q")
     T, Hg, Wg = (int(g) for g in grid)
@@ -347,9 +351,20 @@ def bsa_select_tiling(q, grid, tiles, workspace=None, statistic: str = "mean", p
         if tile_coh.numel() < B * H * n * max_nb:
             raise ValueError("tile_coh workspace too small")
     stat = BSA_STAT_POOLED if statistic == "pooled" else BSA_STAT_MEAN
+    qs = None if q_summaries is None else _q_summaries_arg(q_summaries, q, tiles, S, "q_summaries")
     _check(lib().bsa_select_tiling_ex(_dev(q, "q"), _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, stat, int(bool(pad)),
-                                      _dev(tile_coh), _dev(score), _dev(choice), _stream(q)))
+                                      _dev(tile_coh), _dev(score), _dev(choice), qs, _stream(q)))
     return choice, score, tile_coh
+
+
+def _q_summaries_arg(t, q, tiles, S, what):
+    """Device pointer of a (n, 2, B, H, S // volume, D) q-summary tensor of q's dtype and device."""
+    B, H, _, D = (int(x) for x in q.shape)
+    vol = int(tiles[0][0]) * int(tiles[0][1]) * int(tiles[0][2])
+    want = (len(tiles), 2, B, H, S // max(vol, 1), D)
+    if tuple(t.shape) != want or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous {q.dtype} tensor of shape {want} on {q.device}")
+    return _dev(t, what)
 
 
 def _norms_out(key_norms, B, H, nb, like):
@@ -395,9 +410,10 @@ def bsa_minmax_block_scores(q, k, block: int, out=None, labels=None, key_norms=N
     return scores, summ
 
 
-def bsa_minmax_block_scores_tiled(q, k, grid, tiles, head_choice=None, out=None, key_norms=None):
+def bsa_minmax_block_scores_tiled(q, k, grid, tiles, head_choice=None, out=None, key_norms=None, q_summaries=None):
     """Min/max block scores of T-major q, k, block J = tile J of each head's tiling (key_norms as in
-    bsa_minmax_block_scores)."""
+    bsa_minmax_block_scores).  q_summaries: None, or what bsa_select_tiling(..., q_summaries=) wrote for
+    the same q and tiles; q is then not read again."""
     torch = _torch()
     B, H, S, D = _bhsd(q, "q")
     if _bhsd(k, "k") != (B, H, S, D) or k.dtype != q.dtype:
@@ -415,8 +431,9 @@ def bsa_minmax_block_scores_tiled(q, k, grid, tiles, head_choice=None, out=None,
         scores, summ = out
     hc = None if head_choice is None else _dev(head_choice, "head_choice")
     kn = _norms_out(key_norms, B, H, nb, q)
+    qs = None if q_summaries is None else _q_summaries_arg(q_summaries, q, tiles, S, "q_summaries")
     _check(lib().bsa_minmax_block_scores_tiled(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, T, Hg, Wg, D, arr,
-                                               n, hc, _dev(summ), _dev(scores), kn, _stream(q)))
+                                               n, hc, _dev(summ), _dev(scores), kn, qs, _stream(q)))
     return scores, summ
 
 
@@ -693,6 +710,9 @@ class AdaptiveBlockSparse:
         # each key block's largest row norm, written by the scores pass: the attention kernel skips the
         # running-max update of the key blocks it proves cannot pass it
         self.ws_knorm = None if self.pad else torch.empty((B, H, self.nb), dtype=torch.float32, **f)
+        # fused path: the tiling choice pass also forms q's block summaries of every candidate, so the scores
+        # pass reads only k
+        self.ws_qsumm = (torch.empty((n, 2, B, H, self.nb, D), dtype=dtype, **f) if self.fused else None)
 
     @property
     def choice(self):
@@ -704,7 +724,7 @@ class AdaptiveBlockSparse:
 
     def __call__(self, q, k, v, out=None, attention_hook=None):
         choice, _, _ = bsa_select_tiling(q, self.grid, self.tiles, workspace=self.ws_select, statistic=self.statistic,
-                                         pad=self.pad)
+                                         pad=self.pad, q_summaries=self.ws_qsumm)
         if self.pad:
             for src, dst, lab in ((q, self.qp, self.labels), (k, self.kp, None), (v, self.vp, None)):
                 bsa_tile_permute_padded(src, self.grid, self.tiles, head_choice=choice, Sp=self.Sp, out=(dst, lab))
@@ -714,7 +734,8 @@ class AdaptiveBlockSparse:
         else:
             if self.fused:
                 scores, _ = bsa_minmax_block_scores_tiled(q, k, self.grid, self.tiles, head_choice=choice,
-                                                          out=self.ws_scores, key_norms=self.ws_knorm)
+                                                          out=self.ws_scores, key_norms=self.ws_knorm,
+                                                          q_summaries=self.ws_qsumm)
             else:
                 for src, dst in ((q, self.qp), (k, self.kp), (v, self.vp)):
                     bsa_tile_permute(src, self.grid, self.tiles, head_choice=choice, out=dst)

@@ -43,25 +43,24 @@ struct CohParams {
     uint32_t nb[BSA_MAX_TILINGS];
     TileGeo geo[BSA_MAX_TILINGS];
     float* tile_coh;  // [B*H][n_tiles][max_nb]
+    // optional: each tile's elementwise max and min of q, in q's dtype,
+    // [n_tiles][2][B*H][max_nb][D] (candidates of one volume, no padding)
+    char* qsumm;
+    uint32_t BH;
 };
 
-template <int EPV>
-__device__ __forceinline__ void unpack(const uint4 raw, float (&v)[EPV]) {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    if (EPV == 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) v[i] = __uint_as_float(w[i]);
-    }
+// 1 / sqrt(x) for x > 0 with the hardware's reciprocal square root (about
+// 1 ulp); inputs below 2^-100 are scaled by 2^100 first, since the
+// instruction does not take denormal inputs.
+__device__ __forceinline__ float rsq(float x) {
+    const bool tiny = x < 0x1p-100f;
+    return __builtin_amdgcn_rsqf(tiny ? x * 0x1p100f : x) * (tiny ? 0x1p50f : 1.0f);
 }
 
 // LPT lanes cooperate on one token (16 bytes each); 64/LPT tokens per step.
-template <int EPV, int LPT, bool PAD>
+// SUMM: also the tile's elementwise max and min of q (the block summaries of
+// the tiling, read by the scores pass instead of q itself).
+template <int EPV, int LPT, bool PAD, bool SUMM>
 __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohParams P) {
     constexpr int TPI = 64 / LPT;
     const int lane = threadIdx.x & 63;
@@ -89,14 +88,18 @@ __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohPar
 #pragma unroll
     for (int i = 0; i < EPV; ++i) u[i] = 0.f;
     float n = 0.f;
+    RowRange<EPV> range;
+    range.init();
     // kBatch tokens per lane are loaded before any is used, so that many
     // loads are in flight per wave; a cell outside the tile or the grid loads
     // the head's first row and is then taken as a zero token.
-    for (uint32_t base = 0; base < g.vol; base += TPI * kBatch) {
-        uint4 raw[kBatch];
-        bool real[kBatch];
+    // (with the summaries, fewer rows in flight keep the register count down)
+    constexpr int NB = SUMM ? kBatch / 2 : kBatch;
+    for (uint32_t base = 0; base < g.vol; base += TPI * NB) {
+        uint4 raw[NB];
+        bool real[NB];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
+        for (int j = 0; j < NB; ++j) {
             const uint32_t cell = base + j * TPI + slot;
             real[j] = cell < g.vol;
             uint32_t s = 0;
@@ -107,20 +110,23 @@ __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohPar
                 real[j] = real[j] && t0 + rt < P.T && y0 + ry < P.Hg && x0 + rx < P.Wg;
                 s = real[j] ? ((t0 + rt) * P.Hg + y0 + ry) * P.Wg + x0 + rx : 0u;
             } else {
-                s = real[j] ? origin + cell_offset(cell, g, P.Hg, P.Wg) : 0u;
+                // (a cell past the tile reads the tile's first token: a member of the tile, so the
+                // summaries may take it in again)
+                s = origin + cell_offset(real[j] ? cell : 0u, g, P.Hg, P.Wg);
             }
             raw[j] = *reinterpret_cast<const uint4*>(head + (size_t)s * row_bytes + (size_t)sub * 16);
         }
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
+        for (int j = 0; j < NB; ++j) {
             float v[EPV];
             unpack<EPV>(raw[j], v);
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < EPV; ++i) ss = fmaf(v[i], v[i], ss);
             ss = group_sum<LPT>(ss);
+            if (SUMM) range.add(raw[j]);
             if (real[j] && ss > 0.f) {
-                const float inv = 1.0f / sqrtf(ss);
+                const float inv = rsq(ss);
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) u[i] = fmaf(v[i], inv, u[i]);
                 n += 1.f;
@@ -133,6 +139,17 @@ __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohPar
 #pragma unroll
         for (int i = 0; i < EPV; ++i) u[i] += __shfl_xor(u[i], off);
         n += __shfl_xor(n, off);
+    }
+    if (SUMM) {
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) range.merge_lanes(off);
+        if (slot == 0) {
+            const size_t plane = (size_t)P.BH * P.max_nb * row_bytes;
+            char* dst = P.qsumm + (size_t)(2 * cand) * plane + ((size_t)bh * P.max_nb + tile) * row_bytes +
+                        (size_t)sub * 16;
+            *reinterpret_cast<uint4*>(dst) = range.max_row();
+            *reinterpret_cast<uint4*>(dst + plane) = range.min_row();
+        }
     }
     float uu = 0.f;
 #pragma unroll
@@ -206,9 +223,10 @@ __global__ __launch_bounds__(64) void select_kernel(const SelParams P) {
 int launch_tile_cohesion(const CohParams& P, uint32_t BH, hipStream_t stream, const char* name) {
     dim3 grid((P.max_nb + kWaves - 1) / kWaves, P.n_tiles, BH);
     const int lpt = (int)P.vecs_per_row;
-#define BSA_COH(EPV, LPT)                                                                \
-    (P.pad ? tile_cohesion_kernel<EPV, LPT, true><<<grid, 64 * kWaves, 0, stream>>>(P) \
-           : tile_cohesion_kernel<EPV, LPT, false><<<grid, 64 * kWaves, 0, stream>>>(P))
+#define BSA_COH(EPV, LPT)                                                                            \
+    (P.pad ? tile_cohesion_kernel<EPV, LPT, true, false><<<grid, 64 * kWaves, 0, stream>>>(P)      \
+     : P.qsumm ? tile_cohesion_kernel<EPV, LPT, false, true><<<grid, 64 * kWaves, 0, stream>>>(P) \
+               : tile_cohesion_kernel<EPV, LPT, false, false><<<grid, 64 * kWaves, 0, stream>>>(P))
     if (P.dtype == BSA_BF16) {
         switch (lpt) {
             case 1: BSA_COH(8, 1); break;
@@ -266,7 +284,7 @@ extern "C" int bsa_block_cohesion(const void* x, int dtype, int64_t B, int64_t H
                                   float* coh, bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_block_cohesion";
-    CohParams P;
+    CohParams P{};
     int rc = fill_common(P, x, dtype, B, H, S, D, name);
     if (rc) return rc;
     BSA_REQUIRE(coh != nullptr, "%s: NULL output", name);
@@ -289,7 +307,8 @@ extern "C" int bsa_block_cohesion(const void* x, int dtype, int64_t B, int64_t H
 
 extern "C" int bsa_select_tiling_ex(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
                                     int64_t D, const int32_t* tiles_host, int n_tiles, int statistic, int pad,
-                                    float* tile_coh, float* score, int32_t* choice, bsa_stream_t stream) {
+                                    float* tile_coh, float* score, int32_t* choice, void* q_summaries_or_null,
+                                    bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_select_tiling";
     BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
@@ -297,7 +316,7 @@ extern "C" int bsa_select_tiling_ex(const void* q, int dtype, int64_t B, int64_t
                 statistic);
     BSA_REQUIRE(pad == 0 || pad == 1, "%s: pad must be 0 or 1", name);
     const int64_t S = (int64_t)T * Hg * Wg;
-    CohParams P;
+    CohParams P{};
     int rc = fill_common(P, q, dtype, B, H, S, D, name);
     if (rc) return rc;
     rc = pad ? check_tiles_padded(T, Hg, Wg, tiles_host, n_tiles) : check_tiles(T, Hg, Wg, tiles_host, n_tiles);
@@ -318,6 +337,14 @@ extern "C" int bsa_select_tiling_ex(const void* q, int dtype, int64_t B, int64_t
         if (i < n_tiles && P.nb[i] > P.max_nb) P.max_nb = P.nb[i];
     }
     P.tile_coh = tile_coh;
+    P.qsumm = static_cast<char*>(q_summaries_or_null);
+    P.BH = (uint32_t)(B * H);
+    if (P.qsumm != nullptr) {
+        BSA_REQUIRE(!pad, "%s: q summaries need candidates that divide the grid (pad = 0)", name);
+        BSA_REQUIRE(aligned16(P.qsumm), "%s: q summaries must be 16-byte aligned", name);
+        for (int i = 1; i < n_tiles; ++i)
+            BSA_REQUIRE(P.nb[i] == P.nb[0], "%s: q summaries need candidates of one volume", name);
+    }
     hipStream_t st = (hipStream_t)stream;
     rc = launch_tile_cohesion(P, (uint32_t)(B * H), st, name);
     if (rc) return rc;
@@ -343,5 +370,5 @@ extern "C" int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H,
                                  const int32_t* tiles_host, int n_tiles, float* tile_coh, float* score,
                                  int32_t* choice, bsa_stream_t stream) {
     return bsa_select_tiling_ex(q, dtype, B, H, T, Hg, Wg, D, tiles_host, n_tiles, BSA_STAT_MEAN, 0, tile_coh, score,
-                                choice, stream);
+                                choice, nullptr, stream);
 }

@@ -86,6 +86,103 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// A 16-byte slice of a token row as EPV floats (8 bf16 or 4 fp32 values),
+// and back; bf16 values widened to fp32 pack back exactly.
+template <int EPV>
+__device__ __forceinline__ void unpack(const uint4 raw, float (&v)[EPV]) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    if (EPV == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) v[i] = __uint_as_float(w[i]);
+    }
+}
+
+template <int EPV>
+__device__ __forceinline__ uint4 pack(const float (&v)[EPV]) {
+    uint32_t w[4];
+    if (EPV == 8) {
+        // exact: every value is an input bf16 value widened to fp32
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xffff0000u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Running elementwise max and min of 16-byte row slices (block summaries).
+// bf16 (EPV 8) works on the bits: a pair of bf16 read as two int16 and
+// mapped by key(x) = x ^ ((x >> 15) & 0x7fff), which flips the magnitude
+// bits of negative values, orders like the values (-0 just below +0) and is
+// its own inverse; a pair then costs two packed int16 operations for the key
+// and one each for max and min (as floats, each value also needs a
+// canonicalisation before a max or min).  fp32 (EPV 4) keeps float max/min.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_key(uint32_t w) {
+    const s16x2 x = __builtin_bit_cast(s16x2, w);
+    const s16x2 s = x >> (s16x2){15, 15};
+    return __builtin_bit_cast(uint32_t, x ^ (s & (s16x2){0x7fff, 0x7fff}));
+}
+
+template <int EPV>
+struct RowRange {
+    uint32_t hi[4], lo[4];  // EPV 8: keys of bf16 pairs; EPV 4: fp32 bits
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // -inf and +inf: what a row range with nothing added reports
+            hi[i] = EPV == 8 ? bf16x2_key(0xff80ff80u) : 0xff800000u;
+            lo[i] = EPV == 8 ? bf16x2_key(0x7f807f80u) : 0x7f800000u;
+        }
+    }
+    __device__ __forceinline__ void merge(const uint32_t (&h)[4], const uint32_t (&l)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (EPV == 8) {
+                hi[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, hi[i]),
+                                                                              __builtin_bit_cast(s16x2, h[i])));
+                lo[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(s16x2, lo[i]),
+                                                                              __builtin_bit_cast(s16x2, l[i])));
+            } else {
+                hi[i] = __float_as_uint(fmaxf(__uint_as_float(hi[i]), __uint_as_float(h[i])));
+                lo[i] = __float_as_uint(fminf(__uint_as_float(lo[i]), __uint_as_float(l[i])));
+            }
+        }
+    }
+    __device__ __forceinline__ void add(const uint4 raw) {
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t k[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k[i] = EPV == 8 ? bf16x2_key(w[i]) : w[i];
+        merge(k, k);
+    }
+    // with the lanes `off` apart (shuffles)
+    __device__ __forceinline__ void merge_lanes(int off) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            h[i] = __shfl_xor(hi[i], off);
+            l[i] = __shfl_xor(lo[i], off);
+        }
+        merge(h, l);
+    }
+    __device__ __forceinline__ uint4 max_row() const { return row(hi); }
+    __device__ __forceinline__ uint4 min_row() const { return row(lo); }
+
+  private:
+    __device__ __forceinline__ static uint4 row(const uint32_t (&v)[4]) {
+        if (EPV == 8) return make_uint4(bf16x2_key(v[0]), bf16x2_key(v[1]), bf16x2_key(v[2]), bf16x2_key(v[3]));
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    }
+};
+
 // -------------------------------------------------------- conversions -----
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }

@@ -7,7 +7,9 @@
 //
 // bsa_minmax_block_scores_tiled reads q and k in T-major order, block J of a
 // head being tile J of the head's chosen tiling (the permuted copies are
-// never formed).
+// never formed).  Given q's summaries of every candidate (the tiling choice
+// pass forms them while it reads q), it copies the chosen ones and reads
+// only k.
 //
 // bsa_minmax_block_scores_masked leaves out tokens labelled < 0 (the padding
 // of a padded tiling, [Adaptive tiling (SPADE), "Deviations and notes"]):
@@ -39,36 +41,11 @@ struct SumParams {
     const int32_t* head_choice;
     uint32_t n_tiles, Hg, Wg;
     TileGeo geo[BSA_MAX_TILINGS];
+    // tiled, optional: q's summaries of every candidate, [n_tiles][2][BH][Nb][D]
+    // (bsa_select_tiling_ex writes them); the q half then copies the chosen
+    // candidate's instead of reading q
+    const char* qsumm;
 };
-
-template <int EPV>
-__device__ __forceinline__ void unpack(const uint4 raw, float (&v)[EPV]) {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    if (EPV == 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) v[i] = __uint_as_float(w[i]);
-    }
-}
-
-template <int EPV>
-__device__ __forceinline__ uint4 pack(const float (&v)[EPV]) {
-    uint32_t w[4];
-    if (EPV == 8) {
-        // exact: every value is an input bf16 value widened to fp32
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xffff0000u);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 // blockIdx: x = group of kWaves blocks, y = 0 (q) / 1 (k), z = b*H + h.
 // LABELS: P.labels is set (contiguous blocks only).
@@ -82,31 +59,38 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
     const uint32_t bh = blockIdx.z;
     const size_t row_bytes = (size_t)P.vecs_per_row * 16;
     uint32_t origin = 0;
-    const TileGeo* g = nullptr;
+    TileGeo g{};  // a copy: indexing the by-value parameter through a pointer puts it in scratch memory
     if (TILED) {
         uint32_t c = P.head_choice != nullptr ? (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[bh]) : 0u;
         if (c >= P.n_tiles) c = 0;  // out-of-range choices are caught by bsa_validate_indices
-        g = &P.geo[c];
-        origin = tile_origin(blk, *g, P.Hg, P.Wg);
+        if (which == 0 && P.qsumm != nullptr) {
+            if (lane < LPT) {
+                const size_t plane = (size_t)P.BH * P.nb * row_bytes;
+                const size_t at = ((size_t)bh * P.nb + blk) * row_bytes + (size_t)lane * 16;
+                const char* from = P.qsumm + (size_t)(2 * c) * plane + at;
+                *reinterpret_cast<uint4*>(P.summ + at) = *reinterpret_cast<const uint4*>(from);
+                *reinterpret_cast<uint4*>(P.summ + plane + at) = *reinterpret_cast<const uint4*>(from + plane);
+            }
+            return;
+        }
+        g = P.geo[c];
+        origin = tile_origin(blk, g, P.Hg, P.Wg);
     }
     const char* src = TILED ? (which == 0 ? P.q : P.k) + ((size_t)bh * P.nb * P.block + origin) * row_bytes
                             : (which == 0 ? P.q : P.k) + ((size_t)bh * P.nb + blk) * P.block * row_bytes;
     const int sub = lane % LPT;
     const int slot = lane / LPT;
-    float mx[EPV], mn[EPV];
-#pragma unroll
-    for (int i = 0; i < EPV; ++i) {
-        mx[i] = -__builtin_inff();
-        mn[i] = __builtin_inff();
-    }
+    RowRange<EPV> range;
+    range.init();
     const int32_t* lab = LABELS ? P.labels + ((size_t)bh * P.nb + blk) * P.block : nullptr;
     // key blocks: also the largest squared row norm (a row's LPT lanes add
     // their squares; every pass of the loop keeps the same lanes together)
     const bool norms = which == 1 && P.knorm != nullptr;
     float n2max = 0.f;
     // kBatch rows per lane are loaded before any is used, so that many loads
-    // are in flight per wave; a row past the block or labelled < 0 loads the
-    // block's first row and is then left out.
+    // are in flight per wave; a row past the block loads the block's first
+    // row (which the summaries may take in again, but the norms leave out),
+    // and a row labelled < 0 is left out.
     for (uint32_t t0 = slot; t0 < P.block; t0 += TPI * kBatch) {
         uint4 raw[kBatch];
         bool use[kBatch];
@@ -116,23 +100,17 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
             const uint32_t t = t0 + j * TPI;
             const uint32_t tc = t < P.block ? t : 0u;
             if (LABELS) lv[j] = lab[tc];
-            const uint32_t r = TILED ? cell_offset(tc, *g, P.Hg, P.Wg) : tc;
+            const uint32_t r = TILED ? cell_offset(tc, g, P.Hg, P.Wg) : tc;
             raw[j] = *reinterpret_cast<const uint4*>(src + (size_t)r * row_bytes + (size_t)sub * 16);
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) use[j] = t0 + j * TPI < P.block && (!LABELS || lv[j] >= 0);
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            float v[EPV];
-            unpack<EPV>(raw[j], v);
-            if (use[j]) {
-#pragma unroll
-                for (int i = 0; i < EPV; ++i) {
-                    mx[i] = fmaxf(mx[i], v[i]);
-                    mn[i] = fminf(mn[i], v[i]);
-                }
-            }
+            if (!LABELS || use[j]) range.add(raw[j]);
             if (norms) {
+                float v[EPV];
+                unpack<EPV>(raw[j], v);
                 float n2 = 0.f;
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) n2 = fmaf(v[i], v[i], n2);
@@ -148,18 +126,12 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
         if (lane == 0) P.knorm[(size_t)bh * P.nb + blk] = sqrtf(n2max);
     }
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) {
-            mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], off));
-            mn[i] = fminf(mn[i], __shfl_xor(mn[i], off));
-        }
-    }
+    for (int off = LPT; off < 64; off <<= 1) range.merge_lanes(off);
     if (slot == 0) {
         const size_t plane = (size_t)P.BH * P.nb * row_bytes;
         char* dst = P.summ + (size_t)(2 * which) * plane + ((size_t)bh * P.nb + blk) * row_bytes + (size_t)sub * 16;
-        *reinterpret_cast<uint4*>(dst) = pack<EPV>(mx);
-        *reinterpret_cast<uint4*>(dst + plane) = pack<EPV>(mn);
+        *reinterpret_cast<uint4*>(dst) = range.max_row();
+        *reinterpret_cast<uint4*>(dst + plane) = range.min_row();
     }
 }
 
@@ -445,7 +417,8 @@ extern "C" int bsa_minmax_block_scores_masked(const void* q, const void* k, int 
 extern "C" int bsa_minmax_block_scores_tiled(const void* q, const void* k, int dtype, int64_t B, int64_t H, int T,
                                              int Hg, int Wg, int64_t D, const int32_t* tiles_host, int n_tiles,
                                              const int32_t* head_choice, void* summaries, float* scores,
-                                             float* key_norms_or_null, bsa_stream_t stream) {
+                                             float* key_norms_or_null, const void* q_summaries_or_null,
+                                             bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_minmax_block_scores_tiled";
     BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
@@ -463,6 +436,8 @@ extern "C" int bsa_minmax_block_scores_tiled(const void* q, const void* k, int d
     P.n_tiles = (uint32_t)n_tiles;
     P.Hg = (uint32_t)Hg;
     P.Wg = (uint32_t)Wg;
+    P.qsumm = static_cast<const char*>(q_summaries_or_null);
+    BSA_REQUIRE(aligned16(P.qsumm), "%s: q summaries must be 16-byte aligned", name);
     return minmax_scores(q, k, dtype, B, H, (int64_t)T * Hg * Wg, D, vol, nullptr, P, true, summaries, scores,
                          key_norms_or_null, (hipStream_t)stream, name);
 }

@@ -206,11 +206,19 @@ int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H, int T, int
  * counted by the pooled rule; pad = 0 rejects them like bsa_select_tiling.
  * tile_coh: device float[B*H*n_tiles*maxNb], maxNb = max over candidates of
  * bsa_padded_length/(a*b*c) (per-tile values: the cohesion, or for the
- * pooled rule its numerator).  INVALID_ARG on an unknown statistic, pad not
- * in {0, 1}, or a bad candidate. */
+ * pooled rule its numerator).
+ * q_summaries_or_null: device, 2*n_tiles*B*H*Nb*D elements of `dtype`, or
+ * NULL.  When given, the same pass over q also writes every candidate's block
+ * summaries of q [Adaptive tiling (SPADE), "The idea" step 3: elementwise max
+ * and min of each block], in the order (candidate, max/min, B, H, Nb, D), so
+ * that bsa_minmax_block_scores_tiled need not read q again.  It needs pad = 0
+ * and candidates of one volume (Nb = S / volume).
+ * INVALID_ARG on an unknown statistic, pad not in {0, 1}, a bad candidate,
+ * or q summaries with pad = 1 or candidates of different volumes. */
 int bsa_select_tiling_ex(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
                          int64_t D, const int32_t* tiles_host, int n_tiles, int statistic, int pad,
-                         float* tile_coh, float* score, int32_t* choice, bsa_stream_t stream);
+                         float* tile_coh, float* score, int32_t* choice, void* q_summaries_or_null,
+                         bsa_stream_t stream);
 
 /* Min/max block summaries and estimated block scores of tile-contiguous q, k:
  *   qmax_I = elementwise max over block I of q, qmin_I the min (and kmax, kmin),
@@ -234,11 +242,15 @@ int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, 
  * the tile geometry, so the permuted copies of q and k are never formed
  * (the summaries fused with the permutation [Adaptive tiling (SPADE),
  * "The idea" steps 2 and 3]).  Candidates must divide the grid and share one
- * volume, the block size.  Outputs as bsa_minmax_block_scores. */
+ * volume, the block size.  Outputs as bsa_minmax_block_scores.
+ * q_summaries_or_null: NULL, or the q summaries bsa_select_tiling_ex wrote
+ * for the same q and candidates; the chosen candidate's are then copied into
+ * `summaries` and q itself is not read (trusted to match q). */
 int bsa_minmax_block_scores_tiled(const void* q, const void* k, int dtype, int64_t B, int64_t H,
                                   int T, int Hg, int Wg, int64_t D, const int32_t* tiles_host,
                                   int n_tiles, const int32_t* head_choice, void* summaries,
-                                  float* scores, float* key_norms_or_null, bsa_stream_t stream);
+                                  float* scores, float* key_norms_or_null,
+                                  const void* q_summaries_or_null, bsa_stream_t stream);
 
 /* bsa_minmax_block_scores over labelled tokens only: tokens with
  * labels[b,h,s] < 0 (padding) are left out of the summaries, so a partial

@@ -136,6 +136,7 @@ def test_label_block_lists_bit_exact(L, grid, block, kind):
 FAKE = ctypes.c_void_p(4096)  # never dereferenced: every case below fails validation first
 TILES = (ctypes.c_int32 * 6)(1, 8, 8, 4, 4, 4)
 BAD_TILES = (ctypes.c_int32 * 3)(16, 2, 2)
+MIXED_TILES = (ctypes.c_int32 * 6)(1, 8, 8, 2, 4, 4)
 K_TAB = (ctypes.c_int32 * 2)(81, 130)
 NK_TAB = (ctypes.c_int32 * 2)(480, 768)
 NK_BAD = (ctypes.c_int32 * 2)(480, 769)
@@ -188,11 +189,17 @@ def test_device_calls_reject_bad_arguments(L):
         ("bsa_windowed_attention", (None, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, 2, ctypes.c_float(0.25), 8, None),
          "NULL"),
         ("bsa_validate_block_list", (FAKE, FAKE, 1, 1, 0, 4, 4, None), ">= 1"),
-        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, TILES, 2, 7, 0, FAKE, FAKE, FAKE, None),
+        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, TILES, 2, 7, 0, FAKE, FAKE, FAKE, None, None),
          "statistic"),
-        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, 0, 0, FAKE, FAKE, FAKE, None),
+        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, 0, 0, FAKE, FAKE, FAKE, None,
+                                  None),
          "divide"),
-        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, TILES, 2, 0, 2, FAKE, FAKE, FAKE, None), "pad"),
+        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, TILES, 2, 0, 2, FAKE, FAKE, FAKE, None, None),
+         "pad"),
+        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, TILES, 2, 0, 1, FAKE, FAKE, FAKE, FAKE, None),
+         "pad = 0"),
+        ("bsa_select_tiling_ex", (FAKE, BF, 1, 40, 20, 32, 48, 128, MIXED_TILES, 2, 0, 0, FAKE, FAKE, FAKE, FAKE,
+                                  None), "one volume"),
         ("bsa_tile_permute_padded", (FAKE, ctypes.c_void_p(1 << 30), BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, None,
                                      30720, None, None), "shorter"),
         ("bsa_tile_permute_padded", (FAKE, ctypes.c_void_p(1 << 30), BF, 1, 40, 20, 32, 48, 128, BAD_TILES, 1, None,

@@ -51,6 +51,43 @@ def test_select_tiling_wan_shape_against_oracle():
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("dtype,D,grid,tiles", [("bf16", 128, (4, 16, 16), [(1, 8, 8), (4, 4, 4)]),
+                                                ("f32", 16, (4, 8, 8), [(1, 4, 8), (2, 4, 4), (4, 2, 4)])])
+def test_select_tiling_q_summaries(dtype, D, grid, tiles):
+    """The tiling choice pass's q summaries equal the oracle's block max / min of the permuted q for every
+    candidate (exact), leave the choice unchanged, and give the tiled scores pass the same result as reading
+    q itself."""
+    torch = torch_gpu()
+    H = 3
+    S = grid[0] * grid[1] * grid[2]
+    vol = tiles[0][0] * tiles[0][1] * tiles[0][2]
+    nb, n = S // vol, len(tiles)
+    q, k = (synth.normal_bits((1, H, S, D), seed=1500 + i + D, dtype=dtype) for i in range(2))
+    q[0, 1, 5:40] = 0                                  # zero tokens count in the summaries
+    qg, kg = gpu(q), gpu(k)
+    qs = torch.full((n, 2, 1, H, nb, D), float("nan"), dtype=qg.dtype, device="cuda")
+    choice, score, coh = bsa.bsa_select_tiling(qg, grid, tiles, q_summaries=qs)
+    choice0, score0, _ = bsa.bsa_select_tiling(qg, grid, tiles)
+    assert torch.equal(choice, choice0) and torch.equal(score, score0)
+    got = f64(qs)
+    qf = synth.stored_to_f64(q)
+    for c, t in enumerate(tiles):
+        perm = OT.tile_permutation(grid, t)
+        for h in range(H):
+            mx, mn = OB.block_minmax(OT.permute_tokens(qf[0, h], perm), vol)
+            assert np.array_equal(got[c, 0, 0, h], mx), (c, h)
+            assert np.array_equal(got[c, 1, 0, h], mn), (c, h)
+    kn = torch.empty((1, H, nb), dtype=torch.float32, device="cuda")
+    kn0 = torch.empty_like(kn)
+    sc, summ = bsa.bsa_minmax_block_scores_tiled(qg, kg, grid, tiles, head_choice=choice, key_norms=kn,
+                                                 q_summaries=qs)
+    sc0, summ0 = bsa.bsa_minmax_block_scores_tiled(qg, kg, grid, tiles, head_choice=choice, key_norms=kn0)
+    assert torch.equal(sc, sc0) and torch.equal(summ, summ0) and torch.equal(kn, kn0)
+    with pytest.raises(ValueError, match="q_summaries"):
+        bsa.bsa_select_tiling(qg, grid, tiles, q_summaries=qs[:, :, :, :, :-1])
+
+
+@pytest.mark.gpu
 def test_select_tiling_ties_and_constructed_choice():
     torch = torch_gpu()
     grid = (2, 4, 4)
