@@ -315,10 +315,10 @@ def main():
     for _ in range(12):
         marks.clear()
         mark("start")
-        choice, _, _ = bsa.bsa_select_tiling(qg, wl.grid, TILES, workspace=pipe.ws_select)
+        choice, _, _ = bsa.bsa_select_tiling(qg, wl.grid, TILES, workspace=pipe.ws_select, q_summaries=pipe.ws_qsumm)
         mark("select_tiling")
         scores, _ = bsa.bsa_minmax_block_scores_tiled(qg, kg, wl.grid, TILES, head_choice=choice, out=pipe.ws_scores,
-                                                      key_norms=pipe.ws_knorm)
+                                                      key_norms=pipe.ws_knorm, q_summaries=pipe.ws_qsumm)
         mark("minmax_block_scores (gather on load)")
         kv_idx, kv_cnt2 = bsa.bsa_topk_block_mask(scores, pipe.k, 1, True, max_kept=pipe.max_kept,
                                                   out=pipe.ws_topk)[:2]
