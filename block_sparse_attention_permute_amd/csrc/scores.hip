@@ -296,8 +296,8 @@ __global__ __launch_bounds__(64) void block_scores_mfma_kernel(const uint16_t* _
     auto ld = [&](const uint16_t* base, uint32_t row, uint32_t d) {
         return *reinterpret_cast<const uint4*>(base + head + (size_t)row * D + d);
     };
+    uint4 a[ND > 0 ? ND : 1], b[ND > 0 ? ND : 1], x[ND > 0 ? ND : 1], n[ND > 0 ? ND : 1];
     if (ND > 0) {
-        uint4 a[ND > 0 ? ND : 1], b[ND > 0 ? ND : 1], x[ND > 0 ? ND : 1], n[ND > 0 ? ND : 1];
 #pragma unroll
         for (int s = 0; s < ND; ++s) {
             const uint32_t d = 16 * s + 8 * kg;
@@ -314,16 +314,32 @@ __global__ __launch_bounds__(64) void block_scores_mfma_kernel(const uint16_t* _
             score_step(ld(qmax, I, d), ld(qmin, I, d), ld(kmax, J, d), ld(kmin, J, d), sx, sn);
         }
     }
-    // value v of lane l: row I0 + 8(v/4) + 4(l/32) + v%4, column J0 + l%32
+    // value v of lane l: row I0 + 8(v/4) + 4(l/32) + v%4, column J0 + l%32.
+    // A block with no token (max -inf) scores -inf: with the operands in
+    // registers (ND > 0), lane r < 32 holds element 0 of rows I0 + r and
+    // J0 + r, and the other lanes take theirs by shuffles instead of loads.
     const uint32_t Jc = J0 + r;
+    bool ok_i[16], ok_j;
+    if (ND > 0) {
+        const int qf0 = (int)(a[0].x & 0xffffu), kf0 = (int)(x[0].x & 0xffffu);
+        ok_j = __shfl(kf0, r) != 0xff80;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ok_i[v] = __shfl(qf0, 8 * (v / 4) + 4 * kg + (v % 4)) != 0xff80;
+    }
     if (Jc >= nb) return;
-    const bool ok_j = bf16_to_f32(kmax[head + (size_t)Jc * D]) != -__builtin_inff();
+    if (ND == 0) {
+        ok_j = bf16_to_f32(kmax[head + (size_t)Jc * D]) != -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const uint32_t Ir = min(I0 + 8 * (v / 4) + 4 * kg + (v % 4), nb - 1);
+            ok_i[v] = bf16_to_f32(qmax[head + (size_t)Ir * D]) != -__builtin_inff();
+        }
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const uint32_t Ir = I0 + 8 * (v / 4) + 4 * kg + (v % 4);
         if (Ir >= nb) continue;
-        const bool ok_i = bf16_to_f32(qmax[head + (size_t)Ir * D]) != -__builtin_inff();
-        scores[((size_t)bh * nb + Ir) * nb + Jc] = (ok_i && ok_j) ? fmaxf(sx[v], sn[v]) : -__builtin_inff();
+        scores[((size_t)bh * nb + Ir) * nb + Jc] = (ok_i[v] && ok_j) ? fmaxf(sx[v], sn[v]) : -__builtin_inff();
     }
 }
 
