@@ -124,13 +124,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
         if (TOPP) {
             float c = 0.f;
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) c += (valid[i] && key[i] >= cand) ? w[i] : 0.f;
+            for (int i = 0; i < VPL; ++i) c += key[i] >= cand ? w[i] : 0.f;  // w = 0 where not valid
             if (wave_sum_f(c) >= target) T = cand;
         } else {
-            // wave-wide count from ballots (scalar popcounts, no cross-lane shuffles)
+            // wave-wide count from ballots (scalar popcounts, no cross-lane
+            // shuffles); entries that are not valid hold key 0 < cand
             uint32_t c = 0;
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) c += popc64(__ballot(valid[i] && key[i] >= cand));
+            for (int i = 0; i < VPL; ++i) c += popc64(__ballot(key[i] >= cand));
             if (c >= k_row) T = cand;
         }
     }
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
         uint32_t nt = 0;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
-            gt += (valid[i] && key[i] > T) ? w[i] : 0.f;
+            gt += key[i] > T ? w[i] : 0.f;
             if (valid[i] && key[i] == T) { wt = w[i]; ++nt; }
         }
         gt = wave_sum_f(gt);
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
     } else {
         uint32_t gt = 0;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) gt += popc64(__ballot(valid[i] && key[i] > T));
+        for (int i = 0; i < VPL; ++i) gt += popc64(__ballot(key[i] > T));
         need = row_exists ? k_row - gt : 0u;
     }
 
