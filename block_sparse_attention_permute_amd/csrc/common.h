@@ -86,8 +86,7 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// A 16-byte slice of a token row as EPV floats (8 bf16 or 4 fp32 values),
-// and back; bf16 values widened to fp32 pack back exactly.
+// A 16-byte slice of a token row as EPV floats (8 bf16 or 4 fp32 values).
 template <int EPV>
 __device__ __forceinline__ void unpack(const uint4 raw, float (&v)[EPV]) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -101,20 +100,6 @@ __device__ __forceinline__ void unpack(const uint4 raw, float (&v)[EPV]) {
 #pragma unroll
         for (int i = 0; i < EPV; ++i) v[i] = __uint_as_float(w[i]);
     }
-}
-
-template <int EPV>
-__device__ __forceinline__ uint4 pack(const float (&v)[EPV]) {
-    uint32_t w[4];
-    if (EPV == 8) {
-        // exact: every value is an input bf16 value widened to fp32
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xffff0000u);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Running elementwise max and min of 16-byte row slices (block summaries).
