@@ -173,6 +173,55 @@ def window_rows(q_head, k_head, v_head, rows, window: int, sink: int, scale: flo
     return masked_attention_rows(q_head[rows], k_head, v_head, mask_rows, scale)
 
 
+def block_sparse_rows_gathered(q_head, k_head, v_head, keep_head, block: int, rows, scale: float):
+    """Rows ``rows`` of one head's block-sparse attention over the kept key blocks only.
+
+    The same result as :func:`block_sparse_rows`: a masked key adds exp(-inf)
+    = 0 to the softmax sum and 0 * v to the output, so leaving it out changes
+    nothing but the order of the additions.  For each query block holding
+    sampled rows, the keys of its kept blocks are gathered and dense
+    attention runs over them with no mask.  A query block that keeps no key
+    block has no defined output: RuntimeError.
+    """
+    rows = np.asarray(rows)
+    keep_head = np.asarray(keep_head, dtype=bool)
+    out = np.empty((rows.size, q_head.shape[1]))
+    qb = rows // block
+    for i in np.unique(qb):
+        sel = np.flatnonzero(qb == i)
+        kept = np.flatnonzero(keep_head[i])
+        if kept.size == 0:
+            raise RuntimeError("a query row has no visible key")
+        keys = (kept[:, None] * block + np.arange(block)[None, :]).ravel()
+        out[sel] = masked_attention(q_head[rows[sel]], k_head[keys], v_head[keys], 0.0, scale)
+    return out
+
+
+def window_rows_gathered(q_head, k_head, v_head, rows, window: int, sink: int, scale: float, span: int = 64):
+    """Rows ``rows`` of one head's windowed attention over the keys a row can see.
+
+    The same result as :func:`window_rows`: rows are taken ``span``
+    consecutive positions at a time, and each group is evaluated against the
+    sink keys plus the union of its members' windows, with the window mask
+    of :func:`window_mask` on that key set (keys outside it are masked for
+    every row of the group, so leaving them out changes only the order of
+    the additions).
+    """
+    rows = np.asarray(rows)
+    s = k_head.shape[0]
+    half = window // 2
+    out = np.empty((rows.size, q_head.shape[1]))
+    grp = rows // span
+    for g in np.unique(grp):
+        sel = np.flatnonzero(grp == g)
+        r = rows[sel]
+        lo, hi = max(0, int(r.min()) - half), min(s, int(r.max()) + half + 1)
+        keys = np.union1d(np.arange(min(sink, s)), np.arange(lo, hi))
+        allowed = (np.abs(r[:, None] - keys[None, :]) <= half) | (keys[None, :] < sink)
+        out[sel] = masked_attention(q_head[r], k_head[keys], v_head[keys], np.where(allowed, 0.0, NEG_INF), scale)
+    return out
+
+
 def kept_block_flops(kv_cnt, block_q: int, block_k: int, D: int) -> int:
     """Algorithmic FLOPs of block-sparse attention: 4 * Bq * Bk * D per kept block."""
     return int(np.asarray(kv_cnt, dtype=np.int64).sum()) * 4 * block_q * block_k * D

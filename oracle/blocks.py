@@ -128,24 +128,49 @@ def topk_block_mask(scores, k: int, sink_blocks: int = 1, keep_diag=True) -> np.
     return keep
 
 
+def top_p_ranked_mass(scores_row, scale: float = 1.0):
+    """Ranking and unnormalised softmax weights of one row, for the nucleus rule.
+
+    Returns (order, w): order ranks the blocks (score desc, index asc, NaN
+    last, as topk_row) and w[i] is the weight of block order[i], i.e.
+    exp(scale * (s - max)).  Non-finite scores take the softmax's limit
+    values: NaN carries no weight; when the row's largest score is +inf (or
+    every number in it is -inf) the weight is shared equally by the entries
+    equal to it; otherwise -inf weighs 0.  A row of NaNs has no weight at all.
+    scale must be positive and finite.
+    """
+    if not (math.isfinite(scale) and scale > 0.0):
+        raise ValueError(f"scale must be positive and finite, got {scale}")
+    s = np.asarray(scores_row, dtype=np.float64) * float(scale)
+    n = s.shape[0]
+    order = np.lexsort((np.arange(n), -s))   # NaN last
+    z = s[order]
+    top = z[0]                                # the row's largest score (NaN only if all are)
+    if np.isnan(top):
+        return order, np.zeros(n)
+    if np.isinf(top):
+        return order, np.where(z == top, 1.0, 0.0)
+    return order, np.where(np.isnan(z), 0.0, np.exp(z - top))
+
+
 def top_p_count(scores_row, p: float, scale: float = 1.0) -> int:
     """Smallest number of best-ranked blocks whose softmax mass reaches p.
 
     The pages name top_p_block_mask without defining it ([Adaptive tiling
     (SPADE), "What mlx-arsenal ships"]).  Reading (the nucleus rule): the
-    row's block probabilities are softmax(scale * S_I.) over all key blocks;
+    row's block probabilities are softmax(scale * S_I.) over all key blocks
+    (top_p_ranked_mass, with its limit values for NaN and infinite scores);
     blocks are ranked (score desc, index asc) and the shortest prefix with
     cumulative probability >= p is kept (at least one block).  p in (0, 1].
-    NaN scores rank last (as in topk_row) and carry no probability.
+    A row with no mass at all (every score NaN) keeps its first-ranked
+    block, the lowest index.
     """
     if not (0.0 < p <= 1.0):
         raise ValueError(f"p must be in (0, 1], got {p}")
-    s = np.asarray(scores_row, dtype=np.float64) * float(scale)
-    n = s.shape[0]
-    order = np.lexsort((np.arange(n), -s))
-    z = s[order]
-    w = np.exp(z - z[0])
-    w = np.where(np.isnan(z), 0.0, w)   # NaN scores rank last and weigh nothing
+    _, w = top_p_ranked_mass(scores_row, scale)
+    n = w.shape[0]
+    if w.sum() == 0.0:
+        return 1
     cum = np.cumsum(w) / w.sum()
     m = int(np.searchsorted(cum, p, side="left")) + 1
     return min(max(m, 1), n)
@@ -171,8 +196,13 @@ def keep_to_lists(keep):
 def near_tie_ok(scores_row, k: int, idx: int, rel: float = 1e-5) -> bool:
     """True when block ``idx`` is within ``rel`` (relative) of the row's k-th score.
 
-    Used to allow a top-k membership difference only for near ties.
+    Used to allow a top-k membership difference only for near ties.  The
+    k-th score is the k-th entry in topk_row's ranking (NaN last), so a row
+    with NaN scores ranks them below every number; a NaN entry or a NaN k-th
+    score is never a near tie.
     """
     s = np.asarray(scores_row, dtype=np.float64)
-    kth = np.sort(s)[::-1][k - 1]
-    return abs(s[idx] - kth) < rel * abs(kth)
+    n = s.shape[0]
+    order = np.lexsort((np.arange(n), -s))
+    kth = s[order[k - 1]]
+    return bool(abs(s[idx] - kth) < rel * abs(kth))

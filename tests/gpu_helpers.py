@@ -45,10 +45,9 @@ def top_p_row_ok(gpu_row, scores_row, p, scale, static_row, rel=TOPP_REL):
     want = OB.top_p_block_mask(scores_row[None, :], p, 0, 0, scale)[0] | static_row
     if np.array_equal(gpu_row, want):
         return True
-    row = scores_row * scale
-    order = np.lexsort((np.arange(nk), -row))
-    w = np.exp(row[order] - row[order][0])
-    w = np.where(np.isnan(row[order]), 0.0, w)
+    order, w = OB.top_p_ranked_mass(scores_row, scale)
+    if w.sum() == 0.0:
+        return False
     cum = np.cumsum(w) / w.sum()
     cuts = [c for c in range(1, nk + 1) if np.array_equal(np.isin(np.arange(nk), order[:c]) | static_row, gpu_row)]
     if not cuts:

@@ -158,5 +158,35 @@ def test_block_sparse_matches_library_with_expanded_mask_and_rows_agree():
     np.testing.assert_allclose(wrows, A.windowed_attention(q, k, v, 6, 2, scale=0.4)[0, 0, rows], atol=1e-12)
 
 
+def test_gathered_forms_match_the_library_on_all_rows():
+    """The kept-block and window-slice forms against torch's SDPA with the full boolean mask."""
+    S, D, block = 96, 8, 8
+    q, k, v = (_rand((1, 1, S, D), 70 + i) for i in range(3))
+    rng = np.random.default_rng(71)
+    nb = S // block
+    keep = rng.random((nb, nb)) < 0.35
+    keep[np.arange(nb), np.arange(nb)] = True
+    keep[3] = False
+    keep[3, nb - 1] = True                          # a one-block row at the far end
+    keep[5] = True                                  # a full row
+    allowed = np.kron(keep, np.ones((block, block), bool)).astype(bool)
+    want = _torch_sdpa(q, k, v, allowed, scale=0.3)[0, 0]
+    rows = np.arange(S)
+    got = A.block_sparse_rows_gathered(q[0, 0], k[0, 0], v[0, 0], keep, block, rows, 0.3)
+    np.testing.assert_allclose(got, want, atol=1e-12)
+    some = np.array([95, 0, 17, 40, 41, 3])         # unsorted, several per block
+    got = A.block_sparse_rows_gathered(q[0, 0], k[0, 0], v[0, 0], keep, block, some, 0.3)
+    np.testing.assert_allclose(got, want[some], atol=1e-12)
+    keep[2] = False
+    with pytest.raises(RuntimeError):
+        A.block_sparse_rows_gathered(q[0, 0], k[0, 0], v[0, 0], keep, block, np.array([16]), 0.3)
+    for window, sink, span in [(9, 3, 8), (30, 0, 16), (2, 96, 5), (400, 7, 64)]:
+        i, j = np.arange(S)[:, None], np.arange(S)[None, :]
+        allowed = (np.abs(i - j) <= window // 2) | (j < sink)
+        want = _torch_sdpa(q, k, v, allowed, scale=0.3)[0, 0]
+        got = A.window_rows_gathered(q[0, 0], k[0, 0], v[0, 0], rows, window, sink, 0.3, span)
+        np.testing.assert_allclose(got, want, atol=1e-12)
+
+
 def test_kept_block_flops():
     assert A.kept_block_flops(np.array([[81, 83]]), 64, 64, 128) == 164 * 4 * 64 * 64 * 128

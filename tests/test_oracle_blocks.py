@@ -99,6 +99,31 @@ def test_topk_block_mask_sink_and_diagonal():
 def test_near_tie_rule():
     s = np.array([10.0, 9.99999999, 5.0, 1.0])
     assert K.near_tie_ok(s, 1, 1) and not K.near_tie_ok(s, 1, 2)
+    # the bound is relative to the k-th score, strict, and two-sided
+    s = np.array([4.0, 2.0, 2.0 - 1.9e-5, 2.0 - 2.1e-5, 1.0])
+    assert K.near_tie_ok(s, 2, 2) and not K.near_tie_ok(s, 2, 3)      # below the k-th score
+    assert K.near_tie_ok(s, 3, 1) and not K.near_tie_ok(s, 3, 0)      # above it
+    # negative k-th score: the magnitude sets the bound
+    s = np.array([-1.0, -1.000001, -1.0001, -5.0])
+    assert K.near_tie_ok(s, 1, 1) and not K.near_tie_ok(s, 1, 2)
+    # a k-th score of 0 admits no difference at all (the bound is 0)
+    s = np.array([3.0, 0.0, 0.0, 1e-30, -2.0])
+    assert not K.near_tie_ok(s, 3, 2) and not K.near_tie_ok(s, 3, 3)
+    # NaN ranks last: it is never the k-th score of a row that has k numbers, and never a near tie
+    s = np.array([np.nan, 5.0, 4.99999999, 1.0])
+    assert K.near_tie_ok(s, 1, 2) and not K.near_tie_ok(s, 1, 0)
+    assert not K.near_tie_ok(np.array([1.0, np.nan]), 2, 1)
+
+
+def test_near_tie_rule_brute_force():
+    """Against a plain loop: the k-th largest by sorted(), then the relative gap."""
+    r = np.random.default_rng(17)
+    for _ in range(30):
+        s = np.round(r.standard_normal(25) * 4, 3)           # rounding makes exact ties common
+        k = int(r.integers(1, 26))
+        kth = sorted(s.tolist(), reverse=True)[k - 1]
+        for j in range(25):
+            assert K.near_tie_ok(s, k, j, 1e-3) == (abs(s[j] - kth) < 1e-3 * abs(kth))
 
 
 def _sdpa(q, k, v):

@@ -98,6 +98,84 @@ def test_top_p_brute_force_cumulative():
         assert m == want
 
 
+def _top_p_brute(row, p):
+    """Count of the nucleus by a plain loop: NaN entries removed, softmax of what is left."""
+    fin = [(x, j) for j, x in enumerate(row) if not math.isnan(x)]
+    if not fin:
+        return 1
+    ranked = sorted(fin, key=lambda t: (-t[0], t[1]))
+    top = ranked[0][0]
+    if math.isinf(top):
+        e = [1.0 if x == top else 0.0 for x, _ in ranked]
+    else:
+        e = [math.exp(x - top) for x, _ in ranked]
+    z = sum(e)
+    acc = 0.0
+    for c, w in enumerate(e, start=1):
+        acc += w
+        if acc / z >= p:
+            return c
+    return len(e)
+
+
+def test_top_p_nan_scores_carry_no_mass():
+    """NaN scores: the count equals that of the row with the NaNs removed (a plain loop), and a NaN block
+    is never kept while a number is left out."""
+    r = _rng(31)
+    for trial in range(40):
+        n = int(r.integers(4, 40))
+        s = r.standard_normal(n) * 2
+        nan_at = r.random(n) < 0.3
+        nan_at[int(r.integers(0, n))] = False              # keep at least one number
+        s[nan_at] = np.nan
+        p = float(r.uniform(0.05, 0.95))
+        m = OB.top_p_count(s, p)
+        assert m == _top_p_brute(s.tolist(), p), trial
+        assert m == OB.top_p_count(s[~nan_at], p), trial
+        keep = OB.top_p_block_mask(s[None, :], p, 0, 0)[0]
+        assert keep.sum() == m
+        if keep[nan_at].any():
+            assert keep[~nan_at].all()
+    # NaN ahead of the numbers in index order changes nothing: the numbers rank first
+    s = np.array([np.nan, np.nan, 1.0, 0.0])
+    keep = OB.top_p_block_mask(s[None, :], 0.99, 0, 0)[0]
+    assert list(np.flatnonzero(keep)) == [2, 3]
+
+
+def test_top_p_all_nan_row_keeps_lowest_index():
+    s = np.full(7, np.nan)
+    for p in (0.01, 0.5, 1.0):
+        assert OB.top_p_count(s, p) == 1
+        assert list(np.flatnonzero(OB.top_p_block_mask(s[None, :], p, 0, 0)[0])) == [0]
+
+
+def test_top_p_infinities_take_the_softmax_limit():
+    # two +inf scores share all the mass: 0.5 each
+    s = np.array([1.0, np.inf, 3.0, np.inf, np.nan])
+    assert OB.top_p_count(s, 0.5) == 1
+    assert OB.top_p_count(s, 0.51) == 2
+    assert OB.top_p_count(s, 1.0) == 2
+    assert list(np.flatnonzero(OB.top_p_block_mask(s[None, :], 0.5, 0, 0)[0])) == [1]
+    # only -inf numbers: uniform over them (NaN still weighs nothing)
+    s = np.array([-np.inf, np.nan, -np.inf, -np.inf])
+    assert OB.top_p_count(s, 0.5) == 2
+    assert OB.top_p_count(s, 0.7) == 3
+    # -inf beside a finite maximum weighs 0: probabilities 0.25, 0, 0.75
+    s = np.array([0.0, -np.inf, np.log(3.0)])
+    assert OB.top_p_count(s, 0.75) == 1
+    assert OB.top_p_count(s, 0.8) == 2
+    assert OB.top_p_count(s, 1.0) == 2
+    for row in ([1.0, np.inf, 3.0, np.inf, np.nan], [-np.inf, np.nan, -np.inf, -np.inf], [0.0, -np.inf, 2.0]):
+        for p in (0.2, 0.5, 0.9):
+            assert OB.top_p_count(np.array(row), p) == _top_p_brute(row, p)
+
+
+def test_top_p_rejects_bad_scale():
+    for sc in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(ValueError):
+            OB.top_p_count(np.zeros(4), 0.5, sc)
+
+
 # ---------------------------------------------------------- pooled statistic
 def _pooled_brute(q, grid, tile):
     T, Hg, Wg = grid
