@@ -19,15 +19,18 @@ Workloads (all batch 1, tokens in T-major order ``s = (t*Hg + y)*Wg + x``):
   5. bf16, H=24, grid 32x48x80 (S=122880), D=128; q, k from the Fourier recipe.
 
 Fourier recipe (workloads 4 and 5), per head h, from the features stream:
-  a_h ~ U{t, y, x}                    preferred axis
-  l = (2, 2, 2) with l[a_h] = 8       length scales in grid units
+  a_h ~ U{temporal, spatial}          the head's axis preference
+  l = (8, 2, 2) for a temporal head,  length scales (t, y, x) in grid units:
+      (2, 8, 8) for a spatial head    long along time, or along both axes of a frame
   z_f ~ N(0, I_3), w_f = z_f / l      16 random Fourier frequencies
   phi_f ~ U[0, 2*pi)
   A_f ~ N(0, (2/16) I_D)
   F(p) = sum_f A_f cos(w_f . p + phi_f)   (unit variance per dimension)
   q = F + 0.3 N(0, 1)  (q stream),  k = F + 0.3 N(0, 1)  (k stream)
 q and k share F, so every head has smooth structure that is longer along its
-preferred axis: the spatial or temporal locality that adaptive tiling exploits.
+preferred axes: a temporal head is coherent across frames at one position and
+a spatial head across a frame, the two kinds of heads that adaptive tiling
+serves with different tiles.
 """
 from __future__ import annotations
 
@@ -36,6 +39,7 @@ from dataclasses import dataclass
 import numpy as np
 
 ROLE_Q, ROLE_K, ROLE_V, ROLE_FEAT = 0, 1, 2, 3
+HEAD_TEMPORAL, HEAD_SPATIAL = 0, 1
 SEED_ROOT = 2026
 
 
@@ -115,9 +119,7 @@ def grid_positions(grid) -> np.ndarray:
 def fourier_field(cfg: int, head: int, grid, D: int, n_feat: int = 16) -> np.ndarray:
     """The shared smooth field F of one head, (S, D) float64."""
     g = rng_for(cfg, ROLE_FEAT, head)
-    axis = int(g.integers(0, 3))
-    ell = np.array([2.0, 2.0, 2.0])
-    ell[axis] = 8.0
+    ell = np.array([8.0, 2.0, 2.0]) if int(g.integers(0, 2)) == HEAD_TEMPORAL else np.array([2.0, 8.0, 8.0])
     w = g.standard_normal((n_feat, 3)) / ell
     phi = g.uniform(0.0, 2.0 * np.pi, n_feat)
     amp = g.standard_normal((n_feat, D)) * np.sqrt(2.0 / n_feat)
@@ -125,8 +127,9 @@ def fourier_field(cfg: int, head: int, grid, D: int, n_feat: int = 16) -> np.nda
     return np.cos(pos @ w.T + phi) @ amp
 
 
-def preferred_axis(cfg: int, head: int) -> int:
-    return int(rng_for(cfg, ROLE_FEAT, head).integers(0, 3))
+def head_kind(cfg: int, head: int) -> int:
+    """HEAD_TEMPORAL or HEAD_SPATIAL: the axis preference the Fourier recipe drew for a head."""
+    return int(rng_for(cfg, ROLE_FEAT, head).integers(0, 2))
 
 
 def head_f64(cfg: int, role: int, head: int) -> np.ndarray:
