@@ -13,7 +13,6 @@ there is no fallback: without libbsa.so every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import numpy as np
@@ -24,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libbsa.so")
 BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_INVARIANT, BSA_ERR_UNSUPPORTED, BSA_ERR_DEVICE = range(5)
 BSA_F32, BSA_BF16 = 0, 1
 BSA_STAT_MEAN, BSA_STAT_POOLED = 0, 1
+BSA_LABEL_SPATIAL, BSA_LABEL_TEMPORAL = 0, 1
 BSA_MAX_TILINGS = 8
 
 EXPORTED = (
@@ -34,7 +34,7 @@ EXPORTED = (
     "bsa_tile_permute_padded", "bsa_invert_permute_padded", "bsa_select_tiling_ex",
     "bsa_minmax_block_scores_masked", "bsa_topk_block_mask_tiled", "bsa_block_sparse_attention_labels",
     "bsa_minmax_block_scores_tiled", "bsa_block_sparse_attention_tiled",
-    "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices",
+    "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices", "bsa_video_labels",
 )
 
 
@@ -66,6 +66,7 @@ _SIGS = {
     "bsa_padded_length": (_I64, [_I, _I, _I, _I, _I, _I]),
     "bsa_tile_permutation_padded": (_I, [_I, _I, _I, _I, _I, _I, _P]),
     "bsa_label_block_list": (_I, [_P, _I64, _I, _P, _P, _I]),
+    "bsa_video_labels": (_I, [_I, _I, _I, _I, _P]),
     "bsa_tile_permute_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _I64, _P, _P]),
     "bsa_invert_permute_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _I64, _P]),
     "bsa_select_tiling_ex": (_I, [_P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
@@ -211,6 +212,18 @@ def bsa_tile_permutation_padded(T: int, Hg: int, Wg: int, tile) -> np.ndarray:
     a, b, c = (int(v) for v in tile)
     out = np.empty(max(bsa_padded_length(T, Hg, Wg, tile), 1), dtype=np.int32)
     _check(lib().bsa_tile_permutation_padded(int(T), int(Hg), int(Wg), a, b, c, out.ctypes.data))
+    return out
+
+
+def bsa_video_labels(grid, kind: str) -> np.ndarray:
+    """Host: int32 (S,) labels of spatial-only ("spatial", T-major order) or temporal-only ("temporal",
+    the order of the tiling (T, 1, 1)) attention."""
+    T, Hg, Wg = (int(g) for g in grid)
+    codes = {"spatial": BSA_LABEL_SPATIAL, "temporal": BSA_LABEL_TEMPORAL}
+    if kind not in codes:
+        raise ValueError(f"kind must be 'spatial' or 'temporal', got {kind!r}")
+    out = np.empty(max(T * Hg * Wg, 1), dtype=np.int32)
+    _check(lib().bsa_video_labels(T, Hg, Wg, codes[kind], out.ctypes.data))
     return out
 
 
@@ -634,10 +647,6 @@ def bsa_validate_indices(v, lo: int, hi: int) -> None:
 
 # ----------------------------------------------------------- composition ---
 
-def default_scale(D: int, scale=None) -> float:
-    return float(scale) if scale is not None else 1.0 / math.sqrt(D)
-
-
 class AdaptiveBlockSparse:
     """The adaptive-tiling pipeline as a sequence of libbsa launches on one stream.
 
@@ -655,11 +664,14 @@ class AdaptiveBlockSparse:
     bf16 D = 128 tiles of 64 tokens with an x extent that is a multiple of 4,
     and no padding) reads q, k, v in place through the tile geometry for the
     scores and the attention and writes the output in T-major order, so no
-    permuted copy is formed.
+    permuted copy is formed.  ``validate=True`` checks the device-resident
+    tiling choices and block lists (bsa_validate_indices,
+    bsa_validate_block_list) before the attention runs; each check
+    synchronises the stream and raises RuntimeError on a violation.
     """
 
     def __init__(self, B, H, grid, D, tiles, frac, dtype, device, sink_blocks=1, keep_diag=True, scale=None,
-                 top_p=None, p_scale=1.0, statistic="mean", pad=False, fused=None):
+                 top_p=None, p_scale=1.0, statistic="mean", pad=False, fused=None, validate=False):
         torch = _torch()
         self.grid = tuple(int(g) for g in grid)
         self.tiles = [tuple(int(v) for v in t) for t in tiles]
@@ -676,6 +688,7 @@ class AdaptiveBlockSparse:
         self.nb = self.Sp // self.block
         self.sink_blocks, self.keep_diag, self.scale = int(sink_blocks), _band(keep_diag), scale
         self.top_p, self.p_scale = top_p, float(p_scale)
+        self.validate = bool(validate)
         can_fuse = not self.pad and tiled_attention_supported(dtype, D, self.tiles)
         if fused and not can_fuse:
             raise ValueError("the fused path needs bf16, D = 128, tiles of 64 tokens with x extent % 4 == 0, no pad")
@@ -725,6 +738,8 @@ class AdaptiveBlockSparse:
     def __call__(self, q, k, v, out=None, attention_hook=None):
         choice, _, _ = bsa_select_tiling(q, self.grid, self.tiles, workspace=self.ws_select, statistic=self.statistic,
                                          pad=self.pad, q_summaries=self.ws_qsumm)
+        if self.validate:
+            bsa_validate_indices(choice, 0, len(self.tiles))
         if self.pad:
             for src, dst, lab in ((q, self.qp, self.labels), (k, self.kp, None), (v, self.vp, None)):
                 bsa_tile_permute_padded(src, self.grid, self.tiles, head_choice=choice, Sp=self.Sp, out=(dst, lab))
@@ -747,6 +762,8 @@ class AdaptiveBlockSparse:
             else:
                 kv_idx, kv_cnt, _ = bsa_top_p_block_mask(scores, self.top_p, self.p_scale, self.sink_blocks,
                                                          self.keep_diag, return_mask=True, out=self.ws_topk)
+        if self.validate:
+            bsa_validate_block_list(kv_idx, kv_cnt, self.nb)
         if self.fused:
             if attention_hook is not None:
                 attention_hook(True)
@@ -788,14 +805,8 @@ class VideoLabelAttention:
         self.grid = tuple(int(g) for g in grid)
         T, Hg, Wg = self.grid
         S = T * Hg * Wg
-        if kind == "spatial":
-            lab = np.arange(S, dtype=np.int32) // (Hg * Wg)
-            self.tiles = None
-        elif kind == "temporal":
-            self.tiles = [(T, 1, 1)]
-            lab = (bsa_tile_permutation(T, Hg, Wg, (T, 1, 1)) % (Hg * Wg)).astype(np.int32)
-        else:
-            raise ValueError(f"kind must be 'spatial' or 'temporal', got {kind!r}")
+        lab = bsa_video_labels(self.grid, kind)
+        self.tiles = [(T, 1, 1)] if kind == "temporal" else None
         if S % block:
             raise ValueError(f"block {block} must divide S={S}")
         self.kind, self.block, self.S = kind, int(block), S

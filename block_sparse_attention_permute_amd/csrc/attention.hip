@@ -388,7 +388,7 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         m_used = mf;
     }
     if (my_row >= (int)P.S) return;
-    const float inv = 1.0f / l_row;
+    const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;  // a row that saw no key is written as zeros
     uint16_t* orow = P.out + head + (size_t)my_row * D;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)

@@ -38,7 +38,7 @@ using namespace bsa;
 
 extern "C" const char* bsa_last_error(void) { return g_err; }
 
-extern "C" int bsa_version(void) { return (1 << 16) | 0; }
+extern "C" int bsa_version(void) { return (1 << 16) | 1; }
 
 // Tile-contiguous order.  Permuted position p is (tile index) * vol + (offset
 // inside the tile); both are counted T-major, so walking tiles in T-major
@@ -88,6 +88,22 @@ extern "C" int bsa_tile_permutation_padded(int T, int Hg, int Wg, int a, int b, 
                                             ? (int32_t)(((int64_t)t * Hg + y) * Wg + x)
                                             : -1;
                         }
+    return BSA_OK;
+}
+
+extern "C" int bsa_video_labels(int T, int Hg, int Wg, int kind, int32_t* labels) {
+    clear_error();
+    BSA_REQUIRE(labels != nullptr, "bsa_video_labels: NULL labels");
+    BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "bsa_video_labels: grid must be positive");
+    const int64_t hw = (int64_t)Hg * Wg, S = (int64_t)T * hw;
+    BSA_REQUIRE(S <= INT32_MAX, "bsa_video_labels: grid too large");
+    if (kind == BSA_LABEL_SPATIAL) {
+        for (int64_t s = 0; s < S; ++s) labels[s] = (int32_t)(s / hw);   // frame of a T-major token
+    } else if (kind == BSA_LABEL_TEMPORAL) {
+        for (int64_t p = 0; p < S; ++p) labels[p] = (int32_t)(p / T);   // position of tile order (T, 1, 1)
+    } else {
+        BSA_FAIL(BSA_ERR_INVALID_ARG, "bsa_video_labels: unknown kind %d", kind);
+    }
     return BSA_OK;
 }
 

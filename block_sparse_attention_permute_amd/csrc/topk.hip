@@ -99,9 +99,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
         valid[i] = row_exists && e < nk_row;
         key[i] = valid[i] ? order_key(s[e]) : 0u;
     }
-    // TOPP: softmax weights w = exp(scale * (s - max)); NaN and -inf weigh 0
+    // TOPP: softmax weights w = exp(scale * (s - max)) at their limit values:
+    // NaN weighs 0, and an entry equal to the row max weighs 1 (so a +inf max,
+    // or a row whose numbers are all -inf, shares the mass equally)
     float w[VPL];
     float target = (float)P.k;
+    bool no_mass = false;
     if (TOPP) {
         float m = -__builtin_inff();
 #pragma unroll
@@ -115,7 +118,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
             w[i] = (!valid[i] || key[i] == 0u) ? 0.f : (x == m ? 1.f : __builtin_amdgcn_exp2f((x - m) * P.scale_log2));
             z += w[i];
         }
-        target = P.p * wave_sum_f(z);
+        const float ztot = wave_sum_f(z);
+        target = P.p * ztot;
+        no_mass = ztot == 0.f;  // every score NaN: the first-ranked entry is kept
     }
     // threshold key T: the largest T with count (or mass) of keys >= T reaching the target
     uint32_t T = 0;
@@ -149,6 +154,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
         nt = wave_sum(nt);
         const float t = wt > 0.f ? ceilf((target - gt) / wt) : 1.f;
         need = (uint32_t)fminf(fmaxf(t, 1.f), (float)nt);
+        if (no_mass) {  // all keys are 0 (NaN): take the lowest index among them
+            T = 0u;
+            need = 1u;
+        }
     } else {
         uint32_t gt = 0;
 #pragma unroll

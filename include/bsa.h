@@ -114,6 +114,27 @@ int64_t bsa_padded_length(int T, int Hg, int Wg, int a, int b, int c);
  * gives bsa_tile_permutation).  INVALID_ARG if a size is <= 0. */
 int bsa_tile_permutation_padded(int T, int Hg, int Wg, int a, int b, int c, int32_t* perm_host);
 
+typedef enum {
+    BSA_LABEL_SPATIAL = 0,  /* spatial-only attention: a token sees its own frame */
+    BSA_LABEL_TEMPORAL = 1  /* temporal-only attention: a token sees its own (y, x) in every frame */
+} bsa_label_kind;
+
+/* Token labels of spatial-only or temporal-only attention [ADR-0001,
+ * "Décision" step 1: spatial_only_mask, temporal_only_mask; the pages give
+ * the names only].  Reading: spatial-only lets token i see token j exactly
+ * when they lie in one frame, temporal-only exactly when they sit at one
+ * spatial position; both are the rule labels[i] == labels[j].  The labels
+ * are written in the order the matching attention call runs in:
+ *  BSA_LABEL_SPATIAL:  T-major order; labels_host[s] = t = s / (Hg*Wg), the
+ *                      frame index (frames are contiguous runs of Hg*Wg);
+ *  BSA_LABEL_TEMPORAL: the order of the tiling (T, 1, 1), where position
+ *                      p = (y*Wg + x)*T + t holds token (t*Hg + y)*Wg + x;
+ *                      labels_host[p] = y*Wg + x = p / T, the spatial
+ *                      position (each position's T frames are contiguous).
+ * labels_host: T*Hg*Wg int32 (host, caller-owned).  INVALID_ARG if a size
+ * is <= 0, T*Hg*Wg exceeds 2^31 - 1, or kind is unknown. */
+int bsa_video_labels(int T, int Hg, int Wg, int kind, int32_t* labels_host);
+
 /* Block lists of the "same label" rule: key block J is kept for query block
  * I when some token of I and some token of J carry the same label (labels
  * < 0 never match).  With the frame index as label this is the block
@@ -286,8 +307,11 @@ int bsa_topk_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int N
  * row's block probabilities are softmax(scale * scores[b,h,I,:]); blocks are
  * ranked as in bsa_topk_block_mask and the shortest prefix whose cumulative
  * probability reaches p is kept (at least one block), then the sink blocks
- * and the diagonal band are added.  Weights and sums are fp32; NaN scores
- * weigh 0.  Arguments and outputs as bsa_topk_block_mask.
+ * and the diagonal band are added.  Weights and sums are fp32 and take the
+ * softmax's limit values: NaN scores weigh 0; a +inf row max (or a row whose
+ * numbers are all -inf) shares the mass equally among the entries equal to
+ * it; a row of NaNs keeps its lowest index.  Arguments and outputs as
+ * bsa_topk_block_mask.
  * INVALID_ARG unless 0 < p <= 1, scale > 0, 1 <= Nk <= 4096, sink_blocks >= 0,
  * diag_width >= 0 and max_kept >= Nk. */
 int bsa_top_p_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int Nk, float p,
@@ -329,8 +353,9 @@ int bsa_topk_block_mask_tiled(const float* scores, int64_t B, int64_t H, int Nq,
  * largest L2 norm of a key row of its block (bsa_minmax_block_scores writes
  * them).  It changes only the work, not the result beyond rounding: for
  * bf16, D = 128, block 64 and scale > 0, a key block whose scores cannot
- * pass the running row max by more than 24 in log2 units (|q_i| * norm_J *
- * scale * log2(e), Cauchy-Schwarz) skips the running-max update, so its
+ * pass the smallest running row max of the query block by more than 32 in
+ * log2 units (max_i |q_i| * norm_J * scale * log2(e), Cauchy-Schwarz; so no
+ * weight exceeds 2^32) skips the running-max update, so its
  * softmax weights are taken relative to an older max (an exact shift of the
  * softmax; the weights are rounded to bf16 at a different scale).
  * INVALID_ARG unless block divides S and max_kept >= 1. */
