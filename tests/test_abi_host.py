@@ -131,6 +131,37 @@ def test_label_block_lists_bit_exact(L, grid, block, kind):
         bsa.bsa_label_block_list(lab, block, max_kept=int(cnt.max()) - 1)
 
 
+@pytest.mark.parametrize("grid", [(2, 4, 4), (5, 4, 4), (3, 6, 5), (1, 7, 3), (6, 1, 1), (20, 32, 48)])
+def test_video_labels_bit_exact(L, grid):
+    """bsa_video_labels against the oracle's spatial-only and temporal-only masks: spatial labels in T-major
+    order, temporal labels in the order of the tiling (T, 1, 1); equal labels exactly where the mask keeps."""
+    from oracle import attention as OA
+    T, Hg, Wg = grid
+    S = T * Hg * Wg
+    perm = OT.tile_permutation(grid, (T, 1, 1))
+    sp = bsa.bsa_video_labels(grid, "spatial")
+    tp = bsa.bsa_video_labels(grid, "temporal")
+    assert sp.dtype == np.int32 and tp.dtype == np.int32 and sp.shape == tp.shape == (S,)
+    if S <= 4096:
+        ms = OA.spatial_only_mask(grid) == 0.0
+        mt = (OA.temporal_only_mask(grid) == 0.0)[perm][:, perm]
+        assert np.array_equal(sp[:, None] == sp[None, :], ms)
+        assert np.array_equal(tp[:, None] == tp[None, :], mt)
+        for lab in (sp, tp):                  # and their block lists equal the brute-force block rule
+            for block in (b for b in (4, 8, 16) if S % b == 0):
+                idx, cnt = bsa.bsa_label_block_list(lab, block)
+                lists, ocnt = OB.keep_to_lists(OP.label_block_keep(lab, block))
+                assert np.array_equal(cnt, ocnt)
+                assert all(np.array_equal(idx[i, :cnt[i]], li) for i, li in enumerate(lists))
+    else:                                     # the masks are S x S: compare with the rule they are built on
+        assert np.array_equal(sp, np.arange(S) // (Hg * Wg))
+        assert np.array_equal(tp, perm % (Hg * Wg))
+    with pytest.raises(ValueError):
+        bsa.bsa_video_labels(grid, "diagonal")
+    assert L.bsa_video_labels(T, Hg, Wg, 2, (ctypes.c_int32 * S)()) == bsa.BSA_ERR_INVALID_ARG
+    assert L.bsa_video_labels(0, Hg, Wg, 0, (ctypes.c_int32 * S)()) == bsa.BSA_ERR_INVALID_ARG
+
+
 # --- argument validation of device calls: all rejected on the host --------
 
 FAKE = ctypes.c_void_p(4096)  # never dereferenced: every case below fails validation first

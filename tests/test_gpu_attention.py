@@ -217,3 +217,84 @@ def test_block_sparse_short_and_empty_lists(tiled):
         rows = np.concatenate([np.arange(I * block, (I + 1) * block) for I in range(nb) if keep[0, h, I].any()])
         want = OA.block_sparse_rows(qh, kh, vh, keep[0, h], block, rows, D ** -0.5)
         assert max_abs(oh[rows], want) <= BF16_ATOL, h
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D,block,S", [(64, 32, 640), (128, 32, 512), (64, 64, 512), (32, 32, 256)])
+def test_block_sparse_empty_lists_other_kernels(D, block, S):
+    """Lists of 0 to 3 key blocks on the four-wave MFMA kernel (D = 64 or blocks of 32) and the scalar
+    kernel (D = 32): a query block with an empty list is written as zeros, every other row matches."""
+    torch_gpu()
+    H = 2
+    nb = S // block
+    rng = np.random.default_rng(41 + D + block)
+    keep = np.zeros((1, H, nb, nb), bool)
+    for h in range(H):
+        for I in range(nb):
+            keep[0, h, I, rng.choice(nb, size=I % 4, replace=False)] = True
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=540 + i + D + block) for i in range(3))
+    kv_idx, kv_cnt = _keep_to_gpu_lists(keep)
+    out = f64(bsa.bsa_block_sparse_attention(gpu(q), gpu(k), gpu(v), kv_idx, kv_cnt, block))
+    assert np.all(np.isfinite(out))
+    qf, kf, vf = (synth.stored_to_f64(x)[0] for x in (q, k, v))
+    for h in range(H):
+        empty = np.flatnonzero(~keep[0, h].any(-1))
+        assert empty.size > 0
+        for I in empty:
+            assert np.all(out[0, h, I * block:(I + 1) * block] == 0.0), (h, I)
+        rows = np.concatenate([np.arange(I * block, (I + 1) * block) for I in range(nb) if keep[0, h, I].any()])
+        want = OA.block_sparse_rows_gathered(qf[h], kf[h], vf[h], keep[0, h], block, rows, D ** -0.5)
+        assert max_abs(out[0, h, rows], want) <= BF16_ATOL, h
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("scale", [0.0, -0.06, -0.2])
+@pytest.mark.parametrize("D,block", [(128, 64), (64, 32), (64, 64)])
+def test_block_sparse_non_positive_scale(scale, D, block):
+    """An explicit scale is used as given, also when it is 0 (uniform weights over the visible keys) or
+    negative; the kernels' non-positive-scale paths, with and without key norms."""
+    torch = torch_gpu()
+    H, S = 2, 1024
+    rng = np.random.default_rng(int(D + block - 100 * scale))
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=560 + i + D) for i in range(3))
+    keep = _random_keep(1, H, S // block, rng)
+    kv_idx, kv_cnt = _keep_to_gpu_lists(keep)
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    out = bsa.bsa_block_sparse_attention(qg, kg, vg, kv_idx, kv_cnt, block, scale=scale)
+    want = OA.block_sparse_attention(*(synth.stored_to_f64(x) for x in (q, k, v)), keep, block, scale)
+    assert max_abs(f64(out), want) <= BF16_ATOL
+    if scale == 0.0:                                  # uniform weights: the mean of the visible values
+        vf = synth.stored_to_f64(v)[0, 0]
+        I = 0
+        keys = np.concatenate([np.arange(J * block, (J + 1) * block) for J in np.flatnonzero(keep[0, 0, I])])
+        assert max_abs(f64(out)[0, 0, :block], np.broadcast_to(vf[keys].mean(0), (block, D))) <= BF16_ATOL
+    norms = torch.full((1, H, S // block), 1e3, dtype=torch.float32, device="cuda")
+    out2 = bsa.bsa_block_sparse_attention(qg, kg, vg, kv_idx, kv_cnt, block, scale=scale, key_norms=norms)
+    assert torch.equal(out, out2)                     # the key-norm bound only applies to positive scales
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("scale", [0.0, -0.08])
+@pytest.mark.parametrize("D", [128, 64])
+def test_windowed_non_positive_scale(scale, D):
+    torch_gpu()
+    H, S, window, sink = 2, 700, 130, 5
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=580 + i + D) for i in range(3))
+    out = bsa.bsa_windowed_attention(gpu(q), gpu(k), gpu(v), window=window, sink=sink, scale=scale)
+    want = OA.windowed_attention(*(synth.stored_to_f64(x) for x in (q, k, v)), window, sink, scale=scale)
+    assert max_abs(f64(out), want) <= BF16_ATOL
+
+
+@pytest.mark.gpu
+def test_windowed_workload_every_row_of_one_head():
+    """S=16384, window 2048, sink 64, D=128, H=24 in one launch: every output row of head 5 against the
+    oracle (window-slice form), and sampled rows of two more heads."""
+    torch_gpu()
+    q, k, v = synth.qkv(3)
+    out = f64(bsa.bsa_windowed_attention(gpu(q), gpu(k), gpu(v), window=2048, sink=64, scale=128 ** -0.5,
+                                         chunk=512))
+    S = 16384
+    for h, rows in ((5, np.arange(S)), (0, np.arange(0, S, 97)), (23, np.arange(40, S, 131))):
+        qf, kf, vf = (synth.stored_to_f64(x[0, h]) for x in (q, k, v))
+        want = OA.window_rows_gathered(qf, kf, vf, rows, 2048, 64, 128 ** -0.5)
+        assert max_abs(out[0, h, rows], want) <= BF16_ATOL, h
