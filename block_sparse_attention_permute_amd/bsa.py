@@ -25,6 +25,7 @@ BSA_F32, BSA_BF16 = 0, 1
 BSA_STAT_MEAN, BSA_STAT_POOLED = 0, 1
 BSA_LABEL_SPATIAL, BSA_LABEL_TEMPORAL = 0, 1
 BSA_MAX_TILINGS = 8
+BSA_NOALLOC_TILE_VALUES = 1 << 20
 
 EXPORTED = (
     "bsa_last_error", "bsa_version", "bsa_tile_permutation", "bsa_invert_permutation", "bsa_budget",
@@ -35,6 +36,7 @@ EXPORTED = (
     "bsa_minmax_block_scores_masked", "bsa_topk_block_mask_tiled", "bsa_block_sparse_attention_labels",
     "bsa_minmax_block_scores_tiled", "bsa_block_sparse_attention_tiled",
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices", "bsa_video_labels",
+    "bsa_select_tiling_noalloc",
 )
 
 
@@ -56,6 +58,7 @@ _SIGS = {
     "bsa_invert_permute": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P]),
     "bsa_block_cohesion": (_I, [_P, _I, _I64, _I64, _I64, _I64, _I, _P, _P]),
     "bsa_select_tiling": (_I, [_P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P]),
+    "bsa_select_tiling_noalloc": (_I, [_P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P]),
     "bsa_minmax_block_scores": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P]),
     "bsa_topk_block_mask": (_I, [_P, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "bsa_top_p_block_mask": (_I, [_P, _I64, _I64, _I, _I, _F, _F, _I, _I, _P, _P, _I, _P, _P]),
@@ -368,6 +371,26 @@ def bsa_select_tiling(q, grid, tiles, workspace=None, statistic: str = "mean", p
     _check(lib().bsa_select_tiling_ex(_dev(q, "q"), _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, stat, int(bool(pad)),
                                       _dev(tile_coh), _dev(score), _dev(choice), qs, _stream(q)))
     return choice, score, tile_coh
+
+
+def bsa_select_tiling_noalloc(q, grid, tiles, out):
+    """bsa_select_tiling with no workspace and no allocation: out = (choice int32 (B, H), score float32
+    (B, H, n)), both caller-allocated, are written and returned.  The per-tile values live in a fixed
+    array inside libbsa (BSA_NOALLOC_TILE_VALUES floats per device); calls that overlap on one device race."""
+    torch = _torch()
+    B, H, S, D = _bhsd(q, "q")
+    T, Hg, Wg = (int(g) for g in grid)
+    if T * Hg * Wg != S:
+        raise ValueError(f"grid {tuple(grid)} does not match S={S}")
+    arr, n = _tiles_arr(tiles)
+    choice, score = out
+    if choice.dtype != torch.int32 or choice.numel() != B * H:
+        raise ValueError("choice must be int32 with B*H entries")
+    if score.dtype != torch.float32 or score.numel() != B * H * n:
+        raise ValueError("score must be float32 with B*H*n entries")
+    _check(lib().bsa_select_tiling_noalloc(_dev(q, "q"), _dtype_code(q), B, H, T, Hg, Wg, D, arr, n,
+                                           _dev(score, "score"), _dev(choice, "choice"), _stream(q)))
+    return choice, score
 
 
 def _q_summaries_arg(t, q, tiles, S, what):

@@ -27,6 +27,9 @@
 //    to the numerator and n(n - 1) (n = its real tokens) to the denominator.
 #include "common.h"
 
+#include <algorithm>
+#include <mutex>
+
 namespace bsa {
 namespace {
 
@@ -370,5 +373,67 @@ extern "C" int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H,
                                  const int32_t* tiles_host, int n_tiles, float* tile_coh, float* score,
                                  int32_t* choice, bsa_stream_t stream) {
     return bsa_select_tiling_ex(q, dtype, B, H, T, Hg, Wg, D, tiles_host, n_tiles, BSA_STAT_MEAN, 0, tile_coh, score,
+                                choice, nullptr, stream);
+}
+
+// ------------------------------------------------------ no allocation ---
+// bsa_select_tiling_noalloc keeps the per-tile values in this fixed array
+// instead of a caller workspace.  Every device the library runs on holds its
+// own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device copy: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[BSA_NOALLOC_TILE_VALUES];
+
+namespace bsa {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+int scratch_on_current_device(float** out, const char* name) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        BSA_FAIL(BSA_ERR_DEVICE, "%s: no usable current device (%d)", name, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            BSA_FAIL(BSA_ERR_DEVICE, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", name,
+                     dev, hipGetErrorString(e));
+        g_scratch_dev[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return BSA_OK;
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" int bsa_select_tiling_noalloc(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
+                                         int64_t D, const int32_t* tiles_host, int n_tiles, float* score,
+                                         int32_t* choice, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_select_tiling_noalloc";
+    BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
+    BSA_REQUIRE(B >= 1 && H >= 1, "%s: B and H must be >= 1", name);
+    int rc = check_tiles(T, Hg, Wg, tiles_host, n_tiles);
+    if (rc) return rc;
+    const int64_t S = (int64_t)T * Hg * Wg;
+    int64_t max_nb = 0;
+    for (int i = 0; i < n_tiles; ++i)
+        max_nb = std::max<int64_t>(max_nb, S / ((int64_t)tiles_host[3 * i] * tiles_host[3 * i + 1] *
+                                                tiles_host[3 * i + 2]));
+    const int64_t need = B * H * n_tiles * max_nb;
+    BSA_REQUIRE(need <= (int64_t)BSA_NOALLOC_TILE_VALUES,
+                "%s: B*H*n_tiles*max_tiles = %lld per-tile values exceed the fixed scratch of %d (use "
+                "bsa_select_tiling with a workspace)",
+                name, (long long)need, BSA_NOALLOC_TILE_VALUES);
+    float* ws = nullptr;
+    rc = scratch_on_current_device(&ws, name);
+    if (rc) return rc;
+    return bsa_select_tiling_ex(q, dtype, B, H, T, Hg, Wg, D, tiles_host, n_tiles, BSA_STAT_MEAN, 0, ws, score,
                                 choice, nullptr, stream);
 }

@@ -216,6 +216,24 @@ int bsa_select_tiling(const void* q, int dtype, int64_t B, int64_t H, int T, int
                       int64_t D, const int32_t* tiles_host, int n_tiles, float* tile_coh,
                       float* score, int32_t* choice, bsa_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * bsa_select_tiling without the tile_coh workspace.  The per-tile cohesion
+ * goes to a fixed array inside the library, BSA_NOALLOC_TILE_VALUES floats
+ * (4 MiB) in the memory of each device the library runs on, held until the
+ * process ends; its address is looked up once per device, on the first call
+ * with that device current (make that first call outside graph capture).
+ * Nothing is allocated, and nothing needs clearing: every per-tile value a
+ * call reads is written earlier in the same call.  Calls that overlap on one
+ * device (two streams or two threads) share the array and race: serialise
+ * them.  Arguments, outputs and errors as bsa_select_tiling, plus
+ * INVALID_ARG when B*H*n_tiles*maxNb exceeds BSA_NOALLOC_TILE_VALUES and
+ * BSA_ERR_DEVICE when the array's address cannot be found. */
+#define BSA_NOALLOC_TILE_VALUES (1 << 20)
+int bsa_select_tiling_noalloc(const void* q, int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
+                              int64_t D, const int32_t* tiles_host, int n_tiles, float* score,
+                              int32_t* choice, bsa_stream_t stream);
+
 /* bsa_select_tiling with a choice of statistic and padded candidates.
  * statistic BSA_STAT_MEAN is bsa_select_tiling's rule; BSA_STAT_POOLED is
  * SPADE's engine rule [Adaptive tiling (SPADE), "Deviations and notes",
