@@ -67,45 +67,75 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(q, k, v, wl, block, kk, budget_s=12.0):
-    """Time the oracle on head 0: its own tiling choice, scores, top-k, then the
-    dense-definition attention rows of consecutive query blocks (512 rows per
-    call) until about `budget_s` seconds of attention work are done."""
+def host_description() -> dict:
+    """The host the CPU oracle runs on: logical CPUs, CPU model and numpy's BLAS."""
+    import subprocess
+
     import numpy as np
     from threadpoolctl import threadpool_info
+
+    model = ""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        model = next((ln.split(":", 1)[1].strip() for ln in out.splitlines() if ln.startswith("Model name")), "")
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if not model:
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+        except OSError:
+            pass
+    blas = np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {})
+    pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {
+        "cpu_count": os.cpu_count(),
+        "cpu_model": model or "unknown",
+        "blas": f"{blas.get('name', '?')} {blas.get('version', '')}".strip(),
+        "blas_threads": max([i.get("num_threads", 1) for i in pools] or [1]),
+    }
+
+
+def cpu_baseline(q, k, v, wl, block, kk, budget_s=12.0):
+    """Time the oracle, untuned, on whole heads of the same inputs: per head its tiling choice, permutation,
+    min/max scores and top-k, then every output row in the oracle's gathered kept-block form (the same
+    float64 math as the dense masked definition: masked keys contribute exact zeros).  Heads are taken in
+    order until about `budget_s` seconds have passed (at least one head)."""
+    import numpy as np
 
     from block_sparse_attention_permute_amd import synth
     from oracle import attention as OA
     from oracle import blocks as OB
     from oracle import tiling as OT
 
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    t0 = time.perf_counter()
-    qf, kf, vf = (synth.stored_to_f64(x[0, 0]) for x in (q, k, v))
-    choice, _ = OT.select_tiling(qf[None, None], wl.grid, TILES)
-    perm = OT.tile_permutation(wl.grid, TILES[int(choice[0, 0])])
-    qp, kp, vp = (OT.permute_tokens(x, perm) for x in (qf, kf, vf))
-    keep = OB.topk_block_mask(OB.minmax_block_scores(qp, kp, block), kk, 1, True)
-    t_pre = time.perf_counter() - t0
+    host = host_description()
     scale = wl.D ** -0.5
-    nb = wl.S // block
-    done, t_attn, per_call = 0, 0.0, 8
-    while done < nb and t_attn < budget_s:
-        rows = np.arange(done * block, min(nb, done + per_call) * block)
-        t1 = time.perf_counter()
-        OA.block_sparse_rows(qp, kp, vp, keep, block, rows, scale)
-        t_attn += time.perf_counter() - t1
-        done = min(nb, done + per_call)
-    flops = int(keep[:done].sum()) * 4 * block * block * wl.D
+    rows = np.arange(wl.S)
+    heads, flops, t_total = 0, 0, 0.0
+    while heads < wl.H and (heads == 0 or t_total < budget_s):
+        qf, kf, vf = (synth.stored_to_f64(x[0, heads]) for x in (q, k, v))
+        t0 = time.perf_counter()
+        choice, _ = OT.select_tiling(qf[None, None], wl.grid, TILES)
+        perm = OT.tile_permutation(wl.grid, TILES[int(choice[0, 0])])
+        qp, kp, vp = (OT.permute_tokens(x, perm) for x in (qf, kf, vf))
+        keep = OB.topk_block_mask(OB.minmax_block_scores(qp, kp, block), kk, 1, True)
+        OA.block_sparse_rows_gathered(qp, kp, vp, keep, block, rows, scale)
+        t_total += time.perf_counter() - t0
+        flops += int(keep.sum()) * 4 * block * block * wl.D
+        heads += 1
     return {
-        "value": flops / (t_pre * done / nb + t_attn) / 1e12,
+        "value": flops / t_total / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": host["blas_threads"],
         "kind": "oracle",
-        "sample": (f"head 0 of the same inputs: tiling choice, scores and top-k for the head "
-                   f"({t_pre:.1f} s, prorated to the sample), then the float64 dense-definition attention "
-                   f"rows of query blocks 0..{done - 1} ({done * block} rows, {t_attn:.1f} s); kept-block "
-                   f"FLOPs of those rows / time"),
+        "sample": (f"heads 0..{heads - 1} of {wl.H} of the same inputs, whole heads: tiling choice, scores, "
+                   f"top-k and all {wl.S} output rows in the gathered kept-block form (float64, {t_total:.1f} s; "
+                   f"kept-block FLOPs / time)"),
+        "wall_s": round(t_total, 2),
+        "wall_s_per_call_est": round(t_total / heads * wl.H, 1),
+        "cpu_count": host["cpu_count"],
+        "cpu_model": host["cpu_model"],
+        "blas": host["blas"],
     }
 
 
@@ -137,14 +167,43 @@ def _time(torch, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def oracle_wall(fn, units, total_units):
+    """Run fn(u) for u in units; -> (wall s of the sample, the same scaled to total_units)."""
+    t0 = time.perf_counter()
+    for u in units:
+        fn(u)
+    dt = time.perf_counter() - t0
+    return round(dt, 3), round(dt * total_units / max(len(units), 1), 2)
+
+
 def sweep(args, torch, np, bsa, synth):
     """Kernel timings on the sliding-tile, windowed and long-sequence workloads."""
     dev = torch.device("cuda:0")
     steps, warmup = max(args.steps // 5, 5), max(args.warmup, 2)
 
+    from oracle import attention as OA
+    from oracle import blocks as OB
+    from oracle import pipeline as OP
+    from oracle import tiling as OT
+
+    host = host_description()
+    print(json.dumps({"host": host}), flush=True)
+
+    # tiny windowed fp32: H=2, grid 2x4x4, D=16, window 8, sink 2, scale 1/4
+    wl = synth.WORKLOADS[1]
+    qb, kb, vb = synth.qkv(1)
+    q, k, v = (synth.to_torch(x, dev) for x in (qb, kb, vb))
+    out = torch.empty_like(q)
+    ms = _time(torch, lambda: bsa.bsa_windowed_attention(q, k, v, 8, 2, 0.25, 8, out=out), steps, warmup)
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (qb, kb, vb))
+    wall, _ = oracle_wall(lambda _: OA.windowed_attention(qf, kf, vf, 8, 2, scale=0.25, chunk=8), [0], 1)
+    print(json.dumps({"workload": wl.name, "attention_ms": round(ms, 4), "oracle_wall_s": wall,
+                      "oracle_sample": "the whole call (dense masked float64)"}), flush=True)
+
     # sliding tile: grid 8x16x16, tiles 2x4x4 (block 32), 3x3x3 neighbourhood, D=64, H=8
     wl = synth.WORKLOADS[2]
-    q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(2))
+    qb, kb, vb = synth.qkv(2)
+    q, k, v = (synth.to_torch(x, dev) for x in (qb, kb, vb))
     tile = [(2, 4, 4)]
     idx, cnt = bsa.bsa_sliding_tile_block_list((4, 4, 4))
     kv_idx = torch.from_numpy(np.broadcast_to(idx, (1, wl.H) + idx.shape).copy()).to(dev)
@@ -160,12 +219,19 @@ def sweep(args, torch, np, bsa, synth):
         bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 32, out=out)
         bsa.bsa_invert_permute(out, wl.grid, tile)
     ms_step = _time(torch, step2, steps, warmup)
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (qb, kb, vb))
+    keep, labels = OT.sliding_tile_keep((4, 4, 4)), OT.tile_labels(wl.grid, tile[0])
+    wall, _ = oracle_wall(lambda h: OP.label_mask_attention(qf[0, h], kf[0, h], vf[0, h], labels, keep, wl.D ** -0.5),
+                          range(wl.H), wl.H)
     print(json.dumps({"workload": wl.name, "attention_ms": round(ms, 4), "attention_tflops": round(fl / ms / 1e9, 2),
-                      "step_ms": round(ms_step, 4), "kept_block_flops": fl}), flush=True)
+                      "step_ms": round(ms_step, 4), "kept_block_flops": fl, "oracle_wall_s": wall,
+                      "oracle_sample": "the whole call, all 8 heads (dense masked float64, T-major label form)"}),
+          flush=True)
 
     # windowed: S=16384, window 2048 (half 1024), sink 64, D=128, H=24
     wl = synth.WORKLOADS[3]
-    q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(3))
+    qb, kb, vb = synth.qkv(3)
+    q, k, v = (synth.to_torch(x, dev) for x in (qb, kb, vb))
     out = torch.empty_like(q)
     ms = _time(torch, lambda: bsa.bsa_windowed_attention(q, k, v, 2048, 64, 128 ** -0.5, 512, out=out), steps, warmup)
     S, half, sink = wl.S, 1024, 64
@@ -174,8 +240,13 @@ def sweep(args, torch, np, bsa, synth):
     extra = np.maximum(0, np.minimum(sink, np.maximum(0, i - half)))      # sinks left of the window
     pairs = int((local + extra).sum())
     fl_tok = pairs * 4 * wl.D * wl.H
+    qf, kf, vf = (synth.stored_to_f64(x[0, 0]) for x in (qb, kb, vb))
+    wall, full = oracle_wall(lambda _: OA.window_rows_gathered(qf, kf, vf, np.arange(S), 2048, 64, 128 ** -0.5),
+                             [0], wl.H)
     print(json.dumps({"workload": wl.name, "attention_ms": round(ms, 4),
-                      "attention_tflops_token_exact": round(fl_tok / ms / 1e9, 2), "visible_pairs_per_head": pairs}),
+                      "attention_tflops_token_exact": round(fl_tok / ms / 1e9, 2), "visible_pairs_per_head": pairs,
+                      "oracle_wall_s": wall, "oracle_wall_s_per_call_est": full,
+                      "oracle_sample": "head 0, every row (window-slice form, float64), scaled to 24 heads"}),
           flush=True)
 
     # Wan shape variants: SPADE's static widths, top-p, the pooled statistic, padded (16, 2, 2),
@@ -212,16 +283,32 @@ def sweep(args, torch, np, bsa, synth):
 
     # long sequence: grid 32x48x80 (S=122880), tiles 4x4x4, 10% budget, D=128, H=24
     wl = synth.WORKLOADS[5]
-    q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(5))
+    qb, kb, vb = synth.qkv(5)
+    q, k, v = (synth.to_torch(x, dev) for x in (qb, kb, vb))
     pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, [(4, 4, 4)], 0.10, q.dtype, dev)
     out = torch.empty_like(q)
     ms_step = _time(torch, lambda: pipe(q, k, v, out=out), max(steps // 2, 3), warmup)
     kv_idx, kv_cnt = pipe.kv
     ms = _time(torch, attention_call(bsa, pipe, q, k, v, out), max(steps // 2, 3), warmup)
     fl = int(kv_cnt.sum().item()) * 4 * 64 * 64 * wl.D
+    # the oracle on head 0: permutation, scores and top-k of the head, then 32 query blocks spread over it
+    qf, kf, vf = (synth.stored_to_f64(x[0, 0]) for x in (qb, kb, vb))
+    nb = wl.S // 64
+    t0 = time.perf_counter()
+    perm = OT.tile_permutation(wl.grid, (4, 4, 4))
+    qp, kp, vp = (OT.permute_tokens(x, perm) for x in (qf, kf, vf))
+    keep = OB.topk_block_mask(OB.minmax_block_scores(qp, kp, 64), OB.budget(0.10, nb), 1, True)
+    t_pre = time.perf_counter() - t0
+    blocks = np.linspace(0, nb - 1, 32).astype(int)
+    wall, full = oracle_wall(lambda I: OA.block_sparse_rows_gathered(qp, kp, vp, keep, 64, np.arange(64 * I, 64 * I + 64),
+                                                                     wl.D ** -0.5), blocks, nb)
     print(json.dumps({"workload": wl.name, "attention_ms": round(ms, 4), "attention_tflops": round(fl / ms / 1e9, 2),
                       "step_ms": round(ms_step, 4), "step_tflops": round(fl / ms_step / 1e9, 2),
-                      "kept_block_flops": fl}), flush=True)
+                      "kept_block_flops": fl, "oracle_wall_s": round(t_pre + wall, 3),
+                      "oracle_wall_s_per_call_est": round((t_pre + full) * wl.H, 1),
+                      "oracle_sample": (f"head 0: scores and top-k ({t_pre:.1f} s), then 32 of {nb} query blocks in "
+                                        f"the gathered kept-block form; scaled to all blocks and 24 heads")}),
+          flush=True)
 
 
 def main():
