@@ -273,11 +273,14 @@ def sweep(args, torch, np, bsa, synth):
                           "step_ms": round(ms_step, 4), "step_tflops": round(fl / ms_step / 1e9, 2),
                           "kept_blocks": kept, "heads_per_candidate": choice}), flush=True)
     S, HW = wl.S, wl.grid[1] * wl.grid[2]
-    for kind, pairs in (("spatial", S * HW), ("temporal", S * wl.grid[0])):
-        att = bsa.VideoLabelAttention(1, wl.H, wl.grid, kind, dev)
+    for kind, pairs, direct in (("spatial", S * HW, True), ("temporal", S * wl.grid[0], True),
+                                ("temporal", S * wl.grid[0], False)):
+        att = bsa.VideoLabelAttention(1, wl.H, wl.grid, kind, dev, dtype=q.dtype if direct else None, D=wl.D)
         ms = _time(torch, lambda: att(q, k, v, out=out), max(steps // 2, 3), warmup)
         fl_tok = pairs * 4 * wl.D * wl.H
-        print(json.dumps({"workload": f"wan {kind}-only attention (permute + label attention + inverse)",
+        how = ("label attention on T-major tokens" if kind == "spatial" else
+               "frames gathered on load" if direct else "permute + label attention + inverse")
+        print(json.dumps({"workload": f"wan {kind}-only attention ({how})",
                           "ms": round(ms, 4), "tflops_token_exact": round(fl_tok / ms / 1e9, 2),
                           "visible_pairs_per_head": pairs}), flush=True)
 
@@ -311,6 +314,29 @@ def sweep(args, torch, np, bsa, synth):
           flush=True)
 
 
+def kernel_only(args, torch, bsa, synth):
+    """The hot kernel of one workload alone, --warmup + --steps calls, one line of timing (for profilers)."""
+    cfg = args.kernel_only
+    wl = synth.WORKLOADS[cfg]
+    dev = torch.device("cuda:0")
+    log(f"generating inputs: {wl.name}")
+    q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(cfg))
+    out = torch.empty_like(q)
+    if cfg == 3:
+        def call():
+            bsa.bsa_windowed_attention(q, k, v, 2048, 64, 128 ** -0.5, 512, out=out)
+        name = "attn_solo_kernel<window, positive scale>"
+    else:
+        tiles, frac = (TILES, FRAC) if cfg == 4 else ([(4, 4, 4)], 0.10)
+        pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, tiles, frac, q.dtype, dev)
+        pipe(q, k, v, out=out)
+        call = attention_call(bsa, pipe, q, k, v, out)
+        name = "attn_solo_kernel<block list, positive scale, gather on load, key-norm bound>"
+    ms = _time(torch, call, max(args.steps, 1), args.warmup)
+    print(json.dumps({"kernel_only": wl.name, "kernel": name, "calls": args.warmup + max(args.steps, 1),
+                      "ms_per_call": round(ms, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,6 +346,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line, time the hot-path kernels on the other workloads "
                          "(sliding tile, windowed, long sequence) and print one JSON line per workload")
+    ap.add_argument("--kernel-only", type=int, choices=(3, 4, 5), default=None,
+                    help="only run the hot kernel of one workload (3: windowed attention; 4, 5: block-sparse attention "
+                         "on the pipeline's lists) --warmup + --steps times, for profilers")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -348,6 +377,10 @@ def main():
 
     if args.sweep:
         sweep(args, torch, np, bsa, synth)
+        return
+
+    if args.kernel_only is not None:
+        kernel_only(args, torch, bsa, synth)
         return
 
     wl = synth.WORKLOADS[CFG]

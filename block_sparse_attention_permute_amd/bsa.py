@@ -36,7 +36,7 @@ EXPORTED = (
     "bsa_minmax_block_scores_masked", "bsa_topk_block_mask_tiled", "bsa_block_sparse_attention_labels",
     "bsa_minmax_block_scores_tiled", "bsa_block_sparse_attention_tiled",
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices", "bsa_video_labels",
-    "bsa_select_tiling_noalloc",
+    "bsa_select_tiling_noalloc", "bsa_temporal_only_attention",
 )
 
 
@@ -64,6 +64,7 @@ _SIGS = {
     "bsa_top_p_block_mask": (_I, [_P, _I64, _I64, _I, _I, _F, _F, _I, _I, _P, _P, _I, _P, _P]),
     "bsa_block_sparse_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _F, _P, _P]),
     "bsa_windowed_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _P]),
+    "bsa_temporal_only_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _F, _P]),
     "bsa_validate_block_list": (_I, [_P, _P, _I64, _I64, _I, _I, _I, _P]),
     "bsa_validate_indices": (_I, [_P, _I64, _I, _I, _P]),
     "bsa_padded_length": (_I64, [_I, _I, _I, _I, _I, _I]),
@@ -656,6 +657,20 @@ def bsa_windowed_attention(q, k, v, window: int, sink: int = 0, scale=None, chun
     return o
 
 
+def bsa_temporal_only_attention(q, k, v, grid, scale=None, out=None):
+    """Temporal-only attention of T-major (B, H, S, D) tensors: token i sees token j exactly when they sit
+    at one (y, x).  UnsupportedError outside bf16, D in {64, 128}, T <= 64."""
+    torch = _torch()
+    B, H, S, D = _qkv(q, k, v)
+    T, Hg, Wg = (int(g) for g in grid)
+    if T * Hg * Wg != S:
+        raise ValueError(f"grid {tuple(grid)} does not match S={S}")
+    o = torch.empty_like(q) if out is None else out
+    _check(lib().bsa_temporal_only_attention(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+                                             _dtype_code(q), B, H, T, Hg, Wg, D, _scale(scale), _stream(q)))
+    return o
+
+
 def bsa_validate_block_list(kv_idx, kv_cnt, Nk: int) -> None:
     """Synchronous: RuntimeError unless every row is a non-empty ascending list inside [0, Nk)."""
     B, H, Nq, max_kept = (int(s) for s in kv_idx.shape)
@@ -815,21 +830,26 @@ class VideoLabelAttention:
 
     kind "spatial": a token sees the tokens of its own frame (labels = frame
     index, T-major order, block lists of the frames' blocks).  kind
-    "temporal": a token sees the tokens at its own (y, x) in every frame; the
-    tokens are permuted with tiles (T, 1, 1) so that each position's frames
-    are contiguous, labelled by position, attended, and permuted back.
-    [ADR-0001, "Décision" step 1: spatial_only_mask, temporal_only_mask.]
-    Block lists and labels are built once (host, then copied to the device);
-    a call is a sequence of libbsa launches on the current stream.
+    "temporal": a token sees the tokens at its own (y, x) in every frame.
+    With bf16, D in {64, 128} and T <= 64 (``dtype``, ``D`` given) that is one
+    bsa_temporal_only_attention call, which gathers each position's frames
+    on load; otherwise the tokens are permuted with tiles (T, 1, 1) so that
+    each position's frames are contiguous, labelled by position, attended,
+    and permuted back.  [ADR-0001, "Décision" step 1: spatial_only_mask,
+    temporal_only_mask.]  Block lists and labels are built once (host, then
+    copied to the device); a call is a sequence of libbsa launches on the
+    current stream.
     """
 
-    def __init__(self, B, H, grid, kind: str, device, block: int = 64):
+    def __init__(self, B, H, grid, kind: str, device, block: int = 64, dtype=None, D: int = 128):
         torch = _torch()
         self.grid = tuple(int(g) for g in grid)
         T, Hg, Wg = self.grid
         S = T * Hg * Wg
         lab = bsa_video_labels(self.grid, kind)
         self.tiles = [(T, 1, 1)] if kind == "temporal" else None
+        # temporal-only: one call that gathers each position's frames on load, where it has a kernel
+        self.direct = kind == "temporal" and dtype == _torch().bfloat16 and int(D) in (64, 128) and T <= 64
         if S % block:
             raise ValueError(f"block {block} must divide S={S}")
         self.kind, self.block, self.S = kind, int(block), S
@@ -840,6 +860,8 @@ class VideoLabelAttention:
         self.labels = torch.from_numpy(lab).to(device)
 
     def __call__(self, q, k, v, scale=None, out=None):
+        if self.tiles is not None and self.direct:
+            return bsa_temporal_only_attention(q, k, v, self.grid, scale, out=out)
         if self.tiles is None:
             return bsa_block_sparse_attention_labels(q, k, v, self.kv_idx, self.kv_cnt, self.block, self.labels, scale,
                                                      out=out)
@@ -850,5 +872,5 @@ class VideoLabelAttention:
 
 def video_label_attention(q, k, v, grid, kind: str, block: int = 64, scale=None, out=None):
     """One-shot VideoLabelAttention (builds the block lists on every call)."""
-    B, H, _, _ = _bhsd(q, "q")
-    return VideoLabelAttention(B, H, grid, kind, q.device, block)(q, k, v, scale, out)
+    B, H, _, D = _bhsd(q, "q")
+    return VideoLabelAttention(B, H, grid, kind, q.device, block, q.dtype, D)(q, k, v, scale, out)

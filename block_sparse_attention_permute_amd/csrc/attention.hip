@@ -63,9 +63,11 @@ constexpr int kLgkmcnt0 = 0xC07F;         // all LDS / scalar-memory ops
 static_assert(kVmcnt16 == 0x4F70, "vmcnt(16) encoding");
 
 // kLabels: a block list plus the token rule labels[i] == labels[j] inside
-// the kept blocks (padding of a padded tiling, spatial-only and
-// temporal-only attention).
-enum Mode { kBlockList = 0, kWindow = 1, kLabels = 2 };
+// the kept blocks (padding of a padded tiling, spatial-only attention).
+// kGroups: temporal-only attention of T-major tensors; a query tile holds the
+// T frames of G = 64 / T spatial positions, read straight from T-major
+// memory, and attends to itself under the rule "same position".
+enum Mode { kBlockList = 0, kWindow = 1, kLabels = 2, kGroups = 3 };
 
 struct AttnParams {
     const uint16_t* q;
@@ -91,6 +93,8 @@ struct AttnParams {
     // of a head is tile J of the head's tiling
     const int32_t* head_choice;
     uint32_t n_tiles, Hg, Wg;
+    // groups: T frames per position, G positions per tile, HW positions per frame
+    uint32_t grp_T, grp_G, grp_HW;
     TileGeo geo[BSA_MAX_TILINGS];
     int32_t voff[BSA_MAX_TILINGS][16];  // byte offset of cells 4q..4q+3 from the tile origin
 };
@@ -200,6 +204,8 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         const size_t row = (size_t)bh * P.nq + I;
         n_iter = min(kv_cnt[row], (int)P.max_kept);
         list = kv_idx + row * P.max_kept;
+    } else if (MODE == kGroups) {
+        n_iter = 1;
     } else {
         n_sink_tiles = (P.sink + BLK - 1) / BLK;
         const int lo = max(0, q0 - P.half);
@@ -211,13 +217,28 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
     // tile index of iteration `it` (wave-uniform: it feeds scalar buffer offsets)
     auto tile_at = [&](int it) -> int {
         if (MODE == kBlockList) return __builtin_amdgcn_readfirstlane(list[it]);
+        if (MODE == kGroups) return (int)I;
         return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
+    };
+    // kGroups: tile row r (r < G*T) is frame r % T of position I*G + r / T, at
+    // T-major row (r % T) * HW + position; other rows (and positions past the
+    // grid) are given an offset past the head, so buffer loads read zeros
+    const int oob = (int)head_bytes;
+    auto grp_row = [&](int r) -> int {  // T-major row of tile row r, or -1
+        const int g = r / (int)P.grp_T, f = r - g * (int)P.grp_T;
+        const int pos = (int)I * (int)P.grp_G + g;
+        return (g < (int)P.grp_G && pos < (int)P.grp_HW) ? f * (int)P.grp_HW + pos : -1;
+    };
+    auto row_bytes = [&](int r) -> int {  // byte offset of tile row r from the head
+        if (MODE != kGroups) return (q0 + r) * (D * 2);
+        const int t = grp_row(r);
+        return t >= 0 ? t * (D * 2) : oob;
     };
 
     // ---- Q fragment (B operand): row q0 + 32*wr + col, D cols 16*s + 8*half_id + 0..7
     bf16x8 qf[D / 16];
     {
-        const int voff = (q0 + 32 * wr + col) * (D * 2) + half_id * 16;
+        const int voff = row_bytes(32 * wr + col) + half_id * 16;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
             qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, voff + 32 * s, 0, 0));
@@ -253,7 +274,16 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
     // tile's global loads have two iterations to land before it is written to
     // LDS; LDS is double-buffered (tile it in stage it % 2).
     Staging<D, BLK> st[2];
-    if (n_iter > 0) {
+    if (MODE == kGroups) {  // one tile: the query tile's own rows, gathered
+#pragma unroll
+        for (int j = 0; j < C::CH; ++j) {
+            const int c = tid + C::NT * j;
+            const int voff = row_bytes(c / C::NCH) + (c % C::NCH) * 16;
+            st[0].k[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, voff, 0, 0);
+            st[0].v[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, 0, 0);
+        }
+        stage_store<D, BLK>(st[0], smem, tid);
+    } else if (n_iter > 0) {
         stage_load<D, BLK>(st[0], kr, vr, tile_at(0) * BLK, tid);
         stage_store<D, BLK>(st[0], smem, tid);
     }
@@ -261,8 +291,11 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
     // loop's only outstanding loads are the prefetched tiles': otherwise the
     // compiler's wait tracking makes each tile's QK^T wait for the prefetch.
     __builtin_amdgcn_s_waitcnt(0);
-    if (n_iter > 0) stage_load<D, BLK>(st[1], kr, vr, tile_at(min(1, n_iter - 1)) * BLK, tid);
+    if (MODE != kGroups && n_iter > 0) stage_load<D, BLK>(st[1], kr, vr, tile_at(min(1, n_iter - 1)) * BLK, tid);
     __syncthreads();
+    // kGroups: this lane's row group (-1: a padding row, which sees no key)
+    int my_grp = -1;
+    if (MODE == kGroups) my_grp = grp_row(32 * wr + col) >= 0 ? (32 * wr + col) / (int)P.grp_T : -1;
 
     // One key tile.  CUR (0 or 1) is the LDS stage holding tile `it` and the
     // register set that receives tile it + 2; it is a compile-time constant so
@@ -272,7 +305,7 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         // always issued (the last tile again past the end): a conditional load
         // would make the compiler's wait counts assume it was skipped and wait
         // for every outstanding load before the LDS store below
-        stage_load<D, BLK>(st[CUR], kr, vr, tile_at(min(it + 2, n_iter - 1)) * BLK, tid);
+        if (MODE != kGroups) stage_load<D, BLK>(st[CUR], kr, vr, tile_at(min(it + 2, n_iter - 1)) * BLK, tid);
         const char* stage = smem + CUR * C::STAGE;
 
         // S^T (32 keys x 32 query rows) = K Q^T over D
@@ -305,6 +338,14 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
                     const bool vis = (j < (int)P.S) & (((d <= P.half) & (-d <= P.half)) | (j < P.sink));
                     sacc[v] = vis ? sacc[v] : neg_inf;
                 }
+            }
+        }
+        if (MODE == kGroups) {  // same position: key row j of the tile is in group j / T
+            const float neg_inf = -__builtin_inff();
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int j = 32 * wk + 4 * half_id + 8 * (v / 4) + (v % 4);
+                sacc[v] = (j / (int)P.grp_T == my_grp) ? sacc[v] : neg_inf;
             }
         }
         float smax = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
@@ -349,7 +390,7 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
             }
         }
 
-        if (it + 1 < n_iter) stage_store<D, BLK>(st[1 - CUR], smem + (1 - CUR) * C::STAGE, tid);
+        if (MODE != kGroups && it + 1 < n_iter) stage_store<D, BLK>(st[1 - CUR], smem + (1 - CUR) * C::STAGE, tid);
         __syncthreads();
     };
     int it = 0;
@@ -387,9 +428,11 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         l_row = l_row * a1 + l2 * a2;
         m_used = mf;
     }
-    if (my_row >= (int)P.S) return;
+    int out_row = my_row;
+    if (MODE == kGroups) out_row = grp_row(32 * wr + col);
+    if (out_row < 0 || out_row >= (int)P.S) return;
     const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;  // a row that saw no key is written as zeros
-    uint16_t* orow = P.out + head + (size_t)my_row * D;
+    uint16_t* orow = P.out + head + (size_t)out_row * D;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -1193,5 +1236,40 @@ extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, co
     P.Hg = (uint32_t)Hg;
     P.Wg = (uint32_t)Wg;
     launch_solo<kBlockList, true>(P, (hipStream_t)stream);
+    return check_launch(name);
+}
+
+extern "C" int bsa_temporal_only_attention(const void* q, const void* k, const void* v, void* out, int dtype,
+                                           int64_t B, int64_t H, int T, int Hg, int Wg, int64_t D, float scale,
+                                           bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_temporal_only_attention";
+    BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
+    const int64_t S = (int64_t)T * Hg * Wg;
+    int rc = common_checks(q, k, v, out, dtype, B, H, S, D, name);
+    if (rc) return rc;
+    if (!(dtype == BSA_BF16 && (D == 64 || D == 128) && T <= 64))
+        BSA_FAIL(BSA_ERR_UNSUPPORTED,
+                 "%s: bf16 with D in {64, 128} and T <= 64 only (bsa_video_labels + bsa_block_sparse_attention_labels "
+                 "cover the rest)",
+                 name);
+    const int64_t hw = (int64_t)Hg * Wg, g = 64 / T, nq = (hw + g - 1) / g;
+    const int64_t nwg = B * H * nq;
+    BSA_REQUIRE(nwg < ((int64_t)1 << 31), "%s: too many tiles", name);
+    AttnParams P{};
+    P.q = static_cast<const uint16_t*>(q);
+    P.k = static_cast<const uint16_t*>(k);
+    P.v = static_cast<const uint16_t*>(v);
+    P.out = static_cast<uint16_t*>(out);
+    P.S = (uint32_t)S;
+    P.nq = (uint32_t)nq;
+    P.n_wg = (uint32_t)nwg;
+    P.xcd_remap = (nwg % 8 == 0) ? 1u : 0u;
+    P.scale_log2 = resolve_scale_log2(scale, D);
+    P.grp_T = (uint32_t)T;
+    P.grp_G = (uint32_t)g;
+    P.grp_HW = (uint32_t)hw;
+    if (D == 128) launch_mfma<128, 64, kGroups>(P, (hipStream_t)stream);
+    else launch_mfma<64, 64, kGroups>(P, (hipStream_t)stream);
     return check_launch(name);
 }

@@ -420,6 +420,20 @@ int bsa_block_sparse_attention_labels(const void* q, const void* k, const void* 
                                       int64_t label_head_stride, float scale,
                                       bsa_stream_t stream);
 
+/* Temporal-only attention of T-major q, k, v, out [ADR-0001, "Décision"
+ * step 1: temporal_only_mask; reading: token i sees token j exactly when
+ * both sit at one spatial position (y, x), i.e. the same position in every
+ * frame].  Equals bsa_block_sparse_attention_labels on the tiling (T, 1, 1)
+ * with BSA_LABEL_TEMPORAL labels and their block lists, followed by the
+ * inverse permutation, without forming a permuted copy: each 64-row tile
+ * holds the T frames of 64 / T positions, gathered from T-major memory.
+ * Scale as bsa_block_sparse_attention; out has q's shape and dtype.
+ * UNSUPPORTED unless bf16 with D in {64, 128} and T <= 64 (the label call
+ * covers the rest); INVALID_ARG on bad sizes. */
+int bsa_temporal_only_attention(const void* q, const void* k, const void* v, void* out, int dtype,
+                                int64_t B, int64_t H, int T, int Hg, int Wg, int64_t D, float scale,
+                                bsa_stream_t stream);
+
 /* Symmetric sliding-window attention with sinks: query i sees key j when
  * abs(i - j) <= window/2 (integer division) or j < sink
  * [FastVideo windowed_attention.py, module docstring "Window policy" and

@@ -143,6 +143,22 @@ def label_equal_attention(q_head, k_head, v_head, labels, scale: float, keep_hea
     return attention.masked_attention(q_head, k_head, v_head, mask, scale)
 
 
+def label_rows_gathered(q_head, k_head, v_head, labels, rows, scale: float):
+    """Rows ``rows`` of :func:`label_equal_attention` (no block mask), over the keys of their own label.
+
+    The same result as the dense form: a key of another label adds exact
+    zeros.  Rows are taken one label at a time, against that label's keys.
+    """
+    labels = np.asarray(labels)
+    rows = np.asarray(rows)
+    out = np.empty((rows.size, q_head.shape[1]))
+    for lab in np.unique(labels[rows]):
+        sel = np.flatnonzero(labels[rows] == lab)
+        keys = np.flatnonzero(labels == lab)
+        out[sel] = attention.masked_attention(q_head[rows[sel]], k_head[keys], v_head[keys], 0.0, scale)
+    return out
+
+
 def label_block_keep(labels, block: int) -> np.ndarray:
     """Block mask keeping (I, J) exactly when blocks I and J share some label (brute force)."""
     labels = np.asarray(labels)

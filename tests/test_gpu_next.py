@@ -235,6 +235,65 @@ def test_spatial_temporal_attention_wan_shape(kind):
         assert max_abs(got[0, h], want) <= BF16_ATOL, h
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("grid,D,B", [((5, 4, 4), 128, 1), ((3, 6, 5), 64, 2), ((1, 8, 8), 128, 1),
+                                      ((64, 2, 2), 64, 1), ((7, 3, 5), 128, 1), ((20, 2, 5), 128, 2),
+                                      ((20, 4, 6), 64, 1)])
+def test_temporal_only_gathered_small(grid, D, B):
+    """bsa_temporal_only_attention (each position's frames gathered on load): every output against the
+    oracle's temporal-only mask, including partial last tiles (positions % (64 // T) != 0), T = 1 and T = 64,
+    and against the permute + label-attention + inverse path."""
+    torch = torch_gpu()
+    T, Hg, Wg = grid
+    S, H = T * Hg * Wg, 2
+    q, k, v = (synth.normal_bits((B, H, S, D), seed=860 + i + S + D) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    out = f64(bsa.bsa_temporal_only_attention(qg, kg, vg, grid))
+    mask = OA.temporal_only_mask(grid)
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (q, k, v))
+    for b in range(B):
+        for h in range(H):
+            want = OA.masked_attention(qf[b, h], kf[b, h], vf[b, h], mask, D ** -0.5)
+            assert max_abs(out[b, h], want) <= BF16_ATOL, (b, h)
+    if T == 1:                                   # one key per row: the output is v itself
+        assert np.array_equal(out, vf)
+    if S % 64 == 0:
+        ref = bsa.VideoLabelAttention(B, H, grid, "temporal", qg.device)   # no dtype: the permuted path
+        assert not ref.direct
+        assert max_abs(out, f64(ref(qg, kg, vg))) <= BF16_ATOL
+
+
+@pytest.mark.gpu
+def test_temporal_only_gathered_wan_shape_and_scales():
+    """Wan grid, 40 heads in one launch: every row of head 3 and sampled rows of two more against the
+    oracle (rows over the keys of their own position); explicit scales 0 and < 0; unsupported shapes."""
+    torch = torch_gpu()
+    q, k, v = synth.qkv(4)
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    T, Hg, Wg = WAN_GRID
+    S = T * Hg * Wg
+    pos = np.arange(S) % (Hg * Wg)
+    out = f64(bsa.bsa_temporal_only_attention(qg, kg, vg, WAN_GRID))
+    rng = np.random.default_rng(5)
+    for h, rows in ((3, np.arange(S)), (0, rng.integers(0, S, 300)), (39, rng.integers(0, S, 300))):
+        qf, kf, vf = (synth.stored_to_f64(x[0, h]) for x in (q, k, v))
+        want = OP.label_rows_gathered(qf, kf, vf, pos, rows, 128 ** -0.5)
+        assert max_abs(out[0, h, rows], want) <= BF16_ATOL, h
+    sub = [x[:, :2].contiguous() for x in (qg, kg, vg)]
+    for scale in (0.0, -0.05):
+        got = f64(bsa.bsa_temporal_only_attention(*sub, WAN_GRID, scale=scale))
+        rows = rng.integers(0, S, 200)
+        for h in range(2):
+            qf, kf, vf = (synth.stored_to_f64(x[0, h]) for x in (q, k, v))
+            want = OP.label_rows_gathered(qf, kf, vf, pos, rows, scale)
+            assert max_abs(got[0, h, rows], want) <= BF16_ATOL, (scale, h)
+    with pytest.raises(bsa.UnsupportedError):
+        bsa.bsa_temporal_only_attention(*(x.float() for x in sub), WAN_GRID)
+    x = torch.zeros((1, 1, 65 * 4, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bsa.UnsupportedError):
+        bsa.bsa_temporal_only_attention(x, x, x, (65, 2, 2))
+
+
 # ---------------------------------------------------------- padded recipe ---
 
 @pytest.mark.gpu

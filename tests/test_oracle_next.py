@@ -321,6 +321,23 @@ def test_temporal_only_is_attention_per_position():
         assert np.allclose(got[idx], OA.full_attention(q[idx][None, None], k[idx][None, None], v[idx][None, None], 0.5)[0, 0], atol=1e-12)
 
 
+def test_label_rows_gathered_matches_dense_label_rule():
+    grid = (5, 3, 4)
+    S = 60
+    r = _rng(41)
+    q, k, v = (r.standard_normal((S, 8)) for _ in range(3))
+    for labels in (np.arange(S) % 12, np.arange(S) // 12, r.integers(0, 4, S)):
+        want = OP.label_equal_attention(q, k, v, labels, 0.4)
+        rows = np.arange(S)
+        np.testing.assert_allclose(OP.label_rows_gathered(q, k, v, labels, rows, 0.4), want, atol=1e-12)
+        some = np.array([59, 3, 17, 17, 40])
+        np.testing.assert_allclose(OP.label_rows_gathered(q, k, v, labels, some, 0.4), want[some], atol=1e-12)
+    # temporal-only labels (position of a T-major token) give the oracle's temporal-only mask
+    pos = np.arange(S) % (grid[1] * grid[2])
+    want = OA.masked_attention(q, k, v, OA.temporal_only_mask(grid), 0.4)
+    np.testing.assert_allclose(OP.label_rows_gathered(q, k, v, pos, np.arange(S), 0.4), want, atol=1e-12)
+
+
 def test_label_block_list_covers_the_label_mask():
     grid = (5, 4, 4)
     T, Hg, Wg = grid
