@@ -143,9 +143,9 @@ def attention_call(bsa, pipe, q, k, v, out):
     """The pipeline's attention launch alone, on its current block lists."""
     kv_idx, kv_cnt = pipe.kv
     if pipe.fused:
-        return lambda: bsa.bsa_block_sparse_attention_tiled(q, k, v, pipe.grid, pipe.tiles, kv_idx, kv_cnt,
-                                                            head_choice=pipe.choice, scale=pipe.scale, out=out,
-                                                            key_norms=pipe.ws_knorm)
+        call = bsa.bsa_block_sparse_attention_tiled_padded if pipe.pad else bsa.bsa_block_sparse_attention_tiled
+        return lambda: call(q, k, v, pipe.grid, pipe.tiles, kv_idx, kv_cnt, head_choice=pipe.choice, scale=pipe.scale,
+                            out=out, key_norms=pipe.ws_knorm)
     if pipe.pad:
         return lambda: bsa.bsa_block_sparse_attention_labels(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, pipe.block,
                                                              pipe.labels, pipe.scale, out=pipe.op)
@@ -257,7 +257,10 @@ def sweep(args, torch, np, bsa, synth):
         ("wan sink 5 + band 40", dict(tiles=[(1, 8, 8), (4, 4, 4)], sink_blocks=5, keep_diag=40)),
         ("wan top-p 0.9 (scores / sqrt(D))", dict(tiles=[(1, 8, 8), (4, 4, 4)], top_p=0.9, p_scale=wl.D ** -0.5)),
         ("wan pooled statistic", dict(tiles=[(1, 8, 8), (4, 4, 4)], statistic="pooled")),
-        ("wan padded, candidates (1,8,8) (4,4,4) (16,2,2)", dict(tiles=[(1, 8, 8), (4, 4, 4), (16, 2, 2)], pad=True)),
+        ("wan padded, candidates (1,8,8) (4,4,4) (16,2,2), gather on load",
+         dict(tiles=[(1, 8, 8), (4, 4, 4), (16, 2, 2)], pad=True)),
+        ("wan padded, candidates (1,8,8) (4,4,4) (16,2,2), permuted copies and label kernel",
+         dict(tiles=[(1, 8, 8), (4, 4, 4), (16, 2, 2)], pad=True, fused=False)),
     ]
     out = torch.empty_like(q)
     for name, kw in variants:

@@ -36,7 +36,8 @@ EXPORTED = (
     "bsa_minmax_block_scores_masked", "bsa_topk_block_mask_tiled", "bsa_block_sparse_attention_labels",
     "bsa_minmax_block_scores_tiled", "bsa_block_sparse_attention_tiled",
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices", "bsa_video_labels",
-    "bsa_select_tiling_noalloc", "bsa_temporal_only_attention",
+    "bsa_select_tiling_noalloc", "bsa_temporal_only_attention", "bsa_block_sparse_attention_tiled_padded",
+    "bsa_tiled_attention_supported",
 )
 
 
@@ -82,6 +83,9 @@ _SIGS = {
                                            _P]),
     "bsa_block_sparse_attention_tiled": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
                                               _I, _F, _P, _P]),
+    "bsa_block_sparse_attention_tiled_padded": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P,
+                                                     _P, _P, _I, _F, _P, _P]),
+    "bsa_tiled_attention_supported": (_I, [_I, _I64, _I, _I, _I, _P, _I, _I]),
 }
 
 
@@ -587,11 +591,14 @@ def bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block: int, scale=None, 
     return o
 
 
-def tiled_attention_supported(dtype, D, tiles) -> bool:
-    """Whether bsa_block_sparse_attention_tiled has a kernel for these tilings."""
+def tiled_attention_supported(dtype, D, tiles, grid, pad: bool = False) -> bool:
+    """Whether bsa_block_sparse_attention_tiled (or, with pad, its _padded form) has a kernel for these tilings
+    of the grid (asked of libbsa, nothing launched)."""
     torch = _torch()
-    return (dtype == torch.bfloat16 and int(D) == 128 and
-            all(a * b * c == 64 and c % 4 == 0 for a, b, c in (tuple(int(v) for v in t) for t in tiles)))
+    T, Hg, Wg = (int(g) for g in grid)
+    arr, n = _tiles_arr(tiles)
+    code = BSA_BF16 if dtype == torch.bfloat16 else BSA_F32
+    return bool(lib().bsa_tiled_attention_supported(code, int(D), T, Hg, Wg, arr, n, int(bool(pad))))
 
 
 def bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_choice=None, scale=None, out=None,
@@ -615,6 +622,30 @@ def bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_
                                                   _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, hc, _dev(kv_idx),
                                                   _dev(kv_cnt), int(kv_idx.shape[3]), _scale(scale),
                                                   _norms_out(key_norms, B, H, S // 64, q), _stream(q)))
+    return o
+
+
+def bsa_block_sparse_attention_tiled_padded(q, k, v, grid, tiles, kv_idx, kv_cnt, head_choice=None, scale=None,
+                                            out=None, key_norms=None):
+    """bsa_block_sparse_attention_tiled on each head's zero-padded grid (candidates may leave T undivided):
+    kv lists over the largest padded block count Nq; padding keys are masked and padding rows not written."""
+    torch = _torch()
+    B, H, S, D = _qkv(q, k, v)
+    T, Hg, Wg = (int(g) for g in grid)
+    if T * Hg * Wg != S:
+        raise ValueError(f"grid {tuple(grid)} does not match S={S}")
+    arr, n = _tiles_arr(tiles)
+    nq = padded_rows(grid, tiles) // 64
+    if kv_idx.dtype != torch.int32 or kv_cnt.dtype != torch.int32 or kv_idx.dim() != 4:
+        raise ValueError("kv_idx must be int32 (B, H, Nq, max_kept) and kv_cnt int32 (B, H, Nq)")
+    if tuple(kv_idx.shape[:3]) != (B, H, nq) or tuple(kv_cnt.shape) != (B, H, nq):
+        raise ValueError(f"block lists do not match (B, H, {nq})")
+    o = torch.empty_like(q) if out is None else out
+    hc = None if head_choice is None else _dev(head_choice, "head_choice")
+    _check(lib().bsa_block_sparse_attention_tiled_padded(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
+                                                         _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, hc, _dev(kv_idx),
+                                                         _dev(kv_cnt), int(kv_idx.shape[3]), _scale(scale),
+                                                         _norms_out(key_norms, B, H, nq, q), _stream(q)))
     return o
 
 
@@ -698,14 +729,15 @@ class AdaptiveBlockSparse:
     the grid: every head works on the zero-padded grid of its own choice
     (padding left out of the cohesion and the summaries, masked as keys,
     dropped from the output), with the budget floor(frac * that grid's block
-    count).  ``fused`` (default: whenever the kernels cover the tilings,
-    bf16 D = 128 tiles of 64 tokens with an x extent that is a multiple of 4,
-    and no padding) reads q, k, v in place through the tile geometry for the
-    scores and the attention and writes the output in T-major order, so no
-    permuted copy is formed.  ``validate=True`` checks the device-resident
-    tiling choices and block lists (bsa_validate_indices,
-    bsa_validate_block_list) before the attention runs; each check
-    synchronises the stream and raises RuntimeError on a violation.
+    count.  ``fused`` (default: whenever the kernels cover the tilings, see
+    tiled_attention_supported) reads q, k, v in place through the tile
+    geometry for the attention (and, without padding, for the scores) and
+    writes the output in T-major order, so the attention needs no permuted
+    copy; with padding the scores still read padded permuted copies of q and
+    k.  ``validate=True`` checks the device-resident tiling choices and (without
+    padding) block lists (bsa_validate_indices, bsa_validate_block_list)
+    before the attention runs; each check synchronises the stream and raises
+    RuntimeError on a violation.
     """
 
     def __init__(self, B, H, grid, D, tiles, frac, dtype, device, sink_blocks=1, keep_diag=True, scale=None,
@@ -727,9 +759,9 @@ class AdaptiveBlockSparse:
         self.sink_blocks, self.keep_diag, self.scale = int(sink_blocks), _band(keep_diag), scale
         self.top_p, self.p_scale = top_p, float(p_scale)
         self.validate = bool(validate)
-        can_fuse = not self.pad and tiled_attention_supported(dtype, D, self.tiles)
+        can_fuse = tiled_attention_supported(dtype, D, self.tiles, self.grid, self.pad)
         if fused and not can_fuse:
-            raise ValueError("the fused path needs bf16, D = 128, tiles of 64 tokens with x extent % 4 == 0, no pad")
+            raise ValueError("the fused path needs bf16, D = 128 and tilings tiled_attention_supported accepts")
         self.fused = can_fuse if fused is None else bool(fused)
         if self.pad:
             self.nk_table = [bsa_padded_length(T, Hg, Wg, t) // self.block for t in self.tiles]
@@ -748,8 +780,11 @@ class AdaptiveBlockSparse:
         self.ws_select = (torch.empty((B, H, n, self.nb), dtype=torch.float32, **f),
                           torch.empty((B, H, n), dtype=torch.float32, **f),
                           torch.empty((B, H), dtype=torch.int32, **f))
-        if self.fused:
+        if self.fused and not self.pad:
             self.qp = self.kp = self.vp = self.op = None
+        elif self.fused:   # padded: q, k permuted for the scores only
+            self.qp, self.kp = (torch.empty((B, H, self.Sp, D), dtype=dtype, **f) for _ in range(2))
+            self.vp = self.op = None
         else:
             self.qp, self.kp, self.vp, self.op = (torch.empty((B, H, self.Sp, D), dtype=dtype, **f)
                                                   for _ in range(4))
@@ -760,10 +795,12 @@ class AdaptiveBlockSparse:
                         torch.empty((B, H, self.nb), dtype=torch.int32, **f), None)
         # each key block's largest row norm, written by the scores pass: the attention kernel skips the
         # running-max update of the key blocks it proves cannot pass it
-        self.ws_knorm = None if self.pad else torch.empty((B, H, self.nb), dtype=torch.float32, **f)
+        self.ws_knorm = (torch.empty((B, H, self.nb), dtype=torch.float32, **f) if self.fused or not self.pad
+                         else None)
         # fused path: the tiling choice pass also forms q's block summaries of every candidate, so the scores
         # pass reads only k
-        self.ws_qsumm = (torch.empty((n, 2, B, H, self.nb, D), dtype=dtype, **f) if self.fused else None)
+        self.ws_qsumm = (torch.empty((n, 2, B, H, self.nb, D), dtype=dtype, **f) if self.fused and not self.pad
+                         else None)
 
     @property
     def choice(self):
@@ -779,9 +816,11 @@ class AdaptiveBlockSparse:
         if self.validate:
             bsa_validate_indices(choice, 0, len(self.tiles))
         if self.pad:
-            for src, dst, lab in ((q, self.qp, self.labels), (k, self.kp, None), (v, self.vp, None)):
+            srcs = ((q, self.qp, self.labels), (k, self.kp, None)) + (() if self.fused else ((v, self.vp, None),))
+            for src, dst, lab in srcs:
                 bsa_tile_permute_padded(src, self.grid, self.tiles, head_choice=choice, Sp=self.Sp, out=(dst, lab))
-            scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores, labels=self.labels)
+            scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores, labels=self.labels,
+                                                key_norms=self.ws_knorm)
             kv_idx, kv_cnt = bsa_topk_block_mask_tiled(scores, choice, self.k_table, self.nk_table, self.sink_blocks,
                                                        self.keep_diag, max_kept=self.max_kept, out=self.ws_topk)
         else:
@@ -800,13 +839,14 @@ class AdaptiveBlockSparse:
             else:
                 kv_idx, kv_cnt, _ = bsa_top_p_block_mask(scores, self.top_p, self.p_scale, self.sink_blocks,
                                                          self.keep_diag, return_mask=True, out=self.ws_topk)
-        if self.validate:
+        if self.validate and not self.pad:
             bsa_validate_block_list(kv_idx, kv_cnt, self.nb)
         if self.fused:
             if attention_hook is not None:
                 attention_hook(True)
-            o = bsa_block_sparse_attention_tiled(q, k, v, self.grid, self.tiles, kv_idx, kv_cnt, head_choice=choice,
-                                                 scale=self.scale, out=out, key_norms=self.ws_knorm)
+            call = bsa_block_sparse_attention_tiled_padded if self.pad else bsa_block_sparse_attention_tiled
+            o = call(q, k, v, self.grid, self.tiles, kv_idx, kv_cnt, head_choice=choice, scale=self.scale, out=out,
+                     key_norms=self.ws_knorm)
             if attention_hook is not None:
                 attention_hook(False)
             return o

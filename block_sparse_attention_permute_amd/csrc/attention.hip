@@ -38,6 +38,7 @@
 //    the same key blocks).
 #include "common.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace bsa {
@@ -96,7 +97,11 @@ struct AttnParams {
     // groups: T frames per position, G positions per tile, HW positions per frame
     uint32_t grp_T, grp_G, grp_HW;
     TileGeo geo[BSA_MAX_TILINGS];
-    int32_t voff[BSA_MAX_TILINGS][16];  // byte offset of cells 4q..4q+3 from the tile origin
+    int32_t voff[BSA_MAX_TILINGS][16];   // byte offset of cell 4q (a DMA row group) from the tile origin
+    int32_t rdelta[BSA_MAX_TILINGS][4];  // byte offsets of cells 4q + j from cell 4q (the same for every q)
+    // padded along T: frames of the grid, and each tiling's block count on its padded grid
+    uint32_t T;
+    uint32_t nbt[BSA_MAX_TILINGS];
 };
 
 template <int D, int BLK>
@@ -475,7 +480,11 @@ struct SoloCfg {
     static constexpr int TILE = BLK * D * 2;  // one V tile in LDS
 };
 
-template <int MODE, bool POS, bool TILED, bool BOUND = false>
+// PADT (gather on load): the tilings may pad the grid along T.  Cells of a
+// padding frame lie past the head, so their loads read zeros; their keys are
+// masked and their rows are not stored.  Blocks past the head's own block
+// count (the grid covers the largest) have no tile.
+template <int MODE, bool POS, bool TILED, bool BOUND = false, bool PADT = false>
 __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, const int32_t* __restrict__ kv_idx,
                                                           const int32_t* __restrict__ kv_cnt,
                                                           const float* __restrict__ knorm) {
@@ -503,6 +512,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         tc = (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[bh]);
         if (tc >= P.n_tiles) tc = 0;  // out-of-range choices are caught by bsa_validate_indices
     }
+    if (PADT && I >= P.nbt[tc]) return;
     const TileGeo& geo = P.geo[tc];
     const uint32_t q_origin = TILED ? tile_origin(I, geo, P.Hg, P.Wg) : (uint32_t)q0;
     int kcell[2];
@@ -510,6 +520,14 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     for (int c = 0; c < 2; ++c) kcell[c] = TILED ? (int)cell_offset(32 * c + col, geo, P.Hg, P.Wg) : 32 * c + col;
     auto tile_soff = [&](int t) -> int {  // byte offset of key tile t's first row
         return TILED ? (int)tile_origin((uint32_t)t, geo, P.Hg, P.Wg) * (D * 2) : t * BLK * (D * 2);
+    };
+    // PADT: key rows of tile t that are real cells, a prefix of the tile (cells are T-major inside it)
+    auto tile_keys = [&](int t) -> int {
+        if (!PADT) return BLK;
+        uint32_t tt, rem;
+        fdivmod((uint32_t)t, geo.f_ntyx, tt, rem);
+        const int left = (int)P.T - (int)(tt * geo.a);
+        return left >= (int)geo.a ? BLK : left * (int)(geo.b * geo.c);
     };
 
     int n_iter;
@@ -565,9 +583,11 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     // K tile straight into LDS with the K swizzle: instruction q fills rows
     // 4q..4q+3, lane l physical chunk l % 16 of row 4q + l / 16, which holds
     // logical chunk (l % 16) ^ (row % 8), row % 8 = 4(q % 2) + l / 16
+    // row lane / 16 of a DMA row group lies rrow bytes after the group's first row
+    const int rrow = TILED ? P.rdelta[tc][lane >> 4] : (lane >> 4) * (D * 2);
     int klane[2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) klane[p] = (lane >> 4) * (D * 2) + (((lane & 15) ^ (4 * p + (lane >> 4))) << 4);
+    for (int p = 0; p < 2; ++p) klane[p] = rrow + (((lane & 15) ^ (4 * p + (lane >> 4))) << 4);
     auto dma_k = [&](int soff) {
 #pragma unroll
         for (int q = 0; q < C::TILE / 1024; ++q)
@@ -578,7 +598,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     // instruction q fills LDS bytes [1024q, 1024q + 1024), i.e. rows 4q..4q+3,
     // lane l landing on physical chunk l % 16 of row 4q + l / 16, which holds
     // logical chunk (l % 16) ^ 2(row % 4) (the V swizzle); row % 4 = l / 16.
-    const int vlane = (lane >> 4) * (D * 2) + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
+    const int vlane = rrow + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
     auto dma_v = [&](char* buf, int soff, int q_lo, int q_hi) {
 #pragma unroll
         for (int q = q_lo; q < q_hi; ++q)
@@ -651,11 +671,12 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         q_uniform = __ballot((qlab[0] != q_uni) | (qlab[1] != q_uni)) == 0;
     }
 
-    int soff_cur = 0, v_nxt = 0;
+    int soff_cur = 0, v_nxt = 0, kval_cur = BLK;
     if (n_iter > 0) {
         const int t0 = tile_at(0);
         if (bounded) kn_cur = knorm_head[t0];
         soff_cur = tile_soff(t0);
+        kval_cur = tile_keys(t0);
         dma_k(soff_cur);
         if (MODE == kLabels) klab_next = labs[t0 * BLK + lane];
         v_nxt = tile_ahead(min(1, n_iter - 1));
@@ -709,6 +730,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         if (MODE == kLabels) klab = klab_next;
         v_nxt = tile_ahead(min(it + 2, n_iter - 1));
         const int soff_nxt = tile_soff(nxt_tile);
+        const int kval_nxt = tile_keys(nxt_tile);
         __builtin_amdgcn_s_waitcnt(kLgkmcnt0);  // this tile's K reads are complete
         dma_k(soff_nxt);
         if (MODE == kLabels) klab_next = labs[nxt + lane];
@@ -722,6 +744,18 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                 for (int r = 0; r < 2; ++r)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) sacc[c][r][v] *= P.scale_log2;
+        }
+        if (PADT && kval_cur < BLK) {  // padding keys of a tile at the end of the padded frames
+            const float neg_inf = -__builtin_inff();
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int j = 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4);
+                        sacc[c][r][v] = j < kval_cur ? sacc[c][r][v] : neg_inf;
+                    }
         }
         if (MODE == kWindow) {
             const int j0 = tile_at(it) * BLK;
@@ -860,6 +894,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
 #pragma unroll
         for (int r = 0; r < 2; ++r) l_part[r] += psum[r][0] + psum[r][1];
         soff_cur = soff_nxt;
+        kval_cur = kval_nxt;
     }
 
     // ---- write out (each lane pair holds one row; their partial sums add up)
@@ -981,14 +1016,14 @@ int launch_scalar(const ScalarParams& P, int dtype, int64_t D, hipStream_t st, c
     return check_launch(name);
 }
 
-template <int MODE, bool TILED = false>
+template <int MODE, bool TILED = false, bool PADT = false>
 void launch_solo(const AttnParams& P, hipStream_t st) {
     if (MODE == kBlockList && P.scale_log2 > 0.f && P.knorm != nullptr)
-        attn_solo_kernel<MODE, true, TILED, true><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, P.knorm);
+        attn_solo_kernel<MODE, true, TILED, true, PADT><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, P.knorm);
     else if (P.scale_log2 > 0.f)
-        attn_solo_kernel<MODE, true, TILED><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
+        attn_solo_kernel<MODE, true, TILED, false, PADT><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
     else
-        attn_solo_kernel<MODE, false, TILED><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
+        attn_solo_kernel<MODE, false, TILED, false, PADT><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
 }
 
 template <int D, int BLK, int MODE>
@@ -1182,19 +1217,42 @@ extern "C" int bsa_block_sparse_attention_labels(const void* q, const void* k, c
     return launch_scalar<kLabels>(P, dtype, D, st, name);
 }
 
-extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, const void* v, void* out, int dtype,
-                                                int64_t B, int64_t H, int T, int Hg, int Wg, int64_t D,
-                                                const int32_t* tiles_host, int n_tiles, const int32_t* head_choice,
-                                                const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
-                                                float scale, const float* key_norms_or_null,
-                                                bsa_stream_t stream) {
-    clear_error();
-    const char* name = "bsa_block_sparse_attention_tiled";
+namespace bsa {
+namespace {
+
+// Cell offsets of tiling i for the gather-on-load kernel: the T-major offset
+// of each DMA row group (cells 4q..4q+3) from the tile origin, and of a
+// group's four cells from its first.  A tiling qualifies when it has 64
+// cells and every group has the same four offsets (x extent a multiple of 4,
+// or smaller extents whose cells still pair up evenly, e.g. (16, 2, 2)).
+int fill_tile_rows(AttnParams& P, int i, int Hg, int Wg, int a, int b, int c, int64_t D, const char* name) {
+    if (a * b * c != 64)
+        BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: tiles of 64 tokens only (tile %d is %dx%dx%d)", name, i, a, b, c);
+    auto off = [&](int cell) -> int64_t {
+        const int rt = cell / (b * c), rem = cell % (b * c), ry = rem / c, rx = rem % c;
+        return ((int64_t)rt * Hg + ry) * Wg + rx;
+    };
+    for (int q = 0; q < 16; ++q) {
+        for (int j = 0; j < 4; ++j)
+            if (off(4 * q + j) - off(4 * q) != off(j) - off(0))
+                BSA_FAIL(BSA_ERR_UNSUPPORTED,
+                         "%s: tile %d (%dx%dx%d): its cells, taken four at a time, do not share one row pattern",
+                         name, i, a, b, c);
+        P.voff[i][q] = (int32_t)(off(4 * q) * D * 2);
+    }
+    for (int j = 0; j < 4; ++j) P.rdelta[i][j] = (int32_t)((off(j) - off(0)) * D * 2);
+    return BSA_OK;
+}
+
+int tiled_attention(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B, int64_t H, int T,
+                    int Hg, int Wg, int64_t D, const int32_t* tiles_host, int n_tiles, const int32_t* head_choice,
+                    const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept, float scale, const float* key_norms,
+                    bool pad, bsa_stream_t stream, const char* name) {
     BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
     const int64_t S = (int64_t)T * Hg * Wg;
     int rc = common_checks(q, k, v, out, dtype, B, H, S, D, name);
     if (rc) return rc;
-    rc = check_tiles(T, Hg, Wg, tiles_host, n_tiles);
+    rc = pad ? check_tiles_padded(T, Hg, Wg, tiles_host, n_tiles) : check_tiles(T, Hg, Wg, tiles_host, n_tiles);
     if (rc) return rc;
     BSA_REQUIRE(kv_idx && kv_cnt, "%s: NULL block list", name);
     BSA_REQUIRE(max_kept >= 1, "%s: max_kept must be >= 1", name);
@@ -1202,20 +1260,22 @@ extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, co
         BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: bf16 with D = 128 only (permute and use bsa_block_sparse_attention)",
                  name);
     AttnParams P{};
+    int64_t nq = 0, longest = S;
     for (int i = 0; i < BSA_MAX_TILINGS; ++i) {
         const int j = i < n_tiles ? i : 0;
         const int a = tiles_host[3 * j], b = tiles_host[3 * j + 1], c = tiles_host[3 * j + 2];
-        if (a * b * c != 64 || c % 4 != 0)
-            BSA_FAIL(BSA_ERR_UNSUPPORTED,
-                     "%s: tiles of 64 tokens with an x extent that is a multiple of 4 only (tile %d is %dx%dx%d)",
-                     name, j, a, b, c);
-        P.geo[i] = make_geo(Hg, Wg, a, b, c);
-        for (int qq = 0; qq < 16; ++qq) {
-            const int cell = 4 * qq, rt = cell / (b * c), ry = (cell % (b * c)) / c, rx = cell % c;
-            P.voff[i][qq] = (int32_t)((((int64_t)rt * Hg + ry) * Wg + rx) * D * 2);
-        }
+        if (pad && (Hg % b != 0 || Wg % c != 0))
+            BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: padding along T only (tile %d is %dx%dx%d on a %dx%dx%d grid)", name,
+                     j, a, b, c, T, Hg, Wg);
+        rc = fill_tile_rows(P, i, Hg, Wg, a, b, c, D, name);
+        if (rc) return rc;
+        P.geo[i] = pad ? make_geo_padded(Hg, Wg, a, b, c) : make_geo(Hg, Wg, a, b, c);
+        const int64_t len = padded_length(T, Hg, Wg, a, b, c);
+        P.nbt[i] = (uint32_t)(len / 64);
+        nq = std::max<int64_t>(nq, len / 64);
+        longest = std::max<int64_t>(longest, len);
     }
-    const int64_t nq = S / 64;
+    BSA_REQUIRE(longest * D * 2 < ((int64_t)1 << 31), "%s: the padded head must stay under 2 GiB", name);
     const int64_t nwg = B * H * nq;
     BSA_REQUIRE(nwg < ((int64_t)1 << 31), "%s: too many blocks", name);
     P.q = static_cast<const uint16_t*>(q);
@@ -1223,6 +1283,7 @@ extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, co
     P.v = static_cast<const uint16_t*>(v);
     P.out = static_cast<uint16_t*>(out);
     P.S = (uint32_t)S;
+    P.T = (uint32_t)T;
     P.nq = (uint32_t)nq;
     P.n_wg = (uint32_t)nwg;
     P.xcd_remap = (nwg % 8 == 0) ? 1u : 0u;
@@ -1230,13 +1291,57 @@ extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, co
     P.kv_idx = kv_idx;
     P.kv_cnt = kv_cnt;
     P.max_kept = (uint32_t)max_kept;
-    P.knorm = key_norms_or_null;
+    P.knorm = key_norms;
     P.head_choice = head_choice;
     P.n_tiles = (uint32_t)n_tiles;
     P.Hg = (uint32_t)Hg;
     P.Wg = (uint32_t)Wg;
-    launch_solo<kBlockList, true>(P, (hipStream_t)stream);
+    if (pad) launch_solo<kBlockList, true, true>(P, (hipStream_t)stream);
+    else launch_solo<kBlockList, true>(P, (hipStream_t)stream);
     return check_launch(name);
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, const void* v, void* out, int dtype,
+                                                int64_t B, int64_t H, int T, int Hg, int Wg, int64_t D,
+                                                const int32_t* tiles_host, int n_tiles, const int32_t* head_choice,
+                                                const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
+                                                float scale, const float* key_norms_or_null,
+                                                bsa_stream_t stream) {
+    clear_error();
+    return tiled_attention(q, k, v, out, dtype, B, H, T, Hg, Wg, D, tiles_host, n_tiles, head_choice, kv_idx, kv_cnt,
+                           max_kept, scale, key_norms_or_null, false, stream, "bsa_block_sparse_attention_tiled");
+}
+
+extern "C" int bsa_block_sparse_attention_tiled_padded(const void* q, const void* k, const void* v, void* out,
+                                                       int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
+                                                       int64_t D, const int32_t* tiles_host, int n_tiles,
+                                                       const int32_t* head_choice, const int32_t* kv_idx,
+                                                       const int32_t* kv_cnt, int max_kept, float scale,
+                                                       const float* key_norms_or_null, bsa_stream_t stream) {
+    clear_error();
+    return tiled_attention(q, k, v, out, dtype, B, H, T, Hg, Wg, D, tiles_host, n_tiles, head_choice, kv_idx, kv_cnt,
+                           max_kept, scale, key_norms_or_null, true, stream, "bsa_block_sparse_attention_tiled_padded");
+}
+
+extern "C" int bsa_tiled_attention_supported(int dtype, int64_t D, int T, int Hg, int Wg, const int32_t* tiles_host,
+                                             int n_tiles, int pad) {
+    clear_error();
+    const char* name = "bsa_tiled_attention_supported";
+    if (!(dtype == BSA_BF16 && D == 128) || T <= 0 || Hg <= 0 || Wg <= 0) return 0;
+    if ((pad ? check_tiles_padded(T, Hg, Wg, tiles_host, n_tiles) : check_tiles(T, Hg, Wg, tiles_host, n_tiles)) !=
+        BSA_OK)
+        return 0;
+    AttnParams P{};
+    for (int i = 0; i < n_tiles; ++i) {
+        const int a = tiles_host[3 * i], b = tiles_host[3 * i + 1], c = tiles_host[3 * i + 2];
+        if (pad && (Hg % b != 0 || Wg % c != 0)) return 0;
+        if (fill_tile_rows(P, i, Hg, Wg, a, b, c, D, name) != BSA_OK) return 0;
+    }
+    clear_error();
+    return 1;
 }
 
 extern "C" int bsa_temporal_only_attention(const void* q, const void* k, const void* v, void* out, int dtype,

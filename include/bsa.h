@@ -392,15 +392,41 @@ int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void
  * key_norms_or_null (per tile, as bsa_minmax_block_scores_tiled writes them)
  * as in bsa_block_sparse_attention with S/64 blocks per head.
  * UNSUPPORTED unless dtype is bf16, D = 128 and every candidate has 64
- * tokens with an x extent c that is a multiple of 4 (4 consecutive T-major
- * tokens per LDS-DMA row group); INVALID_ARG if a candidate does not divide
- * the grid. */
+ * cells that, taken four at a time in tile order, all sit at the same four
+ * T-major offsets from the group's first cell (one row pattern per LDS-DMA
+ * row group): an x extent that is a multiple of 4, or e.g. (16, 2, 2),
+ * (8, 8, 1); bsa_tiled_attention_supported answers on the host.
+ * INVALID_ARG if a candidate does not divide the grid. */
 int bsa_block_sparse_attention_tiled(const void* q, const void* k, const void* v, void* out,
                                      int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
                                      int64_t D, const int32_t* tiles_host, int n_tiles,
                                      const int32_t* head_choice, const int32_t* kv_idx,
                                      const int32_t* kv_cnt, int max_kept, float scale,
                                      const float* key_norms_or_null, bsa_stream_t stream);
+
+/* bsa_block_sparse_attention_tiled on the zero-padded grids of candidates
+ * that do not divide T [Adaptive tiling (SPADE), "Deviations and notes": pad
+ * the grid with zero tokens, mask the padded keys].  Each head works on the
+ * padded grid of its own candidate (tiles numbered T-major over it, as
+ * bsa_tile_permutation_padded): cells of a padding frame read as zeros, are
+ * masked as keys and are not written as rows, so the result equals
+ * bsa_tile_permute_padded -> bsa_block_sparse_attention_labels (labels 0 for
+ * real, -1 for padding) -> bsa_invert_permute_padded.  kv_idx / kv_cnt
+ * (and key_norms_or_null) have Nq = the largest padded block count over the
+ * candidates; rows of blocks past a head's own count are ignored.
+ * UNSUPPORTED as bsa_block_sparse_attention_tiled, and when a candidate would
+ * pad along y or x (b must divide Hg and c divide Wg). */
+int bsa_block_sparse_attention_tiled_padded(const void* q, const void* k, const void* v, void* out,
+                                            int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
+                                            int64_t D, const int32_t* tiles_host, int n_tiles,
+                                            const int32_t* head_choice, const int32_t* kv_idx,
+                                            const int32_t* kv_cnt, int max_kept, float scale,
+                                            const float* key_norms_or_null, bsa_stream_t stream);
+
+/* Host: 1 if bsa_block_sparse_attention_tiled (pad = 0) or its _padded form
+ * (pad = 1) has a kernel for these arguments, else 0.  Nothing is launched. */
+int bsa_tiled_attention_supported(int dtype, int64_t D, int T, int Hg, int Wg, const int32_t* tiles_host,
+                                  int n_tiles, int pad);
 
 /* bsa_block_sparse_attention with a token label rule inside the kept
  * blocks: query i sees key j when j's block is kept for i's block AND

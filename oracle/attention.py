@@ -173,15 +173,18 @@ def window_rows(q_head, k_head, v_head, rows, window: int, sink: int, scale: flo
     return masked_attention_rows(q_head[rows], k_head, v_head, mask_rows, scale)
 
 
-def block_sparse_rows_gathered(q_head, k_head, v_head, keep_head, block: int, rows, scale: float):
+def block_sparse_rows_gathered(q_head, k_head, v_head, keep_head, block: int, rows, scale: float, key_valid=None):
     """Rows ``rows`` of one head's block-sparse attention over the kept key blocks only.
 
     The same result as :func:`block_sparse_rows`: a masked key adds exp(-inf)
     = 0 to the softmax sum and 0 * v to the output, so leaving it out changes
     nothing but the order of the additions.  For each query block holding
     sampled rows, the keys of its kept blocks are gathered and dense
-    attention runs over them with no mask.  A query block that keeps no key
-    block has no defined output: RuntimeError.
+    attention runs over them with no mask.  ``key_valid`` (bool (S,), or
+    None) leaves further keys out, the padding of a padded grid
+    ([Adaptive tiling (SPADE), "Deviations and notes": padded keys are
+    masked]).  A query block that sees no key has no defined output:
+    RuntimeError.
     """
     rows = np.asarray(rows)
     keep_head = np.asarray(keep_head, dtype=bool)
@@ -190,9 +193,11 @@ def block_sparse_rows_gathered(q_head, k_head, v_head, keep_head, block: int, ro
     for i in np.unique(qb):
         sel = np.flatnonzero(qb == i)
         kept = np.flatnonzero(keep_head[i])
-        if kept.size == 0:
-            raise RuntimeError("a query row has no visible key")
         keys = (kept[:, None] * block + np.arange(block)[None, :]).ravel()
+        if key_valid is not None:
+            keys = keys[np.asarray(key_valid, dtype=bool)[keys]]
+        if keys.size == 0:
+            raise RuntimeError("a query row has no visible key")
         out[sel] = masked_attention(q_head[rows[sel]], k_head[keys], v_head[keys], 0.0, scale)
     return out
 

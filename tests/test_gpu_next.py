@@ -421,9 +421,18 @@ def test_tiled_attention_rejects_uncovered_tilings():
     idx = torch.zeros((1, 1, 16, 1), dtype=torch.int32).cuda()
     cnt = torch.ones((1, 1, 16), dtype=torch.int32).cuda()
     with pytest.raises(bsa.UnsupportedError):
-        bsa.bsa_block_sparse_attention_tiled(q, q, q, (4, 16, 16), [(4, 8, 2)], idx, cnt)    # x extent 2
-    with pytest.raises(bsa.UnsupportedError):
         bsa.bsa_block_sparse_attention_tiled(q, q, q, (4, 16, 16), [(2, 4, 4)], idx, cnt)    # 32 tokens
+    assert not bsa.tiled_attention_supported(torch.bfloat16, 128, [(2, 4, 4)], (4, 16, 16))
+    assert bsa.tiled_attention_supported(torch.bfloat16, 128, [(4, 8, 2), (4, 16, 1)], (4, 16, 16))
+    # padding along y (10 rows, tiles 8 high) has no gather-on-load kernel; along T it has
+    q10 = gpu(synth.normal_bits((1, 1, 4 * 10 * 16, 128), seed=772))
+    i10 = torch.zeros((1, 1, 16, 1), dtype=torch.int32).cuda()      # the grid padded to 4x16x16: 16 blocks
+    c10 = torch.ones((1, 1, 16), dtype=torch.int32).cuda()
+    with pytest.raises(bsa.UnsupportedError):
+        bsa.bsa_block_sparse_attention_tiled_padded(q10, q10, q10, (4, 10, 16), [(1, 8, 8)], i10, c10)
+    assert not bsa.tiled_attention_supported(torch.bfloat16, 128, [(1, 8, 8)], (4, 10, 16), pad=True)
+    assert bsa.tiled_attention_supported(torch.bfloat16, 128, [(16, 2, 2)], (20, 32, 48), pad=True)
+    assert not bsa.tiled_attention_supported(torch.bfloat16, 128, [(16, 2, 2)], (20, 32, 48), pad=False)
     q64 = gpu(synth.normal_bits((1, 1, 1024, 64), seed=771))
     with pytest.raises(bsa.UnsupportedError):
         bsa.bsa_block_sparse_attention_tiled(q64, q64, q64, (4, 16, 16), [(1, 8, 8)], idx, cnt)
@@ -527,3 +536,137 @@ def test_padded_pipeline_scalar_path_fp32():
                 assert max_abs(out[0, h], ref["out"][0, h]) <= tol, (dtype, h)
                 same += 1
         assert same >= 1, dtype
+
+
+# ------------------------------------- gather on load: row patterns, padding ---
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("tiles", [[(2, 16, 2), (4, 16, 1)], [(8, 8, 1), (4, 8, 2)], [(1, 8, 8), (8, 2, 4)]])
+def test_tiled_attention_row_patterns(tiles):
+    """Tiles whose x extent is 2 or 1 (four cells of a DMA row group on two or four T-major rows): the
+    gather-on-load attention equals permute -> attention -> inverse bit for bit, and the oracle's rows."""
+    torch = torch_gpu()
+    grid, H, D = (8, 16, 16), 2, 128
+    S, nb = 2048, 32
+    assert bsa.tiled_attention_supported(torch.bfloat16, D, tiles, grid)
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=880 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    rng = np.random.default_rng(88)
+    keep = rng.random((1, H, nb, nb)) < 0.3
+    keep[..., np.arange(nb), np.arange(nb)] = True
+    cnt = keep.sum(-1).astype(np.int32)
+    idx = np.full((1, H, nb, int(cnt.max())), -1, np.int32)
+    for h in range(H):
+        for I in range(nb):
+            li = np.flatnonzero(keep[0, h, I])
+            idx[0, h, I, :li.size] = li
+    kv_idx, kv_cnt = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    choice = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
+    out = bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, grid, tiles, kv_idx, kv_cnt, head_choice=choice)
+    qp, kp, vp = (bsa.bsa_tile_permute(x, grid, tiles, head_choice=choice) for x in (qg, kg, vg))
+    ref = bsa.bsa_invert_permute(bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 64), grid, tiles,
+                                 head_choice=choice)
+    assert torch.equal(out, ref)
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (q, k, v))
+    o = f64(out)
+    for h in range(H):
+        perm = OT.tile_permutation(grid, tiles[h])
+        want = OA.block_sparse_rows_gathered(*(OT.permute_tokens(x[0, h], perm) for x in (qf, kf, vf)),
+                                             keep[0, h], 64, np.arange(S), D ** -0.5)
+        assert max_abs(o[0, h, perm], want) <= BF16_ATOL, h
+
+
+def _padded_lists_check_rows(out, q, k, v, grid, tiles, choice, idx, cnt, heads, full_head=None, rng=None):
+    """Every real row (full_head) or a sample of rows of `heads`, against the oracle over the GPU's lists on
+    the head's padded grid, padding keys left out."""
+    torch = torch_gpu()
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (q, k, v))
+    D = q.shape[-1]
+    for h in heads:
+        perm = OT.padded_tile_permutation(grid, tiles[int(choice[0, h])])
+        valid = perm >= 0
+        nb = perm.size // 64
+        gkeep = np.zeros((nb, nb), bool)
+        for I in range(nb):
+            gkeep[I, idx[0, h, I, :cnt[0, h, I]]] = True
+        real = np.flatnonzero(valid)
+        rows = real if h == full_head else np.sort(rng.choice(real, 200, replace=False))
+        qp, kp, vp = (_gather_padded(x[0, h], perm) for x in (qf, kf, vf))
+        want = OA.block_sparse_rows_gathered(qp, kp, vp, gkeep, 64, rows, D ** -0.5, key_valid=valid)
+        got = f64(out[0, h, torch.from_numpy(perm[rows]).cuda()])
+        assert max_abs(got, want) <= BF16_ATOL, h
+
+
+@pytest.mark.gpu
+def test_padded_pipeline_gather_on_load_small():
+    """Candidates (1,8,8), (4,4,4), (16,2,2) on a 20x8x8 grid (T padded to 32 for (16,2,2)): the padded
+    pipeline with attention on T-major tensors gives the same lists as the permuted-copy pipeline, outputs
+    within tolerance of it, and every output within tolerance of the oracle's padded recipe on its lists."""
+    torch = torch_gpu()
+    grid, tiles, H, D = (20, 8, 8), [(1, 8, 8), (4, 4, 4), (16, 2, 2)], 4, 128
+    S = 1280
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=890 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    fused = bsa.AdaptiveBlockSparse(1, H, grid, D, tiles, 0.25, qg.dtype, qg.device, pad=True)
+    plain = bsa.AdaptiveBlockSparse(1, H, grid, D, tiles, 0.25, qg.dtype, qg.device, pad=True, fused=False)
+    assert fused.fused and not plain.fused
+    a, b = fused(qg, kg, vg), plain(qg, kg, vg)
+    assert torch.equal(fused.choice, plain.choice)
+    assert torch.equal(fused.kv[1], plain.kv[1]) and torch.equal(fused.kv[0], plain.kv[0])
+    assert max_abs(f64(a), f64(b)) <= BF16_ATOL
+    choice = fused.choice.cpu().numpy()
+    forced = torch.full((1, H), 2, dtype=torch.int32, device="cuda")     # every head on (16, 2, 2)
+    idx, cnt = fused.kv[0].cpu().numpy(), fused.kv[1].cpu().numpy()
+    _padded_lists_check_rows(a, q, k, v, grid, tiles, choice, idx, cnt, range(H), full_head=0,
+                             rng=np.random.default_rng(0))
+    for h in range(1, H):
+        _padded_lists_check_rows(a, q, k, v, grid, tiles, choice, idx, cnt, [h], full_head=h)
+    # forced (16, 2, 2) on every head through the ABI call directly, against the label kernel on the same lists
+    qp, lab = bsa.bsa_tile_permute_padded(qg, grid, tiles, head_choice=forced)
+    kp, _ = bsa.bsa_tile_permute_padded(kg, grid, tiles, head_choice=forced, labels=False)
+    vp, _ = bsa.bsa_tile_permute_padded(vg, grid, tiles, head_choice=forced, labels=False)
+    scores, _ = bsa.bsa_minmax_block_scores(qp, kp, 64, labels=lab)
+    nbt = [bsa.bsa_padded_length(*grid, t) // 64 for t in tiles]
+    kt = [bsa.bsa_budget(0.25, n) for n in nbt]
+    kv_idx, kv_cnt = bsa.bsa_topk_block_mask_tiled(scores, forced, kt, nbt, 1, 1)
+    got = bsa.bsa_block_sparse_attention_tiled_padded(qg, kg, vg, grid, tiles, kv_idx, kv_cnt, head_choice=forced)
+    op = bsa.bsa_block_sparse_attention_labels(qp, kp, vp, kv_idx, kv_cnt, 64, lab)
+    want = bsa.bsa_invert_permute_padded(op, grid, tiles, head_choice=forced)
+    assert max_abs(f64(got), f64(want)) <= BF16_ATOL
+    _padded_lists_check_rows(got, q, k, v, grid, tiles, np.full((1, H), 2), kv_idx.cpu().numpy(),
+                             kv_cnt.cpu().numpy(), [1], full_head=1)
+
+
+@pytest.mark.gpu
+def test_padded_pipeline_gather_on_load_wan_shape():
+    """The Wan grid with (1,8,8), (4,4,4) and (16,2,2) (T padded from 20 to 32): the temporal heads pick
+    (16,2,2); every row of one such head and sampled rows of others against the oracle on the GPU's lists,
+    which equal the oracle's top-k on the padded summaries except at near ties."""
+    torch = torch_gpu()
+    wl = synth.WORKLOADS[4]
+    tiles = [(1, 8, 8), (4, 4, 4), (16, 2, 2)]
+    q, k, v = synth.qkv(4)
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, tiles, 0.17, qg.dtype, qg.device, pad=True)
+    assert pipe.fused
+    out = pipe(qg, kg, vg)
+    choice = pipe.choice.cpu().numpy()
+    assert set(choice[0].tolist()) == {0, 2}
+    idx, cnt = pipe.kv[0].cpu().numpy(), pipe.kv[1].cpu().numpy()
+    temporal = [h for h in range(wl.H) if choice[0, h] == 2]
+    spatial = [h for h in range(wl.H) if choice[0, h] == 0]
+    qf, kf = synth.stored_to_f64(q), synth.stored_to_f64(k)
+    for h in (temporal[0], spatial[0]):            # lists: the oracle's top-k on the padded summaries
+        perm = OT.padded_tile_permutation(wl.grid, tiles[int(choice[0, h])])
+        valid = perm >= 0
+        nb = perm.size // 64
+        sc = OB.minmax_block_scores_valid(_gather_padded(qf[0, h], perm), _gather_padded(kf[0, h], perm), valid, 64)
+        okeep = OB.topk_block_mask(sc, OB.budget(0.17, nb), 1, True)
+        gkeep = np.zeros((nb, nb), bool)
+        for I in range(nb):
+            gkeep[I, idx[0, h, I, :cnt[0, h, I]]] = True
+        for I, J in zip(*np.nonzero(okeep != gkeep)):
+            assert OB.near_tie_ok(sc[I], OB.budget(0.17, nb), J, TOPK_REL), (h, I, J)
+    _padded_lists_check_rows(out, q, k, v, wl.grid, tiles, choice, idx, cnt,
+                             [temporal[0], temporal[-1], spatial[0]], full_head=temporal[0],
+                             rng=np.random.default_rng(3))

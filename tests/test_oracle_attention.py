@@ -177,6 +177,12 @@ def test_gathered_forms_match_the_library_on_all_rows():
     some = np.array([95, 0, 17, 40, 41, 3])         # unsorted, several per block
     got = A.block_sparse_rows_gathered(q[0, 0], k[0, 0], v[0, 0], keep, block, some, 0.3)
     np.testing.assert_allclose(got, want[some], atol=1e-12)
+    # key validity: the same as masking those keys in the expanded block mask
+    valid = np.random.default_rng(72).random(S) < 0.7
+    allowed = np.kron(keep, np.ones((block, block), bool)).astype(bool) & valid[None, :]
+    want = _torch_sdpa(q, k, v, allowed, scale=0.3)[0, 0]
+    got = A.block_sparse_rows_gathered(q[0, 0], k[0, 0], v[0, 0], keep, block, rows, 0.3, key_valid=valid)
+    np.testing.assert_allclose(got, want, atol=1e-12)
     keep[2] = False
     with pytest.raises(RuntimeError):
         A.block_sparse_rows_gathered(q[0, 0], k[0, 0], v[0, 0], keep, block, np.array([16]), 0.3)
