@@ -61,6 +61,7 @@ constexpr float kSkipSlack = 32.0f;    // log2 units: P may reach 2^32 in a tile
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kVmcnt16 = waitcnt_vm(16);  // all but the 16 most recent vector-memory ops
 constexpr int kLgkmcnt0 = 0xC07F;         // all LDS / scalar-memory ops
+constexpr int kVm16Lgkm0 = kVmcnt16 & ~0x0F00;  // vmcnt(16) and lgkmcnt(0)
 static_assert(kVmcnt16 == 0x4F70, "vmcnt(16) encoding");
 
 // kLabels: a block list plus the token rule labels[i] == labels[j] inside
@@ -78,6 +79,7 @@ struct AttnParams {
     uint32_t S, nq;        // sequence length, query blocks per head
     uint32_t n_wg;         // workgroups in the grid
     uint32_t xcd_remap;    // 1: spread heads over XCDs in contiguous ranges
+    uint32_t xcd_per_head; // single-wave kernel: XCDs that share each head (1, 2, 4 or 8)
     float scale_log2;      // softmax scale * log2(e)
     // block list
     const int32_t* kv_idx;
@@ -474,7 +476,19 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
 //    score steps, and in the P V product the exps of 16-key group m+1 and its
 //    V^T reads are issued beside the MFMAs of group m;
 //  * block-list entries come one tile ahead through buffer loads (vector
-//    memory), so waiting for them never waits on LDS traffic.
+//    memory), so waiting for them never waits on LDS traffic;
+//  * EV (early V): the next tile's V DMA is issued beside the last 8 P V
+//    MFMAs, once this tile's V^T reads have returned, instead of beside the
+//    next tile's score MFMAs; it then has a whole score phase longer to land
+//    (2.3% faster at S = 30720, but 8.5% slower at S = 122880, where fewer
+//    tile reads hit L2 and the earlier requests only add to its load);
+//  * workgroup order: XCD x (workgroup w runs on XCD w % 8) takes a
+//    contiguous range of query blocks, so neighbouring query blocks, which
+//    keep many of the same key blocks, share its L2.  With xcd_per_head = R
+//    > 1, R XCDs share each head (each takes 1/R of its query blocks): lists
+//    whose lengths vary with the data then load the XCDs evenly (top-p at
+//    the Wan shape: the heaviest XCD held 1.59x the mean tiles with whole
+//    heads per XCD and 1.07x with R = 4).
 struct SoloCfg {
     static constexpr int D = 128, BLK = 64;
     static constexpr int TILE = BLK * D * 2;  // one V tile in LDS
@@ -484,7 +498,7 @@ struct SoloCfg {
 // padding frame lie past the head, so their loads read zeros; their keys are
 // masked and their rows are not stored.  Blocks past the head's own block
 // count (the grid covers the largest) have no tile.
-template <int MODE, bool POS, bool TILED, bool BOUND = false, bool PADT = false>
+template <int MODE, bool POS, bool TILED, bool BOUND = false, bool PADT = false, bool EV = true>
 __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, const int32_t* __restrict__ kv_idx,
                                                           const int32_t* __restrict__ kv_cnt,
                                                           const float* __restrict__ knorm) {
@@ -496,9 +510,16 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     const int lane = threadIdx.x;
     const int half_id = lane >> 5, col = lane & 31;
 
-    uint32_t wg = blockIdx.x;
-    if (P.xcd_remap) wg = (wg & 7u) * (P.n_wg >> 3) + (wg >> 3);
-    const uint32_t bh = wg / P.nq, I = wg % P.nq;
+    uint32_t wg = blockIdx.x, bh, I;
+    if (P.xcd_per_head > 1u) {  // XCD x = u + R g shares heads g, g + 8/R, ... with R - 1 others
+        const uint32_t R = P.xcd_per_head, x = wg & 7u, slot = wg >> 3, chunk = P.nq / R;
+        bh = x / R + (slot / chunk) * (8u / R);
+        I = (x % R) * chunk + slot % chunk;
+    } else {
+        if (P.xcd_remap) wg = (wg & 7u) * (P.n_wg >> 3) + (wg >> 3);
+        bh = wg / P.nq;
+        I = wg % P.nq;
+    }
     const size_t head = (size_t)bh * P.S * D;
     const uint32_t head_bytes = P.S * D * 2;
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(P.q + head, head_bytes);
@@ -678,6 +699,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         soff_cur = tile_soff(t0);
         kval_cur = tile_keys(t0);
         dma_k(soff_cur);
+        if (EV) dma_v(vlds, soff_cur, 0, C::TILE / 1024);
         if (MODE == kLabels) klab_next = labs[t0 * BLK + lane];
         v_nxt = tile_ahead(min(1, n_iter - 1));
     }
@@ -687,9 +709,9 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         const int nxt_tile = __builtin_amdgcn_readfirstlane(v_nxt);
         const int nxt = nxt_tile * BLK;
         const float kn_nxt = bounded ? knorm_head[nxt_tile] : 0.f;
-        // this tile's K has landed in LDS (nothing later was issued) and the
-        // previous tile's V reads have completed
-        __builtin_amdgcn_s_waitcnt(0);
+        // this tile's K has landed in LDS (only its V (EV) was issued later) and
+        // the previous tile's V reads have completed
+        __builtin_amdgcn_s_waitcnt(EV ? kVm16Lgkm0 : 0);
 
         // S^T of (key half c, row tile r) = K_c Q_r^T: four independent chains
         f32x16 sacc[2][2];
@@ -714,10 +736,10 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         for (int s = 0; s < D / 16; ++s) {
             const bf16x8 ka = kfa[s % 3], kb = kfb[s % 3];
             sacc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][s], sacc[0][0], 0, 0, 0);
-            dma_v(vlds, soff_cur, 2 * s, 2 * s + 1);
+            if (!EV) dma_v(vlds, soff_cur, 2 * s, 2 * s + 1);
             __builtin_amdgcn_sched_barrier(0);
             sacc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][s], sacc[0][1], 0, 0, 0);
-            dma_v(vlds, soff_cur, 2 * s + 1, 2 * s + 2);
+            if (!EV) dma_v(vlds, soff_cur, 2 * s + 1, 2 * s + 2);
             __builtin_amdgcn_sched_barrier(0);
             sacc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[0][s], sacc[1][0], 0, 0, 0);
             if (s + 2 < D / 16) read_k(s + 2);
@@ -877,9 +899,15 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         }
         __builtin_amdgcn_sched_barrier(0);
         // (one MFMA per fenced region; beside each, one piece of group m+1: two
-        // exps of one row tile and half of one V^T fragment)
+        // exps of one row tile and half of one V^T fragment; EV: beside the
+        // last group's MFMAs, two of the next tile's V DMA instructions each,
+        // the last tile's again past the end)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
+            if (EV && m == 3) {  // every V^T read of this tile has returned
+                __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int i = 0; i < 2 * (D / 32); ++i) {
                 const int t = i / 2, r = i % 2;
@@ -887,6 +915,8 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                 if (m + 1 < 4) {
                     p_piece(m + 1, i / 4, i % 4);
                     v_half(m + 1, t, i % 2);
+                } else if (EV) {
+                    dma_v(vlds, soff_nxt, 2 * i, 2 * i + 2);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -918,6 +948,8 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                 *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half_id) = w;
             }
     }
+    // EV: the V DMA issued past the last tile lands before the wave ends
+    if (EV) __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ----------------------------------------------------------------- scalar ---
@@ -1016,14 +1048,40 @@ int launch_scalar(const ScalarParams& P, int dtype, int64_t D, hipStream_t st, c
     return check_launch(name);
 }
 
+template <int MODE, bool TILED, bool PADT, bool EV>
+void launch_solo_ev(const AttnParams& P, hipStream_t st) {
+    if (MODE == kBlockList && P.scale_log2 > 0.f && P.knorm != nullptr)
+        attn_solo_kernel<MODE, true, TILED, true, PADT, EV><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, P.knorm);
+    else if (P.scale_log2 > 0.f)
+        attn_solo_kernel<MODE, true, TILED, false, PADT, EV><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
+    else
+        attn_solo_kernel<MODE, false, TILED, false, PADT, EV><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
+}
+
+// The early V DMA is used unless a head's K and V exceed kEarlyVBytes (block
+// lists; the other modes always use it).
+constexpr uint64_t kEarlyVBytes = 32ull << 20;
+
 template <int MODE, bool TILED = false, bool PADT = false>
 void launch_solo(const AttnParams& P, hipStream_t st) {
-    if (MODE == kBlockList && P.scale_log2 > 0.f && P.knorm != nullptr)
-        attn_solo_kernel<MODE, true, TILED, true, PADT><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, P.knorm);
-    else if (P.scale_log2 > 0.f)
-        attn_solo_kernel<MODE, true, TILED, false, PADT><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
-    else
-        attn_solo_kernel<MODE, false, TILED, false, PADT><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
+    if constexpr (MODE == kBlockList && !PADT) {
+        if ((uint64_t)P.S * (SoloCfg::D * 4) > kEarlyVBytes) {
+            launch_solo_ev<MODE, TILED, PADT, false>(P, st);
+            return;
+        }
+    }
+    launch_solo_ev<MODE, TILED, PADT, true>(P, st);
+}
+
+// Workgroup order of the single-wave kernel: contiguous ranges of (head,
+// query block) per XCD, or, for lists that may hold every block (their
+// lengths vary with the data), each head shared by 4 XCDs.
+void set_order(AttnParams& P, int64_t BH, int max_kept) {
+    P.xcd_remap = (P.n_wg % 8 == 0) ? 1u : 0u;
+    P.xcd_per_head = 1;
+    constexpr uint32_t R = 4;
+    if (P.xcd_remap && (int64_t)max_kept >= (int64_t)P.nq && BH % (8 / R) == 0 && P.nq % R == 0)
+        P.xcd_per_head = R;
 }
 
 template <int D, int BLK, int MODE>
@@ -1091,6 +1149,7 @@ extern "C" int bsa_block_sparse_attention(const void* q, const void* k, const vo
         P.kv_cnt = kv_cnt;
         P.max_kept = (uint32_t)max_kept;
         P.knorm = key_norms_or_null;
+        set_order(P, B * H, max_kept);
         if (D == 128 && block == 64) launch_solo<kBlockList>(P, st);
         else if (D == 128 && block == 32) launch_mfma<128, 32, kBlockList>(P, st);
         else if (D == 64 && block == 64) launch_mfma<64, 64, kBlockList>(P, st);
@@ -1196,6 +1255,7 @@ extern "C" int bsa_block_sparse_attention_labels(const void* q, const void* k, c
         P.max_kept = (uint32_t)max_kept;
         P.labels = labels;
         P.label_stride = (uint64_t)label_head_stride;
+        set_order(P, B * H, max_kept);
         launch_solo<kLabels>(P, st);
         return check_launch(name);
     }
@@ -1296,6 +1356,7 @@ int tiled_attention(const void* q, const void* k, const void* v, void* out, int 
     P.n_tiles = (uint32_t)n_tiles;
     P.Hg = (uint32_t)Hg;
     P.Wg = (uint32_t)Wg;
+    set_order(P, B * H, max_kept);
     if (pad) launch_solo<kBlockList, true, true>(P, (hipStream_t)stream);
     else launch_solo<kBlockList, true>(P, (hipStream_t)stream);
     return check_launch(name);

@@ -298,3 +298,100 @@ def test_windowed_workload_every_row_of_one_head():
         qf, kf, vf = (synth.stored_to_f64(x[0, h]) for x in (q, k, v))
         want = OA.window_rows_gathered(qf, kf, vf, rows, 2048, 64, 128 ** -0.5)
         assert max_abs(out[0, h, rows], want) <= BF16_ATOL, h
+
+
+def _lists_full_width(keep):
+    """Compact lists of width Nk (a list may hold every block), entries past the count -1."""
+    torch = torch_gpu()
+    B, H, Nq, Nk = keep.shape
+    cnt = keep.sum(-1).astype(np.int32)
+    idx = np.full((B, H, Nq, Nk), -1, np.int32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                li = np.flatnonzero(keep[b, h, i])
+                idx[b, h, i, :li.size] = li
+    return torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+
+
+@pytest.mark.gpu
+def test_lists_of_any_length_every_output():
+    """Lists as wide as the key-block count (their lengths vary with the data, as top-p's do): the kernel
+    then spreads each head over four XCDs.  Lengths 0 to Nq, with and without key norms, on permuted and
+    T-major tensors (equal bit for bit), every output against the oracle."""
+    torch = torch_gpu()
+    grid, tiles, H, D = (4, 32, 32), [(1, 8, 8), (4, 4, 4)], 4, 128
+    S, nb = 4096, 64
+    rng = np.random.default_rng(4242)
+    dens = rng.random((1, H, nb, 1)) ** 3                    # rows from nearly empty to full
+    keep = rng.random((1, H, nb, nb)) < dens
+    keep[0, 0, 3] = False                                    # an empty list
+    keep[0, 1, 5] = True                                     # a full list
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=4300 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    kv_idx, kv_cnt = _lists_full_width(keep)
+    assert kv_idx.shape[-1] == nb
+    kn = torch.full((1, H, nb), -1.0, dtype=torch.float32, device="cuda")
+    bsa.bsa_minmax_block_scores(qg, kg, 64, key_norms=kn)
+    qf, kf, vf = (synth.stored_to_f64(x) for x in (q, k, v))
+
+    def check(o, h, q_h, k_h, v_h, perm=None):
+        """Rows of query blocks with keys against the oracle; an empty list's rows are zeros."""
+        seen = keep[0, h].any(-1)
+        rows = np.flatnonzero(np.repeat(seen, 64))
+        want = OA.block_sparse_rows_gathered(q_h, k_h, v_h, keep[0, h], 64, rows, D ** -0.5)
+        got = o[0, h] if perm is None else o[0, h, perm]
+        assert max_abs(got[rows], want) <= BF16_ATOL, h
+        assert np.all(got[np.repeat(~seen, 64)] == 0.0), h
+
+    assert not keep[0, 0, 3].any()
+    for norms in (None, kn):
+        out = f64(bsa.bsa_block_sparse_attention(qg, kg, vg, kv_idx, kv_cnt, 64, key_norms=norms))
+        for h in range(H):
+            check(out, h, qf[0, h], kf[0, h], vf[0, h])
+    choice = torch.tensor([[0, 1, 1, 0]], dtype=torch.int32, device="cuda")
+    out_t = bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, grid, tiles, kv_idx, kv_cnt, head_choice=choice)
+    qp, kp, vp = (bsa.bsa_tile_permute(x, grid, tiles, head_choice=choice) for x in (qg, kg, vg))
+    ref = bsa.bsa_invert_permute(bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 64), grid, tiles,
+                                 head_choice=choice)
+    assert torch.equal(out_t, ref)
+    o = f64(out_t)
+    for h in range(H):
+        perm = OT.tile_permutation(grid, tiles[int(choice[0, h])])
+        check(o, h, *(OT.permute_tokens(x[0, h], perm) for x in (qf, kf, vf)), perm=perm)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("norms", [False, True])
+def test_long_head_late_v_schedule(norms):
+    """A head whose K and V exceed 32 MB (S = 69632, D = 128) takes the schedule that issues each tile's V
+    DMA beside its own score MFMAs: T-major (17x64x64 grid, tiles 1x8x8) equals permuted bit for bit, and
+    the first and last row of every 16th query block, plus all rows of three blocks, match the oracle."""
+    torch = torch_gpu()
+    grid, tiles, H, D = (17, 64, 64), [(1, 8, 8)], 1, 128
+    S = 17 * 64 * 64
+    nb = S // 64
+    assert S * D * 4 > (32 << 20)
+    rng = np.random.default_rng(6969)
+    keep = rng.random((1, H, nb, nb)) < 0.02
+    keep[..., np.arange(nb), np.arange(nb)] = True
+    keep[..., 0] = True
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=6970 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    kv_idx, kv_cnt = _keep_to_gpu_lists(keep)
+    qp, kp, vp = (bsa.bsa_tile_permute(x, grid, tiles) for x in (qg, kg, vg))
+    kn = None
+    if norms:
+        kn = torch.full((1, H, nb), -1.0, dtype=torch.float32, device="cuda")
+        bsa.bsa_minmax_block_scores(qp, kp, 64, key_norms=kn)
+    outp = bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 64, key_norms=kn)
+    out_t = bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, grid, tiles, kv_idx, kv_cnt, key_norms=kn)
+    assert torch.equal(out_t, bsa.bsa_invert_permute(outp, grid, tiles))
+    perm = OT.tile_permutation(grid, tiles[0])
+    qf, kf, vf = (OT.permute_tokens(synth.stored_to_f64(x)[0, 0], perm) for x in (q, k, v))
+    blocks = np.arange(0, nb, 16)
+    rows = np.concatenate([np.stack([blocks * 64, blocks * 64 + 63], 1).ravel(),
+                           np.arange(64), np.arange(nb // 2 * 64, nb // 2 * 64 + 64), np.arange(S - 64, S)])
+    rows = np.unique(rows)
+    want = OA.block_sparse_rows_gathered(qf, kf, vf, keep[0, 0], 64, rows, D ** -0.5)
+    assert max_abs(f64(outp)[0, 0, rows], want) <= BF16_ATOL
