@@ -167,6 +167,23 @@ def _time(torch, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def _time_steady(torch, fn, warm_ms=150.0, min_ms=60.0, min_steps=5):
+    """Average ms of fn() at a steady clock: calls run back to back for at least warm_ms of wall time (the GPU
+    clock ramps up over the first tens of milliseconds of load), then enough calls to fill min_ms are timed
+    with HIP events on the current stream."""
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= warm_ms:
+                break
+    per_ms = (time.perf_counter() - t0) * 1e3 / n
+    return _time(torch, fn, max(min_steps, int(min_ms / max(per_ms, 1e-3)) + 1), 0)
+
+
 def oracle_wall(fn, units, total_units):
     """Run fn(u) for u in units; -> (wall s of the sample, the same scaled to total_units)."""
     t0 = time.perf_counter()
@@ -177,9 +194,8 @@ def oracle_wall(fn, units, total_units):
 
 
 def sweep(args, torch, np, bsa, synth):
-    """Kernel timings on the sliding-tile, windowed and long-sequence workloads."""
+    """Kernel timings on the sliding-tile, windowed and long-sequence workloads, each at a steady clock."""
     dev = torch.device("cuda:0")
-    steps, warmup = max(args.steps // 5, 5), max(args.warmup, 2)
 
     from oracle import attention as OA
     from oracle import blocks as OB
@@ -194,7 +210,7 @@ def sweep(args, torch, np, bsa, synth):
     qb, kb, vb = synth.qkv(1)
     q, k, v = (synth.to_torch(x, dev) for x in (qb, kb, vb))
     out = torch.empty_like(q)
-    ms = _time(torch, lambda: bsa.bsa_windowed_attention(q, k, v, 8, 2, 0.25, 8, out=out), steps, warmup)
+    ms = _time_steady(torch, lambda: bsa.bsa_windowed_attention(q, k, v, 8, 2, 0.25, 8, out=out))
     qf, kf, vf = (synth.stored_to_f64(x) for x in (qb, kb, vb))
     wall, _ = oracle_wall(lambda _: OA.windowed_attention(qf, kf, vf, 8, 2, scale=0.25, chunk=8), [0], 1)
     print(json.dumps({"workload": wl.name, "attention_ms": round(ms, 4), "oracle_wall_s": wall,
@@ -210,7 +226,7 @@ def sweep(args, torch, np, bsa, synth):
     kv_cnt = torch.from_numpy(np.broadcast_to(cnt, (1, wl.H, 64)).copy()).to(dev)
     qp, kp, vp = (bsa.bsa_tile_permute(x, wl.grid, tile) for x in (q, k, v))
     out = torch.empty_like(qp)
-    ms = _time(torch, lambda: bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 32, out=out), steps, warmup)
+    ms = _time_steady(torch, lambda: bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 32, out=out))
     fl = int(kv_cnt.sum().item()) * 4 * 32 * 32 * wl.D
 
     def step2():
@@ -218,7 +234,7 @@ def sweep(args, torch, np, bsa, synth):
             bsa.bsa_tile_permute(x, wl.grid, tile, out=y)
         bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 32, out=out)
         bsa.bsa_invert_permute(out, wl.grid, tile)
-    ms_step = _time(torch, step2, steps, warmup)
+    ms_step = _time_steady(torch, step2)
     qf, kf, vf = (synth.stored_to_f64(x) for x in (qb, kb, vb))
     keep, labels = OT.sliding_tile_keep((4, 4, 4)), OT.tile_labels(wl.grid, tile[0])
     wall, _ = oracle_wall(lambda h: OP.label_mask_attention(qf[0, h], kf[0, h], vf[0, h], labels, keep, wl.D ** -0.5),
@@ -233,7 +249,7 @@ def sweep(args, torch, np, bsa, synth):
     qb, kb, vb = synth.qkv(3)
     q, k, v = (synth.to_torch(x, dev) for x in (qb, kb, vb))
     out = torch.empty_like(q)
-    ms = _time(torch, lambda: bsa.bsa_windowed_attention(q, k, v, 2048, 64, 128 ** -0.5, 512, out=out), steps, warmup)
+    ms = _time_steady(torch, lambda: bsa.bsa_windowed_attention(q, k, v, 2048, 64, 128 ** -0.5, 512, out=out))
     S, half, sink = wl.S, 1024, 64
     i = np.arange(S)
     local = np.minimum(S - 1, i + half) - np.maximum(0, i - half) + 1
@@ -266,9 +282,9 @@ def sweep(args, torch, np, bsa, synth):
     for name, kw in variants:
         tiles = kw.pop("tiles")
         pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, tiles, 0.17, q.dtype, dev, **kw)
-        ms_step = _time(torch, lambda: pipe(q, k, v, out=out), max(steps // 2, 3), warmup)
+        ms_step = _time_steady(torch, lambda: pipe(q, k, v, out=out))
         kv_idx, kv_cnt = pipe.kv
-        ms = _time(torch, attention_call(bsa, pipe, q, k, v, out), max(steps // 2, 3), warmup)
+        ms = _time_steady(torch, attention_call(bsa, pipe, q, k, v, out))
         kept = int(kv_cnt.sum().item())
         fl = kept * 4 * 64 * 64 * wl.D
         choice = np.bincount(pipe.choice.cpu().numpy().ravel(), minlength=len(tiles)).tolist()
@@ -279,7 +295,7 @@ def sweep(args, torch, np, bsa, synth):
     for kind, pairs, direct in (("spatial", S * HW, True), ("temporal", S * wl.grid[0], True),
                                 ("temporal", S * wl.grid[0], False)):
         att = bsa.VideoLabelAttention(1, wl.H, wl.grid, kind, dev, dtype=q.dtype if direct else None, D=wl.D)
-        ms = _time(torch, lambda: att(q, k, v, out=out), max(steps // 2, 3), warmup)
+        ms = _time_steady(torch, lambda: att(q, k, v, out=out))
         fl_tok = pairs * 4 * wl.D * wl.H
         how = ("label attention on T-major tokens" if kind == "spatial" else
                "frames gathered on load" if direct else "permute + label attention + inverse")
@@ -293,9 +309,9 @@ def sweep(args, torch, np, bsa, synth):
     q, k, v = (synth.to_torch(x, dev) for x in (qb, kb, vb))
     pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, [(4, 4, 4)], 0.10, q.dtype, dev)
     out = torch.empty_like(q)
-    ms_step = _time(torch, lambda: pipe(q, k, v, out=out), max(steps // 2, 3), warmup)
+    ms_step = _time_steady(torch, lambda: pipe(q, k, v, out=out))
     kv_idx, kv_cnt = pipe.kv
-    ms = _time(torch, attention_call(bsa, pipe, q, k, v, out), max(steps // 2, 3), warmup)
+    ms = _time_steady(torch, attention_call(bsa, pipe, q, k, v, out))
     fl = int(kv_cnt.sum().item()) * 4 * 64 * 64 * wl.D
     # the oracle on head 0: permutation, scores and top-k of the head, then 32 query blocks spread over it
     qf, kf, vf = (synth.stored_to_f64(x[0, 0]) for x in (qb, kb, vb))
