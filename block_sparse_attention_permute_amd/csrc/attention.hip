@@ -484,7 +484,9 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
 //    tile reads hit L2 and the earlier requests only add to its load);
 //  * workgroup order: XCD x (workgroup w runs on XCD w % 8) takes a
 //    contiguous range of query blocks, so neighbouring query blocks, which
-//    keep many of the same key blocks, share its L2.  With xcd_per_head = R
+//    keep many of the same key blocks, share its L2.  On padded grids the
+//    range is an eighth of all heads' real blocks (heads differ in their
+//    block counts there).  With xcd_per_head = R
 //    > 1, R XCDs share each head (each takes 1/R of its query blocks): lists
 //    whose lengths vary with the data then load the XCDs evenly (top-p at
 //    the Wan shape: the heaviest XCD held 1.59x the mean tiles with whole
@@ -511,7 +513,24 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     const int half_id = lane >> 5, col = lane & 31;
 
     uint32_t wg = blockIdx.x, bh, I;
-    if (P.xcd_per_head > 1u) {  // XCD x = u + R g shares heads g, g + 8/R, ... with R - 1 others
+    if (PADT && P.xcd_remap && P.head_choice != nullptr) {
+        // heads differ in their block counts (each its own padded grid): the
+        // heads' real blocks are taken in order and XCD x runs the x-th eighth
+        // of them, so that every XCD gets the same work
+        const uint32_t x = wg & 7u, slot = wg >> 3, n_heads = P.n_wg / P.nq;
+        auto blocks_of = [&](uint32_t h) -> uint32_t {
+            const uint32_t c = (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[h]);
+            return P.nbt[c < P.n_tiles ? c : 0u];
+        };
+        uint32_t total = 0;
+        for (uint32_t h = 0; h < n_heads; ++h) total += blocks_of(h);
+        const uint32_t lo = (uint32_t)((uint64_t)total * x / 8u), hi = (uint32_t)((uint64_t)total * (x + 1u) / 8u);
+        if (lo + slot >= hi) return;
+        uint32_t p = lo + slot, h = 0;
+        for (uint32_t n = blocks_of(0); p >= n; n = blocks_of(++h)) p -= n;
+        bh = h;
+        I = p;
+    } else if (P.xcd_per_head > 1u) {  // XCD x = u + R g shares heads g, g + 8/R, ... with R - 1 others
         const uint32_t R = P.xcd_per_head, x = wg & 7u, slot = wg >> 3, chunk = P.nq / R;
         bh = x / R + (slot / chunk) * (8u / R);
         I = (x % R) * chunk + slot % chunk;
