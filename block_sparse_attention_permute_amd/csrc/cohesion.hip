@@ -67,9 +67,18 @@ template <int EPV, int LPT, bool PAD, bool SUMM>
 __global__ __launch_bounds__(64 * kWaves) void tile_cohesion_kernel(const CohParams P) {
     constexpr int TPI = 64 / LPT;
     const int lane = threadIdx.x & 63;
-    const uint32_t tile = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const uint32_t cand = blockIdx.y;
-    const uint32_t bh = blockIdx.z;
+    // Workgroup order: (head, tile group, candidate), the candidate fastest,
+    // and each XCD (workgroup w runs on XCD w % 8) a contiguous range of it.
+    // The candidates' tiles of one group cover about the same frames (every
+    // candidate has the same number of tiles per frame), so the candidates
+    // after the first read q from the XCD's L2.
+    uint32_t w = blockIdx.x;
+    if (gridDim.x % 8u == 0u) w = (w & 7u) * (gridDim.x >> 3) + (w >> 3);
+    const uint32_t cand = w % P.n_tiles;
+    w /= P.n_tiles;
+    const uint32_t groups = (P.max_nb + kWaves - 1) / kWaves;
+    const uint32_t tile = (w % groups) * kWaves + (threadIdx.x >> 6);
+    const uint32_t bh = w / groups;
     if (tile >= P.nb[cand]) return;
     const TileGeo& g = P.geo[cand];
     const uint32_t origin = PAD ? 0u : tile_origin(tile, g, P.Hg, P.Wg);
@@ -224,7 +233,9 @@ __global__ __launch_bounds__(64) void select_kernel(const SelParams P) {
 }
 
 int launch_tile_cohesion(const CohParams& P, uint32_t BH, hipStream_t stream, const char* name) {
-    dim3 grid((P.max_nb + kWaves - 1) / kWaves, P.n_tiles, BH);
+    const uint64_t n_wg = (uint64_t)((P.max_nb + kWaves - 1) / kWaves) * P.n_tiles * BH;
+    BSA_REQUIRE(n_wg < ((uint64_t)1 << 31), "%s: too many tiles", name);
+    const dim3 grid((uint32_t)n_wg);
     const int lpt = (int)P.vecs_per_row;
 #define BSA_COH(EPV, LPT)                                                                            \
     (P.pad ? tile_cohesion_kernel<EPV, LPT, true, false><<<grid, 64 * kWaves, 0, stream>>>(P)      \

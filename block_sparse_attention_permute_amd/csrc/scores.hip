@@ -280,8 +280,15 @@ template <int ND>
 __global__ __launch_bounds__(64) void block_scores_mfma_kernel(const uint16_t* __restrict__ summ, uint32_t BH,
                                                                uint32_t nb, uint32_t D, float* __restrict__ scores) {
     const int lane = threadIdx.x;
-    const uint32_t bh = blockIdx.z;
-    const uint32_t I0 = blockIdx.y * 32, J0 = blockIdx.x * 32;
+    // 1D grid of (head, I tile, J tile), J fastest; each XCD (workgroup w runs
+    // on XCD w % 8) takes a contiguous range, so a head's summaries are read
+    // by one XCD and stay in its L2 (spread over all eight, they were fetched
+    // from beyond L2 about once per output tile)
+    uint32_t w = blockIdx.x;
+    if (gridDim.x % 8u == 0u) w = (w & 7u) * (gridDim.x >> 3) + (w >> 3);
+    const uint32_t n32 = (nb + 31) / 32;
+    const uint32_t bh = w / (n32 * n32);
+    const uint32_t I0 = (w / n32 % n32) * 32, J0 = (w % n32) * 32;
     const size_t plane = (size_t)BH * nb * D;
     const size_t head = (size_t)bh * nb * D;
     const uint16_t* qmax = summ;
@@ -395,8 +402,9 @@ int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
     int rc = check_launch(name);
     if (rc) return rc;
     if (bf && D % 16 == 0) {
-        const unsigned n32 = (unsigned)((nb + 31) / 32);
-        dim3 g3(n32, n32, (unsigned)(B * H));
+        const uint64_t n32 = (uint64_t)((nb + 31) / 32);
+        BSA_REQUIRE(n32 * n32 * (uint64_t)(B * H) < ((uint64_t)1 << 31), "%s: too many score tiles", name);
+        const dim3 g3((uint32_t)(n32 * n32 * (uint64_t)(B * H)));
         const uint16_t* summ = static_cast<const uint16_t*>(summaries);
         if (D == 128)
             block_scores_mfma_kernel<8><<<g3, 64, 0, st>>>(summ, P.BH, P.nb, (uint32_t)D, scores);
