@@ -363,7 +363,8 @@ int bsa_topk_block_mask_tiled(const float* scores, int64_t B, int64_t H, int Nq,
  * q, k, v, out: device (B, H, S, D) in the tile-contiguous order the blocks
  * refer to; out has q's dtype.  kv_idx: device int32 (B, H, S/block,
  * max_kept), ascending without repeats; kv_cnt: device int32 (B, H, S/block)
- * in [1, max_kept] (both trusted; see bsa_validate_block_list).
+ * in [1, max_kept] (both trusted; see bsa_validate_block_list, which reports a
+ * count of 0 as an invariant violation; the kernels write such a row as zeros).
  * bf16: D in {64, 128} and block in {32, 64} run on MFMA; other bf16 / fp32
  * shapes with D <= 128 use a scalar kernel.  Accumulation and softmax are
  * fp32; bf16 outputs are rounded to nearest even once.
