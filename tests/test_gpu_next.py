@@ -670,3 +670,35 @@ def test_padded_pipeline_gather_on_load_wan_shape():
     _padded_lists_check_rows(out, q, k, v, wl.grid, tiles, choice, idx, cnt,
                              [temporal[0], temporal[-1], spatial[0]], full_head=temporal[0],
                              rng=np.random.default_rng(3))
+
+
+@pytest.mark.gpu
+def test_padded_gather_on_load_batch_of_two_mixed_choices():
+    """B = 2, H = 3 with every (b, h) on its own candidate of (1,8,8), (4,4,4) and the padded (16,2,2): the
+    padded gather-on-load attention (whose workgroups walk all heads' real blocks in order) equals the label
+    kernel on padded permuted copies within tolerance, and the oracle's padded recipe on every real row of
+    two heads."""
+    torch = torch_gpu()
+    grid, tiles, B, H, D = (20, 8, 8), [(1, 8, 8), (4, 4, 4), (16, 2, 2)], 2, 3, 128
+    S = 1280
+    q, k, v = (synth.normal_bits((B, H, S, D), seed=930 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    choice_np = np.array([[0, 2, 1], [2, 0, 2]], np.int32)
+    choice = torch.from_numpy(choice_np).cuda()
+    qp, lab = bsa.bsa_tile_permute_padded(qg, grid, tiles, head_choice=choice)
+    kp, _ = bsa.bsa_tile_permute_padded(kg, grid, tiles, head_choice=choice, labels=False)
+    vp, _ = bsa.bsa_tile_permute_padded(vg, grid, tiles, head_choice=choice, labels=False)
+    scores, _ = bsa.bsa_minmax_block_scores(qp, kp, 64, labels=lab)
+    nbt = [bsa.bsa_padded_length(*grid, t) // 64 for t in tiles]
+    assert (B * H * max(nbt)) % 8 == 0 and len(set(nbt)) > 1
+    kt = [bsa.bsa_budget(0.25, n) for n in nbt]
+    kv_idx, kv_cnt = bsa.bsa_topk_block_mask_tiled(scores, choice, kt, nbt, 1, 1)
+    got = bsa.bsa_block_sparse_attention_tiled_padded(qg, kg, vg, grid, tiles, kv_idx, kv_cnt, head_choice=choice)
+    op = bsa.bsa_block_sparse_attention_labels(qp, kp, vp, kv_idx, kv_cnt, 64, lab)
+    want = bsa.bsa_invert_permute_padded(op, grid, tiles, head_choice=choice)
+    assert max_abs(f64(got), f64(want)) <= BF16_ATOL
+    idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    for b, h in ((0, 1), (1, 0)):
+        sel = (slice(b, b + 1),)
+        _padded_lists_check_rows(got[sel], q[sel], k[sel], v[sel], grid, tiles, choice_np[sel], idx[sel], cnt[sel],
+                                 [h], full_head=h)
