@@ -142,15 +142,19 @@ def cpu_baseline(q, k, v, wl, block, kk, budget_s=12.0):
 def attention_call(bsa, pipe, q, k, v, out):
     """The pipeline's attention launch alone, on its current block lists."""
     kv_idx, kv_cnt = pipe.kv
+    if pipe.fused and pipe.pad:
+        return lambda: bsa.bsa_block_sparse_attention_tiled_padded(q, k, v, pipe.grid, pipe.tiles, kv_idx, kv_cnt,
+                                                                   head_choice=pipe.choice, scale=pipe.scale,
+                                                                   out=out, key_norms=pipe.ws_knorm)
     if pipe.fused:
-        call = bsa.bsa_block_sparse_attention_tiled_padded if pipe.pad else bsa.bsa_block_sparse_attention_tiled
-        return lambda: call(q, k, v, pipe.grid, pipe.tiles, kv_idx, kv_cnt, head_choice=pipe.choice, scale=pipe.scale,
-                            out=out, key_norms=pipe.ws_knorm)
+        return lambda: bsa.bsa_block_sparse_attention_tiled(q, k, v, pipe.grid, pipe.tiles, kv_idx, kv_cnt,
+                                                            head_choice=pipe.choice, scale=pipe.scale, out=out,
+                                                            key_norms=pipe.ws_knorm, row_order=pipe.ws_order)
     if pipe.pad:
         return lambda: bsa.bsa_block_sparse_attention_labels(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, pipe.block,
                                                              pipe.labels, pipe.scale, out=pipe.op)
     return lambda: bsa.bsa_block_sparse_attention(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, pipe.block, pipe.scale,
-                                                  out=pipe.op, key_norms=pipe.ws_knorm)
+                                                  out=pipe.op, key_norms=pipe.ws_knorm, row_order=pipe.ws_order)
 
 
 def _time(torch, fn, steps, warmup):

@@ -37,7 +37,7 @@ EXPORTED = (
     "bsa_minmax_block_scores_tiled", "bsa_block_sparse_attention_tiled",
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices", "bsa_video_labels",
     "bsa_select_tiling_noalloc", "bsa_temporal_only_attention", "bsa_block_sparse_attention_tiled_padded",
-    "bsa_tiled_attention_supported",
+    "bsa_tiled_attention_supported", "bsa_row_order", "bsa_row_order_len",
 )
 
 
@@ -63,7 +63,8 @@ _SIGS = {
     "bsa_minmax_block_scores": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P]),
     "bsa_topk_block_mask": (_I, [_P, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "bsa_top_p_block_mask": (_I, [_P, _I64, _I64, _I, _I, _F, _F, _I, _I, _P, _P, _I, _P, _P]),
-    "bsa_block_sparse_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _F, _P, _P]),
+    "bsa_block_sparse_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _P, _P, _I, _F, _P, _P,
+                                        _I64, _P]),
     "bsa_windowed_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _I64, _I, _I, _F, _I, _P]),
     "bsa_temporal_only_attention": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _F, _P]),
     "bsa_validate_block_list": (_I, [_P, _P, _I64, _I64, _I, _I, _I, _P]),
@@ -82,11 +83,16 @@ _SIGS = {
     "bsa_minmax_block_scores_tiled": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P, _P,
                                            _P]),
     "bsa_block_sparse_attention_tiled": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
-                                              _I, _F, _P, _P]),
+                                              _I, _F, _P, _P, _I64, _P]),
     "bsa_block_sparse_attention_tiled_padded": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P,
                                                      _P, _P, _I, _F, _P, _P]),
     "bsa_tiled_attention_supported": (_I, [_I, _I64, _I, _I, _I, _P, _I, _I]),
+    "bsa_row_order": (_I, [_P, _I64, _I64, _P, _I64, _P]),
+    "bsa_row_order_len": (_I64, [_I64, _I64]),
 }
+
+# libbsa's ABI major version these signatures are written for
+ABI_MAJOR = 2
 
 
 def lib() -> ctypes.CDLL:
@@ -100,6 +106,8 @@ def lib() -> ctypes.CDLL:
         for name, (res, args) in _SIGS.items():
             fn = getattr(L, name)
             fn.restype, fn.argtypes = res, args
+        if L.bsa_version() >> 16 != ABI_MAJOR:
+            raise RuntimeError(f"{LIB_PATH} has ABI {L.bsa_version() >> 16}, this binding needs {ABI_MAJOR}: rebuild it")
         _lib = L
     return _lib
 
@@ -569,12 +577,16 @@ def _qkv(q, k, v):
     return shp
 
 
-def bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block: int, scale=None, out=None, key_norms=None):
+def bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block: int, scale=None, out=None, key_norms=None,
+                               row_order=None):
     """Attention of every query block over its kept key blocks -> (B, H, S, D) like q.
 
     key_norms: float32 (B, H, S // block) or None, at least each key block's largest row L2 norm (as
     bsa_minmax_block_scores writes them); it lets the kernel skip the running-max update of key blocks
-    that cannot pass it, which changes the result only by rounding."""
+    that cannot pass it, which changes the result only by rounding.
+    row_order: a launch order as bsa_row_order writes it (1-D int32 / uint32: workgroup w runs row
+    row_order[w] = (b*H + h)*Nq + I, entries past the last row are empty slots), or None: the bf16 kernels
+    start the rows in that order (the result does not depend on it)."""
     torch = _torch()
     B, H, S, D = _qkv(q, k, v)
     if kv_idx.dtype != torch.int32 or kv_cnt.dtype != torch.int32 or kv_idx.dim() != 4:
@@ -587,7 +599,41 @@ def bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block: int, scale=None, 
     _check(lib().bsa_block_sparse_attention(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
                                             _dtype_code(q), B, H, S, D, int(block), _dev(kv_idx), _dev(kv_cnt),
                                             int(kv_idx.shape[3]), _scale(scale),
-                                            _norms_out(key_norms, B, H, S // block, q), _stream(q)))
+                                            _norms_out(key_norms, B, H, S // block, q),
+                                            *_order_args(row_order, B * H * (S // block)), _stream(q)))
+    return o
+
+
+def _order_args(row_order, rows: int):
+    """(pointer, length) of an optional launch order over `rows` rows."""
+    if row_order is None:
+        return None, 0
+    torch = _torch()
+    if row_order.dtype not in (torch.int32, torch.uint32) or row_order.dim() != 1 or row_order.numel() < rows:
+        raise ValueError(f"row_order must be a 1-D int32 / uint32 tensor of at least {rows} entries")
+    return _dev(row_order, "row_order"), int(row_order.numel())
+
+
+def bsa_row_order_len(BH: int, nq: int) -> int:
+    """Length of bsa_row_order's launch plan for BH heads of nq rows (asked of libbsa, nothing launched)."""
+    n = int(lib().bsa_row_order_len(int(BH), int(nq)))
+    if n < 0:
+        raise ValueError(lib().bsa_last_error().decode())
+    return n
+
+
+def bsa_row_order(kv_cnt, out=None):
+    """Launch plan for the block lists of kv_cnt (B, H, Nq) -> int32 (bsa_row_order_len(B*H, Nq),): each XCD
+    gets whole heads (or head ranges) of balanced work, long rows first; empty slots read -1."""
+    torch = _torch()
+    if kv_cnt.dtype != torch.int32 or kv_cnt.dim() != 3:
+        raise ValueError("kv_cnt must be int32 (B, H, Nq)")
+    B, H, nq = (int(s) for s in kv_cnt.shape)
+    n = bsa_row_order_len(B * H, nq)
+    o = torch.empty(n, dtype=torch.int32, device=kv_cnt.device) if out is None else out
+    if o.dtype not in (torch.int32, torch.uint32) or o.dim() != 1 or o.numel() < n:
+        raise ValueError(f"out must be a 1-D int32 / uint32 tensor of at least {n} entries")
+    _check(lib().bsa_row_order(_dev(kv_cnt, "kv_cnt"), B * H, nq, _dev(o, "out"), int(o.numel()), _stream(kv_cnt)))
     return o
 
 
@@ -602,10 +648,10 @@ def tiled_attention_supported(dtype, D, tiles, grid, pad: bool = False) -> bool:
 
 
 def bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_choice=None, scale=None, out=None,
-                                     key_norms=None):
+                                     key_norms=None, row_order=None):
     """Block-sparse attention of T-major tensors, blocks = tiles (gather on load) -> T-major (B, H, S, D).
 
-    key_norms: per tile of each head's tiling, as in bsa_block_sparse_attention."""
+    key_norms and row_order: per tile of each head's tiling, as in bsa_block_sparse_attention."""
     torch = _torch()
     B, H, S, D = _qkv(q, k, v)
     T, Hg, Wg = (int(g) for g in grid)
@@ -621,7 +667,8 @@ def bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_
     _check(lib().bsa_block_sparse_attention_tiled(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
                                                   _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, hc, _dev(kv_idx),
                                                   _dev(kv_cnt), int(kv_idx.shape[3]), _scale(scale),
-                                                  _norms_out(key_norms, B, H, S // 64, q), _stream(q)))
+                                                  _norms_out(key_norms, B, H, S // 64, q),
+                                                  *_order_args(row_order, B * H * (S // 64)), _stream(q)))
     return o
 
 
@@ -793,6 +840,10 @@ class AdaptiveBlockSparse:
                           torch.empty((4, B, H, self.nb, D), dtype=dtype, **f))
         self.ws_topk = (torch.empty((B, H, self.nb, self.max_kept), dtype=torch.int32, **f),
                         torch.empty((B, H, self.nb), dtype=torch.int32, **f), None)
+        # top-p lists differ in length from row to row: a launch plan balances the XCDs and starts long rows
+        # first
+        self.ws_order = (torch.empty(bsa_row_order_len(B * H, self.nb), dtype=torch.int32, **f)
+                         if top_p is not None else None)
         # each key block's largest row norm, written by the scores pass: the attention kernel skips the
         # running-max update of the key blocks it proves cannot pass it
         self.ws_knorm = (torch.empty((B, H, self.nb), dtype=torch.float32, **f) if self.fused or not self.pad
@@ -839,14 +890,20 @@ class AdaptiveBlockSparse:
             else:
                 kv_idx, kv_cnt, _ = bsa_top_p_block_mask(scores, self.top_p, self.p_scale, self.sink_blocks,
                                                          self.keep_diag, return_mask=True, out=self.ws_topk)
+                bsa_row_order(kv_cnt, out=self.ws_order)
         if self.validate and not self.pad:
             bsa_validate_block_list(kv_idx, kv_cnt, self.nb)
         if self.fused:
             if attention_hook is not None:
                 attention_hook(True)
-            call = bsa_block_sparse_attention_tiled_padded if self.pad else bsa_block_sparse_attention_tiled
-            o = call(q, k, v, self.grid, self.tiles, kv_idx, kv_cnt, head_choice=choice, scale=self.scale, out=out,
-                     key_norms=self.ws_knorm)
+            if self.pad:
+                o = bsa_block_sparse_attention_tiled_padded(q, k, v, self.grid, self.tiles, kv_idx, kv_cnt,
+                                                            head_choice=choice, scale=self.scale, out=out,
+                                                            key_norms=self.ws_knorm)
+            else:
+                o = bsa_block_sparse_attention_tiled(q, k, v, self.grid, self.tiles, kv_idx, kv_cnt,
+                                                     head_choice=choice, scale=self.scale, out=out,
+                                                     key_norms=self.ws_knorm, row_order=self.ws_order)
             if attention_hook is not None:
                 attention_hook(False)
             return o
@@ -857,7 +914,7 @@ class AdaptiveBlockSparse:
                                               self.scale, out=self.op)
         else:
             bsa_block_sparse_attention(self.qp, self.kp, self.vp, kv_idx, kv_cnt, self.block, self.scale,
-                                       out=self.op, key_norms=self.ws_knorm)
+                                       out=self.op, key_norms=self.ws_knorm, row_order=self.ws_order)
         if attention_hook is not None:
             attention_hook(False)
         if self.pad:

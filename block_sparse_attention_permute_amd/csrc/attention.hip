@@ -85,6 +85,11 @@ struct AttnParams {
     const int32_t* kv_idx;
     const int32_t* kv_cnt;
     uint32_t max_kept;
+    // block lists: workgroup w runs row row_order[w] = (b*H + h)*nq + I when
+    // not null (entries past the last row are empty slots), in a grid of
+    // `grid` workgroups (0: n_wg, one per row)
+    const uint32_t* row_order;
+    uint32_t grid;
     // window
     int32_t half, sink;
     // block lists: per key block, at least the largest L2 norm of its key rows, or null
@@ -194,7 +199,12 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
     const int half_id = lane >> 5, col = lane & 31;
 
     uint32_t wg = blockIdx.x;
-    if (P.xcd_remap) wg = (wg & 7u) * (P.n_wg >> 3) + (wg >> 3);
+    if (MODE == kBlockList && P.row_order != nullptr) {
+        wg = P.row_order[wg];
+        if (wg >= P.n_wg) return;
+    } else if (P.xcd_remap) {
+        wg = (wg & 7u) * (P.n_wg >> 3) + (wg >> 3);
+    }
     const uint32_t bh = wg / P.nq, I = wg % P.nq;
     const size_t head = (size_t)bh * P.S * D;
     const uint32_t head_bytes = P.S * D * 2;
@@ -513,7 +523,12 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     const int half_id = lane >> 5, col = lane & 31;
 
     uint32_t wg = blockIdx.x, bh, I;
-    if (PADT && P.xcd_remap && P.head_choice != nullptr) {
+    if (MODE == kBlockList && !PADT && P.row_order != nullptr) {
+        const uint32_t r = P.row_order[wg];
+        if (r >= P.n_wg) return;
+        bh = r / P.nq;
+        I = r % P.nq;
+    } else if (PADT && P.xcd_remap && P.head_choice != nullptr) {
         // heads differ in their block counts (each its own padded grid): the
         // heads' real blocks are taken in order and XCD x runs the x-th eighth
         // of them, so that every XCD gets the same work
@@ -1067,14 +1082,16 @@ int launch_scalar(const ScalarParams& P, int dtype, int64_t D, hipStream_t st, c
     return check_launch(name);
 }
 
+uint32_t grid_of(const AttnParams& P) { return P.grid != 0 ? P.grid : P.n_wg; }
+
 template <int MODE, bool TILED, bool PADT, bool EV>
 void launch_solo_ev(const AttnParams& P, hipStream_t st) {
     if (MODE == kBlockList && P.scale_log2 > 0.f && P.knorm != nullptr)
-        attn_solo_kernel<MODE, true, TILED, true, PADT, EV><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, P.knorm);
+        attn_solo_kernel<MODE, true, TILED, true, PADT, EV><<<grid_of(P), 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, P.knorm);
     else if (P.scale_log2 > 0.f)
-        attn_solo_kernel<MODE, true, TILED, false, PADT, EV><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
+        attn_solo_kernel<MODE, true, TILED, false, PADT, EV><<<grid_of(P), 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
     else
-        attn_solo_kernel<MODE, false, TILED, false, PADT, EV><<<P.n_wg, 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
+        attn_solo_kernel<MODE, false, TILED, false, PADT, EV><<<grid_of(P), 64, 0, st>>>(P, P.kv_idx, P.kv_cnt, nullptr);
 }
 
 // The early V DMA is used unless a head's K and V exceed kEarlyVBytes (block
@@ -1095,6 +1112,17 @@ void launch_solo(const AttnParams& P, hipStream_t st) {
 // Workgroup order of the single-wave kernel: contiguous ranges of (head,
 // query block) per XCD, or, for lists that may hold every block (their
 // lengths vary with the data), each head shared by 4 XCDs.
+// A caller's launch order: row_order_len workgroups, workgroup w running row
+// row_order[w] (empty when that is not a row).
+int set_row_order(AttnParams& P, const uint32_t* row_order, int64_t row_order_len, const char* name) {
+    if (row_order == nullptr) return BSA_OK;
+    BSA_REQUIRE(row_order_len >= 1 && row_order_len < ((int64_t)1 << 31), "%s: row_order_len=%lld must be in [1, 2^31)",
+                name, (long long)row_order_len);
+    P.row_order = row_order;
+    P.grid = (uint32_t)row_order_len;
+    return BSA_OK;
+}
+
 void set_order(AttnParams& P, int64_t BH, int max_kept) {
     P.xcd_remap = (P.n_wg % 8 == 0) ? 1u : 0u;
     P.xcd_per_head = 1;
@@ -1106,9 +1134,9 @@ void set_order(AttnParams& P, int64_t BH, int max_kept) {
 template <int D, int BLK, int MODE>
 void launch_mfma(const AttnParams& P, hipStream_t st) {
     if (P.scale_log2 > 0.f)
-        attn_mfma_kernel<D, BLK, MODE, true><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P, P.kv_idx, P.kv_cnt);
+        attn_mfma_kernel<D, BLK, MODE, true><<<grid_of(P), Cfg<D, BLK>::NT, 0, st>>>(P, P.kv_idx, P.kv_cnt);
     else
-        attn_mfma_kernel<D, BLK, MODE, false><<<P.n_wg, Cfg<D, BLK>::NT, 0, st>>>(P, P.kv_idx, P.kv_cnt);
+        attn_mfma_kernel<D, BLK, MODE, false><<<grid_of(P), Cfg<D, BLK>::NT, 0, st>>>(P, P.kv_idx, P.kv_cnt);
 }
 
 int common_checks(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B, int64_t H, int64_t S,
@@ -1139,7 +1167,8 @@ using namespace bsa;
 extern "C" int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B,
                                           int64_t H, int64_t S, int64_t D, int block, const int32_t* kv_idx,
                                           const int32_t* kv_cnt, int max_kept, float scale,
-                                          const float* key_norms_or_null, bsa_stream_t stream) {
+                                          const float* key_norms_or_null, const uint32_t* row_order_or_null,
+                                          int64_t row_order_len, bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_block_sparse_attention";
     int rc = common_checks(q, k, v, out, dtype, B, H, S, D, name);
@@ -1168,6 +1197,8 @@ extern "C" int bsa_block_sparse_attention(const void* q, const void* k, const vo
         P.kv_cnt = kv_cnt;
         P.max_kept = (uint32_t)max_kept;
         P.knorm = key_norms_or_null;
+        rc = set_row_order(P, row_order_or_null, row_order_len, name);
+        if (rc) return rc;
         set_order(P, B * H, max_kept);
         if (D == 128 && block == 64) launch_solo<kBlockList>(P, st);
         else if (D == 128 && block == 32) launch_mfma<128, 32, kBlockList>(P, st);
@@ -1326,7 +1357,8 @@ int fill_tile_rows(AttnParams& P, int i, int Hg, int Wg, int a, int b, int c, in
 int tiled_attention(const void* q, const void* k, const void* v, void* out, int dtype, int64_t B, int64_t H, int T,
                     int Hg, int Wg, int64_t D, const int32_t* tiles_host, int n_tiles, const int32_t* head_choice,
                     const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept, float scale, const float* key_norms,
-                    bool pad, bsa_stream_t stream, const char* name) {
+                    const uint32_t* row_order, int64_t row_order_len, bool pad, bsa_stream_t stream,
+                    const char* name) {
     BSA_REQUIRE(T > 0 && Hg > 0 && Wg > 0, "%s: grid must be positive", name);
     const int64_t S = (int64_t)T * Hg * Wg;
     int rc = common_checks(q, k, v, out, dtype, B, H, S, D, name);
@@ -1375,6 +1407,8 @@ int tiled_attention(const void* q, const void* k, const void* v, void* out, int 
     P.n_tiles = (uint32_t)n_tiles;
     P.Hg = (uint32_t)Hg;
     P.Wg = (uint32_t)Wg;
+    rc = set_row_order(P, row_order, row_order_len, name);
+    if (rc) return rc;
     set_order(P, B * H, max_kept);
     if (pad) launch_solo<kBlockList, true, true>(P, (hipStream_t)stream);
     else launch_solo<kBlockList, true>(P, (hipStream_t)stream);
@@ -1389,10 +1423,12 @@ extern "C" int bsa_block_sparse_attention_tiled(const void* q, const void* k, co
                                                 const int32_t* tiles_host, int n_tiles, const int32_t* head_choice,
                                                 const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
                                                 float scale, const float* key_norms_or_null,
+                                                const uint32_t* row_order_or_null, int64_t row_order_len,
                                                 bsa_stream_t stream) {
     clear_error();
     return tiled_attention(q, k, v, out, dtype, B, H, T, Hg, Wg, D, tiles_host, n_tiles, head_choice, kv_idx, kv_cnt,
-                           max_kept, scale, key_norms_or_null, false, stream, "bsa_block_sparse_attention_tiled");
+                           max_kept, scale, key_norms_or_null, row_order_or_null, row_order_len, false, stream,
+                           "bsa_block_sparse_attention_tiled");
 }
 
 extern "C" int bsa_block_sparse_attention_tiled_padded(const void* q, const void* k, const void* v, void* out,
@@ -1403,7 +1439,8 @@ extern "C" int bsa_block_sparse_attention_tiled_padded(const void* q, const void
                                                        const float* key_norms_or_null, bsa_stream_t stream) {
     clear_error();
     return tiled_attention(q, k, v, out, dtype, B, H, T, Hg, Wg, D, tiles_host, n_tiles, head_choice, kv_idx, kv_cnt,
-                           max_kept, scale, key_norms_or_null, true, stream, "bsa_block_sparse_attention_tiled_padded");
+                           max_kept, scale, key_norms_or_null, nullptr, 0, true, stream,
+                           "bsa_block_sparse_attention_tiled_padded");
 }
 
 extern "C" int bsa_tiled_attention_supported(int dtype, int64_t D, int T, int Hg, int Wg, const int32_t* tiles_host,

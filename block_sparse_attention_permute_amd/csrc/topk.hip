@@ -202,6 +202,141 @@ namespace {
 
 int band_width(int diag_width) { return diag_width >= 1 ? 2 * (diag_width / 2) + 1 : 0; }
 
+// Launch plan for block lists whose lengths differ from row to row (the
+// top-p budget: one query block may keep hundreds of key blocks while most
+// keep a handful).  The attention kernels stream each head's K and V tiles
+// through the L2 of the XCD that runs its rows, so a plan keeps a head's
+// rows on one XCD (units: whole heads, or 2, 4, 8 equal row ranges of a head
+// when there are fewer than 16 heads), balances the XCDs' work and starts
+// long rows first:
+//  1. unit weight = its rows' kept counts plus a fixed cost per row
+//     (kRowCost blocks: the prologue and epilogue of a query block);
+//  2. units, heaviest first, go to the least loaded XCD that has room
+//     (longest-processing-time-first list scheduling; every XCD holds up to
+//     ceil(U/8) + ceil(U/32) units, so the grid carries empty slots);
+//  3. an XCD runs its units in that order, each unit's rows in decreasing
+//     count (in kPlanBins coarse bins: counts >= kPlanBins - 1 rank as one).
+// Workgroup w runs on XCD w % 8, so XCD x's j-th row goes to entry 8j + x.
+constexpr int kPlanThreads = 1024, kPlanWaves = kPlanThreads / 64, kPlanBins = 256, kMaxUnits = 2048;
+constexpr uint32_t kRowCost = 5, kEmptySlot = 0xFFFFFFFFu;
+
+struct Plan {
+    int64_t units, unit_rows, cap;  // cap: rows per XCD
+};
+
+Plan plan_shape(int64_t BH, int64_t nq) {
+    int64_t r = 1;
+    while (r < 8 && BH * r < 16) r *= 2;
+    while (nq % r != 0) r /= 2;
+    Plan p;
+    p.units = BH * r;
+    p.unit_rows = nq / r;
+    p.cap = p.unit_rows * ((p.units + 7) / 8 + (p.units + 31) / 32);
+    return p;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* __restrict__ cnt, uint32_t units,
+                                                                uint32_t unit_rows, uint32_t cap, uint32_t len,
+                                                                uint32_t* __restrict__ order) {
+    __shared__ unsigned long long weight[kMaxUnits];
+    __shared__ uint32_t by_rank[kMaxUnits];
+    __shared__ uint32_t place[kMaxUnits];  // (first position on the XCD) << 3 | XCD
+    __shared__ uint32_t fill[8];
+    __shared__ uint32_t bins[kPlanWaves][kPlanBins];
+    const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+    const uint32_t rows = units * unit_rows;
+    auto kept = [&](uint32_t r) { const int c = cnt[r]; return c < 0 ? 0u : (uint32_t)c; };
+
+    for (uint32_t u = t; u < units; u += kPlanThreads) weight[u] = 0;
+    __syncthreads();
+    {   // thread t sums a contiguous run of rows, one LDS add per unit it touches
+        const uint32_t run = (rows + kPlanThreads - 1) / kPlanThreads;
+        const uint32_t r0 = t * run, r1 = min(rows, r0 + run);
+        unsigned long long acc = 0;
+        for (uint32_t r = r0; r < r1; ++r) {
+            acc += kept(r) + kRowCost;
+            if (r + 1 == r1 || (r + 1) % unit_rows == 0) {
+                atomicAdd(&weight[r / unit_rows], acc);
+                acc = 0;
+            }
+        }
+    }
+    __syncthreads();
+    for (uint32_t u = t; u < units; u += kPlanThreads) {
+        const unsigned long long w = weight[u];
+        uint32_t rank = 0;
+        for (uint32_t v = 0; v < units; ++v) {
+            const unsigned long long x = weight[v];
+            rank += (x > w || (x == w && v < u)) ? 1u : 0u;
+        }
+        by_rank[rank] = u;
+    }
+    __syncthreads();
+    if (t == 0) {
+        unsigned long long load[8];
+        uint32_t f[8];
+        for (int x = 0; x < 8; ++x) load[x] = 0, f[x] = 0;
+        for (uint32_t k = 0; k < units; ++k) {
+            const uint32_t u = by_rank[k];
+            int best = -1;
+            for (int x = 0; x < 8; ++x)
+                if (f[x] + unit_rows <= cap && (best < 0 || load[x] < load[best])) best = x;
+            place[u] = (f[best] << 3) | (uint32_t)best;
+            f[best] += unit_rows;
+            load[best] += weight[u];
+        }
+        for (int x = 0; x < 8; ++x) fill[x] = f[x];
+    }
+    __syncthreads();
+    // slots past each XCD's last row, and past the plan, are empty
+    for (uint32_t e = t; e < len; e += kPlanThreads) {
+        const uint32_t x = e & 7u, p = e >> 3;
+        if (e >= 8u * cap || p >= fill[x]) order[e] = kEmptySlot;
+    }
+    // each wave sorts one unit at a time by decreasing count
+    for (uint32_t base = 0; base < units; base += kPlanWaves) {
+        const uint32_t u = base + wave;
+        const bool active = u < units;
+        uint32_t* b = bins[wave];
+        for (uint32_t i = lane; i < kPlanBins; i += 64) b[i] = 0;
+        __syncthreads();
+        const uint32_t r0 = u * unit_rows;
+        auto bin_of = [&](uint32_t r) { const uint32_t c = kept(r); return c >= kPlanBins - 1 ? 0u : kPlanBins - 1 - c; };
+        if (active)
+            for (uint32_t i = lane; i < unit_rows; i += 64) atomicAdd(&b[bin_of(r0 + i)], 1u);
+        __syncthreads();
+        constexpr int kPer = kPlanBins / 64;
+        uint32_t own[kPer], sum = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            own[j] = b[lane * kPer + j];
+            sum += own[j];
+        }
+        uint32_t incl = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(incl, off);
+            if (lane >= (uint32_t)off) incl += y;
+        }
+        __syncthreads();
+        uint32_t run = incl - sum;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            b[lane * kPer + j] = run;
+            run += own[j];
+        }
+        __syncthreads();
+        if (active) {
+            const uint32_t x = place[u] & 7u, p0 = place[u] >> 3;
+            for (uint32_t i = lane; i < unit_rows; i += 64) {
+                const uint32_t rank = atomicAdd(&b[bin_of(r0 + i)], 1u);
+                order[8u * (p0 + rank) + x] = r0 + i;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 template <bool TOPP>
 int launch_select(TopkParams& P, hipStream_t st, const char* name) {
     const uint64_t blocks = (P.rows + 3) / 4;
@@ -321,4 +456,37 @@ extern "C" int bsa_topk_block_mask_tiled(const float* scores, int64_t B, int64_t
     P.head_choice = head_choice;
     P.n_table = (uint32_t)n_table;
     return launch_select<false>(P, (hipStream_t)stream, name);
+}
+
+extern "C" int64_t bsa_row_order_len(int64_t BH, int64_t nq) {
+    clear_error();
+    if (BH < 1 || nq < 1 || BH * nq >= ((int64_t)1 << 31)) {
+        set_error("bsa_row_order_len: BH=%lld and nq=%lld must be >= 1 with BH*nq < 2^31", (long long)BH,
+                  (long long)nq);
+        return -1;
+    }
+    const Plan p = plan_shape(BH, nq);
+    if (p.units > kMaxUnits) {
+        set_error("bsa_row_order_len: more than %d heads", kMaxUnits);
+        return -1;
+    }
+    if (8 * p.cap >= ((int64_t)1 << 31)) {
+        set_error("bsa_row_order_len: the plan would exceed 2^31 entries");
+        return -1;
+    }
+    return 8 * p.cap;
+}
+
+extern "C" int bsa_row_order(const int32_t* kv_cnt, int64_t BH, int64_t nq, uint32_t* order, int64_t order_len,
+                             bsa_stream_t stream) {
+    const char* name = "bsa_row_order";
+    const int64_t need = bsa_row_order_len(BH, nq);
+    if (need < 0) return BSA_ERR_INVALID_ARG;
+    BSA_REQUIRE(kv_cnt && order, "%s: NULL argument", name);
+    BSA_REQUIRE(order_len >= need && order_len < ((int64_t)1 << 31), "%s: order_len=%lld must be in [%lld, 2^31)",
+                name, (long long)order_len, (long long)need);
+    const Plan p = plan_shape(BH, nq);
+    row_plan_kernel<<<1, kPlanThreads, 0, (hipStream_t)stream>>>(kv_cnt, (uint32_t)p.units, (uint32_t)p.unit_rows,
+                                                                 (uint32_t)p.cap, (uint32_t)order_len, order);
+    return check_launch(name);
 }

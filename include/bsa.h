@@ -337,6 +337,33 @@ int bsa_top_p_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int 
                          int32_t* kv_cnt, int max_kept, uint8_t* mask_or_null,
                          bsa_stream_t stream);
 
+/* Launch plan for block lists whose lengths differ from row to row, as the
+ * top-p lists above do: a scheduling aid that is no step of the method and
+ * changes no result (the attention calls take it as row_order).  The
+ * attention kernels read each head's K and V tiles through the L2 cache of
+ * the XCD that runs the head's rows (workgroup w runs on XCD w % 8), so the
+ * plan keeps each unit's rows on one XCD, where a unit is a head (B*H >= 16)
+ * or 2, 4 or 8 equal ranges of a head's rows (fewer heads; a count that
+ * divides Nq); it gives each unit the weight (sum over its rows of
+ * max(kv_cnt, 0) + 5), assigns the units heaviest first to the least loaded
+ * XCD with room (longest processing time first; each XCD holds up to
+ * ceil(U/8) + ceil(U/32) units of U), and runs an XCD's units in that order,
+ * each unit's rows in decreasing count (counts of 255 or more rank as one;
+ * rows of one rank come in no fixed order).  order[8j + x] is the j-th row
+ * (b*H + h)*Nq + I of XCD x, and 0xFFFFFFFF an empty slot.
+ * kv_cnt: device int32 (BH * Nq); order: device uint32 (order_len).
+ * One workgroup, reading kv_cnt twice.
+ * INVALID_ARG unless order_len >= bsa_row_order_len(BH, Nq) > 0 and
+ * order_len < 2^31. */
+int bsa_row_order(const int32_t* kv_cnt, int64_t BH, int64_t Nq, uint32_t* order, int64_t order_len,
+                  bsa_stream_t stream);
+
+/* Host: the length of bsa_row_order's plan for BH heads of Nq rows (at least
+ * BH * Nq: the plan carries empty slots), or -1 (and bsa_last_error) unless
+ * BH, Nq >= 1, BH * Nq < 2^31, the plan has at most 2048 units and fewer
+ * than 2^31 entries.  Nothing is launched. */
+int64_t bsa_row_order_len(int64_t BH, int64_t Nq);
+
 /* bsa_topk_block_mask with a per-head budget and block count: head (b, h)
  * uses k = k_table[c] and nk = nk_table[c], c = head_choice[b*H + h]
  * (device int32, trusted to lie in [0, n_table)).  Only key blocks J < nk
@@ -377,11 +404,20 @@ int bsa_topk_block_mask_tiled(const float* scores, int64_t B, int64_t H, int Nq,
  * weight exceeds 2^32) skips the running-max update, so its
  * softmax weights are taken relative to an older max (an exact shift of the
  * softmax; the weights are rounded to bf16 at a different scale).
- * INVALID_ARG unless block divides S and max_kept >= 1. */
+ * row_order_or_null, row_order_len: a launch order (as bsa_row_order writes
+ * it) or NULL, 0.  Given one, the bf16 kernels run row_order_len workgroups,
+ * workgroup w taking row row_order[w] = (b*H + h)*(S/block) + I; entries
+ * past the last row are empty slots, each row must appear exactly once
+ * (a row left out is not written).  NULL keeps the library's own order.  The
+ * result does not depend on the order; the fp32 / scalar kernel ignores it.
+ * INVALID_ARG unless block divides S, max_kept >= 1 and, with an order,
+ * 1 <= row_order_len < 2^31. */
 int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void* out, int dtype,
                                int64_t B, int64_t H, int64_t S, int64_t D, int block,
                                const int32_t* kv_idx, const int32_t* kv_cnt, int max_kept,
-                               float scale, const float* key_norms_or_null, bsa_stream_t stream);
+                               float scale, const float* key_norms_or_null,
+                               const uint32_t* row_order_or_null, int64_t row_order_len,
+                               bsa_stream_t stream);
 
 /* Block-sparse attention on T-major q, k, v, out: query/key block J of head
  * (b, h) is tile J of candidate c = head_choice[b*H + h] (0 if NULL), and the
@@ -397,13 +433,17 @@ int bsa_block_sparse_attention(const void* q, const void* k, const void* v, void
  * T-major offsets from the group's first cell (one row pattern per LDS-DMA
  * row group): an x extent that is a multiple of 4, or e.g. (16, 2, 2),
  * (8, 8, 1); bsa_tiled_attention_supported answers on the host.
+ * row_order_or_null, row_order_len: as in bsa_block_sparse_attention, over
+ * the S/64 tiles of each head.
  * INVALID_ARG if a candidate does not divide the grid. */
 int bsa_block_sparse_attention_tiled(const void* q, const void* k, const void* v, void* out,
                                      int dtype, int64_t B, int64_t H, int T, int Hg, int Wg,
                                      int64_t D, const int32_t* tiles_host, int n_tiles,
                                      const int32_t* head_choice, const int32_t* kv_idx,
                                      const int32_t* kv_cnt, int max_kept, float scale,
-                                     const float* key_norms_or_null, bsa_stream_t stream);
+                                     const float* key_norms_or_null,
+                                     const uint32_t* row_order_or_null, int64_t row_order_len,
+                                     bsa_stream_t stream);
 
 /* bsa_block_sparse_attention_tiled on the zero-padded grids of candidates
  * that do not divide T [Adaptive tiling (SPADE), "Deviations and notes": pad

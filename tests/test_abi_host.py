@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_empty_error(L):
-    assert bsa.bsa_version() >> 16 == 1
+    assert bsa.bsa_version() >> 16 == bsa.ABI_MAJOR == 2
     assert isinstance(L.bsa_last_error(), bytes)
 
 
@@ -206,9 +206,20 @@ def test_device_calls_reject_bad_arguments(L):
         ("bsa_top_p_block_mask", (FAKE, 1, 1, 480, 480, ctypes.c_float(0.5), ctypes.c_float(1.0), 1, 1, FAKE, FAKE,
                                   479, None, None), "max_kept"),
         ("bsa_block_sparse_attention",
-         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 100, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None, None), "divide"),
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 100, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None, None, 0, None),
+         "divide"),
         ("bsa_block_sparse_attention",
-         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 0, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None, None), "> 0"),
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 0, 128, 64, FAKE, FAKE, 8, ctypes.c_float(0.1), None, None, 0, None),
+         "> 0"),
+        ("bsa_block_sparse_attention",
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 1, 128, 128, 64, FAKE, FAKE, 2, ctypes.c_float(0.1), None, FAKE, 0, None),
+         "row_order_len"),
+        ("bsa_block_sparse_attention_tiled",
+         (FAKE, FAKE, FAKE, FAKE, BF, 1, 2, 20, 32, 48, 128, TILES, 2, None, FAKE, FAKE, 82, ctypes.c_float(0.1),
+          None, FAKE, 1 << 31, None), "row_order_len"),
+        ("bsa_row_order", (FAKE, 40, 480, FAKE, 26879, None), "order_len"),
+        ("bsa_row_order", (None, 40, 480, FAKE, 26880, None), "NULL"),
+        ("bsa_row_order", (FAKE, 0, 480, FAKE, 26880, None), "BH"),
         ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 0, 2, ctypes.c_float(0.25), 8, None),
          "window"),
         ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, -1, ctypes.c_float(0.25), 8, None),
@@ -255,6 +266,21 @@ def test_device_calls_reject_bad_arguments(L):
         rc, msg = _rc(L, name, *args)
         assert rc == bsa.BSA_ERR_INVALID_ARG, (name, rc, msg)
         assert needle in msg, (name, msg)
+
+
+def test_row_order_len(L):
+    """Plan length = 8 XCDs x rows per XCD, where an XCD holds up to ceil(U/8) + ceil(U/32) units of U."""
+    assert bsa.bsa_row_order_len(40, 480) == 8 * 480 * (5 + 2)      # whole heads
+    assert bsa.bsa_row_order_len(24, 1920) == 8 * 1920 * (3 + 1)
+    assert bsa.bsa_row_order_len(6, 64) == 8 * 16 * (3 + 1)         # 24 units: a quarter head each
+    assert bsa.bsa_row_order_len(1, 480) == 8 * 60 * (1 + 1)        # 8 units of 60 rows
+    assert bsa.bsa_row_order_len(2, 7) == 8 * 7 * (1 + 1)           # 7 rows do not split: whole heads
+    assert bsa.bsa_row_order_len(2048, 3) == 8 * 3 * (256 + 64)
+    for bh, nq in [(40, 480), (6, 64), (1, 1), (3, 5)]:
+        assert bsa.bsa_row_order_len(bh, nq) >= bh * nq
+    for bh, nq in [(0, 4), (4, 0), (2049, 1), (1 << 16, 1 << 15)]:
+        with pytest.raises(ValueError):
+            bsa.bsa_row_order_len(bh, nq)
 
 
 def test_unaligned_tensors_rejected(L):

@@ -1,0 +1,185 @@
+"""Launch plans for block lists of varying length (bsa_row_order).
+
+A plan only decides which workgroup runs which query block, so attention under a plan must equal attention
+without one bit for bit.  The plan itself is checked against the scheduling rule bsa.h states, written out
+here on the host: unit placement exactly, and inside each unit the rows as a set with non-increasing counts
+(rows of one count may come in any order).
+"""
+import numpy as np
+import pytest
+
+from block_sparse_attention_permute_amd import bsa, synth
+from oracle import attention as OA
+from tests.gpu_helpers import BF16_ATOL, f64, gpu, max_abs, torch_gpu
+
+EMPTY = -1          # an empty slot, 0xFFFFFFFF read as int32
+ROW_COST = 5        # fixed cost of a row in the unit weights, in blocks
+BINS = 256          # counts of BINS - 1 or more rank as one
+
+
+def plan_rule(cnt):
+    """(units of each XCD in run order, rows per unit, rows per XCD) for counts cnt of shape (BH, Nq)."""
+    BH, nq = cnt.shape
+    r = 1
+    while r < 8 and BH * r < 16:
+        r *= 2
+    while nq % r:
+        r //= 2
+    ur, U = nq // r, BH * r
+    flat = np.maximum(cnt.reshape(-1).astype(np.int64), 0)
+    weight = [int(flat[u * ur:(u + 1) * ur].sum()) + ROW_COST * ur for u in range(U)]
+    room = -(-U // 8) + -(-U // 32)
+    load, units = [0] * 8, [[] for _ in range(8)]
+    for u in sorted(range(U), key=lambda u: (-weight[u], u)):
+        x = min((x for x in range(8) if len(units[x]) < room), key=lambda x: (load[x], x))
+        units[x].append(u)
+        load[x] += weight[u]
+    return units, ur, room * ur
+
+
+def check_plan(order, cnt):
+    units, ur, cap = plan_rule(cnt)
+    o = order.cpu().numpy().astype(np.int64)
+    assert o.size >= 8 * cap == bsa.bsa_row_order_len(*cnt.shape)
+    assert np.all(o[8 * cap:] == EMPTY)
+    key = np.minimum(np.maximum(cnt.reshape(-1), 0), BINS - 1)
+    for x in range(8):
+        lane = o[:8 * cap][x::8]
+        assert np.all(lane[len(units[x]) * ur:] == EMPTY), x
+        for j, u in enumerate(units[x]):
+            seg = lane[j * ur:(j + 1) * ur]
+            assert np.array_equal(np.sort(seg), np.arange(u * ur, (u + 1) * ur)), (x, u)
+            assert np.all(np.diff(key[seg]) <= 0), (x, u)
+
+
+def skewed_counts(shape, rng, top):
+    """Mostly short lists and a few long ones (the top-p shape), with 0, negative and > 255 entries mixed in."""
+    c = np.minimum(top, (rng.pareto(1.1, shape) * 4).astype(np.int64) + 1)
+    c[rng.random(shape) < 0.02] = 0
+    c[rng.random(shape) < 0.01] = -3
+    c[rng.random(shape) < 0.01] = 300
+    return c.astype(np.int32)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,H,nq", [(1, 40, 480), (2, 3, 64), (1, 1, 7), (1, 5, 12), (1, 2048, 2), (1, 1, 1),
+                                    (3, 8, 40)])
+def test_plan_follows_its_rule(B, H, nq):
+    torch = torch_gpu()
+    rng = np.random.default_rng(B * 1000 + H * 10 + nq)
+    cnt = skewed_counts((B, H, nq), rng, 5000)
+    cg = torch.from_numpy(cnt).cuda()
+    check_plan(bsa.bsa_row_order(cg), cnt.reshape(B * H, nq))
+    n = bsa.bsa_row_order_len(B * H, nq)
+    longer = torch.full((n + 37,), 7, dtype=torch.int32, device="cuda")     # a longer buffer: the rest is empty
+    check_plan(bsa.bsa_row_order(cg, out=longer), cnt.reshape(B * H, nq))
+
+
+def _varying_lists(B, H, nb, rng):
+    """Full-width lists whose lengths run from 0 to nb (density per row cubed), the diagonal kept."""
+    torch = torch_gpu()
+    dens = rng.random((B, H, nb, 1)) ** 3
+    keep = rng.random((B, H, nb, nb)) < dens
+    keep[..., np.arange(nb), np.arange(nb)] |= rng.random((B, H, nb)) < 0.9
+    keep[0, 0, 1] = False                                        # an empty list: written as zeros
+    cnt = keep.sum(-1).astype(np.int32)
+    idx = np.full((B, H, nb, nb), -1, np.int32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                li = np.flatnonzero(keep[b, h, i])
+                idx[b, h, i, :li.size] = li
+    return keep, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+
+
+def _any_order(rows, rng):
+    """A random permutation of the rows with empty slots strewn among them."""
+    torch = torch_gpu()
+    o = np.concatenate([rng.permutation(rows), np.full(rows // 3 + 5, EMPTY)]).astype(np.int32)
+    return torch.from_numpy(rng.permutation(o)).cuda()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D,block", [(128, 64), (64, 64), (128, 32), (64, 32)])
+def test_block_list_attention_under_a_plan(D, block):
+    """bf16 block lists of every length on each MFMA kernel (B = 2, H = 3): the planned launch and a random
+    padded order give the unplanned result bit for bit; rows of head (1, 2) under the plan match the oracle."""
+    torch = torch_gpu()
+    B, H, S = 2, 3, 2048
+    nb = S // block
+    rng = np.random.default_rng(D + block)
+    keep, kv_idx, kv_cnt = _varying_lists(B, H, nb, rng)
+    q, k, v = (synth.normal_bits((B, H, S, D), seed=7100 + D + block + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    ref = bsa.bsa_block_sparse_attention(qg, kg, vg, kv_idx, kv_cnt, block)
+    plan = bsa.bsa_row_order(kv_cnt)
+    check_plan(plan, kv_cnt.cpu().numpy().reshape(B * H, nb))
+    out = bsa.bsa_block_sparse_attention(qg, kg, vg, kv_idx, kv_cnt, block, row_order=plan)
+    assert torch.equal(out, ref)
+    out2 = bsa.bsa_block_sparse_attention(qg, kg, vg, kv_idx, kv_cnt, block, row_order=_any_order(B * H * nb, rng))
+    assert torch.equal(out2, ref)
+    o = f64(out)[1, 2]
+    seen = keep[1, 2].any(-1)
+    rows = np.flatnonzero(np.repeat(seen, block))
+    qf, kf, vf = (synth.stored_to_f64(x)[1, 2] for x in (q, k, v))
+    want = OA.block_sparse_rows_gathered(qf, kf, vf, keep[1, 2], block, rows, D ** -0.5)
+    assert max_abs(o[rows], want) <= BF16_ATOL
+    assert np.all(o[np.repeat(~seen, block)] == 0.0)
+
+
+@pytest.mark.gpu
+def test_f32_attention_ignores_the_plan():
+    torch = torch_gpu()
+    B, H, S, D, block = 1, 2, 256, 32, 32
+    rng = np.random.default_rng(77)
+    _, kv_idx, kv_cnt = _varying_lists(B, H, S // block, rng)
+    q, k, v = (synth.normal_bits((B, H, S, D), seed=7700 + i, dtype="f32") for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    ref = bsa.bsa_block_sparse_attention(qg, kg, vg, kv_idx, kv_cnt, block)
+    out = bsa.bsa_block_sparse_attention(qg, kg, vg, kv_idx, kv_cnt, block, row_order=bsa.bsa_row_order(kv_cnt))
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.gpu
+def test_tiled_attention_under_a_plan():
+    """T-major tensors, two tilings, five heads (not a multiple of 8), lists of every length: the planned
+    launch equals the unplanned one and the permuted path bit for bit; so does a random padded order."""
+    torch = torch_gpu()
+    grid, tiles, H, D = (4, 32, 32), [(1, 8, 8), (4, 4, 4)], 5, 128
+    S, nb = 4096, 64
+    rng = np.random.default_rng(5151)
+    _, kv_idx, kv_cnt = _varying_lists(1, H, nb, rng)
+    q, k, v = (synth.normal_bits((1, H, S, D), seed=5200 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    choice = torch.tensor([[0, 1, 1, 0, 1]], dtype=torch.int32, device="cuda")
+    kn = torch.full((1, H, nb), -1.0, dtype=torch.float32, device="cuda")
+    bsa.bsa_minmax_block_scores_tiled(qg, kg, grid, tiles, head_choice=choice, key_norms=kn)
+    for norms in (None, kn):
+        ref = bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, grid, tiles, kv_idx, kv_cnt, head_choice=choice,
+                                                   key_norms=norms)
+        for order in (bsa.bsa_row_order(kv_cnt), _any_order(H * nb, rng)):
+            out = bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, grid, tiles, kv_idx, kv_cnt, head_choice=choice,
+                                                       key_norms=norms, row_order=order)
+            assert torch.equal(out, ref)
+    qp, kp, vp = (bsa.bsa_tile_permute(x, grid, tiles, head_choice=choice) for x in (qg, kg, vg))
+    perm = bsa.bsa_invert_permute(bsa.bsa_block_sparse_attention(qp, kp, vp, kv_idx, kv_cnt, 64), grid, tiles,
+                                  head_choice=choice)
+    assert torch.equal(ref, perm)
+
+
+@pytest.mark.gpu
+def test_top_p_pipeline_plans_its_launch():
+    """The top-p pipeline plans its attention launch: the plan follows the rule for the pipeline's own lists,
+    and the pipeline's output equals the unplanned attention on the same lists bit for bit."""
+    torch = torch_gpu()
+    grid, tiles, H, D = (4, 32, 32), [(1, 8, 8), (4, 4, 4)], 6, 128
+    q, k, v = (synth.normal_bits((1, H, 4096, D), seed=5300 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    pipe = bsa.AdaptiveBlockSparse(1, H, grid, D, tiles, 0.25, qg.dtype, qg.device, top_p=0.7, p_scale=D ** -0.5)
+    out = pipe(qg, kg, vg)
+    kv_idx, kv_cnt = pipe.kv
+    assert pipe.ws_order is not None
+    check_plan(pipe.ws_order, kv_cnt.cpu().numpy().reshape(H, -1))
+    ref = bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, grid, tiles, kv_idx, kv_cnt, head_choice=pipe.choice,
+                                               key_norms=pipe.ws_knorm)
+    assert torch.equal(out, ref)
