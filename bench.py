@@ -360,6 +360,20 @@ def kernel_only(args, torch, bsa, synth):
                       "ms_per_call": round(ms, 4)}), flush=True)
 
 
+def top_p_pipeline(args, torch, bsa, synth):
+    """The Wan-shape top-p step (tiling choice, scores, top-p lists, launch plan, attention), --warmup + --steps
+    calls, one line of timing (for profilers)."""
+    wl = synth.WORKLOADS[4]
+    dev = torch.device("cuda:0")
+    log(f"generating inputs: {wl.name}")
+    q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(4))
+    out = torch.empty_like(q)
+    pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, TILES, FRAC, q.dtype, dev, top_p=0.9, p_scale=wl.D ** -0.5)
+    ms = _time(torch, lambda: pipe(q, k, v, out=out), max(args.steps, 1), args.warmup)
+    print(json.dumps({"top_p_pipeline": wl.name, "calls": args.warmup + max(args.steps, 1),
+                      "ms_per_step": round(ms, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,6 +386,8 @@ def main():
     ap.add_argument("--kernel-only", type=int, choices=(3, 4, 5), default=None,
                     help="only run the hot kernel of one workload (3: windowed attention; 4, 5: block-sparse attention "
                          "on the pipeline's lists) --warmup + --steps times, for profilers")
+    ap.add_argument("--top-p-pipeline", action="store_true",
+                    help="only run the Wan-shape top-p step (p = 0.9) --warmup + --steps times, for profilers")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -404,6 +420,9 @@ def main():
 
     if args.kernel_only is not None:
         kernel_only(args, torch, bsa, synth)
+        return
+    if args.top_p_pipeline:
+        top_p_pipeline(args, torch, bsa, synth)
         return
 
     wl = synth.WORKLOADS[CFG]

@@ -210,15 +210,21 @@ int band_width(int diag_width) { return diag_width >= 1 ? 2 * (diag_width / 2) +
 // when there are fewer than 16 heads), balances the XCDs' work and starts
 // long rows first:
 //  1. unit weight = its rows' kept counts plus a fixed cost per row
-//     (kRowCost blocks: the prologue and epilogue of a query block);
-//  2. units, heaviest first, go to the least loaded XCD that has room
-//     (longest-processing-time-first list scheduling; every XCD holds up to
-//     ceil(U/8) + ceil(U/32) units, so the grid carries empty slots);
-//  3. an XCD runs its units in that order, each unit's rows in decreasing
-//     count (in kPlanBins coarse bins: counts >= kPlanBins - 1 rank as one).
+//     (kRowCost blocks: the prologue and epilogue of a query block), all
+//     weights shifted right by the bits that bring their total under 2^28
+//     (none at any size met here), so that loads fit 32-bit keys;
+//  2. units, heaviest first, go to the least loaded XCD that holds fewer
+//     than ceil(U/8) units (list scheduling, longest processing time first,
+//     with equal room on every XCD so that the grid needs almost no empty
+//     slots);
+//  3. an XCD runs its units in the order they came, each unit's rows in
+//     decreasing count (in kPlanBins coarse bins: counts >= kPlanBins - 1
+//     rank as one).
 // Workgroup w runs on XCD w % 8, so XCD x's j-th row goes to entry 8j + x.
-constexpr int kPlanThreads = 1024, kPlanWaves = kPlanThreads / 64, kPlanBins = 256, kMaxUnits = 2048;
-constexpr uint32_t kRowCost = 5, kEmptySlot = 0xFFFFFFFFu;
+// One workgroup does it all; the counts are read once into LDS (up to
+// kCacheRows rows; longer lists are read from memory at each step).
+constexpr int kPlanThreads = 1024, kPlanWaves = kPlanThreads / 64, kPlanBins = 256, kMaxUnits = 1024;
+constexpr uint32_t kRowCost = 5, kEmptySlot = 0xFFFFFFFFu, kCacheRows = 49152;
 
 struct Plan {
     int64_t units, unit_rows, cap;  // cap: rows per XCD
@@ -231,61 +237,122 @@ Plan plan_shape(int64_t BH, int64_t nq) {
     Plan p;
     p.units = BH * r;
     p.unit_rows = nq / r;
-    p.cap = p.unit_rows * ((p.units + 7) / 8 + (p.units + 31) / 32);
+    p.cap = p.unit_rows * ((p.units + 7) / 8);
     return p;
+}
+
+__device__ __forceinline__ uint32_t plan_key(uint32_t c) {
+    // bin of a count: longest first, counts of kPlanBins - 1 or more in bin 0
+    return c >= kPlanBins - 1 ? 0u : kPlanBins - 1 - c;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* __restrict__ cnt, uint32_t units,
                                                                 uint32_t unit_rows, uint32_t cap, uint32_t len,
                                                                 uint32_t* __restrict__ order) {
+    __shared__ uint16_t cache[kCacheRows];
     __shared__ unsigned long long weight[kMaxUnits];
+    __shared__ uint32_t weight32[kMaxUnits];
+    __shared__ uint32_t ranked_weight[kMaxUnits];
+    __shared__ unsigned long long partial[kPlanWaves];
     __shared__ uint32_t by_rank[kMaxUnits];
     __shared__ uint32_t place[kMaxUnits];  // (first position on the XCD) << 3 | XCD
     __shared__ uint32_t fill[8];
     __shared__ uint32_t bins[kPlanWaves][kPlanBins];
     const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
     const uint32_t rows = units * unit_rows;
-    auto kept = [&](uint32_t r) { const int c = cnt[r]; return c < 0 ? 0u : (uint32_t)c; };
-
-    for (uint32_t u = t; u < units; u += kPlanThreads) weight[u] = 0;
-    __syncthreads();
-    {   // thread t sums a contiguous run of rows, one LDS add per unit it touches
-        const uint32_t run = (rows + kPlanThreads - 1) / kPlanThreads;
-        const uint32_t r0 = t * run, r1 = min(rows, r0 + run);
-        unsigned long long acc = 0;
-        for (uint32_t r = r0; r < r1; ++r) {
-            acc += kept(r) + kRowCost;
-            if (r + 1 == r1 || (r + 1) % unit_rows == 0) {
-                atomicAdd(&weight[r / unit_rows], acc);
-                acc = 0;
+    const bool cached = rows <= kCacheRows;
+    // counts clamped to [0, 65535], eight loads in flight per lane
+    if (cached) {
+        for (uint32_t base = 0; base < rows; base += 8u * kPlanThreads) {
+            int c[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t r = base + (uint32_t)k * kPlanThreads + t;
+                c[k] = r < rows ? cnt[r] : 0;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t r = base + (uint32_t)k * kPlanThreads + t;
+                if (r < rows) cache[r] = (uint16_t)min(max(c[k], 0), 65535);
             }
         }
     }
     __syncthreads();
+    auto count = [&](uint32_t r) -> uint32_t {
+        if (cached) return cache[r];
+        return (uint32_t)min(max(cnt[r], 0), 65535);
+    };
+    // 1. unit weights, one wave per unit
+    for (uint32_t u = wave; u < units; u += kPlanWaves) {
+        unsigned long long w = 0;
+        for (uint32_t i = lane; i < unit_rows; i += 64) w += count(u * unit_rows + i) + kRowCost;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) w += __shfl_xor(w, off);
+        if (lane == 0) weight[u] = w;
+    }
+    __syncthreads();
+    {   // total weight -> the shift that brings it under 2^28 (units <= kPlanThreads: one unit per thread)
+        unsigned long long w = t < units ? weight[t] : 0ull;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) w += __shfl_xor(w, off);
+        if (lane == 0) partial[wave] = w;
+        __syncthreads();
+        unsigned long long total = 0;
+#pragma unroll
+        for (int i = 0; i < kPlanWaves; ++i) total += partial[i];
+        const int bits = total == 0 ? 0 : 64 - __builtin_clzll(total);
+        const int shift = bits > 28 ? bits - 28 : 0;
+        if (t < units) weight32[t] = (uint32_t)(weight[t] >> shift);
+    }
+    __syncthreads();
+    // units ranked by weight, heaviest first (ties: lower unit first)
     for (uint32_t u = t; u < units; u += kPlanThreads) {
-        const unsigned long long w = weight[u];
+        const uint32_t w = weight32[u];
         uint32_t rank = 0;
         for (uint32_t v = 0; v < units; ++v) {
-            const unsigned long long x = weight[v];
+            const uint32_t x = weight32[v];
             rank += (x > w || (x == w && v < u)) ? 1u : 0u;
         }
         by_rank[rank] = u;
+        ranked_weight[rank] = w;
     }
     __syncthreads();
-    if (t == 0) {
-        unsigned long long load[8];
-        uint32_t f[8];
-        for (int x = 0; x < 8; ++x) load[x] = 0, f[x] = 0;
-        for (uint32_t k = 0; k < units; ++k) {
-            const uint32_t u = by_rank[k];
-            int best = -1;
-            for (int x = 0; x < 8; ++x)
-                if (f[x] + unit_rows <= cap && (best < 0 || load[x] < load[best])) best = x;
-            place[u] = (f[best] << 3) | (uint32_t)best;
-            f[best] += unit_rows;
-            load[best] += weight[u];
+    // 2. list scheduling in wave 0 on wave-uniform values: XCD x's load is kept as the key (load << 3) | x
+    //    (< 2^31), so the least loaded XCD (ties: lower XCD) is the smallest key of those with room, found
+    //    without branches; 64 ranked units at a time are read into a VGPR, one per lane, taken out lane by
+    //    lane, and their placements gathered in a VGPR that is written once
+    if (wave == 0) {
+        const uint32_t room = cap / unit_rows;   // units an XCD may hold: ceil(U/8)
+        uint32_t key[8], held[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) key[x] = (uint32_t)x, held[x] = 0;
+        for (uint32_t k0 = 0; k0 < units; k0 += 64) {
+            const bool has = k0 + lane < units;
+            const uint32_t my_u = has ? by_rank[k0 + lane] : 0u;
+            const uint32_t my_w = has ? ranked_weight[k0 + lane] : 0u;
+            uint32_t my_place = 0;
+            const uint32_t n = min(64u, units - k0);
+            for (uint32_t j = 0; j < n; ++j) {
+                const uint32_t w8 = (uint32_t)__builtin_amdgcn_readlane((int)my_w, (int)j) << 3;
+                uint32_t best = ~0u;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) best = min(best, held[x] < room ? key[x] : ~0u);
+                const uint32_t bx = best & 7u;
+                uint32_t first = 0;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const bool hit = (uint32_t)x == bx;
+                    first = hit ? held[x] : first;
+                    key[x] += hit ? w8 : 0u;
+                    held[x] += hit ? 1u : 0u;
+                }
+                my_place = lane == j ? (((first * unit_rows) << 3) | bx) : my_place;
+            }
+            if (has) place[my_u] = my_place;
         }
-        for (int x = 0; x < 8; ++x) fill[x] = f[x];
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+            if (lane == (uint32_t)x) fill[x] = held[x] * unit_rows;
     }
     __syncthreads();
     // slots past each XCD's last row, and past the plan, are empty
@@ -293,7 +360,7 @@ __global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* _
         const uint32_t x = e & 7u, p = e >> 3;
         if (e >= 8u * cap || p >= fill[x]) order[e] = kEmptySlot;
     }
-    // each wave sorts one unit at a time by decreasing count
+    // 3. each wave sorts one unit at a time by decreasing count
     for (uint32_t base = 0; base < units; base += kPlanWaves) {
         const uint32_t u = base + wave;
         const bool active = u < units;
@@ -301,9 +368,8 @@ __global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* _
         for (uint32_t i = lane; i < kPlanBins; i += 64) b[i] = 0;
         __syncthreads();
         const uint32_t r0 = u * unit_rows;
-        auto bin_of = [&](uint32_t r) { const uint32_t c = kept(r); return c >= kPlanBins - 1 ? 0u : kPlanBins - 1 - c; };
         if (active)
-            for (uint32_t i = lane; i < unit_rows; i += 64) atomicAdd(&b[bin_of(r0 + i)], 1u);
+            for (uint32_t i = lane; i < unit_rows; i += 64) atomicAdd(&b[plan_key(count(r0 + i))], 1u);
         __syncthreads();
         constexpr int kPer = kPlanBins / 64;
         uint32_t own[kPer], sum = 0;
@@ -329,7 +395,7 @@ __global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* _
         if (active) {
             const uint32_t x = place[u] & 7u, p0 = place[u] >> 3;
             for (uint32_t i = lane; i < unit_rows; i += 64) {
-                const uint32_t rank = atomicAdd(&b[bin_of(r0 + i)], 1u);
+                const uint32_t rank = atomicAdd(&b[plan_key(count(r0 + i))], 1u);
                 order[8u * (p0 + rank) + x] = r0 + i;
             }
         }

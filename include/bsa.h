@@ -344,23 +344,26 @@ int bsa_top_p_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int 
  * the XCD that runs the head's rows (workgroup w runs on XCD w % 8), so the
  * plan keeps each unit's rows on one XCD, where a unit is a head (B*H >= 16)
  * or 2, 4 or 8 equal ranges of a head's rows (fewer heads; a count that
- * divides Nq); it gives each unit the weight (sum over its rows of
- * max(kv_cnt, 0) + 5), assigns the units heaviest first to the least loaded
- * XCD with room (longest processing time first; each XCD holds up to
- * ceil(U/8) + ceil(U/32) units of U), and runs an XCD's units in that order,
- * each unit's rows in decreasing count (counts of 255 or more rank as one;
- * rows of one rank come in no fixed order).  order[8j + x] is the j-th row
- * (b*H + h)*Nq + I of XCD x, and 0xFFFFFFFF an empty slot.
+ * divides Nq).  Each unit weighs the sum over its rows of c + 5, with c the
+ * row's kv_cnt clamped to [0, 65535], shifted right by the bits that bring
+ * the total of all weights under 2^28 (none unless that total reaches it);
+ * units, heaviest first (ties: lower unit first), go to the least loaded
+ * XCD (ties: lower XCD first) among those holding fewer than ceil(U/8) of
+ * the U units.  An XCD runs its units
+ * in the order they came, each unit's rows in decreasing c (values of 255 or
+ * more rank as one; rows of one rank come in no fixed order).  order[8j + x] is the j-th row (b*H + h)*Nq + I of XCD x,
+ * and 0xFFFFFFFF an empty slot.
  * kv_cnt: device int32 (BH * Nq); order: device uint32 (order_len).
- * One workgroup, reading kv_cnt twice.
+ * One workgroup; kv_cnt is read once into LDS (more than 49152 rows: read
+ * at each step).
  * INVALID_ARG unless order_len >= bsa_row_order_len(BH, Nq) > 0 and
  * order_len < 2^31. */
 int bsa_row_order(const int32_t* kv_cnt, int64_t BH, int64_t Nq, uint32_t* order, int64_t order_len,
                   bsa_stream_t stream);
 
-/* Host: the length of bsa_row_order's plan for BH heads of Nq rows (at least
- * BH * Nq: the plan carries empty slots), or -1 (and bsa_last_error) unless
- * BH, Nq >= 1, BH * Nq < 2^31, the plan has at most 2048 units and fewer
+/* Host: the length of bsa_row_order's plan for BH heads of Nq rows,
+ * 8 * ceil(U/8) * (rows per unit) >= BH * Nq, or -1 (and bsa_last_error) unless
+ * BH, Nq >= 1, BH * Nq < 2^31, the plan has at most 1024 units and fewer
  * than 2^31 entries.  Nothing is launched. */
 int64_t bsa_row_order_len(int64_t BH, int64_t Nq);
 
