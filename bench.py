@@ -145,7 +145,8 @@ def attention_call(bsa, pipe, q, k, v, out):
     if pipe.fused and pipe.pad:
         return lambda: bsa.bsa_block_sparse_attention_tiled_padded(q, k, v, pipe.grid, pipe.tiles, kv_idx, kv_cnt,
                                                                    head_choice=pipe.choice, scale=pipe.scale,
-                                                                   out=out, key_norms=pipe.ws_knorm)
+                                                                   out=out, key_norms=pipe.ws_knorm,
+                                                                   row_order=pipe.ws_order)
     if pipe.fused:
         return lambda: bsa.bsa_block_sparse_attention_tiled(q, k, v, pipe.grid, pipe.tiles, kv_idx, kv_cnt,
                                                             head_choice=pipe.choice, scale=pipe.scale, out=out,
@@ -360,18 +361,25 @@ def kernel_only(args, torch, bsa, synth):
                       "ms_per_call": round(ms, 4)}), flush=True)
 
 
-def top_p_pipeline(args, torch, bsa, synth):
-    """The Wan-shape top-p step (tiling choice, scores, top-p lists, launch plan, attention), --warmup + --steps
-    calls, one line of timing (for profilers)."""
+def variant_pipeline(args, torch, bsa, synth):
+    """One Wan-shape variant step, --warmup + --steps calls, one line of timing (for profilers): top-p 0.9
+    (tiling choice, scores, top-p lists, launch plan, attention) or the padded candidates (1,8,8) (4,4,4)
+    (16,2,2) (tiling choice, padded copies of q and k, masked scores, per-head top-k, launch plan, attention)."""
     wl = synth.WORKLOADS[4]
     dev = torch.device("cuda:0")
     log(f"generating inputs: {wl.name}")
     q, k, v = (synth.to_torch(x, dev) for x in synth.qkv(4))
     out = torch.empty_like(q)
-    pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, TILES, FRAC, q.dtype, dev, top_p=0.9, p_scale=wl.D ** -0.5)
+    if args.top_p_pipeline:
+        name = "top_p_pipeline"
+        pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, TILES, FRAC, q.dtype, dev, top_p=0.9,
+                                       p_scale=wl.D ** -0.5)
+    else:
+        name = "padded_pipeline"
+        pipe = bsa.AdaptiveBlockSparse(1, wl.H, wl.grid, wl.D, TILES + [(16, 2, 2)], FRAC, q.dtype, dev, pad=True)
     ms = _time(torch, lambda: pipe(q, k, v, out=out), max(args.steps, 1), args.warmup)
-    print(json.dumps({"top_p_pipeline": wl.name, "calls": args.warmup + max(args.steps, 1),
-                      "ms_per_step": round(ms, 4)}), flush=True)
+    print(json.dumps({name: wl.name, "calls": args.warmup + max(args.steps, 1), "ms_per_step": round(ms, 4)}),
+          flush=True)
 
 
 def main():
@@ -388,6 +396,9 @@ def main():
                          "on the pipeline's lists) --warmup + --steps times, for profilers")
     ap.add_argument("--top-p-pipeline", action="store_true",
                     help="only run the Wan-shape top-p step (p = 0.9) --warmup + --steps times, for profilers")
+    ap.add_argument("--padded-pipeline", action="store_true",
+                    help="only run the Wan-shape padded step (candidates (1,8,8) (4,4,4) (16,2,2)) --warmup + "
+                         "--steps times, for profilers")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -421,8 +432,8 @@ def main():
     if args.kernel_only is not None:
         kernel_only(args, torch, bsa, synth)
         return
-    if args.top_p_pipeline:
-        top_p_pipeline(args, torch, bsa, synth)
+    if args.top_p_pipeline or args.padded_pipeline:
+        variant_pipeline(args, torch, bsa, synth)
         return
 
     wl = synth.WORKLOADS[CFG]

@@ -85,7 +85,7 @@ _SIGS = {
     "bsa_block_sparse_attention_tiled": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
                                               _I, _F, _P, _P, _I64, _P]),
     "bsa_block_sparse_attention_tiled_padded": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P,
-                                                     _P, _P, _I, _F, _P, _P]),
+                                                     _P, _P, _I, _F, _P, _P, _I64, _P]),
     "bsa_tiled_attention_supported": (_I, [_I, _I64, _I, _I, _I, _P, _I, _I]),
     "bsa_row_order": (_I, [_P, _I64, _I64, _P, _I64, _P]),
     "bsa_row_order_len": (_I64, [_I64, _I64]),
@@ -673,9 +673,10 @@ def bsa_block_sparse_attention_tiled(q, k, v, grid, tiles, kv_idx, kv_cnt, head_
 
 
 def bsa_block_sparse_attention_tiled_padded(q, k, v, grid, tiles, kv_idx, kv_cnt, head_choice=None, scale=None,
-                                            out=None, key_norms=None):
+                                            out=None, key_norms=None, row_order=None):
     """bsa_block_sparse_attention_tiled on each head's zero-padded grid (candidates may leave T undivided):
-    kv lists over the largest padded block count Nq; padding keys are masked and padding rows not written."""
+    kv lists over the largest padded block count Nq; padding keys are masked and padding rows not written.
+    row_order: a launch order over the Nq rows of each head, as in bsa_block_sparse_attention."""
     torch = _torch()
     B, H, S, D = _qkv(q, k, v)
     T, Hg, Wg = (int(g) for g in grid)
@@ -692,7 +693,8 @@ def bsa_block_sparse_attention_tiled_padded(q, k, v, grid, tiles, kv_idx, kv_cnt
     _check(lib().bsa_block_sparse_attention_tiled_padded(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "out"),
                                                          _dtype_code(q), B, H, T, Hg, Wg, D, arr, n, hc, _dev(kv_idx),
                                                          _dev(kv_cnt), int(kv_idx.shape[3]), _scale(scale),
-                                                         _norms_out(key_norms, B, H, nq, q), _stream(q)))
+                                                         _norms_out(key_norms, B, H, nq, q),
+                                                         *_order_args(row_order, B * H * nq), _stream(q)))
     return o
 
 
@@ -840,10 +842,11 @@ class AdaptiveBlockSparse:
                           torch.empty((4, B, H, self.nb, D), dtype=dtype, **f))
         self.ws_topk = (torch.empty((B, H, self.nb, self.max_kept), dtype=torch.int32, **f),
                         torch.empty((B, H, self.nb), dtype=torch.int32, **f), None)
-        # top-p lists differ in length from row to row: a launch plan balances the XCDs and starts long rows
-        # first
+        # top-p lists differ in length from row to row, and padded candidates give heads different block
+        # counts and budgets: a launch plan balances the XCDs by work and starts long rows first (the fused
+        # attention takes it)
         self.ws_order = (torch.empty(bsa_row_order_len(B * H, self.nb), dtype=torch.int32, **f)
-                         if top_p is not None else None)
+                         if top_p is not None or (self.pad and self.fused) else None)
         # each key block's largest row norm, written by the scores pass: the attention kernel skips the
         # running-max update of the key blocks it proves cannot pass it
         self.ws_knorm = (torch.empty((B, H, self.nb), dtype=torch.float32, **f) if self.fused or not self.pad
@@ -874,6 +877,8 @@ class AdaptiveBlockSparse:
                                                 key_norms=self.ws_knorm)
             kv_idx, kv_cnt = bsa_topk_block_mask_tiled(scores, choice, self.k_table, self.nk_table, self.sink_blocks,
                                                        self.keep_diag, max_kept=self.max_kept, out=self.ws_topk)
+            if self.ws_order is not None:
+                bsa_row_order(kv_cnt, out=self.ws_order)
         else:
             if self.fused:
                 scores, _ = bsa_minmax_block_scores_tiled(q, k, self.grid, self.tiles, head_choice=choice,
@@ -899,7 +904,7 @@ class AdaptiveBlockSparse:
             if self.pad:
                 o = bsa_block_sparse_attention_tiled_padded(q, k, v, self.grid, self.tiles, kv_idx, kv_cnt,
                                                             head_choice=choice, scale=self.scale, out=out,
-                                                            key_norms=self.ws_knorm)
+                                                            key_norms=self.ws_knorm, row_order=self.ws_order)
             else:
                 o = bsa_block_sparse_attention_tiled(q, k, v, self.grid, self.tiles, kv_idx, kv_cnt,
                                                      head_choice=choice, scale=self.scale, out=out,

@@ -523,7 +523,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
     const int half_id = lane >> 5, col = lane & 31;
 
     uint32_t wg = blockIdx.x, bh, I;
-    if (MODE == kBlockList && !PADT && P.row_order != nullptr) {
+    if (MODE == kBlockList && P.row_order != nullptr) {
         const uint32_t r = P.row_order[wg];
         if (r >= P.n_wg) return;
         bh = r / P.nq;
@@ -1436,10 +1436,12 @@ extern "C" int bsa_block_sparse_attention_tiled_padded(const void* q, const void
                                                        int64_t D, const int32_t* tiles_host, int n_tiles,
                                                        const int32_t* head_choice, const int32_t* kv_idx,
                                                        const int32_t* kv_cnt, int max_kept, float scale,
-                                                       const float* key_norms_or_null, bsa_stream_t stream) {
+                                                       const float* key_norms_or_null,
+                                                       const uint32_t* row_order_or_null, int64_t row_order_len,
+                                                       bsa_stream_t stream) {
     clear_error();
     return tiled_attention(q, k, v, out, dtype, B, H, T, Hg, Wg, D, tiles_host, n_tiles, head_choice, kv_idx, kv_cnt,
-                           max_kept, scale, key_norms_or_null, nullptr, 0, true, stream,
+                           max_kept, scale, key_norms_or_null, row_order_or_null, row_order_len, true, stream,
                            "bsa_block_sparse_attention_tiled_padded");
 }
 

@@ -368,8 +368,20 @@ __global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* _
         for (uint32_t i = lane; i < kPlanBins; i += 64) b[i] = 0;
         __syncthreads();
         const uint32_t r0 = u * unit_rows;
-        if (active)
-            for (uint32_t i = lane; i < unit_rows; i += 64) atomicAdd(&b[plan_key(count(r0 + i))], 1u);
+        // (when every active lane has the same key, as a head's equal-length top-k lists give, one lane adds
+        // them all: 64 lanes on one LDS address would serialise)
+        if (active) {
+            for (uint32_t i = lane; i < unit_rows; i += 64) {
+                const uint32_t key = plan_key(count(r0 + i));
+                const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane(key);
+                const uint64_t same = __ballot(key == k0), all = __ballot(true);
+                if (same == all) {
+                    if (lane == (uint32_t)__builtin_ctzll(all)) atomicAdd(&b[k0], (uint32_t)__builtin_popcountll(all));
+                } else {
+                    atomicAdd(&b[key], 1u);
+                }
+            }
+        }
         __syncthreads();
         constexpr int kPer = kPlanBins / 64;
         uint32_t own[kPer], sum = 0;
@@ -395,7 +407,21 @@ __global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* _
         if (active) {
             const uint32_t x = place[u] & 7u, p0 = place[u] >> 3;
             for (uint32_t i = lane; i < unit_rows; i += 64) {
-                const uint32_t rank = atomicAdd(&b[plan_key(count(r0 + i))], 1u);
+                const uint32_t key = plan_key(count(r0 + i));
+                const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane(key);
+                const uint64_t same = __ballot(key == k0), all = __ballot(true);
+                uint32_t rank;
+                if (same == all) {
+                    const uint32_t first = (uint32_t)__builtin_ctzll(all);
+                    uint32_t base = 0;
+                    if (lane == first) base = atomicAdd(&b[k0], (uint32_t)__builtin_popcountll(all));
+                    base = (uint32_t)__shfl((int)base, (int)first);
+                    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(all >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)all, 0u));
+                    rank = base + below;
+                } else {
+                    rank = atomicAdd(&b[key], 1u);
+                }
                 order[8u * (p0 + rank) + x] = r0 + i;
             }
         }

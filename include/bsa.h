@@ -458,6 +458,8 @@ int bsa_block_sparse_attention_tiled(const void* q, const void* k, const void* v
  * real, -1 for padding) -> bsa_invert_permute_padded.  kv_idx / kv_cnt
  * (and key_norms_or_null) have Nq = the largest padded block count over the
  * candidates; rows of blocks past a head's own count are ignored.
+ * row_order_or_null, row_order_len: as in bsa_block_sparse_attention, over
+ * the Nq rows of each head (rows past a head's own count run empty).
  * UNSUPPORTED as bsa_block_sparse_attention_tiled, and when a candidate would
  * pad along y or x (b must divide Hg and c divide Wg). */
 int bsa_block_sparse_attention_tiled_padded(const void* q, const void* k, const void* v, void* out,
@@ -465,7 +467,9 @@ int bsa_block_sparse_attention_tiled_padded(const void* q, const void* k, const 
                                             int64_t D, const int32_t* tiles_host, int n_tiles,
                                             const int32_t* head_choice, const int32_t* kv_idx,
                                             const int32_t* kv_cnt, int max_kept, float scale,
-                                            const float* key_norms_or_null, bsa_stream_t stream);
+                                            const float* key_norms_or_null,
+                                            const uint32_t* row_order_or_null, int64_t row_order_len,
+                                            bsa_stream_t stream);
 
 /* Host: 1 if bsa_block_sparse_attention_tiled (pad = 0) or its _padded form
  * (pad = 1) has a kernel for these arguments, else 0.  Nothing is launched. */

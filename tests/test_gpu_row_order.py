@@ -175,6 +175,29 @@ def test_tiled_attention_under_a_plan():
 
 
 @pytest.mark.gpu
+def test_padded_attention_under_a_plan():
+    """Padded candidates (heads with different block counts and budgets): the padded pipeline plans its launch,
+    and its output equals the unplanned padded attention bit for bit; so does a random padded order."""
+    torch = torch_gpu()
+    grid, tiles, H, D = (6, 16, 16), [(1, 8, 8), (4, 4, 4)], 5, 128          # (4,4,4) pads T from 6 to 8
+    q, k, v = (synth.normal_bits((1, H, 1536, D), seed=5400 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    pipe = bsa.AdaptiveBlockSparse(1, H, grid, D, tiles, 0.3, qg.dtype, qg.device, pad=True)
+    out = pipe(qg, kg, vg)
+    kv_idx, kv_cnt = pipe.kv
+    assert pipe.ws_order is not None
+    check_plan(pipe.ws_order, kv_cnt.cpu().numpy().reshape(H, -1))
+    ref = bsa.bsa_block_sparse_attention_tiled_padded(qg, kg, vg, grid, tiles, kv_idx, kv_cnt,
+                                                      head_choice=pipe.choice, key_norms=pipe.ws_knorm)
+    assert torch.equal(out, ref)
+    rng = np.random.default_rng(5401)
+    out2 = bsa.bsa_block_sparse_attention_tiled_padded(qg, kg, vg, grid, tiles, kv_idx, kv_cnt,
+                                                       head_choice=pipe.choice, key_norms=pipe.ws_knorm,
+                                                       row_order=_any_order(kv_cnt.numel(), rng))
+    assert torch.equal(out2, ref)
+
+
+@pytest.mark.gpu
 def test_top_p_pipeline_plans_its_launch():
     """The top-p pipeline plans its attention launch: the plan follows the rule for the pipeline's own lists,
     and the pipeline's output equals the unplanned attention on the same lists bit for bit."""
