@@ -510,6 +510,15 @@ struct SoloCfg {
 // padding frame lie past the head, so their loads read zeros; their keys are
 // masked and their rows are not stored.  Blocks past the head's own block
 // count (the grid covers the largest) have no tile.
+// Real cells of tile t of a grid padded along T: a prefix of the tile (cells
+// are T-major inside it), all 64 unless the tile reaches into the padding
+__device__ __forceinline__ int padded_tile_cells(const TileGeo& geo, uint32_t T, uint32_t t) {
+    uint32_t tt, rem;
+    fdivmod(t, geo.f_ntyx, tt, rem);
+    const int left = (int)T - (int)(tt * geo.a);
+    return left >= (int)geo.a ? 64 : left * (int)(geo.b * geo.c);
+}
+
 template <int MODE, bool POS, bool TILED, bool BOUND = false, bool PADT = false, bool EV = true>
 __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, const int32_t* __restrict__ kv_idx,
                                                           const int32_t* __restrict__ kv_cnt,
@@ -554,436 +563,460 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         bh = wg / P.nq;
         I = wg % P.nq;
     }
-    const size_t head = (size_t)bh * P.S * D;
-    const uint32_t head_bytes = P.S * D * 2;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(P.q + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(P.k + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(P.v + head, head_bytes);
-    const int q0 = (int)I * BLK;
-    // TILED: the head's tiling, the query tile's T-major origin, and each
-    // lane's two cells (32c + col) as T-major offsets from a tile origin
-    uint32_t tc = 0;
-    if (TILED && P.head_choice != nullptr) {
-        tc = (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[bh]);
-        if (tc >= P.n_tiles) tc = 0;  // out-of-range choices are caught by bsa_validate_indices
-    }
-    if (PADT && I >= P.nbt[tc]) return;
-    const TileGeo& geo = P.geo[tc];
-    const uint32_t q_origin = TILED ? tile_origin(I, geo, P.Hg, P.Wg) : (uint32_t)q0;
-    int kcell[2];
+    // PADT: a query tile whose real cells (a prefix of the tile) fit in its
+    // first 32 rows runs one row tile; the other 32 rows are padding, neither
+    // computed nor stored
+    auto body = [&](auto nr_tag) {
+        constexpr int NR = decltype(nr_tag)::value;
+        const size_t head = (size_t)bh * P.S * D;
+        const uint32_t head_bytes = P.S * D * 2;
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(P.q + head, head_bytes);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(P.k + head, head_bytes);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(P.v + head, head_bytes);
+        const int q0 = (int)I * BLK;
+        // TILED: the head's tiling, the query tile's T-major origin, and each
+        // lane's two cells (32c + col) as T-major offsets from a tile origin
+        uint32_t tc = 0;
+        if (TILED && P.head_choice != nullptr) {
+            tc = (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[bh]);
+            if (tc >= P.n_tiles) tc = 0;  // out-of-range choices are caught by bsa_validate_indices
+        }
+        if (PADT && I >= P.nbt[tc]) return;
+        const TileGeo& geo = P.geo[tc];
+        const uint32_t q_origin = TILED ? tile_origin(I, geo, P.Hg, P.Wg) : (uint32_t)q0;
+        int kcell[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) kcell[c] = TILED ? (int)cell_offset(32 * c + col, geo, P.Hg, P.Wg) : 32 * c + col;
-    auto tile_soff = [&](int t) -> int {  // byte offset of key tile t's first row
-        return TILED ? (int)tile_origin((uint32_t)t, geo, P.Hg, P.Wg) * (D * 2) : t * BLK * (D * 2);
-    };
-    // PADT: key rows of tile t that are real cells, a prefix of the tile (cells are T-major inside it)
-    auto tile_keys = [&](int t) -> int {
-        if (!PADT) return BLK;
-        uint32_t tt, rem;
-        fdivmod((uint32_t)t, geo.f_ntyx, tt, rem);
-        const int left = (int)P.T - (int)(tt * geo.a);
-        return left >= (int)geo.a ? BLK : left * (int)(geo.b * geo.c);
-    };
+        for (int c = 0; c < 2; ++c) kcell[c] = TILED ? (int)cell_offset(32 * c + col, geo, P.Hg, P.Wg) : 32 * c + col;
+        auto tile_soff = [&](int t) -> int {  // byte offset of key tile t's first row
+            return TILED ? (int)tile_origin((uint32_t)t, geo, P.Hg, P.Wg) * (D * 2) : t * BLK * (D * 2);
+        };
+        // PADT: key rows of tile t that are real cells, a prefix of the tile (cells are T-major inside it)
+        auto tile_keys = [&](int t) -> int { return PADT ? padded_tile_cells(geo, P.T, (uint32_t)t) : BLK; };
 
-    int n_iter;
-    const int32_t* list = nullptr;
-    int n_sink_tiles = 0, local_first = 0;
-    if (MODE != kWindow) {
-        const size_t row = (size_t)bh * P.nq + I;
-        n_iter = min(kv_cnt[row], (int)P.max_kept);
-        list = kv_idx + row * P.max_kept;
-    } else {
-        n_sink_tiles = (P.sink + BLK - 1) / BLK;
-        const int lo = max(0, q0 - P.half);
-        const int hi = min((int)P.S, q0 + BLK - 1 + P.half + 1);  // exclusive
-        const int t_lo = lo / BLK, t_hi = (hi - 1) / BLK;
-        local_first = max(t_lo, n_sink_tiles);
-        n_iter = n_sink_tiles + max(0, t_hi - local_first + 1);
-    }
-    auto tile_at = [&](int it) -> int {
-        if (MODE != kWindow) return __builtin_amdgcn_readfirstlane(list[it]);
-        return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
-    };
-    // entry it of the list as a vector value (a buffer load, read one tile ahead)
-    const __amdgpu_buffer_rsrc_t lr = make_rsrc(list, MODE != kWindow ? 4u * (uint32_t)max(n_iter, 0) : 0u);
-    auto tile_ahead = [&](int it) -> int {
-        if (MODE != kWindow) return __builtin_amdgcn_raw_buffer_load_b32(lr, 4 * it, 0, 0);
-        return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
-    };
+        int n_iter;
+        const int32_t* list = nullptr;
+        int n_sink_tiles = 0, local_first = 0;
+        if (MODE != kWindow) {
+            const size_t row = (size_t)bh * P.nq + I;
+            n_iter = min(kv_cnt[row], (int)P.max_kept);
+            list = kv_idx + row * P.max_kept;
+        } else {
+            n_sink_tiles = (P.sink + BLK - 1) / BLK;
+            const int lo = max(0, q0 - P.half);
+            const int hi = min((int)P.S, q0 + BLK - 1 + P.half + 1);  // exclusive
+            const int t_lo = lo / BLK, t_hi = (hi - 1) / BLK;
+            local_first = max(t_lo, n_sink_tiles);
+            n_iter = n_sink_tiles + max(0, t_hi - local_first + 1);
+        }
+        auto tile_at = [&](int it) -> int {
+            if (MODE != kWindow) return __builtin_amdgcn_readfirstlane(list[it]);
+            return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
+        };
+        // entry it of the list as a vector value (a buffer load, read one tile ahead)
+        const __amdgpu_buffer_rsrc_t lr = make_rsrc(list, MODE != kWindow ? 4u * (uint32_t)max(n_iter, 0) : 0u);
+        auto tile_ahead = [&](int it) -> int {
+            if (MODE != kWindow) return __builtin_amdgcn_raw_buffer_load_b32(lr, 4 * it, 0, 0);
+            return it < n_sink_tiles ? it : local_first + (it - n_sink_tiles);
+        };
 
-    // fragments: row (or key) 32*x + col, D cols 16*s + 8*half_id + 0..7;
-    // koff[x] is that row's byte offset from its tile's origin
-    int koff[2];
+        // fragments: row (or key) 32*x + col, D cols 16*s + 8*half_id + 0..7;
+        // koff[x] is that row's byte offset from its tile's origin
+        int koff[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) koff[c] = kcell[c] * (D * 2) + half_id * 16;
-    // Q stays in registers as the B operand of both row tiles
-    bf16x8 qf[2][D / 16];
+        for (int c = 0; c < 2; ++c) koff[c] = kcell[c] * (D * 2) + half_id * 16;
+        // Q stays in registers as the B operand of both row tiles
+        bf16x8 qf[2][D / 16];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            qf[r][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, koff[r] + 32 * s, TILED ? (int)q_origin * (D * 2) : q0 * (D * 2), 0));
-    // LDS address of K fragment (key half 0, step s); key half 1 is 32 rows on
-    int k_addr[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) k_addr[s] = k_lds<D>(col, 2 * s + half_id);
-    // Row group q (rows 4q..4q+3 of a tile) lies goff[q] bytes from the tile's
-    // first row: the same for every lane, so it goes into the DMA's scalar
-    // offset and only the lane's place within the group stays in a VGPR.
-    // TILED: cells 4q..4q+3 are 4 consecutive T-major tokens (tiles with an x
-    // extent that is a multiple of 4), P.voff[tc][q] bytes from the origin.
-    int goff[C::TILE / 1024];
-#pragma unroll
-    for (int q = 0; q < C::TILE / 1024; ++q) goff[q] = TILED ? P.voff[tc][q] : 1024 * q;
-    // K tile straight into LDS with the K swizzle: instruction q fills rows
-    // 4q..4q+3, lane l physical chunk l % 16 of row 4q + l / 16, which holds
-    // logical chunk (l % 16) ^ (row % 8), row % 8 = 4(q % 2) + l / 16
-    // row lane / 16 of a DMA row group lies rrow bytes after the group's first row
-    const int rrow = TILED ? P.rdelta[tc][lane >> 4] : (lane >> 4) * (D * 2);
-    int klane[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) klane[p] = rrow + (((lane & 15) ^ (4 * p + (lane >> 4))) << 4);
-    auto dma_k = [&](int soff) {
-#pragma unroll
-        for (int q = 0; q < C::TILE / 1024; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(klds + 1024 * q), 16,
-                                                     klane[q & 1], soff + goff[q], 0, 0);
-    };
-    // V tile straight into LDS (buffer loads with the LDS destination): wave
-    // instruction q fills LDS bytes [1024q, 1024q + 1024), i.e. rows 4q..4q+3,
-    // lane l landing on physical chunk l % 16 of row 4q + l / 16, which holds
-    // logical chunk (l % 16) ^ 2(row % 4) (the V swizzle); row % 4 = l / 16.
-    const int vlane = rrow + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
-    auto dma_v = [&](char* buf, int soff, int q_lo, int q_hi) {
-#pragma unroll
-        for (int q = q_lo; q < q_hi; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(buf + 1024 * q), 16,
-                                                     vlane, soff + goff[q], 0, 0);
-    };
-
-    f32x16 o[2][D / 32];
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[r][t][v] = 0.f;
-    float m_used[2] = {-1e30f, -1e30f}, l_part[2] = {0.f, 0.f};
-    const float c_scale = POS ? P.scale_log2 : 1.0f;
-    // Key norms given (block lists, positive scale): by Cauchy-Schwarz every
-    // score of this query block against key tile J, times scale * log2(e), is
-    // at most q_lim * knorm[J], q_lim = the largest |q_row| of the block times
-    // scale * log2(e).  When that stays within kSkipSlack of the smallest
-    // running max of the block's rows, m_min, no softmax weight of the tile
-    // can pass 2^kSkipSlack and the tile skips the max.  The test is
-    // knorm[J] <= kn_lim = (m_min + kSkipSlack) / q_lim, on scalars; kn_lim
-    // only moves when a rescale moves the running max.
-    constexpr bool bounded = BOUND && MODE == kBlockList && POS;
-    const float* knorm_head = bounded ? knorm + (size_t)bh * P.nq : nullptr;
-    float q_lim = 0.f, kn_lim = -__builtin_inff(), kn_cur = 0.f;
-    if (bounded) {
-        float n2max = 0.f;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            float n2 = 0.f;
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
             for (int s = 0; s < D / 16; ++s)
+                qf[r][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, koff[r] + 32 * s, TILED ? (int)q_origin * (D * 2) : q0 * (D * 2), 0));
+        // LDS address of K fragment (key half 0, step s); key half 1 is 32 rows on
+        int k_addr[D / 16];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bf16x2 two = {qf[r][s][2 * e], qf[r][s][2 * e + 1]};
-                    n2 = __builtin_amdgcn_fdot2_f32_bf16(two, two, n2, false);
-                }
-            // lanes l and l ^ 32 hold the two halves of row 32r + l % 32
-            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(n2), __float_as_uint(n2), false, false);
-            n2max = fmaxf(n2max, __uint_as_float(pr[0]) + __uint_as_float(pr[1]));
-        }
+        for (int s = 0; s < D / 16; ++s) k_addr[s] = k_lds<D>(col, 2 * s + half_id);
+        // Row group q (rows 4q..4q+3 of a tile) lies goff[q] bytes from the tile's
+        // first row: the same for every lane, so it goes into the DMA's scalar
+        // offset and only the lane's place within the group stays in a VGPR.
+        // TILED: cells 4q..4q+3 are 4 consecutive T-major tokens (tiles with an x
+        // extent that is a multiple of 4), P.voff[tc][q] bytes from the origin.
+        int goff[C::TILE / 1024];
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) n2max = fmaxf(n2max, __shfl_xor(n2max, off));
-        q_lim = sqrtf(__uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(n2max)))) * c_scale;
-    }
-
-    const int g16 = lane >> 4, r16 = lane & 15;
-    const int v_key0 = 4 * (g16 >> 1) + (r16 >> 2);
-    const int v_col0 = 16 * (g16 & 1) + 4 * (r16 & 3);
-    int v_addr[D / 32];
+        for (int q = 0; q < C::TILE / 1024; ++q) goff[q] = TILED ? P.voff[tc][q] : 1024 * q;
+        // K tile straight into LDS with the K swizzle: instruction q fills rows
+        // 4q..4q+3, lane l physical chunk l % 16 of row 4q + l / 16, which holds
+        // logical chunk (l % 16) ^ (row % 8), row % 8 = 4(q % 2) + l / 16
+        // row lane / 16 of a DMA row group lies rrow bytes after the group's first row
+        const int rrow = TILED ? P.rdelta[tc][lane >> 4] : (lane >> 4) * (D * 2);
+        int klane[2];
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-        const int colv = 32 * t + v_col0;
-        v_addr[t] = v_lds<D>(v_key0, colv >> 3) + (colv & 7) * 2;
-    }
-
-    // label rule: this lane's two row labels, whether the whole query block
-    // shares one label, and the key labels of the next tile (lane l holds
-    // key l), fetched with that tile's K
-    int qlab[2] = {0, 0}, q_uni = 0, klab = 0, klab_next = 0;
-    bool q_uniform = true;
-    const int32_t* labs = nullptr;
-    if (MODE == kLabels) {
-        labs = P.labels + (size_t)bh * P.label_stride;
-        qlab[0] = labs[q0 + col];
-        qlab[1] = labs[q0 + 32 + col];
-        q_uni = __builtin_amdgcn_readfirstlane(qlab[0]);
-        q_uniform = __ballot((qlab[0] != q_uni) | (qlab[1] != q_uni)) == 0;
-    }
-
-    int soff_cur = 0, v_nxt = 0, kval_cur = BLK;
-    if (n_iter > 0) {
-        const int t0 = tile_at(0);
-        if (bounded) kn_cur = knorm_head[t0];
-        soff_cur = tile_soff(t0);
-        kval_cur = tile_keys(t0);
-        dma_k(soff_cur);
-        if (EV) dma_v(vlds, soff_cur, 0, C::TILE / 1024);
-        if (MODE == kLabels) klab_next = labs[t0 * BLK + lane];
-        v_nxt = tile_ahead(min(1, n_iter - 1));
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-
-    for (int it = 0; it < n_iter; ++it) {
-        const int nxt_tile = __builtin_amdgcn_readfirstlane(v_nxt);
-        const int nxt = nxt_tile * BLK;
-        const float kn_nxt = bounded ? knorm_head[nxt_tile] : 0.f;
-        // this tile's K has landed in LDS (only its V (EV) was issued later) and
-        // the previous tile's V reads have completed
-        __builtin_amdgcn_s_waitcnt(EV ? kVm16Lgkm0 : 0);
-
-        // S^T of (key half c, row tile r) = K_c Q_r^T: four independent chains
-        f32x16 sacc[2][2];
+        for (int p = 0; p < 2; ++p) klane[p] = rrow + (((lane & 15) ^ (4 * p + (lane >> 4))) << 4);
+        auto dma_k = [&](int soff) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) sacc[c][r][v] = 0.f;
-            }
-        // K fragments of the two key halves, read two steps ahead (ring of three)
-        bf16x8 kfa[3], kfb[3];
-        auto read_k = [&](int s) {
-            kfa[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(klds + k_addr[s]));
-            kfb[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(klds + k_addr[s] + 32 * (D * 2)));
+            for (int q = 0; q < C::TILE / 1024; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(klds + 1024 * q), 16,
+                                                         klane[q & 1], soff + goff[q], 0, 0);
         };
-        read_k(0);
-        read_k(1);
-        // (one MFMA per fenced region, with one V DMA or the K reads of step s+2
-        // beside it)
+        // V tile straight into LDS (buffer loads with the LDS destination): wave
+        // instruction q fills LDS bytes [1024q, 1024q + 1024), i.e. rows 4q..4q+3,
+        // lane l landing on physical chunk l % 16 of row 4q + l / 16, which holds
+        // logical chunk (l % 16) ^ 2(row % 4) (the V swizzle); row % 4 = l / 16.
+        const int vlane = rrow + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
+        auto dma_v = [&](char* buf, int soff, int q_lo, int q_hi) {
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 ka = kfa[s % 3], kb = kfb[s % 3];
-            sacc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][s], sacc[0][0], 0, 0, 0);
-            if (!EV) dma_v(vlds, soff_cur, 2 * s, 2 * s + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            sacc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][s], sacc[0][1], 0, 0, 0);
-            if (!EV) dma_v(vlds, soff_cur, 2 * s + 1, 2 * s + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            sacc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[0][s], sacc[1][0], 0, 0, 0);
-            if (s + 2 < D / 16) read_k(s + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            sacc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[1][s], sacc[1][1], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // this tile's K is read: the next tile's K goes into its LDS (the last tile
-        // again past the end), with the list entry of the tile after it
-        if (MODE == kLabels) klab = klab_next;
-        v_nxt = tile_ahead(min(it + 2, n_iter - 1));
-        const int soff_nxt = tile_soff(nxt_tile);
-        const int kval_nxt = tile_keys(nxt_tile);
-        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);  // this tile's K reads are complete
-        dma_k(soff_nxt);
-        if (MODE == kLabels) klab_next = labs[nxt + lane];
-        __builtin_amdgcn_sched_barrier(0);
+            for (int q = q_lo; q < q_hi; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(buf + 1024 * q), 16,
+                                                         vlane, soff + goff[q], 0, 0);
+        };
 
-        // softmax of both row tiles (32 values of one row per lane and tile)
-        if (!POS) {
+        f32x16 o[2][D / 32];
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-                for (int r = 0; r < 2; ++r)
+            for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) sacc[c][r][v] *= P.scale_log2;
-        }
-        if (PADT && kval_cur < BLK) {  // padding keys of a tile at the end of the padded frames
-            const float neg_inf = -__builtin_inff();
+                for (int v = 0; v < 16; ++v) o[r][t][v] = 0.f;
+        float m_used[2] = {-1e30f, -1e30f}, l_part[2] = {0.f, 0.f};
+        const float c_scale = POS ? P.scale_log2 : 1.0f;
+        // Key norms given (block lists, positive scale): by Cauchy-Schwarz every
+        // score of this query block against key tile J, times scale * log2(e), is
+        // at most q_lim * knorm[J], q_lim = the largest |q_row| of the block times
+        // scale * log2(e).  When that stays within kSkipSlack of the smallest
+        // running max of the block's rows, m_min, no softmax weight of the tile
+        // can pass 2^kSkipSlack and the tile skips the max.  The test is
+        // knorm[J] <= kn_lim = (m_min + kSkipSlack) / q_lim, on scalars; kn_lim
+        // only moves when a rescale moves the running max.
+        constexpr bool bounded = BOUND && MODE == kBlockList && POS;
+        const float* knorm_head = bounded ? knorm + (size_t)bh * P.nq : nullptr;
+        float q_lim = 0.f, kn_lim = -__builtin_inff(), kn_cur = 0.f;
+        if (bounded) {
+            float n2max = 0.f;
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int r = 0; r < NR; ++r) {
+                float n2 = 0.f;
 #pragma unroll
-                for (int r = 0; r < 2; ++r)
+                for (int s = 0; s < D / 16; ++s)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int j = 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4);
-                        sacc[c][r][v] = j < kval_cur ? sacc[c][r][v] : neg_inf;
+                    for (int e = 0; e < 4; ++e) {
+                        const bf16x2 two = {qf[r][s][2 * e], qf[r][s][2 * e + 1]};
+                        n2 = __builtin_amdgcn_fdot2_f32_bf16(two, two, n2, false);
                     }
+                // lanes l and l ^ 32 hold the two halves of row 32r + l % 32
+                const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(n2), __float_as_uint(n2), false, false);
+                n2max = fmaxf(n2max, __uint_as_float(pr[0]) + __uint_as_float(pr[1]));
+            }
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) n2max = fmaxf(n2max, __shfl_xor(n2max, off));
+            q_lim = sqrtf(__uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(n2max)))) * c_scale;
         }
-        if (MODE == kWindow) {
-            const int j0 = tile_at(it) * BLK;
-            const bool full = (j0 + BLK - 1 < P.sink) ||
-                              (q0 + BLK - 1 - j0 <= P.half && j0 + BLK - 1 - q0 <= P.half && j0 + BLK <= (int)P.S);
-            if (!full) {
-                const float neg_inf = -__builtin_inff();
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int r = 0; r < 2; ++r) {
-                        const int my_row = q0 + 32 * r + col;
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int j = j0 + 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4);
-                            const int d = my_row - j;
-                            const bool vis = (j < (int)P.S) & (((d <= P.half) & (-d <= P.half)) | (j < P.sink));
-                            sacc[c][r][v] = vis ? sacc[c][r][v] : neg_inf;
-                        }
-                    }
-            }
-        }
-        if (MODE == kLabels) {
-            // a tile whose keys all carry the query block's single label needs no mask
-            if (!q_uniform || __ballot(klab != q_uni) != 0) {
-                const float neg_inf = -__builtin_inff();
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int kl = __shfl(klab, 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4));
-#pragma unroll
-                        for (int r = 0; r < 2; ++r) sacc[c][r][v] = kl == qlab[r] ? sacc[c][r][v] : neg_inf;
-                    }
-            }
-        }
-        // (the ballot keeps the test in a VGPR compare; as a plain scalar branch
-        // the compiler allocates the loop's registers far worse)
-        const bool skip = bounded && __ballot(kn_cur <= kn_lim) != 0;
-        kn_cur = kn_nxt;
-        if (__builtin_expect(!skip, !bounded)) {
-            float mloc[2];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                float smax = fmaxf(sacc[0][r][0], sacc[1][r][0]);
-#pragma unroll
-                for (int v = 1; v < 16; ++v) smax = fmaxf(fmaxf(smax, sacc[0][r][v]), sacc[1][r][v]);
-                const auto pr =
-                    __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
-                mloc[r] = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * c_scale;
-            }
-            const bool grow0 = mloc[0] > m_used[0] + kRescaleSlack;
-            const bool grow1 = mloc[1] > m_used[1] + kRescaleSlack;
-            if (__ballot(grow0 | grow1)) {
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const bool grow = r == 0 ? grow0 : grow1;
-                    const float m_new = grow ? mloc[r] : m_used[r];
-                    const float alpha = __builtin_amdgcn_exp2f(m_used[r] - m_new);
-                    m_used[r] = m_new;
-                    l_part[r] *= alpha;
-#pragma unroll
-                    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) o[r][t][v] *= alpha;
-                }
-                if (bounded) {
-                    float mm = fminf(m_used[0], m_used[1]);
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) mm = fminf(mm, __shfl_xor(mm, off));
-                    const float m_min = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(mm)));
-                    kn_lim = (m_min + kSkipSlack) / q_lim;
-                }
-            }
-        }
-        // P as bf16 B operands, one 16-key group m at a time (pb[r][m] covers keys
-        // 16m..16m+15); group m+1's exps and V^T reads are issued beside the
-        // MFMAs of group m
-        bf16x8 pb[2][4];
-        float psum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-        // piece j (0..3) of group m for row tile r: accumulator values
-        // 8(m % 2) + 2j and + 1 of key half m / 2, i.e. two of this lane's share
-        // of keys 16m..16m+15
-        auto p_piece = [&](int m, int r, int j) {
-            const int c = m / 2, v = 8 * (m % 2) + 2 * j;
-            const float neg_m = -m_used[r];
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v], c_scale, neg_m));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v + 1], c_scale, neg_m));
-            const bf16x2 two = {(__bf16)p0, (__bf16)p1};
-            psum[r][m % 2] = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, psum[r][m % 2], false);
-            pb[r][m][v % 8] = two[0];
-            pb[r][m][v % 8 + 1] = two[1];
-        };
-        // V^T fragment t of group m (keys 16m..16m+15) in two transposing reads of
-        // 8 keys each; vfr[m % 2] holds a group's four fragments
-        bf16x8 vfr[2][D / 32];
-        s16x4 vlo[D / 32];
-        auto v_half = [&](int m, int t, int h) {
-            const char* va = vlds + v_addr[t] + (16 * m + 8 * h) * (D * 2);
-            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)va);
-            if (h == 0) {
-                vlo[t] = x;
-            } else {
-                const s16x4 a8[2] = {vlo[t], x};
-                vfr[m % 2][t] = __builtin_bit_cast(bf16x8, a8);
-            }
-        };
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p_piece(0, r, j);
-        // O^T += V^T P^T once this tile's V has landed: only the next tile's 16 K
-        // loads and (block lists) its list entry were issued after it
-        __builtin_amdgcn_s_waitcnt(MODE == kWindow ? kVmcnt16 : waitcnt_vm(17));
+
+        const int g16 = lane >> 4, r16 = lane & 15;
+        const int v_key0 = 4 * (g16 >> 1) + (r16 >> 2);
+        const int v_col0 = 16 * (g16 & 1) + 4 * (r16 & 3);
+        int v_addr[D / 32];
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-            v_half(0, t, 0);
-            v_half(0, t, 1);
+            const int colv = 32 * t + v_col0;
+            v_addr[t] = v_lds<D>(v_key0, colv >> 3) + (colv & 7) * 2;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // (one MFMA per fenced region; beside each, one piece of group m+1: two
-        // exps of one row tile and half of one V^T fragment; EV: beside the
-        // last group's MFMAs, two of the next tile's V DMA instructions each,
-        // the last tile's again past the end)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if (EV && m == 3) {  // every V^T read of this tile has returned
-                __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int i = 0; i < 2 * (D / 32); ++i) {
-                const int t = i / 2, r = i % 2;
-                o[r][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m % 2][t], pb[r][m], o[r][t], 0, 0, 0);
-                if (m + 1 < 4) {
-                    p_piece(m + 1, i / 4, i % 4);
-                    v_half(m + 1, t, i % 2);
-                } else if (EV) {
-                    dma_v(vlds, soff_nxt, 2 * i, 2 * i + 2);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) l_part[r] += psum[r][0] + psum[r][1];
-        soff_cur = soff_nxt;
-        kval_cur = kval_nxt;
-    }
 
-    // ---- write out (each lane pair holds one row; their partial sums add up)
+        // label rule: this lane's two row labels, whether the whole query block
+        // shares one label, and the key labels of the next tile (lane l holds
+        // key l), fetched with that tile's K
+        int qlab[2] = {0, 0}, q_uni = 0, klab = 0, klab_next = 0;
+        bool q_uniform = true;
+        const int32_t* labs = nullptr;
+        if (MODE == kLabels) {
+            labs = P.labels + (size_t)bh * P.label_stride;
+            qlab[0] = labs[q0 + col];
+            qlab[1] = labs[q0 + 32 + col];
+            q_uni = __builtin_amdgcn_readfirstlane(qlab[0]);
+            q_uniform = __ballot((qlab[0] != q_uni) | (qlab[1] != q_uni)) == 0;
+        }
+
+        int soff_cur = 0, v_nxt = 0, kval_cur = BLK;
+        if (n_iter > 0) {
+            const int t0 = tile_at(0);
+            if (bounded) kn_cur = knorm_head[t0];
+            soff_cur = tile_soff(t0);
+            kval_cur = tile_keys(t0);
+            dma_k(soff_cur);
+            if (EV) dma_v(vlds, soff_cur, 0, C::TILE / 1024);
+            if (MODE == kLabels) klab_next = labs[t0 * BLK + lane];
+            v_nxt = tile_ahead(min(1, n_iter - 1));
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+
+        for (int it = 0; it < n_iter; ++it) {
+            const int nxt_tile = __builtin_amdgcn_readfirstlane(v_nxt);
+            const int nxt = nxt_tile * BLK;
+            const float kn_nxt = bounded ? knorm_head[nxt_tile] : 0.f;
+            // this tile's K has landed in LDS (only its V (EV) was issued later) and
+            // the previous tile's V reads have completed
+            __builtin_amdgcn_s_waitcnt(EV ? kVm16Lgkm0 : 0);
+
+            // S^T of (key half c, row tile r) = K_c Q_r^T: four independent chains
+            f32x16 sacc[2][2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[r]), __float_as_uint(l_part[r]), false,
-                                                         false);
-        const float l = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-        const float inv = l > 0.f ? 1.0f / l : 0.f;  // a row that saw no key is written as zeros
-        const int my_row = TILED ? (int)q_origin + kcell[r] : q0 + 32 * r + col;
-        if (my_row >= (int)P.S) continue;
-        uint16_t* orow = P.out + head + (size_t)my_row * D;
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t)
+                for (int r = 0; r < NR; ++r) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                bf16x4 w;
+                    for (int v = 0; v < 16; ++v) sacc[c][r][v] = 0.f;
+                }
+            // K fragments of the two key halves, read two steps ahead (ring of three)
+            bf16x8 kfa[3], kfb[3];
+            auto read_k = [&](int s) {
+                kfa[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(klds + k_addr[s]));
+                kfb[s % 3] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(klds + k_addr[s] + 32 * (D * 2)));
+            };
+            read_k(0);
+            read_k(1);
+            // (one MFMA per fenced region, with one V DMA or the K reads of step s+2
+            // beside it)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[r][t][4 * g + e] * inv);
-                *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half_id) = w;
+            for (int s = 0; s < D / 16; ++s) {
+                const bf16x8 ka = kfa[s % 3], kb = kfb[s % 3];
+                sacc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][s], sacc[0][0], 0, 0, 0);
+                if (!EV) dma_v(vlds, soff_cur, 2 * s, NR == 2 ? 2 * s + 1 : 2 * s + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                if (NR == 2) {
+                    sacc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][s], sacc[0][1], 0, 0, 0);
+                    if (!EV) dma_v(vlds, soff_cur, 2 * s + 1, 2 * s + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                sacc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[0][s], sacc[1][0], 0, 0, 0);
+                if (s + 2 < D / 16) read_k(s + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                if (NR == 2) {
+                    sacc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[1][s], sacc[1][1], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
+            // this tile's K is read: the next tile's K goes into its LDS (the last tile
+            // again past the end), with the list entry of the tile after it
+            if (MODE == kLabels) klab = klab_next;
+            v_nxt = tile_ahead(min(it + 2, n_iter - 1));
+            const int soff_nxt = tile_soff(nxt_tile);
+            const int kval_nxt = tile_keys(nxt_tile);
+            __builtin_amdgcn_s_waitcnt(kLgkmcnt0);  // this tile's K reads are complete
+            dma_k(soff_nxt);
+            if (MODE == kLabels) klab_next = labs[nxt + lane];
+            __builtin_amdgcn_sched_barrier(0);
+
+            // softmax of both row tiles (32 values of one row per lane and tile)
+            if (!POS) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int r = 0; r < NR; ++r)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) sacc[c][r][v] *= P.scale_log2;
+            }
+            if (PADT && kval_cur < BLK) {  // padding keys of a tile at the end of the padded frames
+                const float neg_inf = -__builtin_inff();
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int r = 0; r < NR; ++r)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int j = 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4);
+                            sacc[c][r][v] = j < kval_cur ? sacc[c][r][v] : neg_inf;
+                        }
+            }
+            if (MODE == kWindow) {
+                const int j0 = tile_at(it) * BLK;
+                const bool full = (j0 + BLK - 1 < P.sink) ||
+                                  (q0 + BLK - 1 - j0 <= P.half && j0 + BLK - 1 - q0 <= P.half && j0 + BLK <= (int)P.S);
+                if (!full) {
+                    const float neg_inf = -__builtin_inff();
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int r = 0; r < NR; ++r) {
+                            const int my_row = q0 + 32 * r + col;
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) {
+                                const int j = j0 + 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4);
+                                const int d = my_row - j;
+                                const bool vis = (j < (int)P.S) & (((d <= P.half) & (-d <= P.half)) | (j < P.sink));
+                                sacc[c][r][v] = vis ? sacc[c][r][v] : neg_inf;
+                            }
+                        }
+                }
+            }
+            if (MODE == kLabels) {
+                // a tile whose keys all carry the query block's single label needs no mask
+                if (!q_uniform || __ballot(klab != q_uni) != 0) {
+                    const float neg_inf = -__builtin_inff();
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int kl = __shfl(klab, 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4));
+#pragma unroll
+                            for (int r = 0; r < NR; ++r) sacc[c][r][v] = kl == qlab[r] ? sacc[c][r][v] : neg_inf;
+                        }
+                }
+            }
+            // (the ballot keeps the test in a VGPR compare; as a plain scalar branch
+            // the compiler allocates the loop's registers far worse)
+            const bool skip = bounded && __ballot(kn_cur <= kn_lim) != 0;
+            kn_cur = kn_nxt;
+            if (__builtin_expect(!skip, !bounded)) {
+                float mloc[2];
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    float smax = fmaxf(sacc[0][r][0], sacc[1][r][0]);
+#pragma unroll
+                    for (int v = 1; v < 16; ++v) smax = fmaxf(fmaxf(smax, sacc[0][r][v]), sacc[1][r][v]);
+                    const auto pr =
+                        __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+                    mloc[r] = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * c_scale;
+                }
+                const bool grow0 = mloc[0] > m_used[0] + kRescaleSlack;
+                const bool grow1 = NR == 2 && mloc[NR - 1] > m_used[NR - 1] + kRescaleSlack;
+                if (__ballot(grow0 | grow1)) {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        const bool grow = r == 0 ? grow0 : grow1;
+                        const float m_new = grow ? mloc[r] : m_used[r];
+                        const float alpha = __builtin_amdgcn_exp2f(m_used[r] - m_new);
+                        m_used[r] = m_new;
+                        l_part[r] *= alpha;
+#pragma unroll
+                        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) o[r][t][v] *= alpha;
+                    }
+                    if (bounded) {
+                        float mm = fminf(m_used[0], m_used[NR - 1]);
+#pragma unroll
+                        for (int off = 1; off < 64; off <<= 1) mm = fminf(mm, __shfl_xor(mm, off));
+                        const float m_min = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(mm)));
+                        kn_lim = (m_min + kSkipSlack) / q_lim;
+                    }
+                }
+            }
+            // P as bf16 B operands, one 16-key group m at a time (pb[r][m] covers keys
+            // 16m..16m+15); group m+1's exps and V^T reads are issued beside the
+            // MFMAs of group m
+            bf16x8 pb[2][4];
+            float psum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+            // piece j (0..3) of group m for row tile r: accumulator values
+            // 8(m % 2) + 2j and + 1 of key half m / 2, i.e. two of this lane's share
+            // of keys 16m..16m+15
+            auto p_piece = [&](int m, int r, int j) {
+                const int c = m / 2, v = 8 * (m % 2) + 2 * j;
+                const float neg_m = -m_used[r];
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v], c_scale, neg_m));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[c][r][v + 1], c_scale, neg_m));
+                const bf16x2 two = {(__bf16)p0, (__bf16)p1};
+                psum[r][m % 2] = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, psum[r][m % 2], false);
+                pb[r][m][v % 8] = two[0];
+                pb[r][m][v % 8 + 1] = two[1];
+            };
+            // V^T fragment t of group m (keys 16m..16m+15) in two transposing reads of
+            // 8 keys each; vfr[m % 2] holds a group's four fragments
+            bf16x8 vfr[2][D / 32];
+            s16x4 vlo[D / 32];
+            auto v_half = [&](int m, int t, int h) {
+                const char* va = vlds + v_addr[t] + (16 * m + 8 * h) * (D * 2);
+                const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)va);
+                if (h == 0) {
+                    vlo[t] = x;
+                } else {
+                    const s16x4 a8[2] = {vlo[t], x};
+                    vfr[m % 2][t] = __builtin_bit_cast(bf16x8, a8);
+                }
+            };
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p_piece(0, r, j);
+            // O^T += V^T P^T once this tile's V has landed: only the next tile's 16 K
+            // loads and (block lists) its list entry were issued after it
+            __builtin_amdgcn_s_waitcnt(MODE == kWindow ? kVmcnt16 : waitcnt_vm(17));
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) {
+                v_half(0, t, 0);
+                v_half(0, t, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // (one MFMA per fenced region; beside each, the share of group m+1 that
+            // falls to it: with two row tiles two exps of one row tile and half of
+            // one V^T fragment, with one row tile two exps and a whole fragment; EV:
+            // beside the last group's MFMAs, the next tile's V DMA instructions in
+            // equal shares, the last tile's again past the end)
+            constexpr int kPvPerGroup = NR * (D / 32), kDmaPer = (C::TILE / 1024) / kPvPerGroup;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (EV && m == 3) {  // every V^T read of this tile has returned
+                    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int i = 0; i < kPvPerGroup; ++i) {
+                    const int t = NR == 2 ? i / 2 : i, r = NR == 2 ? i % 2 : 0;
+                    o[r][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m % 2][t], pb[r][m], o[r][t], 0, 0, 0);
+                    if (m + 1 < 4) {
+                        if (NR == 2) {
+                            p_piece(m + 1, i / 4, i % 4);
+                            v_half(m + 1, t, i % 2);
+                        } else {
+                            p_piece(m + 1, 0, i);
+                            v_half(m + 1, t, 0);
+                            v_half(m + 1, t, 1);
+                        }
+                    } else if (EV) {
+                        dma_v(vlds, soff_nxt, kDmaPer * i, kDmaPer * (i + 1));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) l_part[r] += psum[r][0] + psum[r][1];
+            soff_cur = soff_nxt;
+            kval_cur = kval_nxt;
+        }
+
+        // ---- write out (each lane pair holds one row; their partial sums add up)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[r]), __float_as_uint(l_part[r]), false,
+                                                             false);
+            const float l = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+            const float inv = l > 0.f ? 1.0f / l : 0.f;  // a row that saw no key is written as zeros
+            const int my_row = TILED ? (int)q_origin + kcell[r] : q0 + 32 * r + col;
+            if (my_row >= (int)P.S) continue;
+            uint16_t* orow = P.out + head + (size_t)my_row * D;
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    bf16x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[r][t][4 * g + e] * inv);
+                    *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half_id) = w;
+                }
+        }
+        // EV: the V DMA issued past the last tile lands before the wave ends
+        if (EV) __builtin_amdgcn_s_waitcnt(0);
+    };
+    if (PADT) {
+        uint32_t tc = 0;
+        if (P.head_choice != nullptr) {
+            tc = (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[bh]);
+            if (tc >= P.n_tiles) tc = 0;
+        }
+        if (I < P.nbt[tc] && padded_tile_cells(P.geo[tc], P.T, I) <= 32) {
+            body(std::integral_constant<int, 1>{});
+            return;
+        }
     }
-    // EV: the V DMA issued past the last tile lands before the wave ends
-    if (EV) __builtin_amdgcn_s_waitcnt(0);
+    body(std::integral_constant<int, 2>{});
 }
 
 // ----------------------------------------------------------------- scalar ---
