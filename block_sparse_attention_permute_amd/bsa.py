@@ -37,7 +37,7 @@ EXPORTED = (
     "bsa_minmax_block_scores_tiled", "bsa_block_sparse_attention_tiled",
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices", "bsa_video_labels",
     "bsa_select_tiling_noalloc", "bsa_temporal_only_attention", "bsa_block_sparse_attention_tiled_padded",
-    "bsa_tiled_attention_supported", "bsa_row_order", "bsa_row_order_len",
+    "bsa_tiled_attention_supported", "bsa_row_order", "bsa_row_order_len", "bsa_minmax_block_scores_tiled_padded",
 )
 
 
@@ -88,6 +88,8 @@ _SIGS = {
                                                      _P, _P, _I, _F, _P, _P, _I64, _P]),
     "bsa_tiled_attention_supported": (_I, [_I, _I64, _I, _I, _I, _P, _I, _I]),
     "bsa_row_order": (_I, [_P, _I64, _I64, _P, _I64, _P]),
+    "bsa_minmax_block_scores_tiled_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P,
+                                                  _P]),
     "bsa_row_order_len": (_I64, [_I64, _I64]),
 }
 
@@ -486,6 +488,32 @@ def bsa_minmax_block_scores_tiled(q, k, grid, tiles, head_choice=None, out=None,
     return scores, summ
 
 
+def bsa_minmax_block_scores_tiled_padded(q, k, grid, tiles, head_choice=None, out=None, key_norms=None):
+    """Min/max block scores of T-major q, k on each head's grid padded along T (block J = tile J of the head's
+    padded tiling; padding cells left out, unread) -> (scores (B, H, Nb, Nb), summaries (4, B, H, Nb, D)), Nb =
+    the largest padded block count (padded_rows(grid, tiles) // block).  key_norms as in bsa_minmax_block_scores."""
+    torch = _torch()
+    B, H, S, D = _bhsd(q, "q")
+    if _bhsd(k, "k") != (B, H, S, D) or k.dtype != q.dtype:
+        raise ValueError("q and k must match")
+    T, Hg, Wg = (int(g) for g in grid)
+    if T * Hg * Wg != S:
+        raise ValueError(f"grid {tuple(grid)} does not match S={S}")
+    arr, n = _tiles_arr(tiles)
+    block = tiles[0][0] * tiles[0][1] * tiles[0][2]
+    nb = padded_rows(grid, tiles) // block
+    if out is None:
+        scores = torch.empty((B, H, nb, nb), dtype=torch.float32, device=q.device)
+        summ = torch.empty((4, B, H, nb, D), dtype=q.dtype, device=q.device)
+    else:
+        scores, summ = out
+    hc = None if head_choice is None else _dev(head_choice, "head_choice")
+    kn = _norms_out(key_norms, B, H, nb, q)
+    _check(lib().bsa_minmax_block_scores_tiled_padded(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, T, Hg, Wg, D,
+                                                      arr, n, hc, _dev(summ), _dev(scores), kn, _stream(q)))
+    return scores, summ
+
+
 def _band(diag_width) -> int:
     """Diagonal band width: True/False mean 1/0 (the diagonal alone / none)."""
     w = int(diag_width)
@@ -780,10 +808,9 @@ class AdaptiveBlockSparse:
     dropped from the output), with the budget floor(frac * that grid's block
     count.  ``fused`` (default: whenever the kernels cover the tilings, see
     tiled_attention_supported) reads q, k, v in place through the tile
-    geometry for the attention (and, without padding, for the scores) and
-    writes the output in T-major order, so the attention needs no permuted
-    copy; with padding the scores still read padded permuted copies of q and
-    k.  ``validate=True`` checks the device-resident tiling choices and (without
+    geometry for the scores and the attention and writes the output in
+    T-major order, so no pass forms a permuted copy (with padding, the cells
+    of the padding frames are left out unread).  ``validate=True`` checks the device-resident tiling choices and (without
     padding) block lists (bsa_validate_indices, bsa_validate_block_list)
     before the attention runs; each check synchronises the stream and raises
     RuntimeError on a violation.
@@ -829,15 +856,12 @@ class AdaptiveBlockSparse:
         self.ws_select = (torch.empty((B, H, n, self.nb), dtype=torch.float32, **f),
                           torch.empty((B, H, n), dtype=torch.float32, **f),
                           torch.empty((B, H), dtype=torch.int32, **f))
-        if self.fused and not self.pad:
+        if self.fused:     # every pass reads q, k, v in place through the tile geometry
             self.qp = self.kp = self.vp = self.op = None
-        elif self.fused:   # padded: q, k permuted for the scores only
-            self.qp, self.kp = (torch.empty((B, H, self.Sp, D), dtype=dtype, **f) for _ in range(2))
-            self.vp = self.op = None
         else:
             self.qp, self.kp, self.vp, self.op = (torch.empty((B, H, self.Sp, D), dtype=dtype, **f)
                                                   for _ in range(4))
-        self.labels = torch.empty((B, H, self.Sp), dtype=torch.int32, **f) if self.pad else None
+        self.labels = torch.empty((B, H, self.Sp), dtype=torch.int32, **f) if self.pad and not self.fused else None
         self.ws_scores = (torch.empty((B, H, self.nb, self.nb), dtype=torch.float32, **f),
                           torch.empty((4, B, H, self.nb, D), dtype=dtype, **f))
         self.ws_topk = (torch.empty((B, H, self.nb, self.max_kept), dtype=torch.int32, **f),
@@ -870,11 +894,15 @@ class AdaptiveBlockSparse:
         if self.validate:
             bsa_validate_indices(choice, 0, len(self.tiles))
         if self.pad:
-            srcs = ((q, self.qp, self.labels), (k, self.kp, None)) + (() if self.fused else ((v, self.vp, None),))
-            for src, dst, lab in srcs:
-                bsa_tile_permute_padded(src, self.grid, self.tiles, head_choice=choice, Sp=self.Sp, out=(dst, lab))
-            scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores, labels=self.labels,
-                                                key_norms=self.ws_knorm)
+            if self.fused:
+                scores, _ = bsa_minmax_block_scores_tiled_padded(q, k, self.grid, self.tiles, head_choice=choice,
+                                                                 out=self.ws_scores, key_norms=self.ws_knorm)
+            else:
+                for src, dst, lab in ((q, self.qp, self.labels), (k, self.kp, None), (v, self.vp, None)):
+                    bsa_tile_permute_padded(src, self.grid, self.tiles, head_choice=choice, Sp=self.Sp,
+                                            out=(dst, lab))
+                scores, _ = bsa_minmax_block_scores(self.qp, self.kp, self.block, out=self.ws_scores,
+                                                    labels=self.labels, key_norms=self.ws_knorm)
             kv_idx, kv_cnt = bsa_topk_block_mask_tiled(scores, choice, self.k_table, self.nk_table, self.sink_blocks,
                                                        self.keep_diag, max_kept=self.max_kept, out=self.ws_topk)
             if self.ws_order is not None:

@@ -14,7 +14,10 @@
 // bsa_minmax_block_scores_masked leaves out tokens labelled < 0 (the padding
 // of a padded tiling, [Adaptive tiling (SPADE), "Deviations and notes"]):
 // a partial block is summarised by its real tokens, and a block with none
-// scores -inf in its row and its column.
+// scores -inf in its row and its column.  bsa_minmax_block_scores_tiled_padded
+// does the same on T-major q and k, block J of a head being tile J of the
+// head's tiling on the grid padded along T: cells of the padding frames lie
+// past the head and are left out without being read.
 //
 // Design: pass 1 is an HBM-bound reduction, one wave per block, that keeps
 // the summaries in the input dtype (a max or min of bf16 values is a bf16
@@ -23,6 +26,8 @@
 // otherwise in fp32 FMAs tiled 64 x 64 per workgroup through LDS, with the
 // two dot products of a score sharing their query operand.
 #include "common.h"
+
+#include <algorithm>
 
 namespace bsa {
 namespace {
@@ -36,11 +41,14 @@ struct SumParams {
     char* summ;  // 4 x (BH, Nb, D) of the input dtype
     float* knorm;  // (BH, Nb): largest L2 norm of a key row in each block, or null
     uint32_t block, nb, vecs_per_row, BH;
+    uint32_t head_len;      // token rows of a head in q and k
     const int32_t* labels;  // (BH, S) or null; tokens labelled < 0 are left out
     // tiled: q, k in T-major order, block = tile of the head's tiling
     const int32_t* head_choice;
     uint32_t n_tiles, Hg, Wg;
     TileGeo geo[BSA_MAX_TILINGS];
+    // padded along T (tiled): each candidate's block count on its padded grid
+    uint32_t nbt[BSA_MAX_TILINGS];
     // tiled, optional: q's summaries of every candidate, [n_tiles][2][BH][Nb][D]
     // (bsa_select_tiling_ex writes them); the q half then copies the chosen
     // candidate's instead of reading q
@@ -49,7 +57,10 @@ struct SumParams {
 
 // blockIdx: x = group of kWaves blocks, y = 0 (q) / 1 (k), z = b*H + h.
 // LABELS: P.labels is set (contiguous blocks only).
-template <int EPV, int LPT, bool TILED, bool LABELS>
+// PADT (tiled): the tiling's grid is padded along T; a cell at or past the
+// head's end is padding, left out and not read, and blocks past the head's
+// own count hold padding only.
+template <int EPV, int LPT, bool TILED, bool LABELS, bool PADT = false>
 __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumParams P) {
     constexpr int TPI = 64 / LPT;
     const int lane = threadIdx.x & 63;
@@ -59,6 +70,7 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
     const uint32_t bh = blockIdx.z;
     const size_t row_bytes = (size_t)P.vecs_per_row * 16;
     uint32_t origin = 0;
+    bool block_real = true;  // PADT: the block is a tile of the head's padded grid
     TileGeo g{};  // a copy: indexing the by-value parameter through a pointer puts it in scratch memory
     if (TILED) {
         uint32_t c = P.head_choice != nullptr ? (uint32_t)__builtin_amdgcn_readfirstlane(P.head_choice[bh]) : 0u;
@@ -74,10 +86,11 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
             return;
         }
         g = P.geo[c];
-        origin = tile_origin(blk, g, P.Hg, P.Wg);
+        if (PADT) block_real = blk < P.nbt[c];
+        origin = block_real ? tile_origin(blk, g, P.Hg, P.Wg) : 0u;
     }
-    const char* src = TILED ? (which == 0 ? P.q : P.k) + ((size_t)bh * P.nb * P.block + origin) * row_bytes
-                            : (which == 0 ? P.q : P.k) + ((size_t)bh * P.nb + blk) * P.block * row_bytes;
+    const char* head_src = (which == 0 ? P.q : P.k) + (size_t)bh * P.head_len * row_bytes;
+    const char* src = TILED ? head_src + (size_t)origin * row_bytes : head_src + (size_t)blk * P.block * row_bytes;
     const int sub = lane % LPT;
     const int slot = lane / LPT;
     RowRange<EPV> range;
@@ -93,21 +106,24 @@ __global__ __launch_bounds__(64 * kWaves) void block_minmax_kernel(const SumPara
     // and a row labelled < 0 is left out.
     for (uint32_t t0 = slot; t0 < P.block; t0 += TPI * kBatch) {
         uint4 raw[kBatch];
-        bool use[kBatch];
+        bool use[kBatch], real[kBatch];
         int32_t lv[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const uint32_t t = t0 + j * TPI;
             const uint32_t tc = t < P.block ? t : 0u;
             if (LABELS) lv[j] = lab[tc];
-            const uint32_t r = TILED ? cell_offset(tc, g, P.Hg, P.Wg) : tc;
-            raw[j] = *reinterpret_cast<const uint4*>(src + (size_t)r * row_bytes + (size_t)sub * 16);
+            uint32_t r = TILED ? cell_offset(tc, g, P.Hg, P.Wg) : tc;
+            real[j] = !PADT || (block_real && origin + r < P.head_len);
+            if (!real[j]) r = 0u;  // padding: the head's first row stands in, and is left out below
+            raw[j] = *reinterpret_cast<const uint4*>((real[j] ? src : head_src) + (size_t)r * row_bytes +
+                                                     (size_t)sub * 16);
         }
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) use[j] = t0 + j * TPI < P.block && (!LABELS || lv[j] >= 0);
+        for (int j = 0; j < kBatch; ++j) use[j] = t0 + j * TPI < P.block && (!LABELS || lv[j] >= 0) && real[j];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            if (!LABELS || use[j]) range.add(raw[j]);
+            if (!(LABELS || PADT) || use[j]) range.add(raw[j]);
             if (norms) {
                 float v[EPV];
                 unpack<EPV>(raw[j], v);
@@ -360,7 +376,7 @@ namespace {
 
 int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H, int64_t S, int64_t D, int block,
                   const int32_t* labels, SumParams& P, bool tiled, void* summaries, float* scores, float* key_norms,
-                  hipStream_t st, const char* name) {
+                  hipStream_t st, const char* name, bool pad = false, int64_t head_len = 0) {
     const int es = elem_size(dtype);
     BSA_REQUIRE(es != 0, "%s: unknown dtype %d", name, dtype);
     BSA_REQUIRE(q && k && summaries && scores, "%s: NULL argument", name);
@@ -383,10 +399,12 @@ int minmax_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H,
     P.BH = (uint32_t)(B * H);
     P.labels = labels;
     P.knorm = key_norms;
+    P.head_len = (uint32_t)(head_len > 0 ? head_len : S);
     dim3 g1((unsigned)((nb + kWaves - 1) / kWaves), 2, (unsigned)(B * H));
-#define BSA_MM(EPV, LPT)                                                                    \
-    (tiled ? block_minmax_kernel<EPV, LPT, true, false><<<g1, 64 * kWaves, 0, st>>>(P)     \
-     : labels ? block_minmax_kernel<EPV, LPT, false, true><<<g1, 64 * kWaves, 0, st>>>(P) \
+#define BSA_MM(EPV, LPT)                                                                                \
+    (pad ? block_minmax_kernel<EPV, LPT, true, false, true><<<g1, 64 * kWaves, 0, st>>>(P)             \
+     : tiled ? block_minmax_kernel<EPV, LPT, true, false><<<g1, 64 * kWaves, 0, st>>>(P)               \
+     : labels ? block_minmax_kernel<EPV, LPT, false, true><<<g1, 64 * kWaves, 0, st>>>(P)              \
               : block_minmax_kernel<EPV, LPT, false, false><<<g1, 64 * kWaves, 0, st>>>(P))
     const bool bf = dtype == BSA_BF16;
     switch (vecs) {
@@ -464,6 +482,37 @@ extern "C" int bsa_minmax_block_scores_tiled(const void* q, const void* k, int d
     BSA_REQUIRE(aligned16(P.qsumm), "%s: q summaries must be 16-byte aligned", name);
     return minmax_scores(q, k, dtype, B, H, (int64_t)T * Hg * Wg, D, vol, nullptr, P, true, summaries, scores,
                          key_norms_or_null, (hipStream_t)stream, name);
+}
+
+extern "C" int bsa_minmax_block_scores_tiled_padded(const void* q, const void* k, int dtype, int64_t B, int64_t H,
+                                                    int T, int Hg, int Wg, int64_t D, const int32_t* tiles_host,
+                                                    int n_tiles, const int32_t* head_choice, void* summaries,
+                                                    float* scores, float* key_norms_or_null, bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_minmax_block_scores_tiled_padded";
+    int rc = check_tiles_padded(T, Hg, Wg, tiles_host, n_tiles);
+    if (rc) return rc;
+    SumParams P{};
+    const int vol = tiles_host[0] * tiles_host[1] * tiles_host[2];
+    int64_t nb = 0;
+    for (int i = 0; i < BSA_MAX_TILINGS; ++i) {
+        const int j = i < n_tiles ? i : 0;
+        const int a = tiles_host[3 * j], b = tiles_host[3 * j + 1], c = tiles_host[3 * j + 2];
+        BSA_REQUIRE(a * b * c == vol, "%s: candidate tiles must share one volume", name);
+        if (Hg % b != 0 || Wg % c != 0)
+            BSA_FAIL(BSA_ERR_UNSUPPORTED, "%s: padding along T only (tile %d is %dx%dx%d on a %dx%dx%d grid)", name,
+                     j, a, b, c, T, Hg, Wg);
+        P.geo[i] = make_geo_padded(Hg, Wg, a, b, c);
+        const int64_t n = padded_length(T, Hg, Wg, a, b, c) / vol;
+        P.nbt[i] = (uint32_t)n;
+        nb = std::max<int64_t>(nb, n);
+    }
+    P.head_choice = head_choice;
+    P.n_tiles = (uint32_t)n_tiles;
+    P.Hg = (uint32_t)Hg;
+    P.Wg = (uint32_t)Wg;
+    return minmax_scores(q, k, dtype, B, H, nb * vol, D, vol, nullptr, P, true, summaries, scores, key_norms_or_null,
+                         (hipStream_t)stream, name, true, (int64_t)T * Hg * Wg);
 }
 
 extern "C" int bsa_minmax_block_scores(const void* q, const void* k, int dtype, int64_t B, int64_t H, int64_t S,

@@ -291,6 +291,26 @@ int bsa_minmax_block_scores_tiled(const void* q, const void* k, int dtype, int64
                                   float* scores, float* key_norms_or_null,
                                   const void* q_summaries_or_null, bsa_stream_t stream);
 
+/* bsa_minmax_block_scores_tiled on each head's grid padded along T (the
+ * candidates need not divide T): block J of head (b, h) is tile J of the
+ * padded grid of candidate c = head_choice[b*H + h] (0 if NULL), tiles
+ * numbered T-major as bsa_tile_permutation_padded.  Cells of the padding
+ * frames lie past the head; they are left out of the summaries and the key
+ * norms without being read, so the result equals
+ * bsa_tile_permute_padded -> bsa_minmax_block_scores_masked (labels 0 for
+ * real, -1 for padding) bit for bit, without the padded copies
+ * [Adaptive tiling (SPADE), "Deviations and notes": pad with zero tokens and
+ * mask them; "The idea" steps 2 and 3].  Nb = the largest padded block
+ * count over the candidates; blocks past a head's own count hold padding
+ * only (scores -inf, key norm 0).  Outputs as bsa_minmax_block_scores with
+ * that Nb.  UNSUPPORTED when a candidate would pad along y or x (b must
+ * divide Hg and c divide Wg); INVALID_ARG as bsa_minmax_block_scores_tiled
+ * otherwise. */
+int bsa_minmax_block_scores_tiled_padded(const void* q, const void* k, int dtype, int64_t B, int64_t H,
+                                         int T, int Hg, int Wg, int64_t D, const int32_t* tiles_host,
+                                         int n_tiles, const int32_t* head_choice, void* summaries,
+                                         float* scores, float* key_norms_or_null, bsa_stream_t stream);
+
 /* bsa_minmax_block_scores over labelled tokens only: tokens with
  * labels[b,h,s] < 0 (padding) are left out of the summaries, so a partial
  * block is summarised by its real tokens [Adaptive tiling (SPADE),

@@ -598,6 +598,36 @@ def _padded_lists_check_rows(out, q, k, v, grid, tiles, choice, idx, cnt, heads,
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("grid,tiles,H,choices", [
+    ((20, 8, 8), [(1, 8, 8), (4, 4, 4), (16, 2, 2)], 4, [0, 2, 1, 2]),      # T = 20 padded to 32 for (16, 2, 2)
+    ((6, 16, 16), [(1, 8, 8), (4, 4, 4)], 3, [1, 0, 1]),                   # T = 6 padded to 8 for (4, 4, 4)
+    ((5, 8, 16), [(1, 8, 8), (2, 4, 8), (4, 4, 4)], 2, [2, 1]),           # every candidate pads but (1, 8, 8)
+])
+def test_padded_scores_gather_on_load_equal_masked_copies(grid, tiles, H, choices):
+    """bsa_minmax_block_scores_tiled_padded on T-major q, k equals bsa_tile_permute_padded followed by
+    bsa_minmax_block_scores_masked bit for bit: summaries, scores (-inf rows and columns of padding-only blocks
+    included) and key norms; B = 2 with different choices per batch."""
+    torch = torch_gpu()
+    B, D = 2, 128
+    S = grid[0] * grid[1] * grid[2]
+    q, k = (synth.normal_bits((B, H, S, D), seed=8100 + i) for i in range(2))
+    qg, kg = gpu(q), gpu(k)
+    choice = torch.tensor([choices, choices[::-1]], dtype=torch.int32, device="cuda")
+    Sp = bsa.padded_rows(grid, tiles)
+    nb = Sp // 64
+    kn_t = torch.full((B, H, nb), -7.0, dtype=torch.float32, device="cuda")
+    sc_t, sm_t = bsa.bsa_minmax_block_scores_tiled_padded(qg, kg, grid, tiles, head_choice=choice, key_norms=kn_t)
+    qp, lab = bsa.bsa_tile_permute_padded(qg, grid, tiles, head_choice=choice, Sp=Sp)
+    kp, _ = bsa.bsa_tile_permute_padded(kg, grid, tiles, head_choice=choice, Sp=Sp, labels=False)
+    kn_p = torch.full((B, H, nb), -7.0, dtype=torch.float32, device="cuda")
+    sc_p, sm_p = bsa.bsa_minmax_block_scores(qp, kp, 64, labels=lab, key_norms=kn_p)
+    assert torch.equal(sm_t, sm_p)
+    assert torch.equal(kn_t, kn_p)
+    assert torch.equal(sc_t.isneginf(), sc_p.isneginf()) and sc_t.isneginf().any()
+    assert torch.equal(sc_t, sc_p)
+
+
+@pytest.mark.gpu
 def test_padded_pipeline_gather_on_load_small():
     """Candidates (1,8,8), (4,4,4), (16,2,2) on a 20x8x8 grid (T padded to 32 for (16,2,2)): the padded
     pipeline with attention on T-major tensors gives the same lists as the permuted-copy pipeline, outputs
