@@ -221,13 +221,17 @@ int band_width(int diag_width) { return diag_width >= 1 ? 2 * (diag_width / 2) +
 //     decreasing count (in kPlanBins coarse bins: counts >= kPlanBins - 1
 //     rank as one).
 // Workgroup w runs on XCD w % 8, so XCD x's j-th row goes to entry 8j + x.
-// One workgroup does it all; the counts are read once into LDS (up to
-// kCacheRows rows; longer lists are read from memory at each step).
+// Three launches: the weights and the sorts run one workgroup per unit, the
+// scheduling one workgroup; the weights and placements pass through the last
+// 3U entries of the order buffer, which the sorts then leave empty.
 constexpr int kPlanThreads = 1024, kPlanWaves = kPlanThreads / 64, kPlanBins = 256, kMaxUnits = 1024;
-constexpr uint32_t kRowCost = 5, kEmptySlot = 0xFFFFFFFFu, kCacheRows = 49152;
+constexpr int kUnitThreads = 256, kUnitWaves = kUnitThreads / 64;
+constexpr uint32_t kRowCost = 5, kEmptySlot = 0xFFFFFFFFu;
 
 struct Plan {
     int64_t units, unit_rows, cap;  // cap: rows per XCD
+    int64_t plan_len() const { return 8 * cap; }
+    int64_t len() const { return 8 * cap + 3 * units; }  // plus the scratch words
 };
 
 Plan plan_shape(int64_t BH, int64_t nq) {
@@ -241,58 +245,53 @@ Plan plan_shape(int64_t BH, int64_t nq) {
     return p;
 }
 
+__device__ __forceinline__ uint32_t plan_count(int c) { return (uint32_t)min(max(c, 0), 65535); }
+
 __device__ __forceinline__ uint32_t plan_key(uint32_t c) {
     // bin of a count: longest first, counts of kPlanBins - 1 or more in bin 0
     return c >= kPlanBins - 1 ? 0u : kPlanBins - 1 - c;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* __restrict__ cnt, uint32_t units,
-                                                                uint32_t unit_rows, uint32_t cap, uint32_t len,
-                                                                uint32_t* __restrict__ order) {
-    __shared__ uint16_t cache[kCacheRows];
+// 1. one workgroup per unit: its weight, as two words at scratch[2u]
+__global__ __launch_bounds__(kUnitThreads) void plan_weight_kernel(const int32_t* __restrict__ cnt,
+                                                                   uint32_t unit_rows, uint32_t* __restrict__ scratch) {
+    __shared__ unsigned long long part[kUnitWaves];
+    const uint32_t u = blockIdx.x, t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+    const int32_t* c = cnt + (size_t)u * unit_rows;
+    unsigned long long w = 0;
+#pragma unroll 4
+    for (uint32_t i = t; i < unit_rows; i += kUnitThreads) w += plan_count(c[i]) + kRowCost;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) w += __shfl_xor(w, off);
+    if (lane == 0) part[wave] = w;
+    __syncthreads();
+    if (t == 0) {
+        unsigned long long sum = 0;
+#pragma unroll
+        for (int i = 0; i < kUnitWaves; ++i) sum += part[i];
+        scratch[2 * u] = (uint32_t)sum;
+        scratch[2 * u + 1] = (uint32_t)(sum >> 32);
+    }
+}
+
+// 2. one workgroup: the weights' shift, the units' rank, list scheduling; the
+// placement of unit u ((first position on its XCD) << 3 | XCD) goes to
+// scratch[2U + u], and the plan's slots past each XCD's rows, and the buffer
+// past the scratch words, are emptied
+__global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(uint32_t units, uint32_t unit_rows, uint32_t cap,
+                                                                  uint32_t len, uint32_t* __restrict__ order) {
     __shared__ unsigned long long weight[kMaxUnits];
     __shared__ uint32_t weight32[kMaxUnits];
     __shared__ uint32_t ranked_weight[kMaxUnits];
-    __shared__ unsigned long long partial[kPlanWaves];
     __shared__ uint32_t by_rank[kMaxUnits];
-    __shared__ uint32_t place[kMaxUnits];  // (first position on the XCD) << 3 | XCD
+    __shared__ unsigned long long partial[kPlanWaves];
     __shared__ uint32_t fill[8];
-    __shared__ uint32_t bins[kPlanWaves][kPlanBins];
     const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
-    const uint32_t rows = units * unit_rows;
-    const bool cached = rows <= kCacheRows;
-    // counts clamped to [0, 65535], eight loads in flight per lane
-    if (cached) {
-        for (uint32_t base = 0; base < rows; base += 8u * kPlanThreads) {
-            int c[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t r = base + (uint32_t)k * kPlanThreads + t;
-                c[k] = r < rows ? cnt[r] : 0;
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t r = base + (uint32_t)k * kPlanThreads + t;
-                if (r < rows) cache[r] = (uint16_t)min(max(c[k], 0), 65535);
-            }
-        }
-    }
-    __syncthreads();
-    auto count = [&](uint32_t r) -> uint32_t {
-        if (cached) return cache[r];
-        return (uint32_t)min(max(cnt[r], 0), 65535);
-    };
-    // 1. unit weights, one wave per unit
-    for (uint32_t u = wave; u < units; u += kPlanWaves) {
-        unsigned long long w = 0;
-        for (uint32_t i = lane; i < unit_rows; i += 64) w += count(u * unit_rows + i) + kRowCost;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) w += __shfl_xor(w, off);
-        if (lane == 0) weight[u] = w;
-    }
-    __syncthreads();
-    {   // total weight -> the shift that brings it under 2^28 (units <= kPlanThreads: one unit per thread)
-        unsigned long long w = t < units ? weight[t] : 0ull;
+    const uint32_t plan_len = 8u * cap;
+    uint32_t* scratch = order + plan_len;
+    {   // the total weight -> the shift that brings it under 2^28 (one unit per thread: units <= kPlanThreads)
+        unsigned long long w = t < units ? ((unsigned long long)scratch[2 * t + 1] << 32) | scratch[2 * t] : 0ull;
+        if (t < units) weight[t] = w;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) w += __shfl_xor(w, off);
         if (lane == 0) partial[wave] = w;
@@ -306,21 +305,21 @@ __global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* _
     }
     __syncthreads();
     // units ranked by weight, heaviest first (ties: lower unit first)
-    for (uint32_t u = t; u < units; u += kPlanThreads) {
-        const uint32_t w = weight32[u];
+    if (t < units) {
+        const uint32_t w = weight32[t];
         uint32_t rank = 0;
         for (uint32_t v = 0; v < units; ++v) {
             const uint32_t x = weight32[v];
-            rank += (x > w || (x == w && v < u)) ? 1u : 0u;
+            rank += (x > w || (x == w && v < t)) ? 1u : 0u;
         }
-        by_rank[rank] = u;
+        by_rank[rank] = t;
         ranked_weight[rank] = w;
     }
     __syncthreads();
-    // 2. list scheduling in wave 0 on wave-uniform values: XCD x's load is kept as the key (load << 3) | x
-    //    (< 2^31), so the least loaded XCD (ties: lower XCD) is the smallest key of those with room, found
-    //    without branches; 64 ranked units at a time are read into a VGPR, one per lane, taken out lane by
-    //    lane, and their placements gathered in a VGPR that is written once
+    // list scheduling in wave 0 on wave-uniform values: XCD x's load is kept as the key (load << 3) | x
+    // (< 2^31), so the least loaded XCD (ties: lower XCD) is the smallest key of those with room, found
+    // without branches; 64 ranked units at a time are read into a VGPR, one per lane, taken out lane by
+    // lane, and their placements gathered in a VGPR that is written once
     if (wave == 0) {
         const uint32_t room = cap / unit_rows;   // units an XCD may hold: ceil(U/8)
         uint32_t key[8], held[8];
@@ -348,84 +347,79 @@ __global__ __launch_bounds__(kPlanThreads) void row_plan_kernel(const int32_t* _
                 }
                 my_place = lane == j ? (((first * unit_rows) << 3) | bx) : my_place;
             }
-            if (has) place[my_u] = my_place;
+            if (has) scratch[2 * units + my_u] = my_place;
         }
 #pragma unroll
         for (int x = 0; x < 8; ++x)
             if (lane == (uint32_t)x) fill[x] = held[x] * unit_rows;
     }
     __syncthreads();
-    // slots past each XCD's last row, and past the plan, are empty
-    for (uint32_t e = t; e < len; e += kPlanThreads) {
-        const uint32_t x = e & 7u, p = e >> 3;
-        if (e >= 8u * cap || p >= fill[x]) order[e] = kEmptySlot;
+    for (uint32_t e = t; e < plan_len; e += kPlanThreads)
+        if ((e >> 3) >= fill[e & 7u]) order[e] = kEmptySlot;
+    for (uint32_t e = plan_len + 3u * units + t; e < len; e += kPlanThreads) order[e] = kEmptySlot;
+}
+
+// 3. one workgroup per unit: its rows by decreasing count into its place; its
+// scratch words are left empty
+__global__ __launch_bounds__(kUnitThreads) void plan_sort_kernel(const int32_t* __restrict__ cnt, uint32_t units,
+                                                                 uint32_t unit_rows, uint32_t cap,
+                                                                 uint32_t* __restrict__ order) {
+    __shared__ uint32_t bins[kPlanBins];
+    __shared__ uint32_t wave_total[kUnitWaves];
+    const uint32_t u = blockIdx.x, t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+    uint32_t* scratch = order + 8u * cap;
+    const uint32_t place = (uint32_t)__builtin_amdgcn_readfirstlane(scratch[2 * units + u]);
+    const uint32_t x = place & 7u, p0 = place >> 3;
+    const uint32_t r0 = u * unit_rows;
+    for (uint32_t i = t; i < kPlanBins; i += kUnitThreads) bins[i] = 0;
+    __syncthreads();
+    // (when every active lane of a wave has the same key, as a head's equal-length top-k lists give, one
+    // lane adds them all: 64 lanes on one LDS address would serialise)
+    for (uint32_t i = t; i < unit_rows; i += kUnitThreads) {
+        const uint32_t key = plan_key(plan_count(cnt[r0 + i]));
+        const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane(key);
+        const uint64_t same = __ballot(key == k0), all = __ballot(true);
+        if (same == all) {
+            if (lane == (uint32_t)__builtin_ctzll(all)) atomicAdd(&bins[k0], (uint32_t)__builtin_popcountll(all));
+        } else {
+            atomicAdd(&bins[key], 1u);
+        }
     }
-    // 3. each wave sorts one unit at a time by decreasing count
-    for (uint32_t base = 0; base < units; base += kPlanWaves) {
-        const uint32_t u = base + wave;
-        const bool active = u < units;
-        uint32_t* b = bins[wave];
-        for (uint32_t i = lane; i < kPlanBins; i += 64) b[i] = 0;
-        __syncthreads();
-        const uint32_t r0 = u * unit_rows;
-        // (when every active lane has the same key, as a head's equal-length top-k lists give, one lane adds
-        // them all: 64 lanes on one LDS address would serialise)
-        if (active) {
-            for (uint32_t i = lane; i < unit_rows; i += 64) {
-                const uint32_t key = plan_key(count(r0 + i));
-                const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane(key);
-                const uint64_t same = __ballot(key == k0), all = __ballot(true);
-                if (same == all) {
-                    if (lane == (uint32_t)__builtin_ctzll(all)) atomicAdd(&b[k0], (uint32_t)__builtin_popcountll(all));
-                } else {
-                    atomicAdd(&b[key], 1u);
-                }
-            }
-        }
-        __syncthreads();
-        constexpr int kPer = kPlanBins / 64;
-        uint32_t own[kPer], sum = 0;
+    __syncthreads();
+    // exclusive scan of the bins, one bin per thread
+    const uint32_t own = bins[t];
+    uint32_t incl = own;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            own[j] = b[lane * kPer + j];
-            sum += own[j];
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= (uint32_t)off) incl += y;
+    }
+    if (lane == 63u) wave_total[wave] = incl;
+    __syncthreads();
+    uint32_t run = incl - own;
+    for (uint32_t i = 0; i < wave; ++i) run += wave_total[i];
+    bins[t] = run;
+    __syncthreads();
+    for (uint32_t i = t; i < unit_rows; i += kUnitThreads) {
+        const uint32_t key = plan_key(plan_count(cnt[r0 + i]));
+        const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane(key);
+        const uint64_t same = __ballot(key == k0), all = __ballot(true);
+        uint32_t rank;
+        if (same == all) {
+            const uint32_t first = (uint32_t)__builtin_ctzll(all);
+            uint32_t base = 0;
+            if (lane == first) base = atomicAdd(&bins[k0], (uint32_t)__builtin_popcountll(all));
+            base = (uint32_t)__shfl((int)base, (int)first);
+            rank = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(all >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)all, 0u));
+        } else {
+            rank = atomicAdd(&bins[key], 1u);
         }
-        uint32_t incl = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(incl, off);
-            if (lane >= (uint32_t)off) incl += y;
-        }
-        __syncthreads();
-        uint32_t run = incl - sum;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            b[lane * kPer + j] = run;
-            run += own[j];
-        }
-        __syncthreads();
-        if (active) {
-            const uint32_t x = place[u] & 7u, p0 = place[u] >> 3;
-            for (uint32_t i = lane; i < unit_rows; i += 64) {
-                const uint32_t key = plan_key(count(r0 + i));
-                const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane(key);
-                const uint64_t same = __ballot(key == k0), all = __ballot(true);
-                uint32_t rank;
-                if (same == all) {
-                    const uint32_t first = (uint32_t)__builtin_ctzll(all);
-                    uint32_t base = 0;
-                    if (lane == first) base = atomicAdd(&b[k0], (uint32_t)__builtin_popcountll(all));
-                    base = (uint32_t)__shfl((int)base, (int)first);
-                    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(all >> 32),
-                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)all, 0u));
-                    rank = base + below;
-                } else {
-                    rank = atomicAdd(&b[key], 1u);
-                }
-                order[8u * (p0 + rank) + x] = r0 + i;
-            }
-        }
-        __syncthreads();
+        order[8u * (p0 + rank) + x] = r0 + i;
+    }
+    if (t == 0) {
+        scratch[2 * u] = kEmptySlot;
+        scratch[2 * u + 1] = kEmptySlot;
+        scratch[2 * units + u] = kEmptySlot;
     }
 }
 
@@ -562,11 +556,11 @@ extern "C" int64_t bsa_row_order_len(int64_t BH, int64_t nq) {
         set_error("bsa_row_order_len: more than %d heads", kMaxUnits);
         return -1;
     }
-    if (8 * p.cap >= ((int64_t)1 << 31)) {
+    if (p.len() >= ((int64_t)1 << 31)) {
         set_error("bsa_row_order_len: the plan would exceed 2^31 entries");
         return -1;
     }
-    return 8 * p.cap;
+    return p.len();
 }
 
 extern "C" int bsa_row_order(const int32_t* kv_cnt, int64_t BH, int64_t nq, uint32_t* order, int64_t order_len,
@@ -578,7 +572,11 @@ extern "C" int bsa_row_order(const int32_t* kv_cnt, int64_t BH, int64_t nq, uint
     BSA_REQUIRE(order_len >= need && order_len < ((int64_t)1 << 31), "%s: order_len=%lld must be in [%lld, 2^31)",
                 name, (long long)order_len, (long long)need);
     const Plan p = plan_shape(BH, nq);
-    row_plan_kernel<<<1, kPlanThreads, 0, (hipStream_t)stream>>>(kv_cnt, (uint32_t)p.units, (uint32_t)p.unit_rows,
-                                                                 (uint32_t)p.cap, (uint32_t)order_len, order);
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t* scratch = order + p.plan_len();
+    const uint32_t units = (uint32_t)p.units, rows = (uint32_t)p.unit_rows, cap = (uint32_t)p.cap;
+    plan_weight_kernel<<<units, kUnitThreads, 0, st>>>(kv_cnt, rows, scratch);
+    plan_place_kernel<<<1, kPlanThreads, 0, st>>>(units, rows, cap, (uint32_t)order_len, order);
+    plan_sort_kernel<<<units, kUnitThreads, 0, st>>>(kv_cnt, units, rows, cap, order);
     return check_launch(name);
 }

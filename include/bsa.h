@@ -369,20 +369,21 @@ int bsa_top_p_block_mask(const float* scores, int64_t B, int64_t H, int Nq, int 
  * the total of all weights under 2^28 (none unless that total reaches it);
  * units, heaviest first (ties: lower unit first), go to the least loaded
  * XCD (ties: lower XCD first) among those holding fewer than ceil(U/8) of
- * the U units.  An XCD runs its units
- * in the order they came, each unit's rows in decreasing c (values of 255 or
- * more rank as one; rows of one rank come in no fixed order).  order[8j + x] is the j-th row (b*H + h)*Nq + I of XCD x,
- * and 0xFFFFFFFF an empty slot.
- * kv_cnt: device int32 (BH * Nq); order: device uint32 (order_len).
- * One workgroup; kv_cnt is read once into LDS (more than 49152 rows: read
- * at each step).
+ * the U units.  An XCD runs its units in the order they came, each unit's
+ * rows in decreasing c (values of 255 or more rank as one; rows of one rank
+ * come in no fixed order).  order[8j + x] is the j-th row (b*H + h)*Nq + I
+ * of XCD x, and 0xFFFFFFFF an empty slot.
+ * kv_cnt: device int32 (BH * Nq); order: device uint32 (order_len).  The
+ * last 3U entries of the plan serve the call as scratch and are left empty.
+ * Three launches: the weights and the per-unit sorts one workgroup per unit,
+ * the scheduling one workgroup; kv_cnt is read twice.
  * INVALID_ARG unless order_len >= bsa_row_order_len(BH, Nq) > 0 and
  * order_len < 2^31. */
 int bsa_row_order(const int32_t* kv_cnt, int64_t BH, int64_t Nq, uint32_t* order, int64_t order_len,
                   bsa_stream_t stream);
 
 /* Host: the length of bsa_row_order's plan for BH heads of Nq rows,
- * 8 * ceil(U/8) * (rows per unit) >= BH * Nq, or -1 (and bsa_last_error) unless
+ * 8 * ceil(U/8) * (rows per unit) + 3U >= BH * Nq, or -1 (and bsa_last_error) unless
  * BH, Nq >= 1, BH * Nq < 2^31, the plan has at most 1024 units and fewer
  * than 2^31 entries.  Nothing is launched. */
 int64_t bsa_row_order_len(int64_t BH, int64_t Nq);

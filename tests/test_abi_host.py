@@ -217,9 +217,9 @@ def test_device_calls_reject_bad_arguments(L):
         ("bsa_block_sparse_attention_tiled",
          (FAKE, FAKE, FAKE, FAKE, BF, 1, 2, 20, 32, 48, 128, TILES, 2, None, FAKE, FAKE, 82, ctypes.c_float(0.1),
           None, FAKE, 1 << 31, None), "row_order_len"),
-        ("bsa_row_order", (FAKE, 40, 480, FAKE, 19199, None), "order_len"),
-        ("bsa_row_order", (None, 40, 480, FAKE, 19200, None), "NULL"),
-        ("bsa_row_order", (FAKE, 0, 480, FAKE, 19200, None), "BH"),
+        ("bsa_row_order", (FAKE, 40, 480, FAKE, 19319, None), "order_len"),
+        ("bsa_row_order", (None, 40, 480, FAKE, 19320, None), "NULL"),
+        ("bsa_row_order", (FAKE, 0, 480, FAKE, 19320, None), "BH"),
         ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 0, 2, ctypes.c_float(0.25), 8, None),
          "window"),
         ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, -1, ctypes.c_float(0.25), 8, None),
@@ -269,14 +269,14 @@ def test_device_calls_reject_bad_arguments(L):
 
 
 def test_row_order_len(L):
-    """Plan length = 8 XCDs x ceil(U/8) units of U x rows per unit."""
-    assert bsa.bsa_row_order_len(40, 480) == 8 * 5 * 480             # whole heads: no empty slot
-    assert bsa.bsa_row_order_len(24, 1920) == 8 * 3 * 1920
-    assert bsa.bsa_row_order_len(6, 64) == 8 * 3 * 16               # 24 units: a quarter head each
-    assert bsa.bsa_row_order_len(1, 480) == 8 * 1 * 60              # 8 units of 60 rows
-    assert bsa.bsa_row_order_len(2, 7) == 8 * 1 * 7                 # 7 rows do not split: whole heads
-    assert bsa.bsa_row_order_len(1024, 3) == 8 * 128 * 3
-    assert bsa.bsa_row_order_len(5, 12) == 8 * 3 * 3                # 20 units of 3 rows
+    """Plan length = 8 XCDs x ceil(U/8) units of U x rows per unit, plus 3U scratch words."""
+    assert bsa.bsa_row_order_len(40, 480) == 8 * 5 * 480 + 3 * 40    # whole heads: no empty slot
+    assert bsa.bsa_row_order_len(24, 1920) == 8 * 3 * 1920 + 3 * 24
+    assert bsa.bsa_row_order_len(6, 64) == 8 * 3 * 16 + 3 * 24       # 24 units: a quarter head each
+    assert bsa.bsa_row_order_len(1, 480) == 8 * 1 * 60 + 3 * 8       # 8 units of 60 rows
+    assert bsa.bsa_row_order_len(2, 7) == 8 * 1 * 7 + 3 * 2          # 7 rows do not split: whole heads
+    assert bsa.bsa_row_order_len(1024, 3) == 8 * 128 * 3 + 3 * 1024
+    assert bsa.bsa_row_order_len(5, 12) == 8 * 3 * 3 + 3 * 20        # 20 units of 3 rows
     for bh, nq in [(40, 480), (6, 64), (1, 1), (3, 5), (41, 480)]:
         assert bsa.bsa_row_order_len(bh, nq) >= bh * nq
     for bh, nq in [(0, 4), (4, 0), (1025, 1), (1 << 16, 1 << 15)]:

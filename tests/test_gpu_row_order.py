@@ -41,9 +41,10 @@ def plan_rule(cnt):
 
 def check_plan(order, cnt):
     units, ur, cap = plan_rule(cnt)
+    n_units = sum(len(us) for us in units)
     o = order.cpu().numpy().astype(np.int64)
-    assert o.size >= 8 * cap == bsa.bsa_row_order_len(*cnt.shape)
-    assert np.all(o[8 * cap:] == EMPTY)
+    assert o.size >= 8 * cap + 3 * n_units == bsa.bsa_row_order_len(*cnt.shape)
+    assert np.all(o[8 * cap:] == EMPTY)          # the scratch words and anything past the plan read as empty
     key = np.clip(cnt.reshape(-1), 0, BINS - 1)
     for x in range(8):
         lane = o[:8 * cap][x::8]
