@@ -831,19 +831,40 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                                   (q0 + BLK - 1 - j0 <= P.half && j0 + BLK - 1 - q0 <= P.half && j0 + BLK <= (int)P.S);
                 if (!full) {
                     const float neg_inf = -__builtin_inff();
+                    if (j0 >= P.sink && j0 + BLK <= (int)P.S) {
+                        // a tile past the sinks and inside the sequence: only the band
+                        // |row - key| <= half.  With base = row - (first key of this
+                        // lane's share), key offset k = 8(v / 4) + v % 4 is visible when
+                        // base - half <= k <= base + half: two compares against a constant
 #pragma unroll
-                    for (int c = 0; c < 2; ++c)
+                        for (int c = 0; c < 2; ++c)
 #pragma unroll
-                        for (int r = 0; r < NR; ++r) {
-                            const int my_row = q0 + 32 * r + col;
+                            for (int r = 0; r < NR; ++r) {
+                                const int base = q0 + 32 * r + col - (j0 + 32 * c + 4 * half_id);
+                                const int lo = base - P.half, hi = base + P.half;
 #pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                const int j = j0 + 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4);
-                                const int d = my_row - j;
-                                const bool vis = (j < (int)P.S) & (((d <= P.half) & (-d <= P.half)) | (j < P.sink));
-                                sacc[c][r][v] = vis ? sacc[c][r][v] : neg_inf;
+                                for (int v = 0; v < 16; ++v) {
+                                    const int kk = 8 * (v / 4) + (v % 4);
+                                    const bool vis = (kk >= lo) & (kk <= hi);
+                                    sacc[c][r][v] = vis ? sacc[c][r][v] : neg_inf;
+                                }
                             }
-                        }
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+#pragma unroll
+                            for (int r = 0; r < NR; ++r) {
+                                const int my_row = q0 + 32 * r + col;
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) {
+                                    const int j = j0 + 32 * c + 4 * half_id + 8 * (v / 4) + (v % 4);
+                                    const int d = my_row - j;
+                                    const bool vis =
+                                        (j < (int)P.S) & (((d <= P.half) & (-d <= P.half)) | (j < P.sink));
+                                    sacc[c][r][v] = vis ? sacc[c][r][v] : neg_inf;
+                                }
+                            }
+                    }
                 }
             }
             if (MODE == kLabels) {
