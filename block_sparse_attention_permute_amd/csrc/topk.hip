@@ -64,6 +64,29 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     return v;
 }
 
+// Wave-wide fp32 sum for the top-p search, on VALU lane exchanges only (the
+// search takes 32 dependent sums per row, and shuffles through the LDS
+// crossbar made it latency-bound): within quads by DPP, then across 8 and 16
+// lanes by DPP row mirrors (once the smaller groups are uniform, pairing lane
+// i with its mirror adds the other half), then across rows by the 16- and
+// 32-lane swaps.  Every lane adds the same two values in the same order, so
+// the result is identical in all lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum_mass(float v) {
+    v = dpp_add<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x141>(v);  // row_half_mirror: lane i with 7 - i
+    v = dpp_add<0x140>(v);  // row_mirror: lane i with 15 - i
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 __device__ __forceinline__ float wave_max_f(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -118,7 +141,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
             w[i] = (!valid[i] || key[i] == 0u) ? 0.f : (x == m ? 1.f : __builtin_amdgcn_exp2f((x - m) * P.scale_log2));
             z += w[i];
         }
-        const float ztot = wave_sum_f(z);
+        const float ztot = wave_sum_mass(z);
         target = P.p * ztot;
         no_mass = ztot == 0.f;  // every score NaN: the first-ranked entry is kept
     }
@@ -130,7 +153,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
             float c = 0.f;
 #pragma unroll
             for (int i = 0; i < VPL; ++i) c += key[i] >= cand ? w[i] : 0.f;  // w = 0 where not valid
-            if (wave_sum_f(c) >= target) T = cand;
+            if (wave_sum_mass(c) >= target) T = cand;
         } else {
             // wave-wide count from ballots (scalar popcounts, no cross-lane
             // shuffles); entries that are not valid hold key 0 < cand
@@ -149,7 +172,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
             gt += key[i] > T ? w[i] : 0.f;
             if (valid[i] && key[i] == T) { wt = w[i]; ++nt; }
         }
-        gt = wave_sum_f(gt);
+        gt = wave_sum_mass(gt);
         wt = wave_max_f(wt);
         nt = wave_sum(nt);
         const float t = wt > 0.f ? ceilf((target - gt) / wt) : 1.f;

@@ -83,6 +83,30 @@ def test_plan_follows_its_rule(B, H, nq):
     check_plan(bsa.bsa_row_order(cg, out=longer), cnt.reshape(B * H, nq))
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ["zeros", "one_heavy_head", "equal"])
+def test_plan_edge_weights(case):
+    """All counts 0 (equal weights: units in index order round the XCDs), one head holding nearly all the work
+    (it gets an XCD of its own share while the others fill the rest), and equal top-k counts."""
+    torch = torch_gpu()
+    B, H, nq = 1, 24, 96
+    if case == "zeros":
+        cnt = np.zeros((B, H, nq), np.int32)
+    elif case == "one_heavy_head":
+        cnt = np.ones((B, H, nq), np.int32)
+        cnt[0, 7] = 4000
+    else:
+        cnt = np.full((B, H, nq), 17, np.int32)
+    order = bsa.bsa_row_order(torch.from_numpy(cnt).cuda())
+    check_plan(order, cnt.reshape(B * H, nq))
+    units, _, _ = plan_rule(cnt.reshape(B * H, nq))
+    if case != "one_heavy_head":
+        assert [len(us) for us in units] == [3] * 8
+    else:
+        heavy = next(x for x in range(8) if 7 in units[x])
+        assert units[heavy][0] == 7
+
+
 def _varying_lists(B, H, nb, rng):
     """Full-width lists whose lengths run from 0 to nb (density per row cubed), the diagonal kept."""
     torch = torch_gpu()
