@@ -120,6 +120,7 @@ struct Cfg {
     static constexpr int CH = BLK * NCH / NT;     // 16-byte chunks per thread per tensor
     static constexpr int MERGE = (NW - NWR) * 64 * (D / 2 + 2) * 4;
     static constexpr int SMEM = (2 * STAGE > MERGE) ? 2 * STAGE : MERGE;
+    static constexpr int SMEM1 = (STAGE > MERGE) ? STAGE : MERGE;  // one key tile: no second stage
     static_assert(CH >= 1 && (BLK * NCH) % NT == 0, "uneven staging");
 };
 
@@ -192,7 +193,9 @@ template <int D, int BLK, int MODE, bool POS>
 __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)) void attn_mfma_kernel(
     const AttnParams P, const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt) {
     using C = Cfg<D, BLK>;
-    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    // groups mode visits one key tile and needs one LDS stage; at D = 128 that
+    // makes room for three workgroups per CU instead of two
+    __shared__ __attribute__((aligned(16))) char smem[MODE == kGroups ? C::SMEM1 : C::SMEM];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave % C::NWR, wk = wave / C::NWR;
@@ -411,7 +414,8 @@ __global__ __launch_bounds__((Cfg<D, BLK>::NT), (Cfg<D, BLK>::NT >= 256 ? 2 : 1)
         __syncthreads();
     };
     int it = 0;
-    for (; it + 1 < n_iter; it += 2) {
+    // (groups mode: one tile, stage 0 only)
+    for (; MODE != kGroups && it + 1 < n_iter; it += 2) {
         body(ic<0>{}, it);
         body(ic<1>{}, it + 1);
     }
