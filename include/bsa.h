@@ -521,7 +521,8 @@ int bsa_block_sparse_attention_labels(const void* q, const void* k, const void* 
  * frame].  Equals bsa_block_sparse_attention_labels on the tiling (T, 1, 1)
  * with BSA_LABEL_TEMPORAL labels and their block lists, followed by the
  * inverse permutation, without forming a permuted copy: each 64-row tile
- * holds the T frames of 64 / T positions, gathered from T-major memory.
+ * holds the T frames of floor(64 / T) positions, gathered from T-major
+ * memory (its remaining rows are padding and are not written).
  * Scale as bsa_block_sparse_attention; out has q's shape and dtype.
  * UNSUPPORTED unless bf16 with D in {64, 128} and T <= 64 (the label call
  * covers the rest); INVALID_ARG on bad sizes. */
