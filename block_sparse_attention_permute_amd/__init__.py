@@ -12,7 +12,7 @@ from .bsa import (  # noqa: F401
     bsa_block_sparse_attention, bsa_block_sparse_attention_labels, bsa_block_sparse_attention_tiled,
     bsa_block_sparse_attention_tiled_padded, bsa_budget,
     bsa_invert_permutation, bsa_invert_permute, bsa_invert_permute_padded, bsa_label_block_list,
-    bsa_minmax_block_scores, bsa_minmax_block_scores_tiled, bsa_minmax_block_scores_tiled_padded, bsa_padded_length, bsa_row_order, bsa_row_order_len, bsa_select_tiling,
+    bsa_minmax_block_scores, bsa_minmax_block_scores_tiled, bsa_minmax_block_scores_tiled_padded, bsa_padded_length, bsa_row_order, bsa_row_order_len, bsa_row_order_by_median, bsa_select_tiling,
     bsa_select_tiling_noalloc, bsa_sliding_tile_block_list, bsa_tile_permutation, bsa_tile_permutation_padded, bsa_tile_permute,
     bsa_tile_permute_padded, bsa_top_p_block_mask, bsa_topk_block_mask, bsa_topk_block_mask_tiled,
     bsa_temporal_only_attention, bsa_validate_block_list, bsa_validate_indices, bsa_version, bsa_video_labels,

@@ -37,7 +37,7 @@ EXPORTED = (
     "bsa_minmax_block_scores_tiled", "bsa_block_sparse_attention_tiled",
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices", "bsa_video_labels",
     "bsa_select_tiling_noalloc", "bsa_temporal_only_attention", "bsa_block_sparse_attention_tiled_padded",
-    "bsa_tiled_attention_supported", "bsa_row_order", "bsa_row_order_len", "bsa_minmax_block_scores_tiled_padded",
+    "bsa_tiled_attention_supported", "bsa_row_order", "bsa_row_order_len", "bsa_row_order_by_median", "bsa_minmax_block_scores_tiled_padded",
 )
 
 
@@ -91,6 +91,7 @@ _SIGS = {
     "bsa_minmax_block_scores_tiled_padded": (_I, [_P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _I, _P, _P, _P, _P,
                                                   _P]),
     "bsa_row_order_len": (_I64, [_I64, _I64]),
+    "bsa_row_order_by_median": (_I, [_P, _P, _I64, _I64, _I, _I64, _P, _I64, _P]),
 }
 
 # libbsa's ABI major version these signatures are written for
@@ -665,6 +666,26 @@ def bsa_row_order(kv_cnt, out=None):
     return o
 
 
+def bsa_row_order_by_median(kv_idx, kv_cnt, nk: int = None, out=None):
+    """Launch order for top-k block lists kv_idx (B, H, Nq, max_kept) / kv_cnt (B, H, Nq) -> int32 (B*H*Nq,): the
+    plain split of the rows over the 8 XCDs, each head's rows sorted by the middle entry of their kept list
+    (nk: key blocks per row, default Nq)."""
+    torch = _torch()
+    if kv_cnt.dtype != torch.int32 or kv_cnt.dim() != 3:
+        raise ValueError("kv_cnt must be int32 (B, H, Nq)")
+    if kv_idx.dtype != torch.int32 or kv_idx.dim() != 4 or tuple(kv_idx.shape[:3]) != tuple(kv_cnt.shape):
+        raise ValueError("kv_idx must be int32 (B, H, Nq, max_kept) over kv_cnt's rows")
+    B, H, nq = (int(s) for s in kv_cnt.shape)
+    n = B * H * nq
+    o = torch.empty(n, dtype=torch.int32, device=kv_cnt.device) if out is None else out
+    if o.dtype not in (torch.int32, torch.uint32) or o.dim() != 1 or o.numel() < n:
+        raise ValueError(f"out must be a 1-D int32 / uint32 tensor of at least {n} entries")
+    _check(lib().bsa_row_order_by_median(_dev(kv_idx, "kv_idx"), _dev(kv_cnt, "kv_cnt"), B * H, nq,
+                                         int(kv_idx.shape[3]), nq if nk is None else int(nk), _dev(o, "out"),
+                                         int(o.numel()), _stream(kv_cnt)))
+    return o
+
+
 def tiled_attention_supported(dtype, D, tiles, grid, pad: bool = False) -> bool:
     """Whether bsa_block_sparse_attention_tiled (or, with pad, its _padded form) has a kernel for these tilings
     of the grid (asked of libbsa, nothing launched)."""
@@ -868,9 +889,16 @@ class AdaptiveBlockSparse:
                         torch.empty((B, H, self.nb), dtype=torch.int32, **f), None)
         # top-p lists differ in length from row to row, and padded candidates give heads different block
         # counts and budgets: a launch plan balances the XCDs by work and starts long rows first (the fused
-        # attention takes it)
-        self.ws_order = (torch.empty(bsa_row_order_len(B * H, self.nb), dtype=torch.int32, **f)
-                         if top_p is not None or (self.pad and self.fused) else None)
+        # attention takes it).  Top-k lists have (nearly) equal lengths: their launch order keeps the plain
+        # XCD ranges and sorts each head's rows by where their kept key blocks lie, so that the query blocks an
+        # XCD runs side by side share more key blocks through its L2
+        self.order_by_median = top_p is None and not self.pad and (B * H * self.nb) % 8 == 0
+        if top_p is not None or (self.pad and self.fused):
+            self.ws_order = torch.empty(bsa_row_order_len(B * H, self.nb), dtype=torch.int32, **f)
+        elif self.order_by_median:
+            self.ws_order = torch.empty(B * H * self.nb, dtype=torch.int32, **f)
+        else:
+            self.ws_order = None
         # each key block's largest row norm, written by the scores pass: the attention kernel skips the
         # running-max update of the key blocks it proves cannot pass it
         self.ws_knorm = (torch.empty((B, H, self.nb), dtype=torch.float32, **f) if self.fused or not self.pad
@@ -920,6 +948,8 @@ class AdaptiveBlockSparse:
             if self.top_p is None:
                 kv_idx, kv_cnt, _ = bsa_topk_block_mask(scores, self.k, self.sink_blocks, self.keep_diag,
                                                         max_kept=self.max_kept, return_mask=True, out=self.ws_topk)
+                if self.order_by_median:
+                    bsa_row_order_by_median(kv_idx, kv_cnt, out=self.ws_order)
             else:
                 kv_idx, kv_cnt, _ = bsa_top_p_block_mask(scores, self.top_p, self.p_scale, self.sink_blocks,
                                                          self.keep_diag, return_mask=True, out=self.ws_topk)

@@ -446,6 +446,68 @@ __global__ __launch_bounds__(kUnitThreads) void plan_sort_kernel(const int32_t* 
     }
 }
 
+// Launch order for block lists of (nearly) equal lengths: the rows of a head
+// sorted by the middle entry of their kept lists, so that the query blocks an
+// XCD runs side by side keep key blocks from the same part of the sequence and
+// share more of them through the XCD's L2.  One workgroup per head: a counting
+// sort over the Nk key blocks (bins in LDS, rows of one bin in no fixed order),
+// then row rank -> slot h*Nq + rank of the plain XCD ranges (XCD x holds slots
+// [x*per_xcd, (x+1)*per_xcd), its j-th at order[8j + x]).
+constexpr uint32_t kMaxMedianBins = 4096;
+
+__global__ __launch_bounds__(kUnitThreads) void median_order_kernel(const int32_t* __restrict__ kv_idx,
+                                                                    const int32_t* __restrict__ kv_cnt, uint32_t nq,
+                                                                    uint32_t max_kept, uint32_t nk, uint32_t per_xcd,
+                                                                    uint32_t* __restrict__ order) {
+    __shared__ uint32_t bins[kMaxMedianBins];
+    __shared__ uint32_t wave_total[kUnitWaves];
+    const uint32_t h = blockIdx.x, t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+    const size_t r0 = (size_t)h * nq;
+    // the key of row i: its middle kept block (lists ascend), 0 for an empty list,
+    // out-of-range entries clamped (bsa_validate_block_list reports them)
+    auto key_of = [&](uint32_t i) -> uint32_t {
+        const int c = min(max(kv_cnt[r0 + i], 0), (int)max_kept);
+        if (c == 0) return 0u;
+        const int32_t j = kv_idx[(r0 + i) * max_kept + (uint32_t)c / 2u];
+        return j < 0 ? 0u : ((uint32_t)j < nk ? (uint32_t)j : nk - 1u);
+    };
+    for (uint32_t b = t; b < nk; b += kUnitThreads) bins[b] = 0;
+    __syncthreads();
+    for (uint32_t i = t; i < nq; i += kUnitThreads) atomicAdd(&bins[key_of(i)], 1u);
+    __syncthreads();
+    // exclusive scan: thread t owns bins [t*per, (t+1)*per)
+    const uint32_t per = (nk + kUnitThreads - 1) / kUnitThreads;
+    uint32_t own = 0;
+    for (uint32_t j = 0; j < per; ++j) {
+        const uint32_t b = t * per + j;
+        if (b < nk) own += bins[b];
+    }
+    uint32_t incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= (uint32_t)off) incl += y;
+    }
+    if (lane == 63u) wave_total[wave] = incl;
+    __syncthreads();
+    uint32_t run = incl - own;
+    for (uint32_t w = 0; w < wave; ++w) run += wave_total[w];
+    for (uint32_t j = 0; j < per; ++j) {
+        const uint32_t b = t * per + j;
+        if (b < nk) {
+            const uint32_t c = bins[b];
+            bins[b] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (uint32_t i = t; i < nq; i += kUnitThreads) {
+        const uint32_t slot = h * nq + atomicAdd(&bins[key_of(i)], 1u);
+        const uint32_t x = slot / per_xcd, j = slot - x * per_xcd;
+        order[8u * j + x] = (uint32_t)(r0 + i);
+    }
+}
+
 template <bool TOPP>
 int launch_select(TopkParams& P, hipStream_t st, const char* name) {
     const uint64_t blocks = (P.rows + 3) / 4;
@@ -601,5 +663,25 @@ extern "C" int bsa_row_order(const int32_t* kv_cnt, int64_t BH, int64_t nq, uint
     plan_weight_kernel<<<units, kUnitThreads, 0, st>>>(kv_cnt, rows, scratch);
     plan_place_kernel<<<1, kPlanThreads, 0, st>>>(units, rows, cap, (uint32_t)order_len, order);
     plan_sort_kernel<<<units, kUnitThreads, 0, st>>>(kv_cnt, units, rows, cap, order);
+    return check_launch(name);
+}
+
+extern "C" int bsa_row_order_by_median(const int32_t* kv_idx, const int32_t* kv_cnt, int64_t BH, int64_t nq,
+                                       int max_kept, int64_t nk, uint32_t* order, int64_t order_len,
+                                       bsa_stream_t stream) {
+    clear_error();
+    const char* name = "bsa_row_order_by_median";
+    BSA_REQUIRE(kv_idx && kv_cnt && order, "%s: NULL argument", name);
+    BSA_REQUIRE(BH >= 1 && nq >= 1 && BH * nq < ((int64_t)1 << 31), "%s: BH=%lld and Nq=%lld must be >= 1 with BH*Nq < 2^31",
+                name, (long long)BH, (long long)nq);
+    BSA_REQUIRE((BH * nq) % 8 == 0, "%s: BH*Nq=%lld must be a multiple of 8 (one equal range of rows per XCD)", name,
+                (long long)(BH * nq));
+    BSA_REQUIRE(max_kept >= 1, "%s: max_kept=%d must be >= 1", name, max_kept);
+    BSA_REQUIRE(nk >= 1 && nk <= (int64_t)kMaxMedianBins, "%s: Nk=%lld must be in [1, %u]", name, (long long)nk,
+                kMaxMedianBins);
+    BSA_REQUIRE(order_len >= BH * nq && order_len < ((int64_t)1 << 31), "%s: order_len=%lld must be in [%lld, 2^31)",
+                name, (long long)order_len, (long long)(BH * nq));
+    median_order_kernel<<<(unsigned)BH, kUnitThreads, 0, (hipStream_t)stream>>>(
+        kv_idx, kv_cnt, (uint32_t)nq, (uint32_t)max_kept, (uint32_t)nk, (uint32_t)(BH * nq / 8), order);
     return check_launch(name);
 }

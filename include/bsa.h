@@ -388,6 +388,27 @@ int bsa_row_order(const int32_t* kv_cnt, int64_t BH, int64_t Nq, uint32_t* order
  * than 2^31 entries.  Nothing is launched. */
 int64_t bsa_row_order_len(int64_t BH, int64_t Nq);
 
+/* Launch order for block lists of (nearly) equal lengths, as top-k lists
+ * are: like bsa_row_order a scheduling aid that is no step of the method and
+ * changes no result (the attention calls take it as row_order, with
+ * row_order_len = BH * Nq).  The rows keep the plain split over the 8 XCDs
+ * (XCD x runs rows x*BH*Nq/8 .. (x+1)*BH*Nq/8 - 1 of the order below, so a
+ * head stays on one XCD when 8 divides BH), but each head's rows come sorted
+ * by the middle entry of their kept list, kv_idx[row][kv_cnt[row] / 2] (0 for
+ * an empty row; rows with one key come in no fixed order).  Query blocks that
+ * an XCD runs side by side then keep key blocks from the same part of the
+ * sequence and share more of them through the XCD's L2.  order[8j + x] is the
+ * j-th row (b*H + h)*Nq + I of XCD x; every slot is filled.
+ * kv_idx, kv_cnt: device int32 as bsa_topk_block_mask writes them (kept
+ * indices ascending, kv_cnt clamped to [0, max_kept], entries outside
+ * [0, Nk) clamped); order: device uint32 (order_len).  One launch, one
+ * workgroup per head.  INVALID_ARG unless BH, Nq >= 1, BH * Nq < 2^31 is a
+ * multiple of 8, max_kept >= 1, 1 <= Nk <= 4096 and
+ * BH * Nq <= order_len < 2^31. */
+int bsa_row_order_by_median(const int32_t* kv_idx, const int32_t* kv_cnt, int64_t BH, int64_t Nq,
+                            int max_kept, int64_t Nk, uint32_t* order, int64_t order_len,
+                            bsa_stream_t stream);
+
 /* bsa_topk_block_mask with a per-head budget and block count: head (b, h)
  * uses k = k_table[c] and nk = nk_table[c], c = head_choice[b*H + h]
  * (device int32, trusted to lie in [0, n_table)).  Only key blocks J < nk
@@ -428,8 +449,8 @@ int bsa_topk_block_mask_tiled(const float* scores, int64_t B, int64_t H, int Nq,
  * weight exceeds 2^32) skips the running-max update, so its
  * softmax weights are taken relative to an older max (an exact shift of the
  * softmax; the weights are rounded to bf16 at a different scale).
- * row_order_or_null, row_order_len: a launch order (as bsa_row_order writes
- * it) or NULL, 0.  Given one, the bf16 kernels run row_order_len workgroups,
+ * row_order_or_null, row_order_len: a launch order (as bsa_row_order or
+ * bsa_row_order_by_median writes it) or NULL, 0.  Given one, the bf16 kernels run row_order_len workgroups,
  * workgroup w taking row row_order[w] = (b*H + h)*(S/block) + I; entries
  * past the last row are empty slots, each row must appear exactly once
  * (a row left out is not written).  NULL keeps the library's own order.  The

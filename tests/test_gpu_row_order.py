@@ -1,9 +1,11 @@
-"""Launch plans for block lists of varying length (bsa_row_order).
+"""Launch plans: bsa_row_order for block lists of varying length, bsa_row_order_by_median for top-k lists.
 
 A plan only decides which workgroup runs which query block, so attention under a plan must equal attention
-without one bit for bit.  The plan itself is checked against the scheduling rule bsa.h states, written out
-here on the host: unit placement exactly, and inside each unit the rows as a set with non-increasing counts
-(rows of one count may come in any order).
+without one bit for bit.  Each plan is checked against the rule bsa.h states, written out here on the host:
+for bsa_row_order unit placement exactly, and inside each unit the rows as a set with non-increasing counts
+(rows of one count may come in any order); for bsa_row_order_by_median the plain XCD ranges over a sequence in
+which each head's rows fill their own slots with non-decreasing middle kept blocks (rows of one key may come in
+any order).
 """
 import numpy as np
 import pytest
@@ -237,4 +239,114 @@ def test_top_p_pipeline_plans_its_launch():
     check_plan(pipe.ws_order, kv_cnt.cpu().numpy().reshape(H, -1))
     ref = bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, grid, tiles, kv_idx, kv_cnt, head_choice=pipe.choice,
                                                key_norms=pipe.ws_knorm)
+    assert torch.equal(out, ref)
+
+
+def check_median_order(order, kv_idx, kv_cnt, nk):
+    """order follows bsa_row_order_by_median's rule for the lists kv_idx (B, H, Nq, max_kept) / kv_cnt (B, H, Nq)."""
+    idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    B, H, nq = cnt.shape
+    BH, max_kept = B * H, idx.shape[-1]
+    n = BH * nq
+    per = n // 8
+    o = order.cpu().numpy().astype(np.int64)
+    assert o.size >= n
+    seq = np.empty(n, dtype=np.int64)            # slot x*per + j holds order[8j + x]
+    for x in range(8):
+        seq[x * per:(x + 1) * per] = o[:n][x::8]
+    assert np.array_equal(np.sort(seq), np.arange(n))
+    idx2, cnt2 = idx.reshape(BH, nq, max_kept), np.clip(cnt.reshape(BH, nq), 0, max_kept)
+
+    def key(r):
+        h, i = divmod(int(r), nq)
+        c = cnt2[h, i]
+        return 0 if c == 0 else int(min(max(idx2[h, i, c // 2], 0), nk - 1))
+
+    for h in range(BH):
+        seg = seq[h * nq:(h + 1) * nq]
+        assert np.array_equal(np.sort(seg), np.arange(h * nq, (h + 1) * nq)), h
+        keys = [key(r) for r in seg]
+        assert all(a <= b for a, b in zip(keys, keys[1:])), h
+
+
+def _sorted_lists(B, H, nq, nk, max_kept, rng, empty_share=0.1):
+    """Ascending kept lists of random length (some empty), padded with -1, as bsa_topk_block_mask writes them."""
+    cnt = rng.integers(1, max_kept + 1, (B, H, nq))
+    cnt[rng.random((B, H, nq)) < empty_share] = 0
+    idx = np.full((B, H, nq, max_kept), -1, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nq):
+                c = int(cnt[b, h, i])
+                idx[b, h, i, :c] = np.sort(rng.choice(nk, c, replace=False))
+    return idx, cnt.astype(np.int32)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,H,nq,nk,max_kept", [(1, 40, 480, 480, 83), (1, 3, 8, 8, 4), (2, 3, 12, 12, 5),
+                                                (1, 1, 8, 4096, 300), (1, 24, 64, 64, 7)])
+def test_median_order_follows_its_rule(B, H, nq, nk, max_kept):
+    """Random ascending lists, empty rows among them; heads that straddle XCD ranges (3 heads of 8 rows over
+    8 ranges of 3), Nk at its 4096 limit."""
+    torch = torch_gpu()
+    rng = np.random.default_rng(7100 + B * H * nq + nk)
+    idx, cnt = _sorted_lists(B, H, nq, nk, max_kept, rng)
+    kv_idx, kv_cnt = (torch.from_numpy(a).to("cuda") for a in (idx, cnt))
+    order = bsa.bsa_row_order_by_median(kv_idx, kv_cnt, nk=nk)
+    check_median_order(order, kv_idx, kv_cnt, nk)
+
+
+@pytest.mark.gpu
+def test_median_order_clamps_bad_entries():
+    """Middle entries outside [0, Nk) and counts outside [0, max_kept] are clamped, not read past."""
+    torch = torch_gpu()
+    rng = np.random.default_rng(7200)
+    B, H, nq, nk, max_kept = 1, 2, 16, 16, 5
+    idx, cnt = _sorted_lists(B, H, nq, nk, max_kept, rng, empty_share=0.0)
+    cnt[0, 0, :4] = [7, -3, 99, 5]                 # clamped to max_kept, 0, max_kept, 5
+    idx[0, 1, :4, 2] = [-5, 16, 1000, 3]           # middle entries of 5-long lists: clamped to 0 or Nk - 1
+    cnt[0, 1, :4] = 5
+    kv_idx, kv_cnt = (torch.from_numpy(a).to("cuda") for a in (idx, cnt))
+    order = bsa.bsa_row_order_by_median(kv_idx, kv_cnt, nk=nk)
+    check_median_order(order, kv_idx, kv_cnt, nk)
+
+
+@pytest.mark.gpu
+def test_attention_under_a_median_order():
+    """Block-sparse attention on permuted copies under the order equals it without one, bit for bit."""
+    torch = torch_gpu()
+    rng = np.random.default_rng(7300)
+    B, H, S, D, block = 1, 4, 1024, 128, 64
+    nb = S // block
+    idx, cnt = _sorted_lists(B, H, nb, nb, 6, rng)
+    kv_idx, kv_cnt = (torch.from_numpy(a).to("cuda") for a in (idx, cnt))
+    q, k, v = (gpu(synth.normal_bits((B, H, S, D), seed=7310 + i)) for i in range(3))
+    order = bsa.bsa_row_order_by_median(kv_idx, kv_cnt)
+    got = bsa.bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block, row_order=order)
+    ref = bsa.bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block)
+    assert torch.equal(got, ref)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("fused", [True, False])
+def test_top_k_pipeline_orders_its_launch(fused):
+    """The top-k pipeline orders its attention launch by the lists' middle blocks: the order follows its rule
+    for the pipeline's own lists, and the output equals the unordered attention on the same lists bit for bit
+    (fused: gather on load; unfused: permuted copies, compared after the inverse permutation)."""
+    torch = torch_gpu()
+    grid, tiles, H, D = (4, 32, 32), [(1, 8, 8), (4, 4, 4)], 6, 128
+    q, k, v = (synth.normal_bits((1, H, 4096, D), seed=7400 + i) for i in range(3))
+    qg, kg, vg = gpu(q), gpu(k), gpu(v)
+    pipe = bsa.AdaptiveBlockSparse(1, H, grid, D, tiles, 0.25, qg.dtype, qg.device, fused=fused)
+    out = pipe(qg, kg, vg)
+    kv_idx, kv_cnt = pipe.kv
+    assert pipe.ws_order is not None and pipe.order_by_median
+    check_median_order(pipe.ws_order, kv_idx, kv_cnt, pipe.nb)
+    if fused:
+        ref = bsa.bsa_block_sparse_attention_tiled(qg, kg, vg, grid, tiles, kv_idx, kv_cnt,
+                                                   head_choice=pipe.choice, key_norms=pipe.ws_knorm)
+    else:
+        op = bsa.bsa_block_sparse_attention(pipe.qp, pipe.kp, pipe.vp, kv_idx, kv_cnt, pipe.block,
+                                            key_norms=pipe.ws_knorm)
+        ref = bsa.bsa_invert_permute(op, grid, tiles, head_choice=pipe.choice)
     assert torch.equal(out, ref)
