@@ -38,6 +38,7 @@ EXPORTED = (
     "bsa_windowed_attention", "bsa_validate_block_list", "bsa_validate_indices", "bsa_video_labels",
     "bsa_select_tiling_noalloc", "bsa_temporal_only_attention", "bsa_block_sparse_attention_tiled_padded",
     "bsa_tiled_attention_supported", "bsa_row_order", "bsa_row_order_len", "bsa_row_order_by_median", "bsa_minmax_block_scores_tiled_padded",
+    "bsa_row_order_by_median_ex",
 )
 
 
@@ -92,6 +93,7 @@ _SIGS = {
                                                   _P]),
     "bsa_row_order_len": (_I64, [_I64, _I64]),
     "bsa_row_order_by_median": (_I, [_P, _P, _I64, _I64, _I, _I64, _P, _I64, _P]),
+    "bsa_row_order_by_median_ex": (_I, [_P, _P, _I64, _I64, _I, _I64, _I64, _P, _I64, _P]),
 }
 
 # libbsa's ABI major version these signatures are written for
@@ -666,10 +668,11 @@ def bsa_row_order(kv_cnt, out=None):
     return o
 
 
-def bsa_row_order_by_median(kv_idx, kv_cnt, nk: int = None, out=None):
+def bsa_row_order_by_median(kv_idx, kv_cnt, nk: int = None, out=None, head_kv_bytes: int = 0):
     """Launch order for top-k block lists kv_idx (B, H, Nq, max_kept) / kv_cnt (B, H, Nq) -> int32 (B*H*Nq,): the
     plain split of the rows over the 8 XCDs, each head's rows sorted by the middle entry of their kept list
-    (nk: key blocks per row, default Nq)."""
+    (nk: key blocks per row, default Nq).  head_kv_bytes: bytes of one head's K and V; libbsa splits heads
+    above 32 MiB over two XCDs (bsa_row_order_by_median_ex)."""
     torch = _torch()
     if kv_cnt.dtype != torch.int32 or kv_cnt.dim() != 3:
         raise ValueError("kv_cnt must be int32 (B, H, Nq)")
@@ -680,9 +683,9 @@ def bsa_row_order_by_median(kv_idx, kv_cnt, nk: int = None, out=None):
     o = torch.empty(n, dtype=torch.int32, device=kv_cnt.device) if out is None else out
     if o.dtype not in (torch.int32, torch.uint32) or o.dim() != 1 or o.numel() < n:
         raise ValueError(f"out must be a 1-D int32 / uint32 tensor of at least {n} entries")
-    _check(lib().bsa_row_order_by_median(_dev(kv_idx, "kv_idx"), _dev(kv_cnt, "kv_cnt"), B * H, nq,
-                                         int(kv_idx.shape[3]), nq if nk is None else int(nk), _dev(o, "out"),
-                                         int(o.numel()), _stream(kv_cnt)))
+    _check(lib().bsa_row_order_by_median_ex(_dev(kv_idx, "kv_idx"), _dev(kv_cnt, "kv_cnt"), B * H, nq,
+                                            int(kv_idx.shape[3]), nq if nk is None else int(nk), int(head_kv_bytes),
+                                            _dev(o, "out"), int(o.numel()), _stream(kv_cnt)))
     return o
 
 
@@ -949,7 +952,8 @@ class AdaptiveBlockSparse:
                 kv_idx, kv_cnt, _ = bsa_topk_block_mask(scores, self.k, self.sink_blocks, self.keep_diag,
                                                         max_kept=self.max_kept, return_mask=True, out=self.ws_topk)
                 if self.order_by_median:
-                    bsa_row_order_by_median(kv_idx, kv_cnt, out=self.ws_order)
+                    bsa_row_order_by_median(kv_idx, kv_cnt, out=self.ws_order,
+                                            head_kv_bytes=2 * k.shape[2] * k.shape[3] * k.element_size())
             else:
                 kv_idx, kv_cnt, _ = bsa_top_p_block_mask(scores, self.top_p, self.p_scale, self.sink_blocks,
                                                          self.keep_diag, return_mask=True, out=self.ws_topk)

@@ -38,7 +38,7 @@ using namespace bsa;
 
 extern "C" const char* bsa_last_error(void) { return g_err; }
 
-extern "C" int bsa_version(void) { return (2 << 16) | 1; }
+extern "C" int bsa_version(void) { return (2 << 16) | 2; }
 
 // Tile-contiguous order.  Permuted position p is (tile index) * vol + (offset
 // inside the tile); both are counted T-major, so walking tiles in T-major

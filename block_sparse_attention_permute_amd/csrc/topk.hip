@@ -452,13 +452,18 @@ __global__ __launch_bounds__(kUnitThreads) void plan_sort_kernel(const int32_t* 
 // share more of them through the XCD's L2.  One workgroup per head: a counting
 // sort over the Nk key blocks (bins in LDS, rows of one bin in no fixed order),
 // then row rank -> slot h*Nq + rank of the plain XCD ranges (XCD x holds slots
-// [x*per_xcd, (x+1)*per_xcd), its j-th at order[8j + x]).
+// [x*per_xcd, (x+1)*per_xcd), its j-th at order[8j + x]).  With R > 1 XCDs per
+// head (R divides Nq, 8/R divides BH) the XCDs form 8/R groups of R, group g
+// runs heads g, g + 8/R, ... in turn, and XCD g*R + i takes the i-th of R
+// contiguous parts of each head's sorted rows: R times fewer heads are in
+// flight at once, while the rows an XCD runs side by side stay as close in
+// the sorted order as with whole heads.
 constexpr uint32_t kMaxMedianBins = 4096;
 
 __global__ __launch_bounds__(kUnitThreads) void median_order_kernel(const int32_t* __restrict__ kv_idx,
                                                                     const int32_t* __restrict__ kv_cnt, uint32_t nq,
                                                                     uint32_t max_kept, uint32_t nk, uint32_t per_xcd,
-                                                                    uint32_t* __restrict__ order) {
+                                                                    uint32_t xcds_per_head, uint32_t* __restrict__ order) {
     __shared__ uint32_t bins[kMaxMedianBins];
     __shared__ uint32_t wave_total[kUnitWaves];
     const uint32_t h = blockIdx.x, t = threadIdx.x, lane = t & 63u, wave = t >> 6;
@@ -501,9 +506,18 @@ __global__ __launch_bounds__(kUnitThreads) void median_order_kernel(const int32_
         }
     }
     __syncthreads();
+    const uint32_t R = xcds_per_head, G = 8u / R, part = nq / R;
     for (uint32_t i = t; i < nq; i += kUnitThreads) {
-        const uint32_t slot = h * nq + atomicAdd(&bins[key_of(i)], 1u);
-        const uint32_t x = slot / per_xcd, j = slot - x * per_xcd;
+        const uint32_t rank = atomicAdd(&bins[key_of(i)], 1u);
+        uint32_t x, j;
+        if (R == 1u) {
+            const uint32_t slot = h * nq + rank;
+            x = slot / per_xcd;
+            j = slot - x * per_xcd;
+        } else {
+            x = (h % G) * R + rank / part;
+            j = (h / G) * part + rank % part;
+        }
         order[8u * j + x] = (uint32_t)(r0 + i);
     }
 }
@@ -666,9 +680,16 @@ extern "C" int bsa_row_order(const int32_t* kv_cnt, int64_t BH, int64_t nq, uint
     return check_launch(name);
 }
 
-extern "C" int bsa_row_order_by_median(const int32_t* kv_idx, const int32_t* kv_cnt, int64_t BH, int64_t nq,
-                                       int max_kept, int64_t nk, uint32_t* order, int64_t order_len,
-                                       bsa_stream_t stream) {
+// Heads whose K and V together exceed this many bytes are split over two
+// XCDs (bsa_row_order_by_median_ex).  Measured with host-built orders on the
+// same lists at S = 122,880, D = 128 (63 MB per head, 24 heads): 2.0-2.9%
+// faster than whole heads per XCD; 4 or 8 XCDs per head 21-40% slower.  At
+// S = 30,720 (16 MB per head) two XCDs per head were 0.6% slower.
+constexpr int64_t kSplitHeadBytes = 32ll << 20;
+
+extern "C" int bsa_row_order_by_median_ex(const int32_t* kv_idx, const int32_t* kv_cnt, int64_t BH, int64_t nq,
+                                          int max_kept, int64_t nk, int64_t head_kv_bytes, uint32_t* order,
+                                          int64_t order_len, bsa_stream_t stream) {
     clear_error();
     const char* name = "bsa_row_order_by_median";
     BSA_REQUIRE(kv_idx && kv_cnt && order, "%s: NULL argument", name);
@@ -681,7 +702,15 @@ extern "C" int bsa_row_order_by_median(const int32_t* kv_idx, const int32_t* kv_
                 kMaxMedianBins);
     BSA_REQUIRE(order_len >= BH * nq && order_len < ((int64_t)1 << 31), "%s: order_len=%lld must be in [%lld, 2^31)",
                 name, (long long)order_len, (long long)(BH * nq));
+    BSA_REQUIRE(head_kv_bytes >= 0, "%s: head_kv_bytes=%lld must be >= 0", name, (long long)head_kv_bytes);
+    const uint32_t R = (head_kv_bytes > kSplitHeadBytes && BH % 4 == 0 && nq % 2 == 0) ? 2u : 1u;
     median_order_kernel<<<(unsigned)BH, kUnitThreads, 0, (hipStream_t)stream>>>(
-        kv_idx, kv_cnt, (uint32_t)nq, (uint32_t)max_kept, (uint32_t)nk, (uint32_t)(BH * nq / 8), order);
+        kv_idx, kv_cnt, (uint32_t)nq, (uint32_t)max_kept, (uint32_t)nk, (uint32_t)(BH * nq / 8), R, order);
     return check_launch(name);
+}
+
+extern "C" int bsa_row_order_by_median(const int32_t* kv_idx, const int32_t* kv_cnt, int64_t BH, int64_t nq,
+                                       int max_kept, int64_t nk, uint32_t* order, int64_t order_len,
+                                       bsa_stream_t stream) {
+    return bsa_row_order_by_median_ex(kv_idx, kv_cnt, BH, nq, max_kept, nk, 0, order, order_len, stream);
 }

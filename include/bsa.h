@@ -409,6 +409,20 @@ int bsa_row_order_by_median(const int32_t* kv_idx, const int32_t* kv_cnt, int64_
                             int max_kept, int64_t Nk, uint32_t* order, int64_t order_len,
                             bsa_stream_t stream);
 
+/* bsa_row_order_by_median for heads of head_kv_bytes bytes of K and V
+ * (2 * S * D * element size; 0 when unknown, which gives exactly
+ * bsa_row_order_by_median).  Heads above 32 MiB, when 4 divides BH and Nq
+ * is even, are split over two XCDs: XCDs 2g and 2g + 1 run heads g, g + 4,
+ * g + 8, ... in turn, XCD 2g + i taking the i-th half of each head's rows in
+ * the same sorted order, so that half as many heads are in flight at once
+ * (order[8j + x] is the j-th row of XCD x; every slot is filled).  A
+ * scheduling aid like bsa_row_order_by_median: no step of the method, no
+ * change to any result.  INVALID_ARG as bsa_row_order_by_median, or when
+ * head_kv_bytes < 0. */
+int bsa_row_order_by_median_ex(const int32_t* kv_idx, const int32_t* kv_cnt, int64_t BH, int64_t Nq,
+                               int max_kept, int64_t Nk, int64_t head_kv_bytes, uint32_t* order,
+                               int64_t order_len, bsa_stream_t stream);
+
 /* bsa_topk_block_mask with a per-head budget and block count: head (b, h)
  * uses k = k_table[c] and nk = nk_table[c], c = head_choice[b*H + h]
  * (device int32, trusted to lie in [0, n_table)).  Only key blocks J < nk

@@ -225,6 +225,9 @@ def test_device_calls_reject_bad_arguments(L):
         ("bsa_row_order_by_median", (FAKE, FAKE, 1, 8, 4, 4097, FAKE, 8, None), "Nk"),
         ("bsa_row_order_by_median", (FAKE, FAKE, 1, 8, 4, 8, FAKE, 7, None), "order_len"),
         ("bsa_row_order_by_median", (FAKE, FAKE, 1, 8, 0, 8, FAKE, 8, None), "max_kept"),
+        ("bsa_row_order_by_median_ex", (FAKE, FAKE, 1, 8, 4, 8, -1, FAKE, 8, None), "head_kv_bytes"),
+        ("bsa_row_order_by_median_ex", (FAKE, None, 1, 8, 4, 8, 0, FAKE, 8, None), "NULL"),
+        ("bsa_row_order_by_median_ex", (FAKE, FAKE, 3, 5, 4, 5, 1 << 30, FAKE, 15, None), "multiple of 8"),
         ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 0, 2, ctypes.c_float(0.25), 8, None),
          "window"),
         ("bsa_windowed_attention", (FAKE, FAKE, FAKE, FAKE, F, 1, 1, 32, 16, 8, -1, ctypes.c_float(0.25), 8, None),

@@ -242,8 +242,9 @@ def test_top_p_pipeline_plans_its_launch():
     assert torch.equal(out, ref)
 
 
-def check_median_order(order, kv_idx, kv_cnt, nk):
-    """order follows bsa_row_order_by_median's rule for the lists kv_idx (B, H, Nq, max_kept) / kv_cnt (B, H, Nq)."""
+def check_median_order(order, kv_idx, kv_cnt, nk, xcds_per_head=1):
+    """order follows bsa_row_order_by_median's rule for the lists kv_idx (B, H, Nq, max_kept) / kv_cnt (B, H, Nq);
+    xcds_per_head = 2: bsa_row_order_by_median_ex's split of each head over XCDs 2g and 2g + 1."""
     idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
     B, H, nq = cnt.shape
     BH, max_kept = B * H, idx.shape[-1]
@@ -251,9 +252,18 @@ def check_median_order(order, kv_idx, kv_cnt, nk):
     per = n // 8
     o = order.cpu().numpy().astype(np.int64)
     assert o.size >= n
-    seq = np.empty(n, dtype=np.int64)            # slot x*per + j holds order[8j + x]
-    for x in range(8):
-        seq[x * per:(x + 1) * per] = o[:n][x::8]
+    seq = np.empty(n, dtype=np.int64)            # the rows of head h at seq[h*nq : (h+1)*nq], in order
+    if xcds_per_head == 1:                       # slot x*per + j holds order[8j + x]
+        for x in range(8):
+            seq[x * per:(x + 1) * per] = o[:n][x::8]
+    else:                                        # head h = g + 4*hl: XCD 2g's slots of that head, then XCD 2g+1's
+        assert xcds_per_head == 2 and BH % 4 == 0 and nq % 2 == 0
+        part = nq // 2
+        for h in range(BH):
+            g, hl = h % 4, h // 4
+            for i in range(2):
+                x = 2 * g + i
+                seq[h * nq + i * part:h * nq + (i + 1) * part] = o[:n][x::8][hl * part:(hl + 1) * part]
     assert np.array_equal(np.sort(seq), np.arange(n))
     idx2, cnt2 = idx.reshape(BH, nq, max_kept), np.clip(cnt.reshape(BH, nq), 0, max_kept)
 
@@ -294,6 +304,40 @@ def test_median_order_follows_its_rule(B, H, nq, nk, max_kept):
     kv_idx, kv_cnt = (torch.from_numpy(a).to("cuda") for a in (idx, cnt))
     order = bsa.bsa_row_order_by_median(kv_idx, kv_cnt, nk=nk)
     check_median_order(order, kv_idx, kv_cnt, nk)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("BH,nq,head_bytes,split", [(8, 64, 64 << 20, True), (24, 40, (32 << 20) + 1, True),
+                                                    (8, 64, 32 << 20, False), (6, 8, 64 << 20, False),
+                                                    (8, 9, 64 << 20, False), (8, 64, 0, False)])
+def test_median_order_split_over_two_xcds(BH, nq, head_bytes, split):
+    """Heads of more than 32 MiB of K and V go to two XCDs, each taking one half of the head's sorted rows,
+    when 4 divides BH and Nq is even; otherwise (and at 32 MiB or with the size unknown) the plain rule."""
+    torch = torch_gpu()
+    rng = np.random.default_rng(7150 + BH * nq)
+    idx, cnt = _sorted_lists(1, BH, nq, nq, 7, rng)
+    kv_idx, kv_cnt = (torch.from_numpy(a).to("cuda") for a in (idx, cnt))
+    order = bsa.bsa_row_order_by_median(kv_idx, kv_cnt, head_kv_bytes=head_bytes)
+    check_median_order(order, kv_idx, kv_cnt, nq, 2 if split else 1)
+    plain = bsa.bsa_row_order_by_median(kv_idx, kv_cnt)
+    assert torch.equal(order, plain) != split
+
+
+@pytest.mark.gpu
+def test_attention_under_a_split_median_order():
+    """Block-sparse attention under the two-XCD order equals it without one, bit for bit."""
+    torch = torch_gpu()
+    rng = np.random.default_rng(7350)
+    B, H, S, D, block = 1, 8, 1024, 128, 64
+    nb = S // block
+    idx, cnt = _sorted_lists(B, H, nb, nb, 6, rng)
+    kv_idx, kv_cnt = (torch.from_numpy(a).to("cuda") for a in (idx, cnt))
+    q, k, v = (gpu(synth.normal_bits((B, H, S, D), seed=7360 + i)) for i in range(3))
+    order = bsa.bsa_row_order_by_median(kv_idx, kv_cnt, head_kv_bytes=1 << 30)
+    check_median_order(order, kv_idx, kv_cnt, nb, 2)
+    got = bsa.bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block, row_order=order)
+    ref = bsa.bsa_block_sparse_attention(q, k, v, kv_idx, kv_cnt, block)
+    assert torch.equal(got, ref)
 
 
 @pytest.mark.gpu
