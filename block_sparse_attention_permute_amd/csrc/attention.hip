@@ -758,6 +758,13 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
             // this tile's K has landed in LDS (only its V (EV) was issued later) and
             // the previous tile's V reads have completed
             __builtin_amdgcn_s_waitcnt(EV ? kVm16Lgkm0 : 0);
+            // Q's fragments are only ever MFMA B operands in the loop: an empty
+            // asm with an accumulation-register constraint keeps them in AGPRs,
+            // which the MFMAs read directly (no per-tile copies to VGPRs)
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(qf[r][s]));
 
             // S^T of (key half c, row tile r) = K_c Q_r^T: four independent chains
             f32x16 sacc[2][2];
