@@ -141,6 +141,18 @@ __device__ __forceinline__ int v_lds(int row, int chunk) {
     return row * (D * 2) + ((chunk ^ ((row & 3) << 1)) << 4);
 }
 
+// The single-wave kernel's tiles (D = 128: 16 chunks per row) use wider
+// swizzles, measured with the LDS bank-conflict counter: the LDS serves 256
+// bytes (64 banks) per pass, i.e. 16 lanes of a 128-bit read or 32 lanes of a
+// 64-bit read, and the narrower swizzles above repeat within such a pass (a
+// 2-way conflict: 4 extra cycles per K read, 2 per V read):
+//  * K, chunk ^ (row % 16): the 16 consecutive rows of a 128-bit read's pass
+//    land on 16 different 4-bank groups;
+//  * V, chunk ^ 4*(row % 4): the 4 rows times 4 chunks of a transposing read's
+//    32-lane pass land on 16 different 4-bank groups.
+__device__ __forceinline__ int k_lds_solo(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ int v_lds_solo(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 2)) << 4); }
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -529,6 +541,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                                                           const float* __restrict__ knorm) {
     using C = SoloCfg;
     constexpr int D = C::D, BLK = C::BLK;
+    static_assert(D * 2 == 256, "k_lds_solo / v_lds_solo assume 256-byte rows");
     // Q (64 rows) and one V tile live in the wave's LDS (32 KB: four waves per CU)
     __shared__ __attribute__((aligned(16))) char klds[C::TILE];
     __shared__ __attribute__((aligned(16))) char vlds[C::TILE];
@@ -638,7 +651,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         // LDS address of K fragment (key half 0, step s); key half 1 is 32 rows on
         int k_addr[D / 16];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) k_addr[s] = k_lds<D>(col, 2 * s + half_id);
+        for (int s = 0; s < D / 16; ++s) k_addr[s] = k_lds_solo(col, 2 * s + half_id);
         // Row group q (rows 4q..4q+3 of a tile) lies goff[q] bytes from the tile's
         // first row: the same for every lane, so it goes into the DMA's scalar
         // offset and only the lane's place within the group stays in a VGPR.
@@ -649,23 +662,23 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
         for (int q = 0; q < C::TILE / 1024; ++q) goff[q] = TILED ? P.voff[tc][q] : 1024 * q;
         // K tile straight into LDS with the K swizzle: instruction q fills rows
         // 4q..4q+3, lane l physical chunk l % 16 of row 4q + l / 16, which holds
-        // logical chunk (l % 16) ^ (row % 8), row % 8 = 4(q % 2) + l / 16
+        // logical chunk (l % 16) ^ (row % 16), row % 16 = 4(q % 4) + l / 16
         // row lane / 16 of a DMA row group lies rrow bytes after the group's first row
         const int rrow = TILED ? P.rdelta[tc][lane >> 4] : (lane >> 4) * (D * 2);
-        int klane[2];
+        int klane[4];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) klane[p] = rrow + (((lane & 15) ^ (4 * p + (lane >> 4))) << 4);
+        for (int p = 0; p < 4; ++p) klane[p] = rrow + (((lane & 15) ^ (4 * p + (lane >> 4))) << 4);
         auto dma_k = [&](int soff) {
 #pragma unroll
             for (int q = 0; q < C::TILE / 1024; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(klds + 1024 * q), 16,
-                                                         klane[q & 1], soff + goff[q], 0, 0);
+                                                         klane[q & 3], soff + goff[q], 0, 0);
         };
         // V tile straight into LDS (buffer loads with the LDS destination): wave
         // instruction q fills LDS bytes [1024q, 1024q + 1024), i.e. rows 4q..4q+3,
         // lane l landing on physical chunk l % 16 of row 4q + l / 16, which holds
-        // logical chunk (l % 16) ^ 2(row % 4) (the V swizzle); row % 4 = l / 16.
-        const int vlane = rrow + (((lane & 15) ^ (2 * (lane >> 4))) << 4);
+        // logical chunk (l % 16) ^ 4(row % 4) (the V swizzle); row % 4 = l / 16.
+        const int vlane = rrow + (((lane & 15) ^ (4 * (lane >> 4))) << 4);
         auto dma_v = [&](char* buf, int soff, int q_lo, int q_hi) {
 #pragma unroll
             for (int q = q_lo; q < q_hi; ++q)
@@ -721,7 +734,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
             const int colv = 32 * t + v_col0;
-            v_addr[t] = v_lds<D>(v_key0, colv >> 3) + (colv & 7) * 2;
+            v_addr[t] = v_lds_solo(v_key0, colv >> 3) + (colv & 7) * 2;
         }
 
         // label rule: this lane's two row labels, whether the whole query block
