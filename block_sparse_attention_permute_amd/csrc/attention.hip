@@ -779,6 +779,11 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
 #pragma unroll
                 for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(qf[r][s]));
 
+            // PADT: a key tile whose real keys (a prefix) fit in its first 32 rows
+            // skips key half 1: its scores stay 0 and are masked to -inf below,
+            // and the P V groups of keys 32..63 are not run
+            const bool khalf = PADT && __builtin_amdgcn_readfirstlane(kval_cur) <= 32;
+
             // S^T of (key half c, row tile r) = K_c Q_r^T: four independent chains
             f32x16 sacc[2][2];
 #pragma unroll
@@ -809,10 +814,10 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                     if (!EV) dma_v(vlds, soff_cur, 2 * s + 1, 2 * s + 2);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                sacc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[0][s], sacc[1][0], 0, 0, 0);
+                if (!khalf) sacc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[0][s], sacc[1][0], 0, 0, 0);
                 if (s + 2 < D / 16) read_k(s + 2);
                 __builtin_amdgcn_sched_barrier(0);
-                if (NR == 2) {
+                if (NR == 2 && !khalf) {
                     sacc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[1][s], sacc[1][1], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -997,6 +1002,7 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
             constexpr int kPvPerGroup = NR * (D / 32), kDmaPer = (C::TILE / 1024) / kPvPerGroup;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
+                if (m >= 2 && khalf) continue;  // keys 32..63 are all padding
                 if (EV && m == 3) {  // every V^T read of this tile has returned
                     __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
                     __builtin_amdgcn_sched_barrier(0);
@@ -1006,19 +1012,27 @@ __global__ __launch_bounds__(64, 1) void attn_solo_kernel(const AttnParams P, co
                     const int t = NR == 2 ? i / 2 : i, r = NR == 2 ? i % 2 : 0;
                     o[r][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[m % 2][t], pb[r][m], o[r][t], 0, 0, 0);
                     if (m + 1 < 4) {
-                        if (NR == 2) {
-                            p_piece(m + 1, i / 4, i % 4);
-                            v_half(m + 1, t, i % 2);
-                        } else {
-                            p_piece(m + 1, 0, i);
-                            v_half(m + 1, t, 0);
-                            v_half(m + 1, t, 1);
+                        if (m + 1 < 2 || !khalf) {
+                            if (NR == 2) {
+                                p_piece(m + 1, i / 4, i % 4);
+                                v_half(m + 1, t, i % 2);
+                            } else {
+                                p_piece(m + 1, 0, i);
+                                v_half(m + 1, t, 0);
+                                v_half(m + 1, t, 1);
+                            }
                         }
                     } else if (EV) {
                         dma_v(vlds, soff_nxt, kDmaPer * i, kDmaPer * (i + 1));
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
+            }
+            if (EV && khalf) {  // the next tile's V, once this tile's V^T reads (groups 0, 1) have returned
+                __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+                __builtin_amdgcn_sched_barrier(0);
+                dma_v(vlds, soff_nxt, 0, C::TILE / 1024);
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int r = 0; r < NR; ++r) l_part[r] += psum[r][0] + psum[r][1];
