@@ -161,6 +161,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkParams P) {
 #pragma unroll
             for (int i = 0; i < VPL; ++i) c += popc64(__ballot(key[i] >= cand));
             if (c >= k_row) T = cand;
+            // exactly k_row keys at or above T: they are the top k_row, and the
+            // threshold the remaining bits would reach is their smallest key
+            if (c == k_row) {
+                uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) mn = key[i] >= T ? min(mn, key[i]) : mn;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+                T = (uint32_t)__builtin_amdgcn_readfirstlane((int)mn);
+                break;
+            }
         }
     }
     uint32_t need;  // ties at T to take, lowest index first
